@@ -1,0 +1,272 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+Every pin takes ``attn`` -- a callable with the signature of
+``oracle.attention`` -- and raises AssertionError when it fails.  The same
+pins run against the real oracle (all must pass) and against builds of the
+oracle with a planted mistake (each build must fail at least one), so that a
+plausible mistake anywhere in the oracle is shown to be caught.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import golden_io
+from workloads import bf16_bits, bf16_to_f32
+
+
+def _rand(seed, *shape):
+    return np.random.default_rng(np.random.SeedSequence([seed, 7])).standard_normal(shape)
+
+
+def _fixture_case(attn, name):
+    g = golden_io.load(name)
+    q, k, v = (g[x][None, None] for x in ("q", "k", "v"))
+    out, w = attn(q, k, v, g["scale"], g["causal"], weights=True)
+    wexp, wtol = g["weights"]
+    oexp, otol = g["out"]
+    assert np.all(np.abs(w[0, 0] - wexp) <= wtol), f"{name}: weights {w[0, 0]} vs {wexp}"
+    assert np.all(np.abs(out[0, 0] - oexp) <= otol), f"{name}: out {out[0, 0]} vs {oexp}"
+
+
+def pin_p2_causal_example(attn):
+    """"Attention from First Principles", section 4: the hand-worked causal
+    example, and its remark that token 0 gets V[0] unchanged."""
+    _fixture_case(attn, "p2_causal_3tok_d2.txt")
+    g = golden_io.load("p2_causal_3tok_d2.txt")
+    out = attn(g["q"][None, None], g["k"][None, None], g["v"][None, None], g["scale"], 1)
+    assert np.array_equal(out[0, 0, 0], g["v"][0]), "row 0 must equal V[0] exactly"
+
+
+def pin_p3_unmasked_example(attn):
+    """kube-dojo "Attention from scratch", Part 2 worked example (d_v != d_k)."""
+    _fixture_case(attn, "p3_unmasked_3tok_dk4_dv2.txt")
+
+
+def _mixed_cases():
+    # (B, H, Sq, Skv, d, causal, kv_lens)
+    return [
+        (2, 2, 5, 5, 3, 1, None),
+        (2, 1, 6, 6, 4, 1, [6, 3]),
+        (3, 2, 2, 7, 3, 1, [7, 4, 1]),
+        (1, 2, 4, 7, 2, 0, None),
+        (2, 1, 1, 9, 5, 0, [9, 2]),
+        (2, 2, 7, 7, 2, 0, [5, 7]),
+        (1, 1, 1, 1, 1, 1, None),
+    ]
+
+
+def _visible(Sq, Skv, causal, L):
+    """Allowed-mask [Sq, Skv] and pad-row flags under the bottom-right reading."""
+    n = min(Sq, L)
+    allowed = np.zeros((Sq, Skv), dtype=bool)
+    for i in range(n):
+        p = L - n + i
+        for j in range(L):
+            allowed[i, j] = (not causal) or j <= p
+    return allowed, np.arange(Sq) >= n
+
+
+def pin_row_sums_and_forbidden_zero(attn):
+    """Rows of weights sum to one over visible keys, and every forbidden entry
+    (future key, pad key, pad query row) is exactly zero -- the invariants the
+    "Attention from scratch" pages assert (rows sum to one; weights for
+    positions after the first are all zero in row 0; upper triangle zero)."""
+    for ci, (B, H, Sq, Skv, d, causal, lens) in enumerate(_mixed_cases()):
+        q, k, v = _rand(ci, B, H, Sq, d), _rand(ci + 50, B, H, Skv, d), _rand(ci + 90, B, H, Skv, d)
+        out, w = attn(q, k, v, 1 / math.sqrt(d), causal, lens, weights=True)
+        for b in range(B):
+            L = Skv if lens is None else lens[b]
+            allowed, pad = _visible(Sq, Skv, causal, L)
+            for h in range(H):
+                assert np.all(w[b, h][~allowed] == 0.0), f"case {ci}: forbidden weight nonzero"
+                sums = w[b, h].sum(axis=-1)
+                assert np.all(np.abs(sums[~pad] - 1.0) <= 1e-12), f"case {ci}: row sums {sums}"
+                assert np.all(out[b, h][pad] == 0.0), f"case {ci}: pad row output nonzero"
+                assert np.all(w[b, h][pad] == 0.0), f"case {ci}: pad row weights nonzero"
+
+
+def pin_future_invariance(attn):
+    """Under the causal mask, changing keys/values at positions >= t leaves
+    every query row at a position < t bitwise unchanged."""
+    B, H, S, d = 1, 2, 8, 4
+    q, k, v = _rand(1, B, H, S, d), _rand(2, B, H, S, d), _rand(3, B, H, S, d)
+    base = attn(q, k, v, 0.5, 1)
+    for t in range(1, S):
+        k2, v2 = k.copy(), v.copy()
+        k2[:, :, t:] = _rand(10 + t, B, H, S - t, d) * 3.0
+        v2[:, :, t:] = _rand(40 + t, B, H, S - t, d) * 3.0
+        out = attn(q, k2, v2, 0.5, 1)
+        assert np.array_equal(out[:, :, :t], base[:, :, :t]), f"rows < {t} changed"
+        assert not np.array_equal(out[:, :, t:], base[:, :, t:]), "later rows must see the change"
+
+
+def pin_zero_query_uniform(attn):
+    """With Q = 0 every visible key gets the same weight, so each output row is
+    the plain mean of its visible value rows (the all-zero exercise on the
+    "Attention from scratch" page); np.mean is the independent reference."""
+    B, H, S, d = 2, 1, 6, 3
+    q = np.zeros((B, H, S, d))
+    k, v = _rand(4, B, H, S, d), _rand(5, B, H, S, d)
+    lens = [6, 4]
+    out = attn(q, k, v, 0.7, 1, lens)
+    for b in range(B):
+        L = lens[b]
+        for i in range(S):
+            if i >= L:
+                assert np.all(out[b, 0, i] == 0.0)
+                continue
+            ref = v[b, 0, : i + 1].mean(axis=0)
+            assert np.allclose(out[b, 0, i], ref, rtol=0, atol=1e-12), (b, i)
+    # decode: one query at the last valid position sees keys 0..L-1
+    out = attn(q[:, :, :1], k, v, 0.7, 0, lens)
+    for b in range(B):
+        ref = v[b, 0, : lens[b]].mean(axis=0)
+        assert np.allclose(out[b, 0, 0], ref, rtol=0, atol=1e-12)
+
+
+def pin_convex_mixture(attn):
+    """Each output is a convex mixture of the visible value rows, so every
+    component lies between their minimum and maximum."""
+    B, H, S, d = 1, 3, 9, 4
+    q, k, v = _rand(6, B, H, S, d) * 3, _rand(7, B, H, S, d) * 3, _rand(8, B, H, S, d)
+    out = attn(q, k, v, 0.5, 1)
+    for h in range(H):
+        for i in range(S):
+            lo, hi = v[0, h, : i + 1].min(axis=0), v[0, h, : i + 1].max(axis=0)
+            assert np.all(out[0, h, i] >= lo - 1e-12) and np.all(out[0, h, i] <= hi + 1e-12)
+
+
+def pin_shift_invariance_large_logits(attn):
+    """softmax is unchanged when one constant is added to every logit of a row.
+    An extra feature with q_e = c and k_e = 1 adds scale*c to every logit; at
+    c = 2e3 an implementation that does not subtract the row maximum
+    overflows."""
+    B, H, S, d = 1, 1, 6, 3
+    q, k, v = _rand(9, B, H, S, d), _rand(10, B, H, S, d), _rand(11, B, H, S, d)
+    base = attn(q, k, v, 0.5, 1)
+    q2 = np.concatenate([q, np.full((B, H, S, 1), 2000.0)], axis=-1)
+    k2 = np.concatenate([k, np.ones((B, H, S, 1))], axis=-1)
+    out = attn(q2, k2, v, 0.5, 1)
+    assert np.all(np.isfinite(out)), "large logits overflowed"
+    assert np.allclose(out, base, rtol=0, atol=1e-9)
+
+
+def pin_two_key_logistic(attn):
+    """Two keys, no mask, d = 1: the weight of key 1 is the logistic function
+    of the logit difference, sigma(scale*q*(k1 - k0)) (textbook identity)."""
+    from scipy.special import expit
+    rng = np.random.default_rng(12)
+    for _ in range(20):
+        q = rng.standard_normal((1, 1, 1, 1))
+        k = rng.standard_normal((1, 1, 2, 1))
+        v = np.array([[[[0.0], [1.0]]]])
+        scale = float(rng.uniform(0.1, 2.0))
+        out = attn(q, k, v, scale, 0)
+        ref = expit(scale * q[0, 0, 0, 0] * (k[0, 0, 1, 0] - k[0, 0, 0, 0]))
+        assert abs(out[0, 0, 0, 0] - ref) <= 1e-14, (out, ref)
+
+
+def pin_matches_torch_sdpa(attn):
+    """Agreement with an independent library routine: torch's CPU
+    scaled_dot_product_attention in float64 (the comparison the kube-dojo
+    page's test script makes), with the boolean allowed-mask built from the
+    causal and padding rules."""
+    import torch
+    import torch.nn.functional as F
+    for ci, (B, H, Sq, Skv, d, causal, lens) in enumerate(_mixed_cases()):
+        q, k, v = _rand(ci, B, H, Sq, d), _rand(ci + 50, B, H, Skv, d), _rand(ci + 90, B, H, Skv, d)
+        out = attn(q, k, v, 1 / math.sqrt(d), causal, lens)
+        for b in range(B):
+            L = Skv if lens is None else lens[b]
+            allowed, pad = _visible(Sq, Skv, causal, L)
+            rows = np.nonzero(~pad)[0]
+            if len(rows) == 0:
+                continue
+            tq = torch.from_numpy(q[b][:, rows])
+            ref = F.scaled_dot_product_attention(
+                tq, torch.from_numpy(k[b]), torch.from_numpy(v[b]),
+                attn_mask=torch.from_numpy(allowed[rows]), scale=1 / math.sqrt(d)).numpy()
+            assert np.allclose(out[b][:, rows], ref, rtol=0, atol=1e-12), f"case {ci} b {b}"
+
+
+def pin_decode_is_last_prefill_row(attn):
+    """A single decode query against the cache equals the last row of causal
+    prefill over the same keys (cached and uncached generation agree)."""
+    B, H, S, d = 2, 2, 7, 3
+    q, k, v = _rand(13, B, H, S, d), _rand(14, B, H, S, d), _rand(15, B, H, S, d)
+    lens = [7, 5]
+    full = attn(q, k, v, 0.6, 1, lens)
+    for b in range(B):
+        L = lens[b]
+        qd = q[b:b + 1, :, L - 1:L]
+        dec = attn(qd, k[b:b + 1], v[b:b + 1], 0.6, 0, [L])
+        assert np.allclose(dec[0, :, 0], full[b, :, L - 1], rtol=0, atol=1e-13)
+        dec1 = attn(qd, k[b:b + 1], v[b:b + 1], 0.6, 1, [L])
+        assert np.array_equal(dec1, dec), "causal flag must not matter for one query"
+
+
+def pin_key_permutation_equivariance(attn):
+    """Without a mask, permuting keys together with their values leaves the
+    output unchanged; permuting heads permutes outputs."""
+    B, H, S, d = 1, 3, 6, 4
+    q, k, v = _rand(16, B, H, 4, d), _rand(17, B, H, S, d), _rand(18, B, H, S, d)
+    base = attn(q, k, v, 0.5, 0)
+    perm = np.random.default_rng(3).permutation(S)
+    out = attn(q, k[:, :, perm], v[:, :, perm], 0.5, 0)
+    assert np.allclose(out, base, rtol=0, atol=1e-13)
+    hp = [2, 0, 1]
+    out = attn(q[:, hp], k[:, hp], v[:, hp], 0.5, 0)
+    assert np.array_equal(out, base[:, hp])
+
+
+def pin_low_precision_inputs_widen_exactly(attn):
+    """bfloat16 bit patterns and float32 inputs are read as their exact values:
+    results equal those of the same numbers passed as float64."""
+    B, H, S, d = 1, 2, 5, 4
+    x = [_rand(20 + i, B, H, S, d).astype(np.float32) for i in range(3)]
+    ref32 = attn(*(a.astype(np.float64) for a in x), 0.5, 1)
+    assert np.array_equal(attn(*x, 0.5, 1), ref32)
+    bits = [bf16_bits(a) for a in x]
+    ref16 = attn(*(bf16_to_f32(b).astype(np.float64) for b in bits), 0.5, 1)
+    assert np.array_equal(attn(*bits, 0.5, 1), ref16)
+
+
+def pin_length_clamp(attn):
+    """Valid lengths are clamped to [0, Skv]: a length above capacity equals
+    capacity, and a non-positive length gives an all-zero sequence."""
+    B, H, S, d = 3, 1, 4, 2
+    q, k, v = _rand(30, B, H, S, d), _rand(31, B, H, S, d), _rand(32, B, H, S, d)
+    a = attn(q, k, v, 0.5, 1, [S + 5, 0, -3])
+    b = attn(q, k, v, 0.5, 1, [S, 0, 0])
+    assert np.array_equal(a, b)
+    assert np.all(a[1:] == 0.0)
+
+
+ALL_PINS = [
+    pin_p2_causal_example,
+    pin_p3_unmasked_example,
+    pin_row_sums_and_forbidden_zero,
+    pin_future_invariance,
+    pin_zero_query_uniform,
+    pin_convex_mixture,
+    pin_shift_invariance_large_logits,
+    pin_two_key_logistic,
+    pin_matches_torch_sdpa,
+    pin_decode_is_last_prefill_row,
+    pin_key_permutation_equivariance,
+    pin_low_precision_inputs_widen_exactly,
+    pin_length_clamp,
+]
+
+
+def failing_pins(attn) -> list:
+    """Names of the pins that fail (or raise) for ``attn``."""
+    bad = []
+    for pin in ALL_PINS:
+        try:
+            pin(attn)
+        except Exception as exc:  # a crash counts as a failed pin
+            bad.append((pin.__name__, f"{type(exc).__name__}: {str(exc)[:120]}"))
+    return bad

@@ -1,0 +1,167 @@
+"""Seeded synthetic inputs shaped like the pages' attention workloads.
+
+This module holds no attention arithmetic.  It draws Q, K, V and per-sequence
+valid lengths from fixed seeds and stores them as float32 or as bfloat16 bit
+patterns (uint16, round-to-nearest-even from the float32 draw).  Both the GPU
+tests and the CPU oracle consume exactly these bits.
+
+Recipe (every draw uses numpy's PCG64 through ``default_rng``):
+  * valid lengths: ``default_rng(SeedSequence([seed, 0]))``, then
+    ``integers(lo, hi + 1, size=B)``, i.e. uniform on [lo, hi] inclusive;
+  * each (tensor t, batch b, head h) slice has its own stream
+    ``default_rng(SeedSequence([seed, t, b, h]))`` with t = 1, 2, 3 for
+    q, k, v; it draws ``standard_normal((rows, d), float32)`` for the slice's
+    valid rows only -- the first n_b query rows and the first L_b key/value
+    rows, where n_b = min(Sq, L_b) -- so any slice can be regenerated on its
+    own and the padded tail is never drawn;
+  * padded rows hold ``pad_fill`` (0.0 by default; NaN for poison tests).
+Values are i.i.d. N(0, 1), as the pages' torch.randn examples are.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Iterable, Optional, Sequence
+
+import numpy as np
+
+TENSOR_IDS = {"q": 1, "k": 2, "v": 3}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One attention forward problem.  Sizes follow [B, H, S, d] layout."""
+    name: str
+    B: int
+    H: int
+    Sq: int
+    Skv: int
+    d: int
+    dtype: str              # "f32" or "bf16"
+    causal: bool
+    seed: int
+    kv_len_range: Optional[tuple] = None   # (lo, hi) inclusive, or None
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        """1/sqrt(d) rounded to float32, returned as that float32's value."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+
+# The pages' shapes: d_model 4096 = 32 heads of 128 ("Attention from First
+# Principles", section 5; "Scaled dot-product attention with masking",
+# "Multi-head attention"), d_k = 64 (kube-dojo module, the scale-factor
+# discussion), prefill S = 2048 against decode over a KV cache ("Attention from
+# First Principles", section 6), and small seeded randn fixtures.
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("tiny_f32", 1, 1, 64, 64, 16, "f32", True, 1,
+                 description="causal single head, S=64, d=16, fp32"),
+        Workload("mha768_bf16", 4, 12, 512, 512, 64, "bf16", True, 2,
+                 description="causal MHA, d_model=768 (12x64), S=512"),
+        Workload("prefill4096_bf16", 1, 32, 4096, 4096, 128, "bf16", True, 3,
+                 description="causal MHA prefill, d_model=4096 (32x128), S=4096"),
+        Workload("padded2048_bf16", 8, 32, 2048, 2048, 128, "bf16", True, 4, (256, 2048),
+                 description="causal + right padding, S=2048, lengths U[256,2048]"),
+        Workload("decode8192_bf16", 64, 32, 1, 8192, 128, "bf16", False, 5, (512, 8192),
+                 description="decode, one query against a KV cache of capacity 8192, "
+                             "lengths U[512,8192]"),
+    ]
+}
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    nan = np.isnan(x)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    if nan.any():
+        r[nan] = 0x7FC0
+    return r
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def kv_lens_for(w: Workload) -> Optional[np.ndarray]:
+    if w.kv_len_range is None:
+        return None
+    lo, hi = w.kv_len_range
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, 0]))
+    return rng.integers(lo, hi + 1, size=w.B).astype(np.int32)
+
+
+def _slice(seed: int, tensor: str, b: int, h: int, rows: int, d: int) -> np.ndarray:
+    rng = np.random.default_rng(np.random.SeedSequence([seed, TENSOR_IDS[tensor], b, h]))
+    return rng.standard_normal((rows, d), dtype=np.float32)
+
+
+def _valid_rows(w: Workload, lens: Optional[np.ndarray], b: int, tensor: str) -> int:
+    L = w.Skv if lens is None else int(min(max(int(lens[b]), 0), w.Skv))
+    if tensor == "q":
+        return min(w.Sq, L)
+    return L
+
+
+def make_tensor(w: Workload, tensor: str, lens: Optional[np.ndarray] = None,
+                pairs: Optional[Iterable[tuple]] = None, pad_fill: float = 0.0) -> np.ndarray:
+    """Draw one of q/k/v.  Returns float32 [B,H,S,d] for "f32" workloads and
+    uint16 bf16 bits for "bf16".  With ``pairs`` (an iterable of (b, h)), only
+    those slices are drawn and the result is [len(pairs), 1, S, d]."""
+    S = w.Sq if tensor == "q" else w.Skv
+    out_dtype = np.float32 if w.dtype == "f32" else np.uint16
+    if pairs is None:
+        sel = [(b, h) for b in range(w.B) for h in range(w.H)]
+        shape = (w.B, w.H, S, w.d)
+    else:
+        sel = list(pairs)
+        shape = (len(sel), 1, S, w.d)
+    if w.dtype == "f32":
+        fill = np.float32(pad_fill)
+    else:
+        fill = bf16_bits(np.array([pad_fill], dtype=np.float32))[0]
+    out = np.empty(shape, dtype=out_dtype)
+    flat = out.reshape(-1, S, w.d)
+    for idx, (b, h) in enumerate(sel):
+        rows = _valid_rows(w, lens, b, tensor)
+        x = _slice(w.seed, tensor, b, h, rows, w.d)
+        flat[idx, :rows] = x if w.dtype == "f32" else bf16_bits(x)
+        flat[idx, rows:] = fill
+    return out
+
+
+def make_inputs(w: Workload, pairs: Optional[Sequence[tuple]] = None,
+                pad_fill: float = 0.0) -> dict:
+    """All inputs of a workload: q, k, v (see ``make_tensor``), kv_lens (int32
+    [B] or None; restricted to the chosen pairs' batch items when ``pairs`` is
+    given) and scale."""
+    lens = kv_lens_for(w)
+    q = make_tensor(w, "q", lens, pairs, pad_fill)
+    k = make_tensor(w, "k", lens, pairs, pad_fill)
+    v = make_tensor(w, "v", lens, pairs, pad_fill)
+    sub_lens = lens
+    if pairs is not None and lens is not None:
+        sub_lens = np.array([lens[b] for b, _ in pairs], dtype=np.int32)
+    return {"q": q, "k": k, "v": v, "kv_lens": sub_lens, "scale": w.scale, "workload": w}
+
+
+def random_problem(seed: int, B: int, H: int, Sq: int, Skv: int, d: int, dtype: str = "f32",
+                   kv_lens: Optional[Sequence[int]] = None, dv: Optional[int] = None) -> dict:
+    """A small ad-hoc problem with every row drawn (pad rows included): used by
+    tests that sweep many shapes.  dtype "f64", "f32" or "bf16" (uint16 bits)."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 99]))
+    dv = d if dv is None else dv
+    q = rng.standard_normal((B, H, Sq, d), dtype=np.float32)
+    k = rng.standard_normal((B, H, Skv, d), dtype=np.float32)
+    v = rng.standard_normal((B, H, Skv, dv), dtype=np.float32)
+    if dtype == "bf16":
+        q, k, v = bf16_bits(q), bf16_bits(k), bf16_bits(v)
+    elif dtype == "f64":
+        q, k, v = (x.astype(np.float64) for x in (q, k, v))
+    lens = None if kv_lens is None else np.asarray(kv_lens, dtype=np.int32)
+    return {"q": q, "k": k, "v": v, "kv_lens": lens,
+            "scale": float(np.float32(1.0 / math.sqrt(d)))}
