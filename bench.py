@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Attention forward throughput on one MI355X.
+
+One step is one pass of the whole path: a causal prefill over
+B=1, H=32, S=4096, d=128 (d_model 4096) and a split-KV decode over
+B=64, H=32, one query against KV caches of capacity 8192 with valid lengths
+drawn uniformly from [512, 8192], all bf16 with fp32 accumulation, inputs
+resident in HBM before timing starts.
+
+Printed (one JSON line): prefill TFLOP/s as `value` (algorithmic flops: 4*d
+per visible (query, key) pair), decode KV-read GB/s under `decode` (bytes of
+the valid K and V rows plus q, out and the lengths), each with a roofline
+entry for its dominant kernel computed from that kernel's own HIP-event
+durations, and the float64 CPU oracle timed on a bounded sample of the same
+workload as `cpu_baseline`.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+
+PREFILL = "prefill4096_bf16"
+DECODE = "decode8192_bf16"
+
+
+def prefill_flops(w, lens=None) -> float:
+    """4*d flops per visible (query, key) pair; padded rows and masked pairs
+    are not counted."""
+    total = 0
+    for b in range(w.B):
+        L = w.Skv if lens is None else int(min(max(int(lens[b]), 0), w.Skv))
+        n = min(w.Sq, L)
+        off = L - n
+        if w.causal:
+            # query i (absolute position off+i) sees off+i+1 keys
+            pairs = n * (off + 1) + n * (n - 1) // 2
+        else:
+            pairs = n * L
+        total += pairs
+    return 4.0 * w.d * w.H * total
+
+
+def decode_bytes(w, lens) -> float:
+    """Bytes the decode must move: valid K and V rows, q, out, kv_lens."""
+    kv = 2 * 2 * w.d * w.H * int(sum(int(min(max(int(x), 0), w.Skv)) for x in lens))
+    qo = 2 * (2 * w.B * w.H * w.d)
+    return float(kv + qo + 4 * w.B)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--parts", default="prefill,decode",
+                    help="comma list of prefill, decode (default both)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="oracle threads for the CPU baseline (default min(16, cores))")
+    return ap.parse_args()
+
+
+def cpu_baseline(threads: int):
+    """Time the oracle on a bounded sample of the prefill workload: the first
+    `threads` heads of B=1, S=4096, d=128 causal (one thread per head)."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    w = W.WORKLOADS[PREFILL]
+    heads = max(1, min(threads, w.H))
+    pairs = [(0, h) for h in range(heads)]
+    x = W.make_inputs(w, pairs=pairs)
+    t0 = time.perf_counter()
+    oracle.attention(x["q"], x["k"], x["v"], x["scale"], w.causal, None, nthreads=threads)
+    dt = time.perf_counter() - t0
+    flops = prefill_flops(w) * heads / w.H
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(threads, heads),
+            "kind": "oracle",
+            "sample": f"{heads} of {w.H} heads of {PREFILL} (B=1, S=4096, d=128, causal), "
+                      f"float64, {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build runs attention on a single MI355X "
+              "and has no multi-GPU path (pass --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    parts = [p.strip() for p in args.parts.split(",") if p.strip()]
+
+    import numpy as np
+    import torch
+    import transformer_scaled_dot_attn_amd as attn
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    runs = []
+    if "prefill" in parts:
+        w = W.WORKLOADS[PREFILL]
+        print(f"[bench] preparing {w.name}", file=sys.stderr, flush=True)
+        x = W.device_inputs(w, dev)
+        out = torch.empty_like(x["q"])
+        runs.append(("prefill", w, x, out))
+    if "decode" in parts:
+        w = W.WORKLOADS[DECODE]
+        print(f"[bench] preparing {w.name}", file=sys.stderr, flush=True)
+        x = W.device_inputs(w, dev)
+        out = torch.empty_like(x["q"])
+        runs.append(("decode", w, x, out))
+
+    def step():
+        for _, w, x, out in runs:
+            attn.fwd(x["q"], x["k"], x["v"], out, causal=w.causal, kv_lens=x["kv_lens"],
+                     scale=x["scale"])
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    attn.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = attn.profile_read()
+    attn.profile_enable(False)
+    ms_per_step = wall * 1e3 / args.steps
+
+    def avg_ms(name):
+        n, ms = prof[name]
+        return ms / n if n else float("nan")
+
+    result = {
+        "metric": "attn fwd TFLOP/s (causal prefill) + KV-read GB/s (decode), 1×MI355X",
+        "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": " + ".join(w.name for _, w, _, _ in runs)},
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    for kind, w, x, out in runs:
+        cfg = {"B": w.B, "H": w.H, "Sq": w.Sq, "Skv": w.Skv, "d": w.d, "causal": w.causal}
+        if kind == "prefill":
+            flops = prefill_flops(w, x["kv_lens_host"])
+            kms = avg_ms("prefill_bf16_mfma")
+            tflops = flops / (kms * 1e-3) / 1e12
+            result["value"] = tflops
+            result["config"]["prefill"] = cfg
+            result["roofline"] = {
+                "kernel": "prefill_bf16_mfma", "bound": "mfma", "achieved": tflops,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+                "traffic": None, "algorithmic_flop_per_launch": flops, "avg_launch_ms": kms}
+        else:
+            lens = x["kv_lens_host"]
+            nbytes = decode_bytes(w, lens)
+            p_ms = avg_ms("decode_bf16_partial")
+            c_ms = avg_ms("decode_bf16_combine")
+            kv_bytes = nbytes - 2 * 2 * w.B * w.H * w.d  # what the partial kernel reads
+            gbs_op = nbytes / ((p_ms + c_ms) * 1e-3) / 1e9
+            gbs_k = kv_bytes / (p_ms * 1e-3) / 1e9
+            cfg["kv_len_range"] = list(w.kv_len_range)
+            cfg["sum_kv_len"] = int(np.sum(lens))
+            result["config"]["decode"] = cfg
+            result["decode"] = {
+                "metric": "KV-read GB/s (decode)", "value": gbs_op, "unit": "GB/s",
+                "ms_per_call": p_ms + c_ms,
+                "roofline": {
+                    "kernel": "decode_bf16_partial", "bound": "hbm", "achieved": gbs_k,
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs_k / PEAK_HBM_GBS,
+                    "traffic": None, "algorithmic_bytes_per_launch": kv_bytes,
+                    "avg_launch_ms": p_ms},
+                "combine_avg_launch_ms": c_ms,
+            }
+    if result["value"] is None and "decode" in result:
+        result["value"] = result["decode"]["value"]
+        result["unit"] = "GB/s"
+        result["roofline"] = result["decode"]["roofline"]
+
+    if not args.no_cpu_baseline and "prefill" in parts:
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        print(f"[bench] cpu baseline with {threads} threads", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(threads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

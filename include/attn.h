@@ -1,0 +1,159 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) scaled dot-product attention forward.
+ *
+ * The operation is the forward pass of multi-head scaled dot-product
+ * attention with the mask added to the logits before the softmax:
+ *
+ *     out = softmax(scale * Q K^T + M) V
+ *
+ * as stated on "Self-Attention" (blog-15c notes), sections "Scaled
+ * Dot-Product Attention" and "Causal Masking", and worked by hand on
+ * "Attention from First Principles", section 4.  Heads are independent
+ * attention computations laid out as a batch-like axis ("Attention from
+ * First Principles", section 5, "Why multiple heads").
+ *
+ * Mask M (the readings taken where the pages leave the rule open):
+ *   - kv_lens[b] = L_b is the valid length of sequence b (right padding,
+ *     as in the kube-dojo page's padding-mask example); keys j >= L_b are
+ *     invisible to every query.  Values outside [0, Skv] are clamped to it.
+ *     kv_lens == NULL means L_b = Skv for every b.
+ *   - The queries of sequence b are its last n_b = min(Sq, L_b) valid
+ *     positions: query row i is at absolute position p = L_b - n_b + i
+ *     (bottom-right alignment; with Sq == 1 the query is the newest token
+ *     and sees the whole cache, as "Scaled dot-product attention with
+ *     masking" says of decode).  Rows i >= n_b are padding.
+ *   - causal != 0 additionally hides keys j > p (M = -inf there, 0 else).
+ *   - A padded query row, or a row with no visible key, is written as 0.
+ *
+ * Layout: q and out are [B][H][Sq][d], k and v are [B][H][Skv][d], all
+ * row-major, densely packed, of the one element type `dtype`; out has the
+ * inputs' type.  At decode Skv is the cache capacity and L_b <= Skv the
+ * filled part.  All five base pointers must be 16-byte aligned.
+ *
+ * Pointers: q, k, v, out, kv_lens and workspace are DEVICE pointers on the
+ * current HIP device.  stream is a hipStream_t (NULL = the null stream).
+ * Every compute call only enqueues work on `stream` and returns; results are
+ * ready when that stream's work has completed.  The caller owns every buffer
+ * and keeps it alive until then.  q, k, v and kv_lens are only read; out is
+ * only written; the padded tails of k and v (rows >= L_b) are never read, so
+ * they may hold anything.
+ *
+ * Errors: every function returns an attn_status and never throws.  All
+ * argument checks run on the host before any HIP call; a failed check
+ * enqueues nothing and leaves out untouched.  ATTN_E_LAUNCH reports a HIP
+ * launch failure, after which out is undefined.
+ */
+#ifndef TSDA_ATTN_H
+#define TSDA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_E_NULL = 1,        /* q, k, v or out is NULL (or workspace, where required) */
+    ATTN_E_SHAPE = 2,       /* B, H, Sq, Skv or d <= 0, Sq > Skv, or sizes overflow */
+    ATTN_E_UNSUPPORTED = 3, /* valid request outside the kernels' support matrix */
+    ATTN_E_DTYPE = 4,       /* dtype is not an attn_dtype value */
+    ATTN_E_ALIGN = 5,       /* a base pointer is not 16-byte aligned */
+    ATTN_E_WORKSPACE = 6,   /* caller workspace smaller than attn_workspace_bytes() */
+    ATTN_E_ARG = 7,         /* scale is not finite */
+    ATTN_E_LAUNCH = 8,      /* a HIP call or kernel launch failed */
+    ATTN_E_NOMEM = 9        /* the library could not allocate its workspace */
+} attn_status;
+
+typedef enum {
+    ATTN_F32 = 0,  /* IEEE binary32 in and out */
+    ATTN_BF16 = 1  /* bfloat16 in and out; fp32 accumulation and softmax */
+} attn_dtype;
+
+/*
+ * Support matrix (anything else valid returns ATTN_E_UNSUPPORTED -- there is
+ * no silent slow fallback, the hazard "Attention from First Principles"
+ * section 8 warns of):
+ *   ATTN_F32 : any Sq <= Skv, 1 <= d <= 128          (VALU kernel)
+ *   ATTN_BF16: Sq == 1, d in {64, 128}                (split-KV decode)
+ *              Sq >= 2, d in {64, 128}                (MFMA prefill)
+ */
+
+/*
+ * attn_fwd -- out = softmax(scale * Q K^T + M) V, arguments as above.
+ * scale: the logit multiplier, normally 1/sqrt(d) ("Self-Attention",
+ * section "Why divide by sqrt(d_k)?").  causal: 0 or nonzero.
+ * Temporary memory comes from a library-owned workspace on the current
+ * device, grown on demand (the call that grows it synchronizes the device
+ * first).  Calls that use the library workspace must not run concurrently
+ * on different streams of one device; use attn_fwd_ws for that.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq,
+             int Skv, int d, float scale, int causal, const int32_t* kv_lens, int dtype,
+             void* stream);
+
+/*
+ * attn_workspace_bytes -- device bytes attn_fwd_ws needs for this problem
+ * (0 when the chosen kernel needs none).  Returns 0 for invalid arguments.
+ */
+size_t attn_workspace_bytes(int B, int H, int Sq, int Skv, int d, int dtype);
+
+/*
+ * attn_fwd_ws -- attn_fwd with caller-owned temporary memory.  workspace is
+ * a device buffer of at least attn_workspace_bytes(...) bytes, 256-byte
+ * aligned, not used by any other call until this one's stream work ends.
+ * Its contents need no initialisation and are garbage afterwards.  workspace
+ * may be NULL only when attn_workspace_bytes(...) is 0.
+ */
+int attn_fwd_ws(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq,
+                int Skv, int d, float scale, int causal, const int32_t* kv_lens, int dtype,
+                void* stream, void* workspace, size_t workspace_bytes);
+
+/*
+ * attn_validate -- the host-side checks of attn_fwd alone: returns what
+ * attn_fwd would return before enqueueing anything.  Makes no HIP call.
+ */
+int attn_validate(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq,
+                  int Skv, int d, float scale, int causal, int dtype);
+
+/*
+ * attn_kernel_for -- name of the kernel family attn_fwd would launch for
+ * these sizes ("prefill_bf16_mfma", "decode_bf16_splitkv", "generic_f32"),
+ * or NULL when the request is invalid or unsupported.  Makes no HIP call.
+ * The string is static.
+ */
+const char* attn_kernel_for(int Sq, int Skv, int d, int dtype);
+
+/* Human-readable text for an attn_status value (static string). */
+const char* attn_status_string(int status);
+
+/* ATTN_ABI_VERSION of the loaded library. */
+int attn_abi_version(void);
+
+/*
+ * attn_release -- frees the library-owned workspace of every device.  The
+ * caller must ensure no enqueued attn_fwd call is still running.
+ */
+void attn_release(void);
+
+/*
+ * Kernel timing, for benchmarks.  While enabled, every kernel the library
+ * launches is bracketed by HIP events recorded on the launch stream.
+ * attn_profile_read synchronizes on those events and returns, for kernel
+ * family `kernel` (the index into the list attn_profile_name enumerates),
+ * the number of launches and their summed duration in milliseconds since the
+ * last reset.  Enabling or resetting discards earlier records.
+ */
+int attn_profile_enable(int on);
+int attn_profile_reset(void);
+int attn_profile_read(int kernel, long* launches, double* total_ms);
+const char* attn_profile_name(int kernel); /* NULL past the last kernel */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSDA_ATTN_H */

@@ -1,0 +1,113 @@
+"""The C-ABI library on the host: it loads, exports every declared entry
+point, and its argument checks and kernel choice behave as documented.
+No compute call is made (none of these reach a HIP API)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import transformer_scaled_dot_attn_amd as attn
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "attn.h")
+
+A = 0x10000          # fake, 16-byte aligned device addresses (never dereferenced)
+F32, BF16 = attn.F32, attn.BF16
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    assert "attn_fwd" in names and "attn_fwd_ws" in names and len(names) >= 10, names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(attn.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_abi_version_and_status_strings():
+    assert attn.abi_version() == attn.ABI_VERSION
+    for s in range(10):
+        assert attn.status_string(s) and attn.status_string(s) != "unknown status"
+    assert attn.status_string(99) == "unknown status"
+
+
+def v(B=1, H=1, Sq=4, Skv=4, d=64, scale=0.125, causal=1, dtype=BF16, q=A, k=A, vv=A, out=A):
+    return attn.validate(q, k, vv, out, B, H, Sq, Skv, d, scale, causal, dtype)
+
+
+def test_validate_accepts_supported_requests():
+    assert v() == attn.OK
+    assert v(d=128) == attn.OK
+    assert v(Sq=1, Skv=8192, d=128) == attn.OK
+    assert v(dtype=F32, d=16) == attn.OK
+    assert v(dtype=F32, d=1, Sq=1, Skv=1) == attn.OK
+    assert v(dtype=F32, d=128, Sq=3, Skv=7) == attn.OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), attn.E_NULL), (dict(k=0), attn.E_NULL), (dict(vv=0), attn.E_NULL),
+    (dict(out=0), attn.E_NULL),
+    (dict(dtype=2), attn.E_DTYPE), (dict(dtype=-1), attn.E_DTYPE),
+    (dict(B=0), attn.E_SHAPE), (dict(H=-1), attn.E_SHAPE), (dict(Sq=0), attn.E_SHAPE),
+    (dict(Skv=0), attn.E_SHAPE), (dict(d=0), attn.E_SHAPE), (dict(Sq=5, Skv=4), attn.E_SHAPE),
+    (dict(B=1 << 20, H=1 << 10, Sq=1, Skv=1 << 16, d=128), attn.E_SHAPE),
+    (dict(scale=float("inf")), attn.E_ARG), (dict(scale=float("nan")), attn.E_ARG),
+    (dict(q=A + 8), attn.E_ALIGN), (dict(out=A + 2), attn.E_ALIGN),
+    (dict(d=32), attn.E_UNSUPPORTED), (dict(d=96), attn.E_UNSUPPORTED),
+    (dict(d=256), attn.E_UNSUPPORTED), (dict(dtype=F32, d=129), attn.E_UNSUPPORTED),
+])
+def test_validate_rejects(kw, code):
+    assert v(**kw) == code
+
+
+def test_check_order_null_before_shape():
+    assert v(q=0, B=0) == attn.E_NULL
+    assert v(B=0, scale=float("nan")) == attn.E_SHAPE
+
+
+def test_kernel_choice():
+    assert attn.kernel_for(4096, 4096, 128, BF16) == "prefill_bf16_mfma"
+    assert attn.kernel_for(512, 512, 64, BF16) == "prefill_bf16_mfma"
+    assert attn.kernel_for(2, 9, 64, BF16) == "prefill_bf16_mfma"
+    assert attn.kernel_for(1, 8192, 128, BF16) == "decode_bf16_splitkv"
+    assert attn.kernel_for(64, 64, 16, F32) == "generic_f32"
+    assert attn.kernel_for(1, 64, 16, F32) == "generic_f32"
+    assert attn.kernel_for(4, 4, 48, BF16) is None
+    assert attn.kernel_for(5, 4, 64, BF16) is None
+
+
+def test_workspace_sizes():
+    # decode needs (m, l, acc[d]) partials; the other kernels need none
+    assert attn.workspace_bytes(1, 32, 4096, 4096, 128, BF16) == 0
+    assert attn.workspace_bytes(1, 1, 64, 64, 16, F32) == 0
+    w = attn.workspace_bytes(64, 32, 1, 8192, 128, BF16)
+    assert w >= 64 * 32 * (8192 // 512) * (128 + 2) * 4
+    assert w % 256 == 0
+    assert attn.workspace_bytes(0, 32, 1, 8192, 128, BF16) == 0
+
+
+def test_profile_names():
+    names = attn.profile_names()
+    assert names == ["prefill_bf16_mfma", "decode_bf16_partial", "decode_bf16_combine",
+                     "generic_f32"]
+
+
+def test_python_layer_rejects_bad_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError, match="GPU device"):
+        attn.fwd(q, q, q)
+    with pytest.raises(ValueError, match="4-D"):
+        attn.fwd(q[0], q, q)
+    with pytest.raises(ValueError):
+        attn.fwd(q.to(torch.float16), q, q)

@@ -1,0 +1,164 @@
+"""GPU kernels against the CPU oracle on the same seeded bits (MI355X).
+
+Small and ragged problems are compared element by element; the workloads at
+full size run in the same launch configuration the benchmark times and are
+compared on sampled (batch, head) slices, which the oracle computes on its
+own (heads and batch items are independent).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import golden_io
+import oracle
+import transformer_scaled_dot_attn_amd as attn
+import workloads as W
+from gpu_util import BF16_TOL, F32_TOL, assert_matches, check_problem, gpu_run
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------- fp32 path
+def test_tiny_f32_workload():
+    w = W.WORKLOADS["tiny_f32"]
+    x = W.make_inputs(w)
+    _say("tiny_f32", w)
+    got, _ = gpu_run(x["q"], x["k"], x["v"], x["scale"], w.causal)
+    ref = oracle.attention(x["q"], x["k"], x["v"], x["scale"], w.causal)
+    assert_matches(got, ref, F32_TOL, what="tiny_f32")
+
+
+@pytest.mark.parametrize("name", ["p2_causal_3tok_d2.txt", "p3_unmasked_3tok_dk4_dv2.txt"])
+def test_worked_examples_zero_padded(name):
+    """The pages' two worked examples through the fp32 kernel: features
+    zero-padded to 16 (zero features add nothing to a dot product, zero value
+    columns give zero outputs), with the page's own scale."""
+    g = golden_io.load(name)
+    T = g["q"].shape[0]
+    q = np.zeros((1, 1, T, 16), np.float32)
+    k = np.zeros((1, 1, T, 16), np.float32)
+    v = np.zeros((1, 1, T, 16), np.float32)
+    q[0, 0, :, :g["q"].shape[1]] = g["q"]
+    k[0, 0, :, :g["k"].shape[1]] = g["k"]
+    v[0, 0, :, :g["v"].shape[1]] = g["v"]
+    got, _ = gpu_run(q, k, v, float(np.float32(g["scale"])), g["causal"])
+    ref = oracle.attention(q, k, v, float(np.float32(g["scale"])), g["causal"])
+    assert_matches(got, ref, F32_TOL, what=name)
+    oexp, otol = g["out"]
+    dv = oexp.shape[1]
+    assert np.all(np.abs(got[0, 0, :, :dv] - oexp) <= otol)
+    assert np.all(got[0, 0, :, dv:] == 0.0)
+
+
+F32_CASES = [
+    # seed, B, H, Sq, Skv, d, causal, kv_lens
+    (1, 1, 1, 64, 64, 16, 1, None),
+    (2, 2, 3, 77, 77, 5, 1, None),
+    (3, 2, 2, 130, 130, 33, 1, [130, 61]),
+    (4, 1, 2, 100, 100, 64, 0, [57]),
+    (5, 2, 1, 40, 129, 128, 1, [129, 80]),
+    (6, 3, 2, 1, 300, 100, 0, [300, 1, 0]),
+    (7, 1, 1, 1, 1, 1, 1, None),
+    (8, 2, 2, 70, 70, 128, 1, [70, 0]),
+    (9, 1, 3, 65, 65, 64, 1, [200]),          # length above capacity: clamped
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: f"s{c[0]}")
+def test_f32_shapes(case):
+    seed, B, H, Sq, Skv, d, causal, lens = case
+    _say("f32 case", case)
+    prob = W.random_problem(seed, B, H, Sq, Skv, d, "f32", lens)
+    check_problem(prob, causal, F32_TOL, f"f32 {case}")
+
+
+# --------------------------------------------------------- bf16 prefill path
+PREFILL_CASES = [
+    (11, 1, 1, 64, 64, 128, 1, None),
+    (12, 2, 3, 300, 300, 128, 1, None),
+    (13, 1, 2, 200, 200, 64, 1, [137]),
+    (14, 2, 2, 129, 129, 64, 1, [129, 3]),
+    (15, 1, 2, 190, 190, 128, 0, None),
+    (16, 2, 1, 257, 257, 128, 0, [250, 100]),
+    (17, 1, 2, 70, 333, 128, 1, [300]),        # fewer queries than keys
+    (18, 2, 2, 2, 515, 64, 1, [515, 40]),
+    (19, 3, 1, 384, 384, 128, 1, [384, 1, 0]),
+    (20, 1, 1, 2, 2, 128, 1, None),
+    (21, 1, 4, 96, 96, 64, 0, None),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: f"s{c[0]}")
+def test_bf16_prefill_shapes(case):
+    seed, B, H, Sq, Skv, d, causal, lens = case
+    _say("prefill case", case)
+    assert attn.kernel_for(Sq, Skv, d, attn.BF16) == "prefill_bf16_mfma"
+    prob = W.random_problem(seed, B, H, Sq, Skv, d, "bf16", lens)
+    check_problem(prob, causal, BF16_TOL, f"prefill {case}")
+
+
+# ---------------------------------------------------------- bf16 decode path
+DECODE_CASES = [
+    (31, 1, 1, 1, 1, 128, 0, None),
+    (32, 3, 4, 1, 1000, 128, 0, [1, 513, 1000]),
+    (33, 2, 3, 1, 700, 64, 0, [700, 65]),
+    (34, 4, 2, 1, 2048, 128, 1, [0, 2048, 5000, 777]),
+    (35, 1, 8, 1, 4100, 128, 0, None),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"s{c[0]}")
+def test_bf16_decode_shapes(case):
+    seed, B, H, Sq, Skv, d, causal, lens = case
+    _say("decode case", case)
+    assert attn.kernel_for(Sq, Skv, d, attn.BF16) == "decode_bf16_splitkv"
+    prob = W.random_problem(seed, B, H, Sq, Skv, d, "bf16", lens)
+    check_problem(prob, causal, BF16_TOL, f"decode {case}")
+
+
+# ------------------------------------------------- workloads at full size
+def _sampled(w, pairs):
+    """Run the full workload on the GPU; oracle on the chosen (b, h) slices."""
+    import torch
+    _say("workload", w.name, "pairs", pairs)
+    x = W.device_inputs(w)
+    out = attn.fwd(x["q"], x["k"], x["v"], causal=w.causal, kv_lens=x["kv_lens"],
+                   scale=x["scale"])
+    torch.cuda.synchronize()
+    sub = W.make_inputs(w, pairs=pairs)
+    ref = oracle.attention(sub["q"], sub["k"], sub["v"], sub["scale"], w.causal, sub["kv_lens"])
+    got = np.stack([W.from_torch(out[b, h]) for b, h in pairs])[:, None]
+    # the sampled slices must be the very bits the GPU consumed
+    for idx, (b, h) in enumerate(pairs):
+        assert np.array_equal(W.bits_from_torch(x["q"][b, h]), sub["q"][idx, 0])
+    return assert_matches(got, ref, BF16_TOL, sub["kv_lens"], w.Skv, w.name)
+
+
+def test_workload_mha768_full():
+    w = W.WORKLOADS["mha768_bf16"]
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    _sampled(w, pairs)
+
+
+def test_workload_prefill4096_sampled():
+    w = W.WORKLOADS["prefill4096_bf16"]
+    _sampled(w, [(0, 0), (0, 13), (0, 31)])
+
+
+def test_workload_padded2048_sampled():
+    w = W.WORKLOADS["padded2048_bf16"]
+    lens = W.kv_lens_for(w)
+    short = int(np.argmin(lens))
+    _sampled(w, [(short, 0), (short, 31), (0, 5), (3, 17), (int(np.argmax(lens)), 2)])
+
+
+def test_workload_decode8192_sampled():
+    w = W.WORKLOADS["decode8192_bf16"]
+    lens = W.kv_lens_for(w)
+    bs = [int(np.argmin(lens)), int(np.argmax(lens)), 0, 17, 40, 63]
+    _sampled(w, [(b, h) for b in bs for h in (0, 11, 31)])

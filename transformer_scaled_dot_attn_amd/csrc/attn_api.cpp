@@ -1,0 +1,298 @@
+// C-ABI front end: argument checks, kernel choice, workspace, timing.
+//
+// The checks are a pure host function (attn_validate) that runs before any
+// HIP call.  Requests outside the kernels' support matrix are refused with
+// ATTN_E_UNSUPPORTED instead of running a slower path without saying so
+// ("Attention from First Principles", section 8, on silent kernel
+// fallbacks).  Prefill and decode get different kernels, since their shapes
+// and bottlenecks are opposite (same page, sections 6 and 8).
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <mutex>
+#include <vector>
+
+#include "attn.h"
+#include "launch.h"
+
+namespace tsda {
+namespace {
+
+enum Path { kPathNone = -1, kPathGenericF32 = 0, kPathPrefill = 1, kPathDecode = 2 };
+
+Path choose_path(int Sq, int d, int dtype) {
+    if (dtype == ATTN_F32) return d <= 128 ? kPathGenericF32 : kPathNone;
+    if (dtype == ATTN_BF16 && (d == 64 || d == 128)) return Sq == 1 ? kPathDecode : kPathPrefill;
+    return kPathNone;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(int B, int H, int Sq, int Skv, int d) {
+    if (B <= 0 || H <= 0 || Sq <= 0 || Skv <= 0 || d <= 0 || Sq > Skv) return ATTN_E_SHAPE;
+    // element counts of the k/v tensors and the launch grids must stay in range
+    const long double kv = (long double)B * H * Skv * d;
+    if (kv > (long double)(INT64_MAX / 8)) return ATTN_E_SHAPE;
+    const long double rows = (long double)B * H * ((Sq + 63) / 64);
+    if (rows > (long double)INT_MAX) return ATTN_E_SHAPE;
+    const long double splits = (long double)B * H * ((Skv + 63) / 64);
+    if (splits > (long double)INT_MAX) return ATTN_E_SHAPE;
+    return ATTN_OK;
+}
+
+struct DeviceWorkspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::vector<DeviceWorkspace> g_ws;  // indexed by device ordinal
+
+// ---- timing -------------------------------------------------------------
+struct Record {
+    int kernel;
+    hipEvent_t start, stop;
+};
+
+class EventTimer final : public KernelTimer {
+  public:
+    void begin(int kernel, hipStream_t s) override {
+        std::lock_guard<std::mutex> g(mu_);
+        Record r{kernel, take(), take()};
+        (void)hipEventRecord(r.start, s);
+        open_.push_back(r);
+    }
+    void end(int kernel, hipStream_t s) override {
+        std::lock_guard<std::mutex> g(mu_);
+        for (size_t i = open_.size(); i-- > 0;) {
+            if (open_[i].kernel == kernel) {
+                (void)hipEventRecord(open_[i].stop, s);
+                done_.push_back(open_[i]);
+                open_.erase(open_.begin() + i);
+                return;
+            }
+        }
+    }
+    int read(int kernel, long* launches, double* total_ms) {
+        std::lock_guard<std::mutex> g(mu_);
+        long n = 0;
+        double ms = 0.0;
+        for (const Record& r : done_) {
+            if (r.kernel != kernel) continue;
+            if (hipEventSynchronize(r.stop) != hipSuccess) return ATTN_E_LAUNCH;
+            float t = 0.0f;
+            if (hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess) return ATTN_E_LAUNCH;
+            ms += t;
+            ++n;
+        }
+        if (launches) *launches = n;
+        if (total_ms) *total_ms = ms;
+        return ATTN_OK;
+    }
+    void reset() {
+        std::lock_guard<std::mutex> g(mu_);
+        for (Record& r : done_) { give(r.start); give(r.stop); }
+        for (Record& r : open_) { give(r.start); give(r.stop); }
+        done_.clear();
+        open_.clear();
+    }
+    ~EventTimer() override {
+        reset();
+        for (hipEvent_t e : pool_) (void)hipEventDestroy(e);
+    }
+
+  private:
+    hipEvent_t take() {
+        if (!pool_.empty()) {
+            hipEvent_t e = pool_.back();
+            pool_.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        (void)hipEventCreate(&e);
+        return e;
+    }
+    void give(hipEvent_t e) {
+        if (e) pool_.push_back(e);
+    }
+    std::mutex mu_;
+    std::vector<Record> open_, done_;
+    std::vector<hipEvent_t> pool_;
+};
+
+EventTimer* g_timer = nullptr;
+bool g_timing_on = false;
+std::mutex g_timer_mu;
+
+int run(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq, int Skv,
+        int d, float scale, int causal, const int32_t* kv_lens, int dtype, void* stream,
+        void* workspace, size_t workspace_bytes, bool library_ws) {
+    int st = attn_validate(q, k, v, out, B, H, Sq, Skv, d, scale, causal, dtype);
+    if (st != ATTN_OK) return st;
+    const Path path = choose_path(Sq, d, dtype);
+    const size_t need = attn_workspace_bytes(B, H, Sq, Skv, d, dtype);
+    if (library_ws) {
+        workspace = nullptr;
+        if (need > 0) {
+            int dev = 0;
+            if (hipGetDevice(&dev) != hipSuccess) return ATTN_E_LAUNCH;
+            std::lock_guard<std::mutex> g(g_ws_mu);
+            if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+            DeviceWorkspace& w = g_ws[dev];
+            if (w.bytes < need) {
+                // earlier calls may still be using the old buffer
+                if (hipDeviceSynchronize() != hipSuccess) return ATTN_E_LAUNCH;
+                if (w.ptr) (void)hipFree(w.ptr);
+                w.ptr = nullptr;
+                w.bytes = 0;
+                if (hipMalloc(&w.ptr, need) != hipSuccess) {
+                    w.ptr = nullptr;
+                    return ATTN_E_NOMEM;
+                }
+                w.bytes = need;
+            }
+            workspace = w.ptr;
+            workspace_bytes = w.bytes;
+        }
+    } else {
+        if (workspace_bytes < need) return ATTN_E_WORKSPACE;
+        if (need > 0 && (workspace == nullptr)) return ATTN_E_NULL;
+        if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_E_ALIGN;
+    }
+    LaunchArgs a{q, k, v, out, B, H, Sq, Skv, d, scale, causal ? 1 : 0, kv_lens,
+                 static_cast<hipStream_t>(stream), workspace, workspace_bytes};
+    hipError_t e = hipSuccess;
+    switch (path) {
+        case kPathGenericF32: e = launch_generic_f32(a); break;
+        case kPathPrefill: e = launch_prefill_bf16(a); break;
+        case kPathDecode: e = launch_decode_bf16(a); break;
+        default: return ATTN_E_UNSUPPORTED;
+    }
+    return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+}  // namespace
+
+KernelTimer* active_timer() { return g_timing_on ? g_timer : nullptr; }
+
+}  // namespace tsda
+
+using namespace tsda;
+
+extern "C" {
+
+int attn_validate(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq,
+                  int Skv, int d, float scale, int causal, int dtype) {
+    (void)causal;
+    if (!q || !k || !v || !out) return ATTN_E_NULL;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_E_DTYPE;
+    int st = check_shape(B, H, Sq, Skv, d);
+    if (st != ATTN_OK) return st;
+    if (!std::isfinite(scale)) return ATTN_E_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_E_ALIGN;
+    if (choose_path(Sq, d, dtype) == kPathNone) return ATTN_E_UNSUPPORTED;
+    return ATTN_OK;
+}
+
+const char* attn_kernel_for(int Sq, int Skv, int d, int dtype) {
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return nullptr;
+    if (check_shape(1, 1, Sq, Skv, d) != ATTN_OK) return nullptr;
+    switch (choose_path(Sq, d, dtype)) {
+        case kPathGenericF32: return "generic_f32";
+        case kPathPrefill: return "prefill_bf16_mfma";
+        case kPathDecode: return "decode_bf16_splitkv";
+        default: return nullptr;
+    }
+}
+
+size_t attn_workspace_bytes(int B, int H, int Sq, int Skv, int d, int dtype) {
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
+    if (check_shape(B, H, Sq, Skv, d) != ATTN_OK) return 0;
+    if (choose_path(Sq, d, dtype) != kPathDecode) return 0;
+    return decode_workspace_bytes(B, H, Skv, d);
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq,
+             int Skv, int d, float scale, int causal, const int32_t* kv_lens, int dtype,
+             void* stream) {
+    return run(q, k, v, out, B, H, Sq, Skv, d, scale, causal, kv_lens, dtype, stream, nullptr, 0,
+               true);
+}
+
+int attn_fwd_ws(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq,
+                int Skv, int d, float scale, int causal, const int32_t* kv_lens, int dtype,
+                void* stream, void* workspace, size_t workspace_bytes) {
+    return run(q, k, v, out, B, H, Sq, Skv, d, scale, causal, kv_lens, dtype, stream, workspace,
+               workspace_bytes, false);
+}
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_E_NULL: return "null pointer argument";
+        case ATTN_E_SHAPE: return "invalid shape (a size <= 0, Sq > Skv, or too large)";
+        case ATTN_E_UNSUPPORTED: return "unsupported combination of dtype and head size";
+        case ATTN_E_DTYPE: return "unknown dtype";
+        case ATTN_E_ALIGN: return "pointer not aligned (16 bytes; workspace 256 bytes)";
+        case ATTN_E_WORKSPACE: return "workspace too small";
+        case ATTN_E_ARG: return "scale is not finite";
+        case ATTN_E_LAUNCH: return "HIP launch or runtime failure";
+        case ATTN_E_NOMEM: return "device allocation failed";
+        default: return "unknown status";
+    }
+}
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+void attn_release(void) {
+    std::lock_guard<std::mutex> g(g_ws_mu);
+    int cur = 0;
+    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+    for (size_t dev = 0; dev < g_ws.size(); ++dev) {
+        if (g_ws[dev].ptr) {
+            (void)hipSetDevice((int)dev);
+            (void)hipFree(g_ws[dev].ptr);
+        }
+        g_ws[dev] = DeviceWorkspace{};
+    }
+    if (have_cur) (void)hipSetDevice(cur);
+}
+
+int attn_profile_enable(int on) {
+    std::lock_guard<std::mutex> g(g_timer_mu);
+    if (!g_timer) g_timer = new EventTimer();
+    g_timer->reset();
+    g_timing_on = on != 0;
+    return ATTN_OK;
+}
+
+int attn_profile_reset(void) {
+    std::lock_guard<std::mutex> g(g_timer_mu);
+    if (g_timer) g_timer->reset();
+    return ATTN_OK;
+}
+
+int attn_profile_read(int kernel, long* launches, double* total_ms) {
+    if (kernel < 0 || kernel >= kNumKernels) return ATTN_E_ARG;
+    std::lock_guard<std::mutex> g(g_timer_mu);
+    if (!g_timer) {
+        if (launches) *launches = 0;
+        if (total_ms) *total_ms = 0.0;
+        return ATTN_OK;
+    }
+    return g_timer->read(kernel, launches, total_ms);
+}
+
+const char* attn_profile_name(int kernel) {
+    switch (kernel) {
+        case kPrefillBf16: return "prefill_bf16_mfma";
+        case kDecodePartialBf16: return "decode_bf16_partial";
+        case kDecodeCombineBf16: return "decode_bf16_combine";
+        case kGenericF32: return "generic_f32";
+        default: return nullptr;
+    }
+}
+
+}  // extern "C"

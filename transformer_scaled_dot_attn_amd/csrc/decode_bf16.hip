@@ -1,0 +1,219 @@
+// bfloat16 decode: one query per (b, h) against a KV cache, split over keys.
+//
+// Decode reads the whole valid cache and does little arithmetic per byte
+// ("Attention from First Principles", section 6: a matrix-vector product
+// whose intensity is about 1 for multi-head attention), so this path is
+// built for HBM bandwidth, not for the matrix cores:
+//   * partial kernel: one block per (b, h, split of `chunk` keys).  Each key
+//     row (d bf16 = 2d bytes) is read by d/8 lanes with one 16-byte load
+//     each, so every wave-wide load covers whole contiguous rows.  Logits use
+//     v_dot2 on the raw bf16 pairs (exact products, fp32 sums), reduced over
+//     the row's lanes with DPP.  Each lane group keeps a running maximum m,
+//     normaliser l and an fp32 accumulator for its 8 columns (the online
+//     softmax recurrence); the block merges its groups in LDS and writes one
+//     (m, l, acc[d]) partial.  Keys past the valid length are never loaded.
+//   * combine kernel: per (b, h), merges the partials with the log-sum-exp
+//     rule  M = max m_s,  l = sum l_s 2^(m_s - M),
+//     out = (sum acc_s 2^(m_s - M)) / l, and rounds to bf16.  L_b = 0 gives 0.
+// Logits are kept in base 2 (scale * log2 e folded in), which leaves the
+// softmax unchanged.
+#include "device_common.h"
+#include "launch.h"
+
+namespace tsda {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kUnroll = 4;
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_partial_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ kv_lens, int H, int Skv,
+    float scale_log2, int chunk, int nsplit, float* __restrict__ ws_acc,
+    float* __restrict__ ws_ml) {
+    constexpr int G = D / 8;            // lanes per key row
+    constexpr int KPW = 64 / G;         // key rows per wave per load
+    constexpr int SLOTS = kWaves * KPW; // key rows per block per load
+    __shared__ float s_m[SLOTS];
+    __shared__ float s_l[SLOTS];
+    __shared__ float s_acc[SLOTS][D];
+
+    const int unit = blockIdx.x;
+    const int bh = unit / nsplit;
+    const int split = unit - bh * nsplit;
+    const int b = bh / H;
+    const int L = valid_length(kv_lens, b, Skv);
+    const int k0 = split * chunk;
+    if (k0 >= L) return;  // the combine kernel reads only splits below L
+    const int k1 = min(k0 + chunk, L);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int slot = (tid >> 6) * KPW + lane / G;
+    const int part = lane % G;
+
+    const u32x4 qw = ldg16(q + (size_t)bh * D + part * 8);
+    const uint16_t* kp = k + (size_t)bh * Skv * D + part * 8;
+    const uint16_t* vp = v + (size_t)bh * Skv * D + part * 8;
+
+    float m = -INFINITY, l = 0.0f;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+
+    for (int base = k0; base < k1; base += SLOTS * kUnroll) {
+        u32x4 kr[kUnroll], vr[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int j = base + u * SLOTS + slot;
+            if (j < k1) {
+                kr[u] = ldg16(kp + (size_t)j * D);
+                vr[u] = ldg16(vp + (size_t)j * D);
+            } else {
+                kr[u] = u32x4{0, 0, 0, 0};
+                vr[u] = u32x4{0, 0, 0, 0};
+            }
+        }
+        float s[kUnroll];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float dot = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dot = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kr[u][i]), as_bf16x2(qw[i]), dot,
+                                                      false);
+            dot = group_sum<G>(dot);
+            const int j = base + u * SLOTS + slot;
+            s[u] = j < k1 ? dot * scale_log2 : -INFINITY;
+            mx = fmaxf(mx, s[u]);
+        }
+        const float m_new = fmaxf(m, mx);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = fast_exp2(m - m_use);
+        l *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const float p = fast_exp2(s[u] - m_use);
+            l += p;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] = fmaf(p, bf16_lo(vr[u][i]), acc[2 * i]);
+                acc[2 * i + 1] = fmaf(p, bf16_hi(vr[u][i]), acc[2 * i + 1]);
+            }
+        }
+        m = m_new;
+    }
+
+    if (part == 0) {
+        s_m[slot] = m;
+        s_l[slot] = l;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_acc[slot][part * 8 + e] = acc[e];
+    __syncthreads();
+    if (tid < D) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int s2 = 0; s2 < SLOTS; ++s2) M = fmaxf(M, s_m[s2]);
+        float lt = 0.0f, at = 0.0f;
+#pragma unroll
+        for (int s2 = 0; s2 < SLOTS; ++s2) {
+            const float w = s_m[s2] == -INFINITY ? 0.0f : fast_exp2(s_m[s2] - M);
+            lt = fmaf(s_l[s2], w, lt);
+            at = fmaf(s_acc[s2][tid], w, at);
+        }
+        ws_acc[(size_t)unit * D + tid] = at;
+        if (tid == 0) {
+            ws_ml[(size_t)unit * 2] = M;
+            ws_ml[(size_t)unit * 2 + 1] = lt;
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(
+    const int32_t* __restrict__ kv_lens, int H, int Skv, int chunk, int nsplit,
+    const float* __restrict__ ws_acc, const float* __restrict__ ws_ml, uint16_t* __restrict__ out) {
+    const int bh = blockIdx.x;
+    const int b = bh / H;
+    const int t = threadIdx.x;
+    const int L = valid_length(kv_lens, b, Skv);
+    uint16_t* o = out + (size_t)bh * D;
+    if (L == 0) {
+        o[t] = 0;
+        return;
+    }
+    const int nv = (L + chunk - 1) / chunk;
+    const float* ml = ws_ml + (size_t)bh * nsplit * 2;
+    const float* ac = ws_acc + (size_t)bh * nsplit * D;
+    float M = -INFINITY;
+    for (int s = 0; s < nv; ++s) M = fmaxf(M, ml[2 * s]);
+    float lt = 0.0f, at = 0.0f;
+    for (int s = 0; s < nv; ++s) {
+        const float w = fast_exp2(ml[2 * s] - M);
+        lt = fmaf(ml[2 * s + 1], w, lt);
+        at = fmaf(ac[(size_t)s * D + t], w, at);
+    }
+    o[t] = to_bf16(at / lt);
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+DecodePlan decode_plan(int B, int H, int Skv) {
+    int chunk = 512;
+    while (chunk > 64 && (long)B * H * ((Skv + chunk - 1) / chunk) < 8192) chunk /= 2;
+    return DecodePlan{chunk, (Skv + chunk - 1) / chunk};
+}
+
+size_t decode_workspace_bytes(int B, int H, int Skv, int d) {
+    const DecodePlan p = decode_plan(B, H, Skv);
+    const size_t units = (size_t)B * H * p.nsplit;
+    return round256(units * d * sizeof(float)) + round256(units * 2 * sizeof(float));
+}
+
+hipError_t launch_decode_bf16(const LaunchArgs& a) {
+    const DecodePlan p = decode_plan(a.B, a.H, a.Skv);
+    const size_t units = (size_t)a.B * a.H * p.nsplit;
+    float* ws_acc = static_cast<float*>(a.workspace);
+    float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
+                                            round256(units * a.d * sizeof(float)));
+    const uint16_t* q = static_cast<const uint16_t*>(a.q);
+    const uint16_t* k = static_cast<const uint16_t*>(a.k);
+    const uint16_t* v = static_cast<const uint16_t*>(a.v);
+    uint16_t* o = static_cast<uint16_t*>(a.out);
+    const float sl = a.scale * kLog2e;
+    KernelTimer* t = active_timer();
+    hipError_t e;
+    if (t) t->begin(kDecodePartialBf16, a.stream);
+    if (a.d == 128)
+        hipLaunchKernelGGL(decode_partial_kernel<128>, dim3((unsigned)units), dim3(256), 0,
+                           a.stream, q, k, v, a.kv_lens, a.H, a.Skv, sl, p.chunk, p.nsplit, ws_acc,
+                           ws_ml);
+    else
+        hipLaunchKernelGGL(decode_partial_kernel<64>, dim3((unsigned)units), dim3(256), 0,
+                           a.stream, q, k, v, a.kv_lens, a.H, a.Skv, sl, p.chunk, p.nsplit, ws_acc,
+                           ws_ml);
+    e = hipGetLastError();
+    if (t) t->end(kDecodePartialBf16, a.stream);
+    if (e != hipSuccess) return e;
+    if (t) t->begin(kDecodeCombineBf16, a.stream);
+    const unsigned pairs = (unsigned)((size_t)a.B * a.H);
+    if (a.d == 128)
+        hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(pairs), dim3(128), 0, a.stream,
+                           a.kv_lens, a.H, a.Skv, p.chunk, p.nsplit, ws_acc, ws_ml, o);
+    else
+        hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(pairs), dim3(64), 0, a.stream,
+                           a.kv_lens, a.H, a.Skv, p.chunk, p.nsplit, ws_acc, ws_ml, o);
+    e = hipGetLastError();
+    if (t) t->end(kDecodeCombineBf16, a.stream);
+    return e;
+}
+
+}  // namespace tsda

@@ -1,0 +1,145 @@
+// Float32 attention forward on the vector ALUs (any d <= 128, any Sq <= Skv).
+//
+// One wavefront per block and one query row per lane; the block's 64 query
+// rows share K/V tiles of 32 keys staged in LDS (every lane reads the same
+// LDS word, a broadcast).  Per tile each lane computes its 32 logits, then
+// updates its running maximum m and normaliser l and rescales its output
+// accumulator once (the online-softmax recurrence), so the score matrix is
+// never materialised ("Scaled dot-product attention with masking", section
+// "The memory problem").  Keys past the valid length are never read; rows
+// past the valid query count are written as zeros.
+#include "device_common.h"
+#include "launch.h"
+
+namespace tsda {
+
+namespace {
+
+constexpr int kRows = 64;   // query rows per block
+constexpr int kKeys = 32;   // keys per LDS tile
+
+template <int DP>  // d rounded up to 16, 32, 64 or 128
+__global__ __launch_bounds__(64) void generic_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    float* __restrict__ out, const int32_t* __restrict__ kv_lens, int H, int Sq, int Skv, int d,
+    float scale_log2, int causal) {
+    __shared__ float ks[kKeys][DP];
+    __shared__ float vs[kKeys][DP];
+
+    const int lane = threadIdx.x;
+    const int nqt = (Sq + kRows - 1) / kRows;
+    const int bh = blockIdx.x / nqt;
+    const int b = bh / H;
+    const int L = valid_length(kv_lens, b, Skv);
+    const int n = Sq < L ? Sq : L;
+    const int row0 = (blockIdx.x - bh * nqt) * kRows;
+    const int i = row0 + lane;
+    const bool live = i < n;
+    const int p = L - n + i;  // absolute position of this lane's query
+
+    // keys any row of this block may see
+    int kv_hi = L;
+    if (causal) {
+        const int last = (row0 + kRows < n ? row0 + kRows : n) - 1;
+        kv_hi = min(L, L - n + last + 1);
+    }
+    if (row0 >= n) kv_hi = 0;
+
+    float qr[DP];
+    float acc[DP];
+    const float* qrow = q + ((size_t)bh * Sq + (live ? i : 0)) * d;
+#pragma unroll
+    for (int c = 0; c < DP; ++c) {
+        qr[c] = (live && c < d) ? qrow[c] : 0.0f;
+        acc[c] = 0.0f;
+    }
+    float m = -INFINITY, l = 0.0f;
+
+    const float* kb = k + (size_t)bh * Skv * d;
+    const float* vb = v + (size_t)bh * Skv * d;
+    for (int j0 = 0; j0 < kv_hi; j0 += kKeys) {
+        const int nk = min(kKeys, kv_hi - j0);
+        __syncthreads();
+        // stage the tile: the tile is contiguous in global memory
+        for (int e = lane; e < kKeys * d; e += 64) {
+            const int r = e / d, c = e - r * d;
+            const bool ok = r < nk;
+            ks[r][c] = ok ? kb[(size_t)j0 * d + e] : 0.0f;
+            vs[r][c] = ok ? vb[(size_t)j0 * d + e] : 0.0f;
+        }
+        if (d < DP) {
+            for (int e = lane; e < kKeys * (DP - d); e += 64) {
+                const int r = e / (DP - d), c = d + e - r * (DP - d);
+                ks[r][c] = 0.0f;
+                vs[r][c] = 0.0f;
+            }
+        }
+        __syncthreads();
+
+        float s[kKeys];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < kKeys; ++r) {
+            float dot = 0.0f;
+#pragma unroll
+            for (int c = 0; c < DP; ++c) dot = fmaf(qr[c], ks[r][c], dot);
+            const int j = j0 + r;
+            const bool vis = r < nk && (!causal || j <= p);
+            s[r] = vis ? dot * scale_log2 : -INFINITY;
+            tmax = fmaxf(tmax, s[r]);
+        }
+        const float m_new = fmaxf(m, tmax);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = fast_exp2(m - m_use);
+        l *= alpha;
+#pragma unroll
+        for (int c = 0; c < DP; ++c) acc[c] *= alpha;
+#pragma unroll
+        for (int r = 0; r < kKeys; ++r) {
+            const float pr = fast_exp2(s[r] - m_use);
+            l += pr;
+#pragma unroll
+            for (int c = 0; c < DP; ++c) acc[c] = fmaf(pr, vs[r][c], acc[c]);
+        }
+        m = m_new;
+    }
+
+    if (i < Sq) {
+        float* orow = out + ((size_t)bh * Sq + i) * d;
+        const float inv = (live && l > 0.0f) ? 1.0f / l : 0.0f;
+#pragma unroll
+        for (int c = 0; c < DP; ++c)
+            if (c < d) orow[c] = live ? acc[c] * inv : 0.0f;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_generic_f32(const LaunchArgs& a) {
+    dim3 grid((unsigned)(((a.Sq + kRows - 1) / kRows) * (long)a.B * a.H));
+    dim3 block(64);
+    const float sl = a.scale * kLog2e;
+    const float* q = static_cast<const float*>(a.q);
+    const float* k = static_cast<const float*>(a.k);
+    const float* v = static_cast<const float*>(a.v);
+    float* o = static_cast<float*>(a.out);
+    KernelTimer* t = active_timer();
+    if (t) t->begin(kGenericF32, a.stream);
+    if (a.d <= 16)
+        hipLaunchKernelGGL(generic_f32_kernel<16>, grid, block, 0, a.stream, q, k, v, o, a.kv_lens,
+                           a.H, a.Sq, a.Skv, a.d, sl, a.causal);
+    else if (a.d <= 32)
+        hipLaunchKernelGGL(generic_f32_kernel<32>, grid, block, 0, a.stream, q, k, v, o, a.kv_lens,
+                           a.H, a.Sq, a.Skv, a.d, sl, a.causal);
+    else if (a.d <= 64)
+        hipLaunchKernelGGL(generic_f32_kernel<64>, grid, block, 0, a.stream, q, k, v, o, a.kv_lens,
+                           a.H, a.Sq, a.Skv, a.d, sl, a.causal);
+    else
+        hipLaunchKernelGGL(generic_f32_kernel<128>, grid, block, 0, a.stream, q, k, v, o,
+                           a.kv_lens, a.H, a.Sq, a.Skv, a.d, sl, a.causal);
+    hipError_t e = hipGetLastError();
+    if (t) t->end(kGenericF32, a.stream);
+    return e;
+}
+
+}  // namespace tsda

@@ -1,0 +1,46 @@
+// Internal interface between the C-ABI front end and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tsda {
+
+struct LaunchArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    int B, H, Sq, Skv, d;
+    float scale;
+    int causal;
+    const int32_t* kv_lens;
+    hipStream_t stream;
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+// Decode split plan: keys per split and number of splits per (b, h).
+struct DecodePlan {
+    int chunk;
+    int nsplit;
+};
+DecodePlan decode_plan(int B, int H, int Skv);
+size_t decode_workspace_bytes(int B, int H, int Skv, int d);
+
+// Profiling hook: the front end brackets each launch when timing is on.
+struct KernelTimer {
+    virtual void begin(int kernel, hipStream_t s) = 0;
+    virtual void end(int kernel, hipStream_t s) = 0;
+    virtual ~KernelTimer() = default;
+};
+KernelTimer* active_timer();  // nullptr when timing is off
+
+enum KernelId { kPrefillBf16 = 0, kDecodePartialBf16 = 1, kDecodeCombineBf16 = 2, kGenericF32 = 3,
+                kNumKernels = 4 };
+
+hipError_t launch_generic_f32(const LaunchArgs& a);
+hipError_t launch_prefill_bf16(const LaunchArgs& a);
+hipError_t launch_decode_bf16(const LaunchArgs& a);
+
+}  // namespace tsda

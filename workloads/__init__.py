@@ -165,3 +165,55 @@ def random_problem(seed: int, B: int, H: int, Sq: int, Skv: int, d: int, dtype: 
     lens = None if kv_lens is None else np.asarray(kv_lens, dtype=np.int32)
     return {"q": q, "k": k, "v": v, "kv_lens": lens,
             "scale": float(np.float32(1.0 / math.sqrt(d)))}
+
+
+# ---- moving inputs to and from a GPU (torch only moves the bits) ----------
+def to_torch(x: np.ndarray, device="cuda"):
+    """float32 array -> float32 tensor; uint16 bf16 bits -> bfloat16 tensor."""
+    import torch
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(device).view(torch.bfloat16)
+    if x.dtype == np.float32:
+        return torch.from_numpy(x).to(device)
+    raise ValueError(f"cannot upload dtype {x.dtype}")
+
+
+def from_torch(t) -> np.ndarray:
+    """bfloat16 or float32 tensor -> the same values as a float64 array."""
+    import torch
+    t = t.detach().contiguous()
+    if t.dtype == torch.bfloat16:
+        bits = t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return bf16_to_f32(bits).astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def bits_from_torch(t) -> np.ndarray:
+    """Raw stored bits of a bfloat16 (uint16) or float32 (uint32) tensor."""
+    import torch
+    t = t.detach().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy().view(np.uint32)
+
+
+def device_inputs(w: Workload, device="cuda", pad_fill: float = 0.0) -> dict:
+    """The workload's q, k, v as device tensors, drawn and uploaded one batch
+    item at a time (bounded host memory), plus kv_lens (device int32 or None),
+    the host copy of the lengths, and scale."""
+    import torch
+    lens = kv_lens_for(w)
+    tdtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    res = {}
+    for name, S in (("q", w.Sq), ("k", w.Skv), ("v", w.Skv)):
+        t = torch.empty((w.B, w.H, S, w.d), dtype=tdtype, device=device)
+        for b in range(w.B):
+            part = make_tensor(w, name, lens, pairs=[(b, h) for h in range(w.H)],
+                               pad_fill=pad_fill)
+            t[b].copy_(to_torch(part.reshape(w.H, S, w.d), device))
+        res[name] = t
+    res["kv_lens"] = None if lens is None else torch.from_numpy(lens).to(device)
+    res["kv_lens_host"] = lens
+    res["scale"] = w.scale
+    return res
