@@ -30,6 +30,8 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 
+COPY_BYTES = 1 << 30        # calibration copy size
+
 PREFILL = "prefill4096_bf16"
 DECODE = "decode8192_bf16"
 
@@ -58,13 +60,43 @@ def decode_bytes(w, lens) -> float:
     return float(kv + qo + 4 * w.B)
 
 
+def profiled_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 summary of this kernel
+    and workload (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known
+    size), or None when there is none or the kernel's sources have changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":", 1)[0] in (
+                "traffic_bytes_per_launch", "kernel_sources", "kernel_source_sha256"):
+            key, val = line.split(":", 1)
+            fields[key] = val.strip()
+    if len(fields) != 3:
+        return None
+    h = hashlib.sha256()
+    for f in fields["kernel_sources"].split():
+        src = os.path.join(ROOT, "transformer_scaled_dot_attn_amd", "csrc", f)
+        if not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
+    if h.hexdigest() != fields["kernel_source_sha256"]:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--parts", default="prefill,decode",
-                    help="comma list of prefill, decode (default both)")
+                    help="comma list of prefill, decode, copy (default prefill,decode); "
+                         "copy adds a plain 1 GiB device-to-device copy per step, the "
+                         "known-size kernel that scales the HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="oracle threads for the CPU baseline (default min(16, cores))")
@@ -72,23 +104,19 @@ def parse():
 
 
 def cpu_baseline(threads: int):
-    """Time the oracle on a bounded sample of the prefill workload: the first
-    `threads` heads of B=1, S=4096, d=128 causal (one thread per head)."""
-    import numpy as np
+    """Time the oracle on the prefill workload (B=1, H=32, S=4096, d=128,
+    causal), all 32 heads, one thread per head up to `threads`."""
     import oracle
     import workloads as W
     w = W.WORKLOADS[PREFILL]
-    heads = max(1, min(threads, w.H))
-    pairs = [(0, h) for h in range(heads)]
-    x = W.make_inputs(w, pairs=pairs)
+    x = W.make_inputs(w)
     t0 = time.perf_counter()
     oracle.attention(x["q"], x["k"], x["v"], x["scale"], w.causal, None, nthreads=threads)
     dt = time.perf_counter() - t0
-    flops = prefill_flops(w) * heads / w.H
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(threads, heads),
-            "kind": "oracle",
-            "sample": f"{heads} of {w.H} heads of {PREFILL} (B=1, S=4096, d=128, causal), "
-                      f"float64, {dt:.2f} s wall"}
+    return {"value": prefill_flops(w) / dt / 1e12, "unit": "TFLOP/s",
+            "cores": min(threads, w.B * w.H), "kind": "oracle",
+            "sample": f"all {w.H} heads of {PREFILL} (B=1, S=4096, d=128, causal), float64, "
+                      f"{dt:.2f} s wall"}
 
 
 def main():
@@ -123,10 +151,17 @@ def main():
         out = torch.empty_like(x["q"])
         runs.append(("decode", w, x, out))
 
+    copy_src = copy_dst = None
+    if "copy" in parts:
+        copy_src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        copy_dst = torch.empty_like(copy_src)
+
     def step():
         for _, w, x, out in runs:
             attn.fwd(x["q"], x["k"], x["v"], out, causal=w.causal, kv_lens=x["kv_lens"],
                      scale=x["scale"])
+        if copy_src is not None:
+            copy_dst.copy_(copy_src)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -167,7 +202,8 @@ def main():
             result["roofline"] = {
                 "kernel": "prefill_bf16_mfma", "bound": "mfma", "achieved": tflops,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
-                "traffic": None, "algorithmic_flop_per_launch": flops, "avg_launch_ms": kms}
+                "traffic": profiled_traffic("prefill_bf16_mfma", w.name),
+                "algorithmic_flop_per_launch": flops, "avg_launch_ms": kms}
         else:
             lens = x["kv_lens_host"]
             nbytes = decode_bytes(w, lens)
@@ -185,7 +221,8 @@ def main():
                 "roofline": {
                     "kernel": "decode_bf16_partial", "bound": "hbm", "achieved": gbs_k,
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs_k / PEAK_HBM_GBS,
-                    "traffic": None, "algorithmic_bytes_per_launch": kv_bytes,
+                    "traffic": profiled_traffic("decode_bf16_partial", w.name),
+                    "algorithmic_bytes_per_launch": kv_bytes,
                     "avg_launch_ms": p_ms},
                 "combine_avg_launch_ms": c_ms,
             }
