@@ -6,22 +6,18 @@
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation, and the S x S score
 // matrix never leaves registers.
 //
-// Block = 4 wavefronts = 128 query rows of one (b, h); wave w owns rows
-// 32w..32w+31.  The block walks the keys in tiles of 64, staged K and V
-// tiles in LDS (two buffers: the next tile's global loads are in flight
-// while the current tile is computed).
+// Block = 8 wavefronts = 256 query rows of one (b, h); wave w owns rows
+// 32w..32w+31, and two waves share each SIMD.  The block walks the keys in
+// tiles of 64, staging K and V tiles in LDS rings (K: 2 slots, V: 3 slots).
 //
-// Transposed products.  Each wave computes S^T = K Q^T (K from LDS as the A
-// operand, Q^T held in registers as the B operand).  In the accumulator of
-// a 32x32 MFMA a lane holds one column, so every lane owns ONE query and 16
-// of its keys; lane l and lane l^32 hold the other 16.  Row maximum and row
-// sum are therefore lane-local plus one permlane32 swap.  The mixture is
-// computed as O^T = V^T P^T: P^T is the B operand straight from the score
-// registers (cast to bf16, as the "Attention from scratch" readable model
-// casts its fp32 softmax weights before multiplying by V), and V^T is read
-// from the row-major V tile with ds_read_b64_tr_b16 transposing loads.  The
-// output accumulator again has one query per lane, so the online-softmax
-// rescale is a per-lane scalar multiply.
+// Ping-pong.  Within a wave the work of a tile is a chain: Q K^T on the
+// matrix cores, then the softmax on the vector ALU, then P V on the matrix
+// cores.  Waves 0-3 (group A) run that chain for tile t in iteration t;
+// waves 4-7 (group B) run the softmax and P V of tile t-1 and then Q K^T of
+// tile t.  After each barrier the two waves sharing a SIMD therefore start
+// in complementary phases -- one on the matrix cores while the other
+// exponentiates -- instead of stalling on the same dependency at the same
+// time.
 //
 // Masking.  Key j is visible to the query at absolute position p iff
 // j < L_b and (not causal or j <= p).  Tiles past the block's last visible
@@ -42,52 +38,54 @@ namespace tsda {
 
 namespace {
 
-constexpr int kBM = 128;   // query rows per block
+constexpr int kBM = 256;   // query rows per block
 constexpr int kBN = 64;    // keys per tile
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
 template <int D>
 struct Shape {
-    static constexpr int kChunks = D / 8;                     // 16-byte chunks per row
-    static constexpr int kKSteps = D / 16;                    // MFMA k-steps of Q K^T
-    static constexpr int kDBlocks = D / 32;                   // 32-row blocks of O^T
-    static constexpr int kTile = kBN * D;                     // elements per K or V tile
+    static constexpr int kChunks = D / 8;                        // 16-byte chunks per row
+    static constexpr int kKSteps = D / 16;                       // MFMA k-steps of Q K^T
+    static constexpr int kDBlocks = D / 32;                      // 32-row blocks of O^T
     static constexpr int kPerThread = kBN * kChunks / kThreads;  // 16-byte loads per thread
-    static_assert(kPerThread * kThreads == kBN * kChunks, "tile must split evenly");
+    static constexpr int kRowsPerPass = kThreads / kChunks;      // tile rows per load pass
+    static_assert(kPerThread >= 1 && kPerThread * kThreads == kBN * kChunks,
+                  "tile must split evenly");
+    // LDS row strides in elements.  A K row is padded by 16 bytes, so 8
+    // consecutive rows start in 8 different 16-byte bank groups of a 128-byte
+    // bank row (the K operand loads: 8 lanes per LDS cycle, 8 rows, one chunk
+    // each).  A V row is padded by 32 bytes, so the 4 rows x 2 chunks that a
+    // 16-lane group reads with one transposing load fall in 8 different bank
+    // groups.  Every LDS address is then a per-lane base plus a constant.
+    static constexpr int kStrideK = D + 8;
+    static constexpr int kStrideV = D + 16;
+    static constexpr int kTileK = kBN * kStrideK;
+    static constexpr int kTileV = kBN * kStrideV;
 };
-
-// Position of 16-byte chunk c of LDS row r.  The XOR keeps both access
-// patterns free of bank conflicts: 8 consecutive rows reading one chunk
-// (the K operand loads) and 4 consecutive rows reading two neighbouring
-// chunks (the transposing V loads).
-template <int D>
-__device__ __forceinline__ int swizzle(int r, int c) {
-    if constexpr (D == 128)
-        return c ^ ((r & 7) << 1);
-    else
-        return c ^ (((r >> 1) & 3) << 1);
-}
-
-template <int D>
-__device__ __forceinline__ int lds_offset(int r, int c) {
-    return r * D + swizzle<D>(r, c) * 8;
-}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// Scheduling fence: the compiler moves no instruction across it, which keeps
+// a batch of LDS reads issued ahead of the MFMAs that consume them.
+__device__ __forceinline__ void pin_schedule() { __builtin_amdgcn_sched_barrier(0); }
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
     const int32_t* __restrict__ kv_lens, int BH, int H, int Sq, int Skv, float scale_log2,
     int causal, int nqt) {
     using S = Shape<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][S::kTile];  // [buffer][K, V]
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][S::kTileK];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v[3][S::kTileV];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int half = lane >> 5;
+    const bool group_b = wave >= kWaves / 2;
 
     const int bid = blockIdx.x;
     const int qt = nqt - 1 - bid / BH;
@@ -116,6 +114,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const int p_lo = off + qw;
     const int p_hi = off + min(qw + 32, n) - 1;
     const int kv_hi_w = wave_live ? (causal ? min(L, p_hi + 1) : L) : 0;
+    const int ntiles_w = (kv_hi_w + kBN - 1) / kBN;  // tiles this wave computes
     const int kfull_w = causal ? min(L, p_lo + 1) : L;
 
     // this lane's query
@@ -133,153 +132,218 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
             qf[ks] = q_live ? ldg16(qrow + ks * 16) : u32x4{0, 0, 0, 0};
     }
 
-    const uint16_t* kg = k + (size_t)bh * Skv * D;
-    const uint16_t* vg = v + (size_t)bh * Skv * D;
-
+    // ---- tile staging: thread t moves 16-byte chunks t + 512 i of the
+    // row-major tile, so consecutive threads read consecutive global bytes.
+    // The loads are branch-free, so they stay in flight through the tile's
+    // compute (no wait until the stash): a row at or past L is redirected to row 0 of the same head
+    // (always valid) and zeroed when stashed, so padded rows are never read.
+    const int st_row = tid / S::kChunks;
+    const int st_col = (tid % S::kChunks) * 8;
+    const size_t head_off = (size_t)bh * Skv * D + st_col;
     u32x4 kreg[S::kPerThread], vreg[S::kPerThread];
-    auto fetch = [&](int tile) {
+    bool row_ok[S::kPerThread];
+    auto fetch_k = [&](int tile) {
         const int kbase = tile * kBN;
 #pragma unroll
         for (int i = 0; i < S::kPerThread; ++i) {
-            const int idx = tid + i * kThreads;
-            const int r = idx / S::kChunks, c = idx % S::kChunks;
-            if (kbase + r < L) {
-                const size_t g = (size_t)(kbase + r) * D + c * 8;
-                kreg[i] = ldg16(kg + g);
-                vreg[i] = ldg16(vg + g);
-            } else {
-                kreg[i] = u32x4{0, 0, 0, 0};
-                vreg[i] = u32x4{0, 0, 0, 0};
-            }
+            const int row = kbase + st_row + i * S::kRowsPerPass;
+            row_ok[i] = row < L;
+            kreg[i] = ldg16(k + head_off + (size_t)(row_ok[i] ? row : 0) * D);
         }
     };
-    auto stash = [&](int buf) {
+    auto fetch_v = [&](int tile) {
+        const int kbase = tile * kBN;
 #pragma unroll
         for (int i = 0; i < S::kPerThread; ++i) {
-            const int idx = tid + i * kThreads;
-            const int r = idx / S::kChunks, c = idx % S::kChunks;
-            const int o = lds_offset<D>(r, c);
-            *reinterpret_cast<u32x4*>(&lds[buf][0][o]) = kreg[i];
-            *reinterpret_cast<u32x4*>(&lds[buf][1][o]) = vreg[i];
+            const int row = kbase + st_row + i * S::kRowsPerPass;
+            vreg[i] = ldg16(v + head_off + (size_t)(row < L ? row : 0) * D);
         }
     };
+    auto stash = [&](int tile) {
+        uint16_t* dk = lds_k[tile & 1] + st_row * S::kStrideK + st_col;
+        uint16_t* dv = lds_v[tile % 3] + st_row * S::kStrideV + st_col;
+        const u32x4 z = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < S::kPerThread; ++i) {
+            *reinterpret_cast<u32x4*>(dk + i * S::kRowsPerPass * S::kStrideK) = row_ok[i] ? kreg[i] : z;
+            *reinterpret_cast<u32x4*>(dv + i * S::kRowsPerPass * S::kStrideV) = row_ok[i] ? vreg[i] : z;
+        }
+    };
+
+    // Per-lane LDS read bases (element offsets within a slot).
+    //  K operand of S^T: row 32*kb + lane%32, features 16*ks + 8*(lane/32).
+    const int k_rd = (lane & 31) * S::kStrideK + half * 8;
+    //  V^T operand via ds_read_b64_tr_b16: within each 16-lane group, source
+    //  lane i reads features col0 + 4*(i%4) .. +3 of key row key0 + i/4, and
+    //  result lane n then holds V[key0 + 0..3][col0 + n].  Lanes of the
+    //  second half take keys 4..7 (and 12..15) of each 16-key step, which
+    //  matches the keys their P^T fragment holds.
+    const int n16 = lane & 15;
+    const int v_rd = (4 * half + (n16 >> 2)) * S::kStrideV + 16 * ((lane >> 4) & 1) + 4 * (n16 & 3);
 
     f32x16 oacc[S::kDBlocks];
 #pragma unroll
     for (int db = 0; db < S::kDBlocks; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
-    float m_run = -INFINITY;  // running maximum of raw logits (this lane's query)
+    float m_run = -INFINITY;  // reference maximum of raw logits (this lane's query)
     float l_run = 0.0f;       // this lane's share of the normaliser
+    f32x16 sacc[2];           // S^T of the tile scored last (two 32-key blocks)
 
-    fetch(0);
-    stash(0);
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        const int kbase = t * kBN;
-        if (t + 1 < ntiles) fetch(t + 1);
-
-        if (kbase < kv_hi_w) {
-            const uint16_t* kl = lds[buf][0];
-            const uint16_t* vl = lds[buf][1];
-
-            // ---- S^T = K Q^T: two 32-key blocks
-            f32x16 sacc[2];
+    // ---- S^T(tile) = K Q^T: two 32-key blocks, their MFMA chains
+    // interleaved; K operands are requested kAheadK k-steps ahead of use, so
+    // LDS latency hides behind the MFMAs already issued.
+    auto qk = [&](int tile) {
+        constexpr int kAheadK = 3;
+        const uint16_t* kl = lds_k[tile & 1] + k_rd;
+        u32x4 ka[kAheadK + 1][2];
+        auto kread = [&](int ks) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < 2; ++kb)
+                ka[ks % (kAheadK + 1)][kb] =
+                    *reinterpret_cast<const u32x4*>(kl + kb * 32 * S::kStrideK + ks * 16);
+        };
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
-                const int row = kb * 32 + (lane & 31);
+        for (int ks = 0; ks < kAheadK; ++ks) kread(ks);
 #pragma unroll
-                for (int ks = 0; ks < S::kKSteps; ++ks) {
-                    const u32x4 a =
-                        *reinterpret_cast<const u32x4*>(kl + lds_offset<D>(row, 2 * ks + half));
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a),
-                                                                       as_bf16x8(qf[ks]),
-                                                                       sacc[kb], 0, 0, 0);
-                }
-            }
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+        pin_schedule();
+#pragma unroll
+        for (int ks = 0; ks < S::kKSteps; ++ks) {
+            if (ks + kAheadK < S::kKSteps) kread(ks + kAheadK);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(ka[ks % (kAheadK + 1)][kb]), as_bf16x8(qf[ks]), sacc[kb], 0, 0, 0);
+        }
+    };
 
-            // ---- mask (diagonal / length tiles only)
-            if (kbase + kBN > kfull_w) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int j = kbase + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                        const bool vis = j < L && (!causal || j <= p);
-                        if (!vis) sacc[kb][r] = -INFINITY;
-                    }
-            }
-
-            // ---- online softmax, base 2
-            float mx = -INFINITY;
+    // ---- mask (tiles cutting the diagonal or the valid length), then the
+    // online-softmax reference update.  A row's reference maximum moves only
+    // when its tile maximum exceeds it by more than kRescaleLog2 (log2
+    // units); otherwise the tile is exponentiated against the old reference,
+    // so P stays below 2^kRescaleLog2 and the result is unchanged (weights and
+    // normaliser share one reference).  The decision is per row -- a row that
+    // does not move multiplies by exactly 1 -- so each row's arithmetic
+    // depends on its own keys only; the wave merely skips the multiplies when
+    // no row moves.  Runs after every P V MFMA of the previous tile.
+    auto mask_and_reference = [&](int tile) {
+        const int kbase = tile * kBN;
+        if (kbase + kBN > kfull_w) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-            mx = halves_max(mx);
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-            const float alpha = fast_exp2((m_run - m_use) * scale_log2);
-            const float mc = m_use * scale_log2;
+                for (int r = 0; r < 16; ++r) {
+                    const int j = kbase + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    const bool vis = j < L && (!causal || j <= p);
+                    if (!vis) sacc[kb][r] = -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        mx = halves_max(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const bool grow = (m_new - m_run) * scale_log2 > kRescaleLog2;  // true if m_run = -inf
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float alpha = grow ? fast_exp2((m_run - m_new) * scale_log2) : 1.0f;
+            m_run = grow ? m_new : m_run;
             l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < S::kDBlocks; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            m_run = m_new;
-
-            u32x4 pf[2][2];  // P^T fragments: [key block][16-key step]
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                float pr[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    pr[r] = fast_exp2(fmaf(sacc[kb][r], scale_log2, -mc));
-                    l_run += pr[r];
-                }
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        pf[kb][h2][i] = pack_bf16(pr[8 * h2 + 2 * i], pr[8 * h2 + 2 * i + 1]);
-            }
-
-            // ---- O^T += V^T P^T
-            const int g16 = lane >> 4;   // 16-lane group
-            const int n16 = lane & 15;
-#pragma unroll
-            for (int db = 0; db < S::kDBlocks; ++db) {
-                const int col = db * 32 + 16 * (g16 & 1) + 4 * (n16 & 3);
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        const int r1 = kb * 32 + h2 * 16 + 4 * half + (n16 >> 2);
-                        const int r2 = r1 + 8;
-                        const uint16_t* a1 = vl + lds_offset<D>(r1, col >> 3) + (col & 7);
-                        const uint16_t* a2 = vl + lds_offset<D>(r2, col >> 3) + (col & 7);
-                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (TSDA_LDS i16x4*)(a1));
-                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (TSDA_LDS i16x4*)(a2));
-                        u32x4 a;
-                        a[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-                        a[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-                        a[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-                        a[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            as_bf16x8(a), as_bf16x8(pf[kb][h2]), oacc[db], 0, 0, 0);
-                    }
-            }
         }
+    };
 
-        if (t + 1 < ntiles) stash(buf ^ 1);
+    // ---- P = 2^(s*scale*log2e - reference) packed to bf16 P^T fragments
+    // (the normaliser sums the bf16 weights the mixture uses), then
+    // O^T += V^T(tile) P^T, output blocks innermost (consecutive MFMAs
+    // independent).  The transposing V reads run kAhead MFMAs ahead of use,
+    // the first kAhead issued before the exponentials.
+    auto mix = [&](int tile) {
+        constexpr int kHalf = 2 * S::kDBlocks;  // MFMAs per 32-key block
+        const uint16_t* vl = lds_v[tile % 3] + v_rd;
+        auto vread = [&](int st, i16x4 (&dst)[2]) {
+            const int db = st % S::kDBlocks, kk = st / S::kDBlocks;  // kk = 2*kb + h2
+            const uint16_t* a1 = vl + kk * 16 * S::kStrideV + db * 32;
+            dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TSDA_LDS i16x4*)(a1));
+            dst[1] =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((TSDA_LDS i16x4*)(a1 + 8 * S::kStrideV));
+        };
+        auto vmfma = [&](int st, const i16x4 (&src)[2], const u32x4& p) {
+            const int db = st % S::kDBlocks;
+            u32x4 a;
+            a[0] = (uint32_t)(uint16_t)src[0][0] | ((uint32_t)(uint16_t)src[0][1] << 16);
+            a[1] = (uint32_t)(uint16_t)src[0][2] | ((uint32_t)(uint16_t)src[0][3] << 16);
+            a[2] = (uint32_t)(uint16_t)src[1][0] | ((uint32_t)(uint16_t)src[1][1] << 16);
+            a[3] = (uint32_t)(uint16_t)src[1][2] | ((uint32_t)(uint16_t)src[1][3] << 16);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(p),
+                                                               oacc[db], 0, 0, 0);
+        };
+        const float mc = m_run == -INFINITY ? 0.0f : m_run * scale_log2;
+        auto exponentiate = [&](int kb, u32x4 (&pf)[2]) {
+            float pr[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(fmaf(sacc[kb][r], scale_log2, -mc));
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pf[h2][i] = pack_bf16(pr[8 * h2 + 2 * i], pr[8 * h2 + 2 * i + 1]);
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pf[h2][i]),
+                                                            as_bf16x2(0x3F803F80u), l_run, false);
+                }
+        };
+        constexpr int kAhead = 4;  // V operands in flight ahead of their MFMA
+        constexpr int kPV = 2 * kHalf;
+        i16x4 vr[kAhead + 1][2];
+        u32x4 pf[2][2];
+#pragma unroll
+        for (int st = 0; st < kAhead; ++st) vread(st, vr[st]);
+        pin_schedule();
+        exponentiate(0, pf[0]);
+        exponentiate(1, pf[1]);
+#pragma unroll
+        for (int st = 0; st < kPV; ++st) {
+            if (st + kAhead < kPV) vread(st + kAhead, vr[(st + kAhead) % (kAhead + 1)]);
+            vmfma(st, vr[st % (kAhead + 1)], pf[st / kHalf][(st % kHalf) / S::kDBlocks]);
+        }
+    };
+
+    fetch_k(0);
+    fetch_v(0);
+    stash(0);
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        // Next tile's loads are issued between this wave's compute phases,
+        // so the memory pipeline drains while the other wave on the SIMD
+        // computes (issued all at once they stall every wave).
+        const bool more = t + 1 < ntiles;
+        if (!group_b) {
+            if (t < ntiles_w) qk(t);
+            if (more) fetch_k(t + 1);
+            if (t < ntiles_w) mask_and_reference(t);
+            if (more) fetch_v(t + 1);
+            if (t < ntiles_w) mix(t);
+        } else {
+            if (t >= 1 && t - 1 < ntiles_w) mix(t - 1);
+            if (more) fetch_k(t + 1);
+            if (t < ntiles_w) qk(t);
+            if (more) fetch_v(t + 1);
+            if (t < ntiles_w) mask_and_reference(t);
+        }
+        if (t + 1 < ntiles) stash(t + 1);
         __syncthreads();
     }
+    // group B: the last tile it scored is mixed after the loop when it was
+    // the block's last tile
+    if (group_b && ntiles_w > 0 && ntiles_w == ntiles) mix(ntiles_w - 1);
 
     // ---- epilogue: out = acc / l, rows past n_b are zero
     if (qi < Sq) {
