@@ -8,7 +8,8 @@
 //     row (d bf16 = 2d bytes) is read by d/8 lanes with one 16-byte load
 //     each, so every wave-wide load covers whole contiguous rows.  Logits use
 //     v_dot2 on the raw bf16 pairs (exact products, fp32 sums), reduced over
-//     the row's lanes with DPP.  Each lane group keeps a running maximum m,
+//     the row's lanes with DPP.  K and V are read once, with non-temporal
+//     loads; each lane keeps two steps of 4 rows in flight.  Each lane group keeps a running maximum m,
 //     normaliser l and an fp32 accumulator for its 8 columns (the online
 //     softmax recurrence); the block merges its groups in LDS and writes one
 //     (m, l, acc[d]) partial.  Keys past the valid length are never loaded.
@@ -25,7 +26,7 @@ namespace tsda {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 4;  // key rows per lane per step (two steps in flight)
 
 template <int D>
 __global__ __launch_bounds__(256) void decode_partial_kernel(
@@ -63,19 +64,21 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
 
-    for (int base = k0; base < k1; base += SLOTS * kUnroll) {
-        u32x4 kr[kUnroll], vr[kUnroll];
+    // Rows of one step: base + u*SLOTS + slot for u < kUnroll.  Loads are
+    // branch-free (a row past k1 is redirected to row k0, which is valid, and
+    // its logit is masked), so the next step's loads stay in flight while the
+    // current step is computed.
+    constexpr int kStep = SLOTS * kUnroll;
+    auto load = [&](int base, u32x4 (&kr)[kUnroll], u32x4 (&vr)[kUnroll]) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int j = base + u * SLOTS + slot;
-            if (j < k1) {
-                kr[u] = ldg16(kp + (size_t)j * D);
-                vr[u] = ldg16(vp + (size_t)j * D);
-            } else {
-                kr[u] = u32x4{0, 0, 0, 0};
-                vr[u] = u32x4{0, 0, 0, 0};
-            }
+            const size_t row = (size_t)(j < k1 ? j : k0) * D;
+            kr[u] = ldg16_stream(kp + row);
+            vr[u] = ldg16_stream(vp + row);
         }
+    };
+    auto consume = [&](int base, const u32x4 (&kr)[kUnroll], const u32x4 (&vr)[kUnroll]) {
         float s[kUnroll];
         float mx = -INFINITY;
 #pragma unroll
@@ -107,6 +110,15 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
             }
         }
         m = m_new;
+    };
+    u32x4 ka[kUnroll], va[kUnroll], kb[kUnroll], vb[kUnroll];
+    load(k0, ka, va);
+    for (int base = k0; base < k1; base += 2 * kStep) {
+        if (base + kStep < k1) load(base + kStep, kb, vb);
+        consume(base, ka, va);
+        if (base + kStep >= k1) break;
+        if (base + 2 * kStep < k1) load(base + 2 * kStep, ka, va);
+        consume(base + kStep, kb, vb);
     }
 
     if (part == 0) {
@@ -167,8 +179,12 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 DecodePlan decode_plan(int B, int H, int Skv) {
-    int chunk = 512;
-    while (chunk > 64 && (long)B * H * ((Skv + chunk - 1) / chunk) < 8192) chunk /= 2;
+    // Splits of 128 keys (64 KiB of K+V at d = 128) measured fastest on the
+    // ragged decode workload: many short units spread the reads of the valid
+    // prefixes of all caches evenly over the memory system.  Smaller problems
+    // split finer so the grid still fills the GPU.
+    int chunk = 128;
+    if ((long)B * H * ((Skv + chunk - 1) / chunk) < 8192) chunk = 64;
     return DecodePlan{chunk, (Skv + chunk - 1) / chunk};
 }
 
