@@ -148,30 +148,51 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 }
 
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(
+__global__ __launch_bounds__(2 * D) void decode_combine_kernel(
     const int32_t* __restrict__ kv_lens, int H, int Skv, int chunk, int nsplit,
     const float* __restrict__ ws_acc, const float* __restrict__ ws_ml, uint16_t* __restrict__ out) {
+    // Two halves of the block each merge every other split of one (b, h)
+    // (independent loads, unrolled), then one thread per column merges the
+    // two halves.
+    __shared__ float s_m[2], s_l[2];
+    __shared__ float s_a[2][D];
     const int bh = blockIdx.x;
     const int b = bh / H;
-    const int t = threadIdx.x;
+    const int t = threadIdx.x % D;
+    const int h2 = threadIdx.x / D;
     const int L = valid_length(kv_lens, b, Skv);
     uint16_t* o = out + (size_t)bh * D;
     if (L == 0) {
-        o[t] = 0;
+        if (h2 == 0) o[t] = 0;
         return;
     }
     const int nv = (L + chunk - 1) / chunk;
     const float* ml = ws_ml + (size_t)bh * nsplit * 2;
     const float* ac = ws_acc + (size_t)bh * nsplit * D;
     float M = -INFINITY;
-    for (int s = 0; s < nv; ++s) M = fmaxf(M, ml[2 * s]);
+#pragma unroll 4
+    for (int s = h2; s < nv; s += 2) M = fmaxf(M, ml[2 * s]);
     float lt = 0.0f, at = 0.0f;
-    for (int s = 0; s < nv; ++s) {
+#pragma unroll 4
+    for (int s = h2; s < nv; s += 2) {
         const float w = fast_exp2(ml[2 * s] - M);
         lt = fmaf(ml[2 * s + 1], w, lt);
         at = fmaf(ac[(size_t)s * D + t], w, at);
     }
-    o[t] = to_bf16(at / lt);
+    if (t == 0) {
+        s_m[h2] = M;
+        s_l[h2] = lt;
+    }
+    s_a[h2][t] = at;
+    __syncthreads();
+    if (h2 == 0) {
+        // a half with no split has M = -inf and contributes nothing
+        const float Mt = fmaxf(s_m[0], s_m[1]);
+        const float w0 = s_m[0] == -INFINITY ? 0.0f : fast_exp2(s_m[0] - Mt);
+        const float w1 = s_m[1] == -INFINITY ? 0.0f : fast_exp2(s_m[1] - Mt);
+        const float l = s_l[0] * w0 + s_l[1] * w1;
+        o[t] = to_bf16((s_a[0][t] * w0 + s_a[1][t] * w1) / l);
+    }
 }
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -222,10 +243,10 @@ hipError_t launch_decode_bf16(const LaunchArgs& a) {
     if (t) t->begin(kDecodeCombineBf16, a.stream);
     const unsigned pairs = (unsigned)((size_t)a.B * a.H);
     if (a.d == 128)
-        hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(pairs), dim3(128), 0, a.stream,
+        hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(pairs), dim3(256), 0, a.stream,
                            a.kv_lens, a.H, a.Skv, p.chunk, p.nsplit, ws_acc, ws_ml, o);
     else
-        hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(pairs), dim3(64), 0, a.stream,
+        hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(pairs), dim3(128), 0, a.stream,
                            a.kv_lens, a.H, a.Skv, p.chunk, p.nsplit, ws_acc, ws_ml, o);
     e = hipGetLastError();
     if (t) t->end(kDecodeCombineBf16, a.stream);
