@@ -14,7 +14,8 @@
  *
  * Mask M (the readings taken where the pages leave the rule open):
  *   - kv_lens[b] = L_b is the valid length of sequence b (right padding,
- *     as in the kube-dojo page's padding-mask example); keys j >= L_b are
+ *     as in the padding-mask example of "Attention from Scratch",
+ *     KubeDojo module 1.4.3, Part 3); keys j >= L_b are
  *     invisible to every query.  Values outside [0, Skv] are clamped to it.
  *     kv_lens == NULL means L_b = Skv for every b.
  *   - The queries of sequence b are its last n_b = min(Sq, L_b) valid

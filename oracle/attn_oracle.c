@@ -13,7 +13,7 @@
  *     (M_ij = 0 for j <= i and -inf for j > i, added before the softmax);
  *   - "Attention from First Principles", section 4 "Tiny example" (scores,
  *     scale, causal mask, row softmax, multiply by V, in that order);
- *   - "Attention from scratch" (kube-dojo module 1.4.3), Part 2's teaching
+ *   - "Attention from Scratch" (KubeDojo module 1.4.3), Part 2's teaching
  *     implementation (forbidden logits get exactly zero probability, the
  *     softmax runs over the key axis, d_v may differ from d_k) and Part 3
  *     (causal and padding allowed-masks combined by logical AND).
@@ -30,7 +30,7 @@
  *   - query rows i >= n_b are padding and their output is exactly 0, and so
  *     is any row with no visible key;
  *   - the softmax subtracts the row maximum before exponentiating, the stable
- *     form the kube-dojo page's debugging section asks for.
+ *     form that page's Part 7 (debugging) asks for.
  *
  * Inputs may be float64, float32 or bfloat16 bit patterns; each element is
  * widened exactly to double before any arithmetic.  All arithmetic is in

@@ -40,7 +40,7 @@ def pin_p2_causal_example(attn):
 
 
 def pin_p3_unmasked_example(attn):
-    """kube-dojo "Attention from scratch", Part 2 worked example (d_v != d_k)."""
+    """KubeDojo "Attention from Scratch" (module 1.4.3), Part 2 worked example (d_v != d_k)."""
     _fixture_case(attn, "p3_unmasked_3tok_dk4_dv2.txt")
 
 
@@ -71,7 +71,8 @@ def _visible(Sq, Skv, causal, L):
 def pin_row_sums_and_forbidden_zero(attn):
     """Rows of weights sum to one over visible keys, and every forbidden entry
     (future key, pad key, pad query row) is exactly zero -- the invariants the
-    "Attention from scratch" pages assert (rows sum to one; weights for
+    "Attention from scratch" pages assert (Open LLM Engineering's readable model
+    and KubeDojo Part 7: rows sum to one; weights for
     positions after the first are all zero in row 0; upper triangle zero)."""
     for ci, (B, H, Sq, Skv, d, causal, lens) in enumerate(_mixed_cases()):
         q, k, v = _rand(ci, B, H, Sq, d), _rand(ci + 50, B, H, Skv, d), _rand(ci + 90, B, H, Skv, d)
@@ -105,7 +106,8 @@ def pin_future_invariance(attn):
 def pin_zero_query_uniform(attn):
     """With Q = 0 every visible key gets the same weight, so each output row is
     the plain mean of its visible value rows (the all-zero exercise on the
-    "Attention from scratch" page); np.mean is the independent reference."""
+    Open LLM Engineering "Attention from scratch" exercises); np.mean is the
+    independent reference."""
     B, H, S, d = 2, 1, 6, 3
     q = np.zeros((B, H, S, d))
     k, v = _rand(4, B, H, S, d), _rand(5, B, H, S, d)
@@ -170,7 +172,7 @@ def pin_two_key_logistic(attn):
 
 def pin_matches_torch_sdpa(attn):
     """Agreement with an independent library routine: torch's CPU
-    scaled_dot_product_attention in float64 (the comparison the kube-dojo
+    scaled_dot_product_attention in float64 (the comparison the KubeDojo
     page's test script makes), with the boolean allowed-mask built from the
     causal and padding rules."""
     import torch

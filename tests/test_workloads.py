@@ -50,7 +50,7 @@ def test_lengths_are_seeded():
 
 
 def test_dot_product_variance_and_scale():
-    # kube-dojo "Attention from scratch": with unit-variance entries the dot
+    # KubeDojo "Attention from Scratch" (module 1.4.3), Part 2: with unit-variance entries the dot
     # product's variance is about d_k (64) and about 1 after the 1/sqrt(d_k)
     # scale; and "Scaled dot-product attention with masking" gives the scale
     # at d_k = 128 as about 0.088.

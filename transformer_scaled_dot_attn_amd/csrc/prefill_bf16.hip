@@ -10,6 +10,23 @@
 // 32w..32w+31, and two waves share each SIMD.  The block walks the keys in
 // tiles of 64, staging K and V tiles in LDS rings (K: 2 slots, V: 3 slots).
 //
+// Transposed products.  Each wave computes S^T = K Q^T (K from LDS as the A
+// operand, Q^T held in registers as the B operand).  In the accumulator of
+// a 32x32 MFMA a lane holds one column, so every lane owns ONE query and 16
+// of its keys; lane l and lane l^32 hold the other 16.  Row maximum and row
+// sum are therefore lane-local plus one permlane32 swap.  The mixture is
+// computed as O^T = V^T P^T: P^T is the B operand straight from the score
+// registers (cast to bf16, as the readable model of "Attention from
+// scratch", Open LLM Engineering, casts its fp32 softmax weights before
+// multiplying by V), and V^T is read from the row-major V tile with
+// ds_read_b64_tr_b16 transposing loads.  The output accumulator again has
+// one query per lane, so the online-softmax rescale is a per-lane scalar
+// multiply.
+//
+// Staging.  All 512 threads load the next K and V tile with branch-free
+// 16-byte loads issued between compute phases and write them to LDS at the
+// end of the iteration, one barrier per tile.
+//
 // Ping-pong.  Within a wave the work of a tile is a chain: Q K^T on the
 // matrix cores, then the softmax on the vector ALU, then P V on the matrix
 // cores.  Waves 0-3 (group A) run that chain for tile t in iteration t;

@@ -51,7 +51,7 @@ class Workload:
 
 # The pages' shapes: d_model 4096 = 32 heads of 128 ("Attention from First
 # Principles", section 5; "Scaled dot-product attention with masking",
-# "Multi-head attention"), d_k = 64 (kube-dojo module, the scale-factor
+# "Multi-head attention"), d_k = 64 ("Attention from Scratch", KubeDojo module 1.4.3, the scale-factor
 # discussion), prefill S = 2048 against decode over a KV cache ("Attention from
 # First Principles", section 6), and small seeded randn fixtures.
 WORKLOADS = {
