@@ -8,7 +8,7 @@
 //
 // Block = 8 wavefronts = 256 query rows of one (b, h); wave w owns rows
 // 32w..32w+31, and two waves share each SIMD.  The block walks the keys in
-// tiles of 64, staging K and V tiles in LDS rings (K: 2 slots, V: 3 slots).
+// tiles of 64, staging K and V tiles in two-slot LDS rings.
 //
 // Transposed products.  Each wave computes S^T = K Q^T (K from LDS as the A
 // operand, Q^T held in registers as the B operand).  In the accumulator of
@@ -23,18 +23,18 @@
 // one query per lane, so the online-softmax rescale is a per-lane scalar
 // multiply.
 //
-// Staging.  All 512 threads load the next K and V tile with branch-free
-// 16-byte loads issued between compute phases and write them to LDS at the
+// Staging.  All 512 threads load the next K and V tiles with branch-free
+// 16-byte loads issued between compute blocks and write them to LDS at the
 // end of the iteration, one barrier per tile.
 //
-// Ping-pong.  Within a wave the work of a tile is a chain: Q K^T on the
-// matrix cores, then the softmax on the vector ALU, then P V on the matrix
-// cores.  Waves 0-3 (group A) run that chain for tile t in iteration t;
-// waves 4-7 (group B) run the softmax and P V of tile t-1 and then Q K^T of
-// tile t.  After each barrier the two waves sharing a SIMD therefore start
-// in complementary phases -- one on the matrix cores while the other
-// exponentiates -- instead of stalling on the same dependency at the same
-// time.
+// Software pipeline.  Within a wave the work of a tile is a chain: Q K^T on
+// the matrix cores, then the softmax on the vector ALU, then P V on the
+// matrix cores.  Each iteration t overlaps two tiles: the MFMAs of
+// S^T(t+1) = K(t+1) Q^T are interleaved with the exponentials of tile t,
+// and the P V MFMAs of tile t with the row-maximum scan of tile t+1.  The
+// scores of two tiles are therefore live at once (two register sets that
+// swap roles every iteration), and the vector work runs while the matrix
+// cores are busy instead of between MFMA phases.
 //
 // Masking.  Key j is visible to the query at absolute position p iff
 // j < L_b and (not causal or j <= p).  Tiles past the block's last visible
@@ -96,13 +96,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     int causal, int nqt) {
     using S = Shape<D>;
     __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][S::kTileK];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v[3][S::kTileV];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][S::kTileV];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int half = lane >> 5;
-    const bool group_b = wave >= kWaves / 2;
 
     const int bid = blockIdx.x;
     const int qt = nqt - 1 - bid / BH;
@@ -151,40 +150,38 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 
     // ---- tile staging: thread t moves 16-byte chunks t + 512 i of the
     // row-major tile, so consecutive threads read consecutive global bytes.
-    // The loads are branch-free, so they stay in flight through the tile's
-    // compute (no wait until the stash): a row at or past L is redirected to row 0 of the same head
-    // (always valid) and zeroed when stashed, so padded rows are never read.
+    // The loads are branch-free, so they stay in flight through the compute
+    // (no wait until the stash): a row at or past L is redirected to row 0 of
+    // the same head (always valid) and zeroed when stashed, so padded rows
+    // are never read.  K runs two tiles ahead of the scores, V one tile.
     const int st_row = tid / S::kChunks;
     const int st_col = (tid % S::kChunks) * 8;
     const size_t head_off = (size_t)bh * Skv * D + st_col;
     u32x4 kreg[S::kPerThread], vreg[S::kPerThread];
-    bool row_ok[S::kPerThread];
-    auto fetch_k = [&](int tile) {
+    bool kok[S::kPerThread], vok[S::kPerThread];
+    auto fetch = [&](const uint16_t* __restrict__ src, int tile, u32x4 (&dst)[S::kPerThread],
+                     bool (&ok)[S::kPerThread]) {
         const int kbase = tile * kBN;
 #pragma unroll
         for (int i = 0; i < S::kPerThread; ++i) {
             const int row = kbase + st_row + i * S::kRowsPerPass;
-            row_ok[i] = row < L;
-            kreg[i] = ldg16(k + head_off + (size_t)(row_ok[i] ? row : 0) * D);
+            ok[i] = row < L;
+            dst[i] = ldg16(src + head_off + (size_t)(ok[i] ? row : 0) * D);
         }
     };
-    auto fetch_v = [&](int tile) {
-        const int kbase = tile * kBN;
-#pragma unroll
-        for (int i = 0; i < S::kPerThread; ++i) {
-            const int row = kbase + st_row + i * S::kRowsPerPass;
-            vreg[i] = ldg16(v + head_off + (size_t)(row < L ? row : 0) * D);
-        }
-    };
-    auto stash = [&](int tile) {
+    auto stash_k = [&](int tile) {
         uint16_t* dk = lds_k[tile & 1] + st_row * S::kStrideK + st_col;
-        uint16_t* dv = lds_v[tile % 3] + st_row * S::kStrideV + st_col;
         const u32x4 z = {0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < S::kPerThread; ++i) {
-            *reinterpret_cast<u32x4*>(dk + i * S::kRowsPerPass * S::kStrideK) = row_ok[i] ? kreg[i] : z;
-            *reinterpret_cast<u32x4*>(dv + i * S::kRowsPerPass * S::kStrideV) = row_ok[i] ? vreg[i] : z;
-        }
+        for (int i = 0; i < S::kPerThread; ++i)
+            *reinterpret_cast<u32x4*>(dk + i * S::kRowsPerPass * S::kStrideK) = kok[i] ? kreg[i] : z;
+    };
+    auto stash_v = [&](int tile) {
+        uint16_t* dv = lds_v[tile & 1] + st_row * S::kStrideV + st_col;
+        const u32x4 z = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < S::kPerThread; ++i)
+            *reinterpret_cast<u32x4*>(dv + i * S::kRowsPerPass * S::kStrideV) = vok[i] ? vreg[i] : z;
     };
 
     // Per-lane LDS read bases (element offsets within a slot).
@@ -205,48 +202,74 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
     float m_run = -INFINITY;  // reference maximum of raw logits (this lane's query)
     float l_run = 0.0f;       // this lane's share of the normaliser
-    f32x16 sacc[2];           // S^T of the tile scored last (two 32-key blocks)
+    f32x16 s0[2], s1[2];      // S^T of two consecutive tiles (two 32-key blocks each)
+    u32x4 pf[2][2];           // P^T fragments of the tile being mixed
 
-    // ---- S^T(tile) = K Q^T: two 32-key blocks, their MFMA chains
-    // interleaved; K operands are requested kAheadK k-steps ahead of use, so
-    // LDS latency hides behind the MFMAs already issued.
-    auto qk = [&](int tile) {
-        constexpr int kAheadK = 3;
+    constexpr int kQK = 2 * S::kKSteps;       // MFMAs of S^T per tile
+    constexpr int kHalf = 2 * S::kDBlocks;    // P V MFMAs per 32-key block
+    constexpr int kPV = 2 * kHalf;            // P V MFMAs per tile
+    constexpr int kAheadK = 2;                // K operand k-steps in flight
+    constexpr int kAheadV = 3;                // V operands in flight
+
+    // ---- pieces of S^T(tile) = K Q^T: two 32-key blocks, chains interleaved
+    auto kread = [&](const uint16_t* kl, int ks, u32x4 (&dst)[2]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            dst[kb] = *reinterpret_cast<const u32x4*>(kl + kb * 32 * S::kStrideK + ks * 16);
+    };
+    // ---- one pair of weights of P = 2^(s*scale*log2e - reference), packed to
+    // bf16; the normaliser sums the bf16 weights the mixture uses, in the
+    // fixed order kb, h2, i.
+    auto exp_pair = [&](const f32x16 (&sc)[2], int e, float mc) {
+        const int kb = e >> 3, h2 = (e >> 2) & 1, i = e & 3;
+        const float a0 = fast_exp2(fmaf(sc[kb][8 * h2 + 2 * i], scale_log2, -mc));
+        const float a1 = fast_exp2(fmaf(sc[kb][8 * h2 + 2 * i + 1], scale_log2, -mc));
+        pf[kb][h2][i] = pack_bf16(a0, a1);
+        // an empty volatile use keeps the pair where it is issued (under the
+        // MFMAs) instead of letting it sink to the P V block that reads it
+        asm volatile("" : "+v"(pf[kb][h2][i]));
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pf[kb][h2][i]), as_bf16x2(0x3F803F80u),
+                                                l_run, false);
+    };
+    auto ref_log2 = [&]() { return m_run == -INFINITY ? 0.0f : m_run * scale_log2; };
+
+    // S^T(tile) into sn; when sc is given, the 16 weight pairs of the tile
+    // before it are formed under these MFMAs (pairs per MFMA = 16 / kQK).
+    auto score = [&](int tile, f32x16 (&sn)[2], const f32x16 (*sc)[2]) {
         const uint16_t* kl = lds_k[tile & 1] + k_rd;
+        const float mc = ref_log2();
         u32x4 ka[kAheadK + 1][2];
-        auto kread = [&](int ks) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                ka[ks % (kAheadK + 1)][kb] =
-                    *reinterpret_cast<const u32x4*>(kl + kb * 32 * S::kStrideK + ks * 16);
-        };
-#pragma unroll
-        for (int ks = 0; ks < kAheadK; ++ks) kread(ks);
+        for (int ks = 0; ks < kAheadK; ++ks) kread(kl, ks, ka[ks]);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) sn[kb][r] = 0.0f;
         pin_schedule();
 #pragma unroll
         for (int ks = 0; ks < S::kKSteps; ++ks) {
-            if (ks + kAheadK < S::kKSteps) kread(ks + kAheadK);
+            if (ks + kAheadK < S::kKSteps) kread(kl, ks + kAheadK, ka[(ks + kAheadK) % (kAheadK + 1)]);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    as_bf16x8(ka[ks % (kAheadK + 1)][kb]), as_bf16x8(qf[ks]), sacc[kb], 0, 0, 0);
+            for (int kb = 0; kb < 2; ++kb) {
+                sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(ka[ks % (kAheadK + 1)][kb]), as_bf16x8(qf[ks]), sn[kb], 0, 0, 0);
+                if (sc) {
+                    constexpr int kPer = 16 / kQK;
+#pragma unroll
+                    for (int e = 0; e < kPer; ++e) exp_pair(*sc, (2 * ks + kb) * kPer + e, mc);
+                }
+                pin_schedule();
+            }
         }
     };
-
-    // ---- mask (tiles cutting the diagonal or the valid length), then the
-    // online-softmax reference update.  A row's reference maximum moves only
-    // when its tile maximum exceeds it by more than kRescaleLog2 (log2
-    // units); otherwise the tile is exponentiated against the old reference,
-    // so P stays below 2^kRescaleLog2 and the result is unchanged (weights and
-    // normaliser share one reference).  The decision is per row -- a row that
-    // does not move multiplies by exactly 1 -- so each row's arithmetic
-    // depends on its own keys only; the wave merely skips the multiplies when
-    // no row moves.  Runs after every P V MFMA of the previous tile.
-    auto mask_and_reference = [&](int tile) {
+    // weights of a tile with no next tile to score under them
+    auto weigh = [&](const f32x16 (&sc)[2]) {
+        const float mc = ref_log2();
+#pragma unroll
+        for (int e = 0; e < 16; ++e) exp_pair(sc, e, mc);
+    };
+    // per-element mask of S^T(tile) when the tile cuts the diagonal or L
+    auto mask = [&](int tile, f32x16 (&sn)[2]) {
         const int kbase = tile * kBN;
         if (kbase + kBN > kfull_w) {
 #pragma unroll
@@ -255,14 +278,62 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                 for (int r = 0; r < 16; ++r) {
                     const int j = kbase + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
                     const bool vis = j < L && (!causal || j <= p);
-                    if (!vis) sacc[kb][r] = -INFINITY;
+                    if (!vis) sn[kb][r] = -INFINITY;
                 }
         }
+    };
+    // O^T += V^T(tile) P^T, output blocks innermost (consecutive MFMAs
+    // independent); when sn is given, the maximum of the next tile's scores
+    // is scanned under these MFMAs.  Returns that maximum (lane-local).
+    auto mix = [&](int tile, const f32x16 (*sn)[2]) {
+        const uint16_t* vl = lds_v[tile & 1] + v_rd;
+        auto vread = [&](int st, i16x4 (&dst)[2]) {
+            const int db = st % S::kDBlocks, kk = st / S::kDBlocks;  // kk = 2*kb + h2
+            const uint16_t* a1 = vl + kk * 16 * S::kStrideV + db * 32;
+            dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TSDA_LDS i16x4*)(a1));
+            dst[1] =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((TSDA_LDS i16x4*)(a1 + 8 * S::kStrideV));
+        };
+        i16x4 vr[kAheadV + 1][2];
+#pragma unroll
+        for (int st = 0; st < kAheadV; ++st) vread(st, vr[st]);
         float mx = -INFINITY;
+        pin_schedule();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int st = 0; st < kPV; ++st) {
+            if (st + kAheadV < kPV) vread(st + kAheadV, vr[(st + kAheadV) % (kAheadV + 1)]);
+            const i16x4 (&src)[2] = vr[st % (kAheadV + 1)];
+            u32x4 a;
+            a[0] = (uint32_t)(uint16_t)src[0][0] | ((uint32_t)(uint16_t)src[0][1] << 16);
+            a[1] = (uint32_t)(uint16_t)src[0][2] | ((uint32_t)(uint16_t)src[0][3] << 16);
+            a[2] = (uint32_t)(uint16_t)src[1][0] | ((uint32_t)(uint16_t)src[1][1] << 16);
+            a[3] = (uint32_t)(uint16_t)src[1][2] | ((uint32_t)(uint16_t)src[1][3] << 16);
+            const int db = st % S::kDBlocks;
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                as_bf16x8(a), as_bf16x8(pf[st / kHalf][(st % kHalf) / S::kDBlocks]), oacc[db], 0, 0,
+                0);
+            if (sn) {
+                constexpr int kPer = 32 / kPV;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+                for (int e = 0; e < kPer; ++e) {
+                    const int x = st * kPer + e;
+                    mx = fmaxf(mx, (*sn)[x >> 4][x & 15]);
+                }
+            }
+            pin_schedule();
+        }
+        return mx;
+    };
+    // Online-softmax reference update from a tile's maximum.  A row's
+    // reference moves only when the tile maximum exceeds it by more than
+    // kRescaleLog2 (log2 units); otherwise the tile is exponentiated against
+    // the old reference, so P stays below 2^kRescaleLog2 and the result is
+    // unchanged (weights and normaliser share one reference).  The decision
+    // is per row -- a row that does not move multiplies by exactly 1 -- so
+    // each row's arithmetic depends on its own keys only; the wave merely
+    // skips the multiplies when no row moves.  Runs after every P V MFMA of
+    // the tiles before.
+    auto reference = [&](float mx) {
         mx = halves_max(mx);
         const float m_new = fmaxf(m_run, mx);
         const bool grow = (m_new - m_run) * scale_log2 > kRescaleLog2;  // true if m_run = -inf
@@ -276,91 +347,62 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                 for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
     };
-
-    // ---- P = 2^(s*scale*log2e - reference) packed to bf16 P^T fragments
-    // (the normaliser sums the bf16 weights the mixture uses), then
-    // O^T += V^T(tile) P^T, output blocks innermost (consecutive MFMAs
-    // independent).  The transposing V reads run kAhead MFMAs ahead of use,
-    // the first kAhead issued before the exponentials.
-    auto mix = [&](int tile) {
-        constexpr int kHalf = 2 * S::kDBlocks;  // MFMAs per 32-key block
-        const uint16_t* vl = lds_v[tile % 3] + v_rd;
-        auto vread = [&](int st, i16x4 (&dst)[2]) {
-            const int db = st % S::kDBlocks, kk = st / S::kDBlocks;  // kk = 2*kb + h2
-            const uint16_t* a1 = vl + kk * 16 * S::kStrideV + db * 32;
-            dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TSDA_LDS i16x4*)(a1));
-            dst[1] =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((TSDA_LDS i16x4*)(a1 + 8 * S::kStrideV));
-        };
-        auto vmfma = [&](int st, const i16x4 (&src)[2], const u32x4& p) {
-            const int db = st % S::kDBlocks;
-            u32x4 a;
-            a[0] = (uint32_t)(uint16_t)src[0][0] | ((uint32_t)(uint16_t)src[0][1] << 16);
-            a[1] = (uint32_t)(uint16_t)src[0][2] | ((uint32_t)(uint16_t)src[0][3] << 16);
-            a[2] = (uint32_t)(uint16_t)src[1][0] | ((uint32_t)(uint16_t)src[1][1] << 16);
-            a[3] = (uint32_t)(uint16_t)src[1][2] | ((uint32_t)(uint16_t)src[1][3] << 16);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(p),
-                                                               oacc[db], 0, 0, 0);
-        };
-        const float mc = m_run == -INFINITY ? 0.0f : m_run * scale_log2;
-        auto exponentiate = [&](int kb, u32x4 (&pf)[2]) {
-            float pr[16];
+    auto scan = [&](const f32x16 (&sn)[2]) {
+        float mx = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(fmaf(sacc[kb][r], scale_log2, -mc));
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pf[h2][i] = pack_bf16(pr[8 * h2 + 2 * i], pr[8 * h2 + 2 * i + 1]);
-                    l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pf[h2][i]),
-                                                            as_bf16x2(0x3F803F80u), l_run, false);
-                }
-        };
-        constexpr int kAhead = 4;  // V operands in flight ahead of their MFMA
-        constexpr int kPV = 2 * kHalf;
-        i16x4 vr[kAhead + 1][2];
-        u32x4 pf[2][2];
-#pragma unroll
-        for (int st = 0; st < kAhead; ++st) vread(st, vr[st]);
-        pin_schedule();
-        exponentiate(0, pf[0]);
-        exponentiate(1, pf[1]);
-#pragma unroll
-        for (int st = 0; st < kPV; ++st) {
-            if (st + kAhead < kPV) vread(st + kAhead, vr[(st + kAhead) % (kAhead + 1)]);
-            vmfma(st, vr[st % (kAhead + 1)], pf[st / kHalf][(st % kHalf) / S::kDBlocks]);
-        }
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sn[kb][r]);
+        return mx;
     };
 
-    fetch_k(0);
-    fetch_v(0);
-    stash(0);
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        // Next tile's loads are issued between this wave's compute phases,
-        // so the memory pipeline drains while the other wave on the SIMD
-        // computes (issued all at once they stall every wave).
-        const bool more = t + 1 < ntiles;
-        if (!group_b) {
-            if (t < ntiles_w) qk(t);
-            if (more) fetch_k(t + 1);
-            if (t < ntiles_w) mask_and_reference(t);
-            if (more) fetch_v(t + 1);
-            if (t < ntiles_w) mix(t);
+    // One iteration: tile t's scores are in sc and its reference is set; on
+    // entry LDS holds K(t+1) and V(t).  The next tiles' loads are issued
+    // between the two compute blocks.
+    auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+        const bool more = t + 1 < ntiles, more2 = t + 2 < ntiles;
+        if (more2) fetch(k, t + 2, kreg, kok);
+        if (t + 1 < ntiles_w) {
+            // S^T(t+1) under which P(t) is formed
+            score(t + 1, sn, &sc);
+            if (more) fetch(v, t + 1, vreg, vok);
+            mask(t + 1, sn);
+            // P(t) V(t) under which the maximum of S^T(t+1) is found
+            const float mx = mix(t, &sn);
+            reference(mx);
         } else {
-            if (t >= 1 && t - 1 < ntiles_w) mix(t - 1);
-            if (more) fetch_k(t + 1);
-            if (t < ntiles_w) qk(t);
-            if (more) fetch_v(t + 1);
-            if (t < ntiles_w) mask_and_reference(t);
+            if (more) fetch(v, t + 1, vreg, vok);
+            if (t < ntiles_w) {
+                weigh(sc);
+                mix(t, nullptr);
+            }
         }
-        if (t + 1 < ntiles) stash(t + 1);
+        if (more2) stash_k(t + 2);
+        if (more) stash_v(t + 1);
         __syncthreads();
+    };
+
+    // prologue: K(0), V(0), K(1) staged; S^T(0) scored and its reference set
+    fetch(k, 0, kreg, kok);
+    fetch(v, 0, vreg, vok);
+    stash_k(0);
+    stash_v(0);
+    if (ntiles > 1) {
+        fetch(k, 1, kreg, kok);
+        stash_k(1);
     }
-    // group B: the last tile it scored is mixed after the loop when it was
-    // the block's last tile
-    if (group_b && ntiles_w > 0 && ntiles_w == ntiles) mix(ntiles_w - 1);
+    __syncthreads();
+    if (ntiles_w > 0) {
+        score(0, s0, nullptr);
+        mask(0, s0);
+        reference(scan(s0));
+    }
+    __syncthreads();  // K(0) is read by every wave before K(2) replaces it
+
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, s0, s1);
+        if (t + 1 < ntiles) step(t + 1, s1, s0);
+    }
 
     // ---- epilogue: out = acc / l, rows past n_b are zero
     if (qi < Sq) {
