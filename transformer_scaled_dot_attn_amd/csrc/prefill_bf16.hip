@@ -220,16 +220,29 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // ---- one pair of weights of P = 2^(s*scale*log2e - reference), packed to
     // bf16; the normaliser sums the bf16 weights the mixture uses, in the
     // fixed order kb, h2, i.
-    auto exp_pair = [&](const f32x16 (&sc)[2], int e, float mc) {
-        const int kb = e >> 3, h2 = (e >> 2) & 1, i = e & 3;
-        const float a0 = fast_exp2(fmaf(sc[kb][8 * h2 + 2 * i], scale_log2, -mc));
-        const float a1 = fast_exp2(fmaf(sc[kb][8 * h2 + 2 * i + 1], scale_log2, -mc));
-        pf[kb][h2][i] = pack_bf16(a0, a1);
-        // an empty volatile use keeps the pair where it is issued (under the
-        // MFMAs) instead of letting it sink to the P V block that reads it
-        asm volatile("" : "+v"(pf[kb][h2][i]));
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pf[kb][h2][i]), as_bf16x2(0x3F803F80u),
-                                                l_run, false);
+    // Three stages per pair e = 8 kb + 4 h2 + i, issued in a rolling window
+    // (exponentials of pair e, bf16 packing of pair e-1, normaliser update
+    // of pair e-2), so no instruction waits on the result of the one just
+    // before it; empty volatile uses keep each stage where it is issued
+    // (under the MFMAs) instead of letting it sink to its first reader.
+    float ex[2][2];  // exponentials of the two most recent pairs
+    auto pair_stage = [&](const f32x16 (&sc)[2], int e, float mc) {
+        if (e < 16) {
+            const int kb = e >> 3, h2 = (e >> 2) & 1, i = e & 3;
+            ex[e & 1][0] = fast_exp2(fmaf(sc[kb][8 * h2 + 2 * i], scale_log2, -mc));
+            ex[e & 1][1] = fast_exp2(fmaf(sc[kb][8 * h2 + 2 * i + 1], scale_log2, -mc));
+        }
+        if (e >= 1 && e - 1 < 16) {
+            const int f = e - 1, kb = f >> 3, h2 = (f >> 2) & 1, i = f & 3;
+            pf[kb][h2][i] = pack_bf16(ex[f & 1][0], ex[f & 1][1]);
+            asm volatile("" : "+v"(pf[kb][h2][i]));
+        }
+        if (e >= 2 && e - 2 < 16) {
+            const int f = e - 2, kb = f >> 3, h2 = (f >> 2) & 1, i = f & 3;
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pf[kb][h2][i]), as_bf16x2(0x3F803F80u),
+                                                    l_run, false);
+            asm volatile("" : "+v"(l_run));
+        }
     };
     auto ref_log2 = [&]() { return m_run == -INFINITY ? 0.0f : m_run * scale_log2; };
 
@@ -256,17 +269,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                 if (sc) {
                     constexpr int kPer = 16 / kQK;
 #pragma unroll
-                    for (int e = 0; e < kPer; ++e) exp_pair(*sc, (2 * ks + kb) * kPer + e, mc);
+                    for (int e = 0; e < kPer; ++e) pair_stage(*sc, (2 * ks + kb) * kPer + e, mc);
                 }
                 pin_schedule();
             }
+        }
+        if (sc) {
+            pair_stage(*sc, 16, mc);
+            pair_stage(*sc, 17, mc);
         }
     };
     // weights of a tile with no next tile to score under them
     auto weigh = [&](const f32x16 (&sc)[2]) {
         const float mc = ref_log2();
 #pragma unroll
-        for (int e = 0; e < 16; ++e) exp_pair(sc, e, mc);
+        for (int e = 0; e < 18; ++e) pair_stage(sc, e, mc);
     };
     // per-element mask of S^T(tile) when the tile cuts the diagonal or L
     auto mask = [&](int tile, f32x16 (&sn)[2]) {
@@ -359,26 +376,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // One iteration: tile t's scores are in sc and its reference is set; on
     // entry LDS holds K(t+1) and V(t).  The next tiles' loads are issued
     // between the two compute blocks.
+    // The staging loads and stores run unconditionally: past the block's
+    // last tile they move rows that are in bounds (rows at or past L are
+    // redirected) into LDS slots nobody reads again, and with no load under
+    // a branch the compiler's wait counts stay exact (each stash waits only
+    // for its own loads).
     auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-        const bool more = t + 1 < ntiles, more2 = t + 2 < ntiles;
-        if (more2) fetch(k, t + 2, kreg, kok);
-        if (t + 1 < ntiles_w) {
-            // S^T(t+1) under which P(t) is formed
-            score(t + 1, sn, &sc);
-            if (more) fetch(v, t + 1, vreg, vok);
+        const bool pipe = t + 1 < ntiles_w;  // this wave scores tile t+1
+        fetch(k, t + 2, kreg, kok);
+        // S^T(t+1) under which P(t) is formed
+        if (pipe) score(t + 1, sn, &sc);
+        fetch(v, t + 1, vreg, vok);
+        if (pipe) {
             mask(t + 1, sn);
             // P(t) V(t) under which the maximum of S^T(t+1) is found
             const float mx = mix(t, &sn);
             reference(mx);
-        } else {
-            if (more) fetch(v, t + 1, vreg, vok);
-            if (t < ntiles_w) {
-                weigh(sc);
-                mix(t, nullptr);
-            }
+        } else if (t < ntiles_w) {
+            weigh(sc);
+            mix(t, nullptr);
         }
-        if (more2) stash_k(t + 2);
-        if (more) stash_v(t + 1);
+        stash_k(t + 2);
+        stash_v(t + 1);
         __syncthreads();
     };
 
@@ -387,10 +406,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     fetch(v, 0, vreg, vok);
     stash_k(0);
     stash_v(0);
-    if (ntiles > 1) {
-        fetch(k, 1, kreg, kok);
-        stash_k(1);
-    }
+    fetch(k, 1, kreg, kok);
+    stash_k(1);
     __syncthreads();
     if (ntiles_w > 0) {
         score(0, s0, nullptr);
