@@ -52,6 +52,11 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_attn_fwd.restype = i
     lib.oracle_attn_fwd_weights.argtypes = [p, p, p, i, p, p, i, i, i, i, i, i, d, i, p, i]
     lib.oracle_attn_fwd_weights.restype = i
+    lib.oracle_attn_fwd_gqa.argtypes = [p, p, p, i, p, i, i, i, i, i, i, i, d, i, p, i]
+    lib.oracle_attn_fwd_gqa.restype = i
+    lib.oracle_attn_fwd_weights_gqa.argtypes = [p, p, p, i, p, p, i, i, i, i, i, i, i, d, i, p,
+                                                i]
+    lib.oracle_attn_fwd_weights_gqa.restype = i
     lib.oracle_default_threads.argtypes = []
     lib.oracle_default_threads.restype = i
     return lib
@@ -81,8 +86,10 @@ def default_threads() -> int:
 def attention(q, k, v, scale, causal, kv_lens=None, *, weights=False, nthreads=0, lib=None):
     """Reference attention forward.
 
-    q: [B,H,Sq,d], k: [B,H,Skv,d], v: [B,H,Skv,dv] numpy arrays of one dtype:
-    float64, float32, or uint16 holding bfloat16 bit patterns (widened exactly).
+    q: [B,H,Sq,d], k: [B,Hkv,Skv,d], v: [B,Hkv,Skv,dv] numpy arrays of one
+    dtype: float64, float32, or uint16 holding bfloat16 bit patterns (widened
+    exactly).  Hkv = H is multi-head attention; a divisor Hkv of H groups the
+    query heads (query head h reads key/value head h // (H // Hkv)).
     scale: the multiplier of QK^T (a float; pass float32 values widened).
     kv_lens: None or int array [B] of valid lengths (clamped to [0, Skv]).
     Returns out [B,H,Sq,dv] float64, and with weights=True also the weight
@@ -98,10 +105,12 @@ def attention(q, k, v, scale, causal, kv_lens=None, *, weights=False, nthreads=0
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be 4-D [B,H,S,d]")
     B, H, Sq, d = q.shape
-    Skv = k.shape[2]
+    Hkv, Skv = k.shape[1], k.shape[2]
     dv = v.shape[3]
-    if k.shape != (B, H, Skv, d) or v.shape[:3] != (B, H, Skv):
+    if k.shape != (B, Hkv, Skv, d) or v.shape[:3] != (B, Hkv, Skv):
         raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    if Hkv <= 0 or H % Hkv != 0:
+        raise ValueError(f"query heads {H} are not a multiple of key/value heads {Hkv}")
     lens_arr = None
     lens_ptr = None
     if kv_lens is not None:
@@ -114,13 +123,14 @@ def attention(q, k, v, scale, causal, kv_lens=None, *, weights=False, nthreads=0
     code = DTYPE_CODES[q.dtype]
     if weights:
         w = np.empty((B, H, Sq, Skv), dtype=np.float64)
-        rc = lib.oracle_attn_fwd_weights(q.ctypes.data, k.ctypes.data, v.ctypes.data, code,
-                                         out.ctypes.data, w.ctypes.data, B, H, Sq, Skv, d, dv,
-                                         float(scale), int(bool(causal)), lens_ptr, int(nthreads))
+        rc = lib.oracle_attn_fwd_weights_gqa(q.ctypes.data, k.ctypes.data, v.ctypes.data, code,
+                                             out.ctypes.data, w.ctypes.data, B, H, Hkv, Sq, Skv,
+                                             d, dv, float(scale), int(bool(causal)), lens_ptr,
+                                             int(nthreads))
     else:
-        rc = lib.oracle_attn_fwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, code,
-                                 out.ctypes.data, B, H, Sq, Skv, d, dv, float(scale),
-                                 int(bool(causal)), lens_ptr, int(nthreads))
+        rc = lib.oracle_attn_fwd_gqa(q.ctypes.data, k.ctypes.data, v.ctypes.data, code,
+                                     out.ctypes.data, B, H, Hkv, Sq, Skv, d, dv, float(scale),
+                                     int(bool(causal)), lens_ptr, int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle error {rc}: {ERRORS.get(rc, 'unknown')}")
     return (out, w) if weights else out

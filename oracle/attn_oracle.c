@@ -32,6 +32,15 @@
  *   - the softmax subtracts the row maximum before exponentiating, the stable
  *     form that page's Part 7 (debugging) asks for.
  *
+ * Grouped heads (GQA / MQA): with H_kv key/value heads for H query heads
+ * (H a multiple of H_kv), query head h reads key/value head h / (H / H_kv).
+ * That is the grouping of "Attention from First Principles", section "MHA,
+ * GQA, MQA -- the KV cache lever" (consecutive query heads share one K/V
+ * head), and what the repeat_interleave expansion of K and V along the head
+ * axis in "Scaled dot-product attention with masking", section
+ * "Grouped-query attention (GQA)", computes.  H_kv = H is multi-head
+ * attention.
+ *
  * Inputs may be float64, float32 or bfloat16 bit patterns; each element is
  * widened exactly to double before any arithmetic.  All arithmetic is in
  * double, sums in ascending index order.  Built without -ffast-math.
@@ -62,7 +71,7 @@ typedef struct {
     int dtype;
     double* out;      /* [B,H,Sq,dv] */
     double* weights;  /* optional [B,H,Sq,Skv] */
-    int B, H, Sq, Skv, d, dv;
+    int B, H, Hkv, Sq, Skv, d, dv;
     double scale;
     int causal;
     const int32_t* kv_lens;
@@ -100,9 +109,10 @@ static void one_row(const job_t* J, int b, int h, int i, double* out_row, double
     const int Sq = J->Sq, Skv = J->Skv, dv = J->dv;
     const int L = valid_len(J, b);
     const int n = Sq < L ? Sq : L;
+    const int hk = h / (J->H / J->Hkv); /* the key/value head of query head h */
     const size_t qrow = (((size_t)b * J->H + h) * Sq + i) * (size_t)J->d;
-    const size_t kbase = ((size_t)b * J->H + h) * (size_t)Skv * J->d;
-    const size_t vbase = ((size_t)b * J->H + h) * (size_t)Skv * dv;
+    const size_t kbase = ((size_t)b * J->Hkv + hk) * (size_t)Skv * J->d;
+    const size_t vbase = ((size_t)b * J->Hkv + hk) * (size_t)Skv * dv;
 
     for (int c = 0; c < dv; ++c) out_row[c] = 0.0;
     if (w_row)
@@ -160,7 +170,7 @@ static int run(job_t* J, int nthreads) {
     if (!J->q || !J->k || !J->v || !J->out) return OR_E_NULL;
     if (J->dtype != OR_F64 && J->dtype != OR_F32 && J->dtype != OR_BF16) return OR_E_DTYPE;
     if (J->B <= 0 || J->H <= 0 || J->Sq <= 0 || J->Skv <= 0 || J->d <= 0 || J->dv <= 0 ||
-        J->Sq > J->Skv)
+        J->Sq > J->Skv || J->Hkv <= 0 || J->H % J->Hkv != 0)
         return OR_E_SHAPE;
     if (!isfinite(J->scale)) return OR_E_ARG;
     if (nthreads <= 0) {
@@ -191,35 +201,53 @@ static int run(job_t* J, int nthreads) {
     return failed ? OR_E_NOMEM : OR_OK;
 }
 
-/* out is [B,H,Sq,dv] float64; q is [B,H,Sq,d], k is [B,H,Skv,d], v is
-   [B,H,Skv,dv], row-major, all of one dtype (0 f64, 1 f32, 2 bf16 bits).
+/* out is [B,H,Sq,dv] float64; q is [B,H,Sq,d], k is [B,Hkv,Skv,d], v is
+   [B,Hkv,Skv,dv], row-major, all of one dtype (0 f64, 1 f32, 2 bf16 bits).
    kv_lens is a host int32[B] or NULL (every sequence has Skv valid keys).
-   Returns 0, or 1 null pointer, 2 bad shape (a size <= 0 or Sq > Skv),
-   4 bad dtype, 7 non-finite scale, 9 out of memory.
+   Returns 0, or 1 null pointer, 2 bad shape (a size <= 0, Sq > Skv, or H
+   not a multiple of Hkv), 4 bad dtype, 7 non-finite scale, 9 out of memory.
    nthreads <= 0 uses every online core. */
-int oracle_attn_fwd(const void* q, const void* k, const void* v, int dtype, double* out, int B,
-                    int H, int Sq, int Skv, int d, int dv, double scale, int causal,
-                    const int32_t* kv_lens, int nthreads) {
+int oracle_attn_fwd_gqa(const void* q, const void* k, const void* v, int dtype, double* out,
+                        int B, int H, int Hkv, int Sq, int Skv, int d, int dv, double scale,
+                        int causal, const int32_t* kv_lens, int nthreads) {
     job_t J;
     memset(&J, 0, sizeof J);
     J.q = q; J.k = k; J.v = v; J.dtype = dtype; J.out = out; J.weights = NULL;
-    J.B = B; J.H = H; J.Sq = Sq; J.Skv = Skv; J.d = d; J.dv = dv;
+    J.B = B; J.H = H; J.Hkv = Hkv; J.Sq = Sq; J.Skv = Skv; J.d = d; J.dv = dv;
     J.scale = scale; J.causal = causal ? 1 : 0; J.kv_lens = kv_lens;
     return run(&J, nthreads);
 }
 
-/* As oracle_attn_fwd, and also the weight tensor [B,H,Sq,Skv] (float64),
+/* Multi-head attention: oracle_attn_fwd_gqa with Hkv = H. */
+int oracle_attn_fwd(const void* q, const void* k, const void* v, int dtype, double* out, int B,
+                    int H, int Sq, int Skv, int d, int dv, double scale, int causal,
+                    const int32_t* kv_lens, int nthreads) {
+    return oracle_attn_fwd_gqa(q, k, v, dtype, out, B, H, H, Sq, Skv, d, dv, scale, causal,
+                               kv_lens, nthreads);
+}
+
+/* As oracle_attn_fwd_gqa, and also the weight tensor [B,H,Sq,Skv] (float64),
    with every forbidden entry exactly 0. */
-int oracle_attn_fwd_weights(const void* q, const void* k, const void* v, int dtype, double* out,
-                            double* weights, int B, int H, int Sq, int Skv, int d, int dv,
-                            double scale, int causal, const int32_t* kv_lens, int nthreads) {
+int oracle_attn_fwd_weights_gqa(const void* q, const void* k, const void* v, int dtype,
+                                double* out, double* weights, int B, int H, int Hkv, int Sq,
+                                int Skv, int d, int dv, double scale, int causal,
+                                const int32_t* kv_lens, int nthreads) {
     if (!weights) return OR_E_NULL;
     job_t J;
     memset(&J, 0, sizeof J);
     J.q = q; J.k = k; J.v = v; J.dtype = dtype; J.out = out; J.weights = weights;
-    J.B = B; J.H = H; J.Sq = Sq; J.Skv = Skv; J.d = d; J.dv = dv;
+    J.B = B; J.H = H; J.Hkv = Hkv; J.Sq = Sq; J.Skv = Skv; J.d = d; J.dv = dv;
     J.scale = scale; J.causal = causal ? 1 : 0; J.kv_lens = kv_lens;
     return run(&J, nthreads);
+}
+
+/* As oracle_attn_fwd, and also the weight tensor (oracle_attn_fwd_weights_gqa
+   with Hkv = H). */
+int oracle_attn_fwd_weights(const void* q, const void* k, const void* v, int dtype, double* out,
+                            double* weights, int B, int H, int Sq, int Skv, int d, int dv,
+                            double scale, int causal, const int32_t* kv_lens, int nthreads) {
+    return oracle_attn_fwd_weights_gqa(q, k, v, dtype, out, weights, B, H, H, Sq, Skv, d, dv,
+                                       scale, causal, kv_lens, nthreads);
 }
 
 /* Number of threads a call with nthreads <= 0 uses. */

@@ -246,6 +246,33 @@ def pin_length_clamp(attn):
     assert np.all(a[1:] == 0.0)
 
 
+def pin_grouped_heads_match_expansion(attn):
+    """Grouped key/value heads ("Scaled dot-product attention with masking",
+    section "Grouped-query attention (GQA)"): the result equals plain
+    multi-head attention after K and V are expanded along the head axis with
+    repeat_interleave, here computed by torch's CPU scaled_dot_product_attention
+    in float64 on the expanded tensors (an independent routine).  Covers MQA
+    (one K/V head), GQA and MHA, causal with right padding, and B > 1."""
+    import torch
+    import torch.nn.functional as F
+    B, H, Sq, Skv, d = 2, 4, 5, 7, 3
+    lens = [7, 4]
+    for ci, Hkv in enumerate((1, 2, 4)):
+        q = _rand(60 + ci, B, H, Sq, d)
+        k, v = _rand(70 + ci, B, Hkv, Skv, d), _rand(80 + ci, B, Hkv, Skv, d)
+        out = attn(q, k, v, 0.7, 1, lens)
+        ke = torch.from_numpy(k).repeat_interleave(H // Hkv, dim=1)
+        ve = torch.from_numpy(v).repeat_interleave(H // Hkv, dim=1)
+        for b in range(B):
+            allowed, pad = _visible(Sq, Skv, 1, lens[b])
+            rows = np.nonzero(~pad)[0]
+            ref = F.scaled_dot_product_attention(
+                torch.from_numpy(q[b][:, rows]), ke[b], ve[b],
+                attn_mask=torch.from_numpy(allowed[rows]), scale=0.7).numpy()
+            assert np.allclose(out[b][:, rows], ref, rtol=0, atol=1e-12), f"Hkv {Hkv} b {b}"
+            assert np.all(out[b][:, pad] == 0.0)
+
+
 ALL_PINS = [
     pin_p2_causal_example,
     pin_p3_unmasked_example,
@@ -260,6 +287,7 @@ ALL_PINS = [
     pin_key_permutation_equivariance,
     pin_low_precision_inputs_widen_exactly,
     pin_length_clamp,
+    pin_grouped_heads_match_expansion,
 ]
 
 

@@ -35,6 +35,9 @@ MUTANTS = {
     "max_not_tracked": [("if (s[j] > m) m = s[j];", "", 1)],
     "mask_after_softmax": [("if (key_visible(J, j, p, L)) l += exp(s[j] - m);",
                             "l += exp(score(J, qrow, kbase, j) - m);", 1)],
+    "kv_head_modulo": [("const int hk = h / (J->H / J->Hkv);", "const int hk = h % J->Hkv;", 1)],
+    "kv_base_strides_query_heads": [("((size_t)b * J->Hkv + hk) * (size_t)Skv * J->d;",
+                                     "((size_t)b * J->H + hk) * (size_t)Skv * J->d;", 1)],
     "bf16_widening_off": [("[idx] << 16;", "[idx] << 16 | 0x8000u;", 1)],
     "f32_read_as_rounded": [("return (double)((const float*)base)[idx];",
                              "return (double)(float)(((const float*)base)[idx] * 1.0001f);", 1)],
