@@ -26,10 +26,20 @@
  *   - causal != 0 additionally hides keys j > p (M = -inf there, 0 else).
  *   - A padded query row, or a row with no visible key, is written as 0.
  *
- * Layout: q and out are [B][H][Sq][d], k and v are [B][H][Skv][d], all
- * row-major, densely packed, of the one element type `dtype`; out has the
- * inputs' type.  At decode Skv is the cache capacity and L_b <= Skv the
- * filled part.  All five base pointers must be 16-byte aligned.
+ * Layout: q and out are [B][H][Sq][d], k and v are [B][H][Skv][d] (for the
+ * _gqa entry points [B][H_kv][Skv][d]), all row-major, densely packed, of
+ * the one element type `dtype`; out has the inputs' type.  At decode Skv is
+ * the cache capacity and L_b <= Skv the filled part.  All five base
+ * pointers must be 16-byte aligned.
+ *
+ * Grouped key/value heads (the _gqa entry points): H_kv K/V heads serve H
+ * query heads, H a multiple of H_kv, and query head h reads K/V head
+ * h / (H / H_kv) -- consecutive query heads share one K/V head, the grouping
+ * of "Attention from First Principles", section "MHA, GQA, MQA -- the KV
+ * cache lever", and what repeating K and V with repeat_interleave along the
+ * head axis computes ("Scaled dot-product attention with masking", section
+ * "Grouped-query attention (GQA)").  H_kv = H is multi-head attention (the
+ * entry points without _gqa), H_kv = 1 multi-query attention.
  *
  * Pointers: q, k, v, out, kv_lens and workspace are DEVICE pointers on the
  * current HIP device.  stream is a hipStream_t (NULL = the null stream).
@@ -54,12 +64,12 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 typedef enum {
     ATTN_OK = 0,
     ATTN_E_NULL = 1,        /* q, k, v or out is NULL (or workspace, where required) */
-    ATTN_E_SHAPE = 2,       /* B, H, Sq, Skv or d <= 0, Sq > Skv, or sizes overflow */
+    ATTN_E_SHAPE = 2,       /* a size <= 0, Sq > Skv, H % H_kv != 0, or sizes overflow */
     ATTN_E_UNSUPPORTED = 3, /* valid request outside the kernels' support matrix */
     ATTN_E_DTYPE = 4,       /* dtype is not an attn_dtype value */
     ATTN_E_ALIGN = 5,       /* a base pointer is not 16-byte aligned */
@@ -112,6 +122,30 @@ size_t attn_workspace_bytes(int B, int H, int Sq, int Skv, int d, int dtype);
 int attn_fwd_ws(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq,
                 int Skv, int d, float scale, int causal, const int32_t* kv_lens, int dtype,
                 void* stream, void* workspace, size_t workspace_bytes);
+
+/*
+ * attn_fwd_gqa -- attn_fwd with H_kv key/value heads (layout and head
+ * grouping above; k and v are [B][H_kv][Skv][d]).  H_kv must divide H, else
+ * ATTN_E_SHAPE.  The decode kernel reads each K/V row once for all the query
+ * heads it serves (up to 8 per pass), so decode bytes fall by up to H / H_kv.
+ * Other arguments, ownership and errors as attn_fwd.
+ */
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* out, int B, int H, int H_kv,
+                 int Sq, int Skv, int d, float scale, int causal, const int32_t* kv_lens,
+                 int dtype, void* stream);
+
+/* attn_workspace_bytes for attn_fwd_gqa_ws (0 also for invalid arguments). */
+size_t attn_workspace_bytes_gqa(int B, int H, int H_kv, int Sq, int Skv, int d, int dtype);
+
+/* attn_fwd_gqa with caller-owned temporary memory, as attn_fwd_ws. */
+int attn_fwd_gqa_ws(const void* q, const void* k, const void* v, void* out, int B, int H,
+                    int H_kv, int Sq, int Skv, int d, float scale, int causal,
+                    const int32_t* kv_lens, int dtype, void* stream, void* workspace,
+                    size_t workspace_bytes);
+
+/* The host-side checks of attn_fwd_gqa alone (as attn_validate). */
+int attn_validate_gqa(const void* q, const void* k, const void* v, void* out, int B, int H,
+                      int H_kv, int Sq, int Skv, int d, float scale, int causal, int dtype);
 
 /*
  * attn_validate -- the host-side checks of attn_fwd alone: returns what

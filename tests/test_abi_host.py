@@ -96,6 +96,36 @@ def test_workspace_sizes():
     assert attn.workspace_bytes(0, 32, 1, 8192, 128, BF16) == 0
 
 
+def vg(B=2, H=8, Hkv=2, Sq=4, Skv=4, d=64, scale=0.125, causal=1, dtype=BF16):
+    return attn.library().attn_validate_gqa(A, A, A, A, B, H, Hkv, Sq, Skv, d, scale, causal,
+                                            dtype)
+
+
+def test_validate_gqa():
+    # H_kv must divide H; H_kv = H is the multi-head case
+    for Hkv in (1, 2, 4, 8):
+        assert vg(Hkv=Hkv) == attn.OK
+        assert vg(Hkv=Hkv, Sq=1, Skv=100, d=128) == attn.OK
+        assert vg(Hkv=Hkv, dtype=F32, d=20) == attn.OK
+    for Hkv in (0, -2, 3, 5, 16):
+        assert vg(Hkv=Hkv) == attn.E_SHAPE, Hkv
+    assert vg(Hkv=2, d=32) == attn.E_UNSUPPORTED
+    assert vg(H=6, Hkv=3) == attn.OK and vg(H=6, Hkv=4) == attn.E_SHAPE
+
+
+def test_gqa_workspace_sizes():
+    lib = attn.library()
+    # one partial per query head and split, whatever the K/V head count
+    for Hkv in (1, 8, 32):
+        w = lib.attn_workspace_bytes_gqa(64, 32, Hkv, 1, 8192, 128, BF16)
+        assert w >= 64 * 32 * (8192 // 128) * (128 + 2) * 4 and w % 256 == 0
+        assert attn.workspace_bytes(64, 32, 1, 8192, 128, BF16, kv_heads=Hkv) == w
+    assert lib.attn_workspace_bytes_gqa(64, 32, 32, 1, 8192, 128, BF16) == \
+        attn.workspace_bytes(64, 32, 1, 8192, 128, BF16)
+    assert lib.attn_workspace_bytes_gqa(64, 32, 5, 1, 8192, 128, BF16) == 0
+    assert lib.attn_workspace_bytes_gqa(1, 32, 8, 2048, 2048, 128, BF16) == 0
+
+
 def test_profile_names():
     names = attn.profile_names()
     assert names == ["prefill_bf16_mfma", "decode_bf16_partial", "decode_bf16_combine",
@@ -111,3 +141,7 @@ def test_python_layer_rejects_bad_tensors():
         attn.fwd(q[0], q, q)
     with pytest.raises(ValueError):
         attn.fwd(q.to(torch.float16), q, q)
+    q3 = torch.zeros(1, 3, 4, 64)
+    k2 = torch.zeros(1, 2, 4, 64)
+    with pytest.raises(ValueError):
+        attn.fwd(q3, k2, k2)

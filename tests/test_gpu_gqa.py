@@ -1,0 +1,104 @@
+"""Grouped key/value heads (GQA / MQA) on the GPU against the CPU oracle.
+
+Query head h reads K/V head h // (H // H_kv).  Every kernel family is run
+with K/V heads in {1, 2, ..., H} on ragged shapes and compared element by
+element with the oracle; prefill and fp32 results must also equal, bit for
+bit, the multi-head call on K and V expanded with repeat_interleave (the
+kernels' per-head arithmetic does not depend on where a head's K/V lives).
+The full-size grouped workloads run in the benchmark's launch configuration
+and are compared on sampled (batch, head) slices.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import transformer_scaled_dot_attn_amd as attn
+import workloads as W
+from gpu_util import BF16_TOL, F32_TOL, assert_matches, gpu_run
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+CASES = [
+    # seed, dtype, B, H, Hkv, Sq, Skv, d, causal, kv_lens
+    (41, "f32", 2, 4, 1, 70, 70, 32, 1, [70, 33]),
+    (42, "f32", 1, 6, 3, 1, 150, 128, 0, None),
+    (43, "bf16", 2, 8, 2, 300, 300, 128, 1, [300, 129]),
+    (44, "bf16", 1, 8, 1, 200, 200, 64, 1, None),
+    (45, "bf16", 2, 4, 4, 130, 260, 128, 1, [260, 90]),
+    (46, "bf16", 1, 16, 4, 64, 64, 128, 0, None),
+    (47, "bf16", 3, 8, 2, 1, 1000, 128, 0, [1000, 1, 0]),
+    (48, "bf16", 2, 16, 1, 1, 700, 64, 0, [700, 65]),
+    (49, "bf16", 2, 32, 8, 1, 2100, 128, 0, [2100, 777]),
+    (50, "bf16", 1, 12, 6, 1, 513, 128, 0, None),
+    (51, "bf16", 2, 24, 3, 1, 300, 128, 0, [300, 17]),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}")
+def test_gqa_shapes(case):
+    seed, dtype, B, H, Hkv, Sq, Skv, d, causal, lens = case
+    _say("gqa case", case)
+    prob = W.random_problem(seed, B, H, Sq, Skv, d, dtype, lens, Hkv=Hkv)
+    q, k, v, scale = prob["q"], prob["k"], prob["v"], prob["scale"]
+    got, _ = gpu_run(q, k, v, scale, causal, lens)
+    clamped = None if lens is None else np.clip(lens, 0, Skv)
+    ref = oracle.attention(q, k, v, scale, causal, clamped)
+    tol = F32_TOL if dtype == "f32" else BF16_TOL
+    assert_matches(got, ref, tol, clamped, Skv, f"gqa {case}")
+    # the multi-head call on expanded K/V
+    g = H // Hkv
+    ke, ve = np.repeat(k, g, axis=1), np.repeat(v, g, axis=1)
+    exp, _ = gpu_run(q, ke, ve, scale, causal, lens)
+    if Sq > 1 or dtype == "f32":
+        assert np.array_equal(got, exp), f"gqa {case}: differs from the expanded MHA call"
+    else:
+        assert_matches(got, exp, BF16_TOL, clamped, Skv, f"gqa {case} vs expanded")
+
+
+def test_gqa_rejects_uneven_groups():
+    import torch
+    q = torch.zeros(1, 6, 4, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 4, 4, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="multiple"):
+        attn.fwd(q, k, k)
+    lib = attn.library()
+    out = torch.empty_like(q)
+    rc = lib.attn_fwd_gqa(q.data_ptr(), k.data_ptr(), k.data_ptr(), out.data_ptr(), 1, 6, 4, 4,
+                          4, 64, 0.125, 1, None, attn.BF16, None)
+    assert rc == attn.E_SHAPE
+
+
+def _sampled(w, pairs):
+    import torch
+    _say("workload", w.name, "pairs", pairs)
+    x = W.device_inputs(w)
+    assert x["k"].shape[1] == w.kv_heads
+    out = attn.fwd(x["q"], x["k"], x["v"], causal=w.causal, kv_lens=x["kv_lens"],
+                   scale=x["scale"])
+    torch.cuda.synchronize()
+    sub = W.make_inputs(w, pairs=pairs)
+    ref = oracle.attention(sub["q"], sub["k"], sub["v"], sub["scale"], w.causal, sub["kv_lens"])
+    got = np.stack([W.from_torch(out[b, h]) for b, h in pairs])[:, None]
+    g = w.H // w.kv_heads
+    for idx, (b, h) in enumerate(pairs):
+        assert np.array_equal(W.bits_from_torch(x["q"][b, h]), sub["q"][idx, 0])
+        assert np.array_equal(W.bits_from_torch(x["k"][b, h // g]), sub["k"][idx, 0])
+    return assert_matches(got, ref, BF16_TOL, sub["kv_lens"], w.Skv, w.name)
+
+
+def test_workload_gqa_prefill2048_sampled():
+    w = W.WORKLOADS["gqa_prefill2048_bf16"]
+    _sampled(w, [(0, 0), (0, 3), (0, 4), (1, 17), (1, 31)])
+
+
+@pytest.mark.parametrize("name", ["gqa_decode8192_bf16", "mqa_decode8192_bf16"])
+def test_workload_grouped_decode_sampled(name):
+    w = W.WORKLOADS[name]
+    lens = W.kv_lens_for(w)
+    bs = [int(np.argmin(lens)), int(np.argmax(lens)), 0, 33]
+    _sampled(w, [(b, h) for b in bs for h in (0, 3, 4, 31)])

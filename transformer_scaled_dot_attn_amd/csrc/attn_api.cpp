@@ -31,10 +31,11 @@ Path choose_path(int Sq, int d, int dtype) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_shape(int B, int H, int Sq, int Skv, int d) {
+int check_shape(int B, int H, int Hkv, int Sq, int Skv, int d) {
     if (B <= 0 || H <= 0 || Sq <= 0 || Skv <= 0 || d <= 0 || Sq > Skv) return ATTN_E_SHAPE;
-    // element counts of the k/v tensors and the launch grids must stay in range
-    const long double kv = (long double)B * H * Skv * d;
+    if (Hkv <= 0 || H % Hkv != 0) return ATTN_E_SHAPE;
+    // element counts of the q/k/v tensors and the launch grids must stay in range
+    const long double kv = (long double)B * H * Skv * d;  // >= the k/v counts (Hkv <= H)
     if (kv > (long double)(INT64_MAX / 8)) return ATTN_E_SHAPE;
     const long double rows = (long double)B * H * ((Sq + 63) / 64);
     if (rows > (long double)INT_MAX) return ATTN_E_SHAPE;
@@ -126,13 +127,13 @@ EventTimer* g_timer = nullptr;
 bool g_timing_on = false;
 std::mutex g_timer_mu;
 
-int run(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq, int Skv,
-        int d, float scale, int causal, const int32_t* kv_lens, int dtype, void* stream,
+int run(const void* q, const void* k, const void* v, void* out, int B, int H, int Hkv, int Sq,
+        int Skv, int d, float scale, int causal, const int32_t* kv_lens, int dtype, void* stream,
         void* workspace, size_t workspace_bytes, bool library_ws) {
-    int st = attn_validate(q, k, v, out, B, H, Sq, Skv, d, scale, causal, dtype);
+    int st = attn_validate_gqa(q, k, v, out, B, H, Hkv, Sq, Skv, d, scale, causal, dtype);
     if (st != ATTN_OK) return st;
     const Path path = choose_path(Sq, d, dtype);
-    const size_t need = attn_workspace_bytes(B, H, Sq, Skv, d, dtype);
+    const size_t need = attn_workspace_bytes_gqa(B, H, Hkv, Sq, Skv, d, dtype);
     if (library_ws) {
         workspace = nullptr;
         if (need > 0) {
@@ -161,7 +162,7 @@ int run(const void* q, const void* k, const void* v, void* out, int B, int H, in
         if (need > 0 && (workspace == nullptr)) return ATTN_E_NULL;
         if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_E_ALIGN;
     }
-    LaunchArgs a{q, k, v, out, B, H, Sq, Skv, d, scale, causal ? 1 : 0, kv_lens,
+    LaunchArgs a{q, k, v, out, B, H, Hkv, Sq, Skv, d, scale, causal ? 1 : 0, kv_lens,
                  static_cast<hipStream_t>(stream), workspace, workspace_bytes};
     hipError_t e = hipSuccess;
     switch (path) {
@@ -183,12 +184,12 @@ using namespace tsda;
 
 extern "C" {
 
-int attn_validate(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq,
-                  int Skv, int d, float scale, int causal, int dtype) {
+int attn_validate_gqa(const void* q, const void* k, const void* v, void* out, int B, int H,
+                      int Hkv, int Sq, int Skv, int d, float scale, int causal, int dtype) {
     (void)causal;
     if (!q || !k || !v || !out) return ATTN_E_NULL;
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_E_DTYPE;
-    int st = check_shape(B, H, Sq, Skv, d);
+    int st = check_shape(B, H, Hkv, Sq, Skv, d);
     if (st != ATTN_OK) return st;
     if (!std::isfinite(scale)) return ATTN_E_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_E_ALIGN;
@@ -196,9 +197,14 @@ int attn_validate(const void* q, const void* k, const void* v, void* out, int B,
     return ATTN_OK;
 }
 
+int attn_validate(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq,
+                  int Skv, int d, float scale, int causal, int dtype) {
+    return attn_validate_gqa(q, k, v, out, B, H, H, Sq, Skv, d, scale, causal, dtype);
+}
+
 const char* attn_kernel_for(int Sq, int Skv, int d, int dtype) {
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return nullptr;
-    if (check_shape(1, 1, Sq, Skv, d) != ATTN_OK) return nullptr;
+    if (check_shape(1, 1, 1, Sq, Skv, d) != ATTN_OK) return nullptr;
     switch (choose_path(Sq, d, dtype)) {
         case kPathGenericF32: return "generic_f32";
         case kPathPrefill: return "prefill_bf16_mfma";
@@ -207,32 +213,52 @@ const char* attn_kernel_for(int Sq, int Skv, int d, int dtype) {
     }
 }
 
-size_t attn_workspace_bytes(int B, int H, int Sq, int Skv, int d, int dtype) {
+size_t attn_workspace_bytes_gqa(int B, int H, int Hkv, int Sq, int Skv, int d, int dtype) {
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
-    if (check_shape(B, H, Sq, Skv, d) != ATTN_OK) return 0;
+    if (check_shape(B, H, Hkv, Sq, Skv, d) != ATTN_OK) return 0;
     if (choose_path(Sq, d, dtype) != kPathDecode) return 0;
-    return decode_workspace_bytes(B, H, Skv, d);
+    return decode_workspace_bytes(B, H, Hkv, Skv, d);
+}
+
+size_t attn_workspace_bytes(int B, int H, int Sq, int Skv, int d, int dtype) {
+    return attn_workspace_bytes_gqa(B, H, H, Sq, Skv, d, dtype);
+}
+
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* out, int B, int H, int Hkv,
+                 int Sq, int Skv, int d, float scale, int causal, const int32_t* kv_lens,
+                 int dtype, void* stream) {
+    return run(q, k, v, out, B, H, Hkv, Sq, Skv, d, scale, causal, kv_lens, dtype, stream,
+               nullptr, 0, true);
+}
+
+int attn_fwd_gqa_ws(const void* q, const void* k, const void* v, void* out, int B, int H,
+                    int Hkv, int Sq, int Skv, int d, float scale, int causal,
+                    const int32_t* kv_lens, int dtype, void* stream, void* workspace,
+                    size_t workspace_bytes) {
+    return run(q, k, v, out, B, H, Hkv, Sq, Skv, d, scale, causal, kv_lens, dtype, stream,
+               workspace, workspace_bytes, false);
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq,
              int Skv, int d, float scale, int causal, const int32_t* kv_lens, int dtype,
              void* stream) {
-    return run(q, k, v, out, B, H, Sq, Skv, d, scale, causal, kv_lens, dtype, stream, nullptr, 0,
-               true);
+    return run(q, k, v, out, B, H, H, Sq, Skv, d, scale, causal, kv_lens, dtype, stream, nullptr,
+               0, true);
 }
 
 int attn_fwd_ws(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq,
                 int Skv, int d, float scale, int causal, const int32_t* kv_lens, int dtype,
                 void* stream, void* workspace, size_t workspace_bytes) {
-    return run(q, k, v, out, B, H, Sq, Skv, d, scale, causal, kv_lens, dtype, stream, workspace,
-               workspace_bytes, false);
+    return run(q, k, v, out, B, H, H, Sq, Skv, d, scale, causal, kv_lens, dtype, stream,
+               workspace, workspace_bytes, false);
 }
 
 const char* attn_status_string(int status) {
     switch (status) {
         case ATTN_OK: return "ok";
         case ATTN_E_NULL: return "null pointer argument";
-        case ATTN_E_SHAPE: return "invalid shape (a size <= 0, Sq > Skv, or too large)";
+        case ATTN_E_SHAPE:
+            return "invalid shape (a size <= 0, Sq > Skv, H not a multiple of H_kv, or too large)";
         case ATTN_E_UNSUPPORTED: return "unsupported combination of dtype and head size";
         case ATTN_E_DTYPE: return "unknown dtype";
         case ATTN_E_ALIGN: return "pointer not aligned (16 bytes; workspace 256 bytes)";

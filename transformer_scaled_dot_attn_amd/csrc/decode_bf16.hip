@@ -4,7 +4,14 @@
 // ("Attention from First Principles", section 6: a matrix-vector product
 // whose intensity is about 1 for multi-head attention), so this path is
 // built for HBM bandwidth, not for the matrix cores:
-//   * partial kernel: one block per (b, h, split of `chunk` keys).  Each key
+//   * partial kernel: one block per (b, K/V head, group of HB query heads,
+//     split of `chunk` keys).  With grouped key/value heads (GQA / MQA:
+//     query head h reads K/V head h / (H / H_kv), "Attention from First
+//     Principles", section "MHA, GQA, MQA -- the KV cache lever") the block
+//     scores each K/V row against all HB query heads it serves, so K and V
+//     are read once per group instead of once per query head -- the rise in
+//     decode intensity to H / H_kv that the same page's section 6 derives.
+//     Each key
 //     row (d bf16 = 2d bytes) is read by d/8 lanes with one 16-byte load
 //     each, so every wave-wide load covers whole contiguous rows.  Logits use
 //     v_dot2 on the raw bf16 pairs (exact products, fp32 sums), reduced over
@@ -28,23 +35,28 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kUnroll = 4;  // key rows per lane per step (two steps in flight)
 
-template <int D>
+template <int D, int HB>
 __global__ __launch_bounds__(256) void decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const int32_t* __restrict__ kv_lens, int H, int Skv,
-    float scale_log2, int chunk, int nsplit, float* __restrict__ ws_acc,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ kv_lens, int H, int Hkv,
+    int Skv, float scale_log2, int chunk, int nsplit, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml) {
     constexpr int G = D / 8;            // lanes per key row
     constexpr int KPW = 64 / G;         // key rows per wave per load
     constexpr int SLOTS = kWaves * KPW; // key rows per block per load
-    __shared__ float s_m[SLOTS];
-    __shared__ float s_l[SLOTS];
+    __shared__ float s_m[HB][SLOTS];
+    __shared__ float s_l[HB][SLOTS];
     __shared__ float s_acc[SLOTS][D];
 
     const int unit = blockIdx.x;
-    const int bh = unit / nsplit;
-    const int split = unit - bh * nsplit;
-    const int b = bh / H;
+    const int gunit = unit / nsplit;  // (b, K/V head, query-head group)
+    const int split = unit - gunit * nsplit;
+    const int group = H / Hkv;        // query heads per K/V head
+    const int ngrp = group / HB;      // blocks per K/V head
+    const int bk = gunit / ngrp;      // b * Hkv + K/V head
+    const int hg = gunit - bk * ngrp;
+    const int b = bk / Hkv;
+    const int h0 = (bk - b * Hkv) * group + hg * HB;  // first query head served
     const int L = valid_length(kv_lens, b, Skv);
     const int k0 = split * chunk;
     if (k0 >= L) return;  // the combine kernel reads only splits below L
@@ -55,14 +67,21 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     const int slot = (tid >> 6) * KPW + lane / G;
     const int part = lane % G;
 
-    const u32x4 qw = ldg16(q + (size_t)bh * D + part * 8);
-    const uint16_t* kp = k + (size_t)bh * Skv * D + part * 8;
-    const uint16_t* vp = v + (size_t)bh * Skv * D + part * 8;
-
-    float m = -INFINITY, l = 0.0f;
-    float acc[8];
+    u32x4 qw[HB];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+    for (int i = 0; i < HB; ++i) qw[i] = ldg16(q + ((size_t)b * H + h0 + i) * D + part * 8);
+    const uint16_t* kp = k + (size_t)bk * Skv * D + part * 8;
+    const uint16_t* vp = v + (size_t)bk * Skv * D + part * 8;
+
+    float m[HB], l[HB];
+    float acc[HB][8];
+#pragma unroll
+    for (int i = 0; i < HB; ++i) {
+        m[i] = -INFINITY;
+        l[i] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
+    }
 
     // Rows of one step: base + u*SLOTS + slot for u < kUnroll.  Loads are
     // branch-free (a row past k1 is redirected to row k0, which is valid, and
@@ -79,37 +98,40 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
         }
     };
     auto consume = [&](int base, const u32x4 (&kr)[kUnroll], const u32x4 (&vr)[kUnroll]) {
-        float s[kUnroll];
-        float mx = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            float dot = 0.0f;
+        for (int i = 0; i < HB; ++i) {
+            float s[kUnroll];
+            float mx = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dot = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kr[u][i]), as_bf16x2(qw[i]), dot,
-                                                      false);
-            dot = group_sum<G>(dot);
-            const int j = base + u * SLOTS + slot;
-            s[u] = j < k1 ? dot * scale_log2 : -INFINITY;
-            mx = fmaxf(mx, s[u]);
-        }
-        const float m_new = fmaxf(m, mx);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = fast_exp2(m - m_use);
-        l *= alpha;
+            for (int u = 0; u < kUnroll; ++u) {
+                float dot = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] *= alpha;
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const float p = fast_exp2(s[u] - m_use);
-            l += p;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[2 * i] = fmaf(p, bf16_lo(vr[u][i]), acc[2 * i]);
-                acc[2 * i + 1] = fmaf(p, bf16_hi(vr[u][i]), acc[2 * i + 1]);
+                for (int c = 0; c < 4; ++c)
+                    dot = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kr[u][c]), as_bf16x2(qw[i][c]),
+                                                          dot, false);
+                dot = group_sum<G>(dot);
+                const int j = base + u * SLOTS + slot;
+                s[u] = j < k1 ? dot * scale_log2 : -INFINITY;
+                mx = fmaxf(mx, s[u]);
             }
+            const float m_new = fmaxf(m[i], mx);
+            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+            const float alpha = fast_exp2(m[i] - m_use);
+            l[i] *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[i][e] *= alpha;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const float pw = fast_exp2(s[u] - m_use);
+                l[i] += pw;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    acc[i][2 * c] = fmaf(pw, bf16_lo(vr[u][c]), acc[i][2 * c]);
+                    acc[i][2 * c + 1] = fmaf(pw, bf16_hi(vr[u][c]), acc[i][2 * c + 1]);
+                }
+            }
+            m[i] = m_new;
         }
-        m = m_new;
     };
     u32x4 ka[kUnroll], va[kUnroll], kb[kUnroll], vb[kUnroll];
     load(k0, ka, va);
@@ -121,28 +143,37 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
         consume(base + kStep, kb, vb);
     }
 
+    // merge the block's SLOTS row groups, one query head at a time
     if (part == 0) {
-        s_m[slot] = m;
-        s_l[slot] = l;
+#pragma unroll
+        for (int i = 0; i < HB; ++i) {
+            s_m[i][slot] = m[i];
+            s_l[i][slot] = l[i];
+        }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s_acc[slot][part * 8 + e] = acc[e];
-    __syncthreads();
-    if (tid < D) {
-        float M = -INFINITY;
+    for (int i = 0; i < HB; ++i) {
+        if (i > 0) __syncthreads();  // the previous head's merge has read s_acc
 #pragma unroll
-        for (int s2 = 0; s2 < SLOTS; ++s2) M = fmaxf(M, s_m[s2]);
-        float lt = 0.0f, at = 0.0f;
+        for (int e = 0; e < 8; ++e) s_acc[slot][part * 8 + e] = acc[i][e];
+        __syncthreads();
+        if (tid < D) {
+            float M = -INFINITY;
 #pragma unroll
-        for (int s2 = 0; s2 < SLOTS; ++s2) {
-            const float w = s_m[s2] == -INFINITY ? 0.0f : fast_exp2(s_m[s2] - M);
-            lt = fmaf(s_l[s2], w, lt);
-            at = fmaf(s_acc[s2][tid], w, at);
-        }
-        ws_acc[(size_t)unit * D + tid] = at;
-        if (tid == 0) {
-            ws_ml[(size_t)unit * 2] = M;
-            ws_ml[(size_t)unit * 2 + 1] = lt;
+            for (int s2 = 0; s2 < SLOTS; ++s2) M = fmaxf(M, s_m[i][s2]);
+            float lt = 0.0f, at = 0.0f;
+#pragma unroll
+            for (int s2 = 0; s2 < SLOTS; ++s2) {
+                const float w = s_m[i][s2] == -INFINITY ? 0.0f : fast_exp2(s_m[i][s2] - M);
+                lt = fmaf(s_l[i][s2], w, lt);
+                at = fmaf(s_acc[s2][tid], w, at);
+            }
+            const size_t uq = ((size_t)b * H + h0 + i) * nsplit + split;  // partial of head h0+i
+            ws_acc[uq * D + tid] = at;
+            if (tid == 0) {
+                ws_ml[uq * 2] = M;
+                ws_ml[uq * 2 + 1] = lt;
+            }
         }
     }
 }
@@ -199,44 +230,70 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-DecodePlan decode_plan(int B, int H, int Skv) {
+int decode_heads_per_block(int H, int Hkv) {
+    const int group = H / Hkv;
+    for (int hb = 8; hb > 1; hb >>= 1)
+        if (group % hb == 0) return hb;
+    return 1;
+}
+
+DecodePlan decode_plan(int B, int H, int Hkv, int Skv) {
     // Splits of 128 keys (64 KiB of K+V at d = 128) measured fastest on the
     // ragged decode workload: many short units spread the reads of the valid
     // prefixes of all caches evenly over the memory system.  Smaller problems
     // split finer so the grid still fills the GPU.
+    const long groups = (long)B * Hkv * (H / Hkv / decode_heads_per_block(H, Hkv));
     int chunk = 128;
-    if ((long)B * H * ((Skv + chunk - 1) / chunk) < 8192) chunk = 64;
+    if (groups * ((Skv + chunk - 1) / chunk) < 8192) chunk = 64;
     return DecodePlan{chunk, (Skv + chunk - 1) / chunk};
 }
 
-size_t decode_workspace_bytes(int B, int H, int Skv, int d) {
-    const DecodePlan p = decode_plan(B, H, Skv);
-    const size_t units = (size_t)B * H * p.nsplit;
+size_t decode_workspace_bytes(int B, int H, int Hkv, int Skv, int d) {
+    const DecodePlan p = decode_plan(B, H, Hkv, Skv);
+    const size_t units = (size_t)B * H * p.nsplit;  // one partial per query head and split
     return round256(units * d * sizeof(float)) + round256(units * 2 * sizeof(float));
 }
 
+namespace {
+
+template <int D, int HB>
+void launch_partial(const LaunchArgs& a, const DecodePlan& p, float sl, float* ws_acc,
+                    float* ws_ml) {
+    const size_t blocks = (size_t)a.B * a.H / HB * p.nsplit;
+    hipLaunchKernelGGL((decode_partial_kernel<D, HB>), dim3((unsigned)blocks), dim3(256), 0,
+                       a.stream, static_cast<const uint16_t*>(a.q),
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                       a.kv_lens, a.H, a.Hkv, a.Skv, sl, p.chunk, p.nsplit, ws_acc, ws_ml);
+}
+
+template <int D>
+void launch_partial_d(const LaunchArgs& a, const DecodePlan& p, float sl, float* ws_acc,
+                      float* ws_ml) {
+    switch (decode_heads_per_block(a.H, a.Hkv)) {
+        case 8: launch_partial<D, 8>(a, p, sl, ws_acc, ws_ml); break;
+        case 4: launch_partial<D, 4>(a, p, sl, ws_acc, ws_ml); break;
+        case 2: launch_partial<D, 2>(a, p, sl, ws_acc, ws_ml); break;
+        default: launch_partial<D, 1>(a, p, sl, ws_acc, ws_ml); break;
+    }
+}
+
+}  // namespace
+
 hipError_t launch_decode_bf16(const LaunchArgs& a) {
-    const DecodePlan p = decode_plan(a.B, a.H, a.Skv);
+    const DecodePlan p = decode_plan(a.B, a.H, a.Hkv, a.Skv);
     const size_t units = (size_t)a.B * a.H * p.nsplit;
     float* ws_acc = static_cast<float*>(a.workspace);
     float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
                                             round256(units * a.d * sizeof(float)));
-    const uint16_t* q = static_cast<const uint16_t*>(a.q);
-    const uint16_t* k = static_cast<const uint16_t*>(a.k);
-    const uint16_t* v = static_cast<const uint16_t*>(a.v);
     uint16_t* o = static_cast<uint16_t*>(a.out);
     const float sl = a.scale * kLog2e;
     KernelTimer* t = active_timer();
     hipError_t e;
     if (t) t->begin(kDecodePartialBf16, a.stream);
     if (a.d == 128)
-        hipLaunchKernelGGL(decode_partial_kernel<128>, dim3((unsigned)units), dim3(256), 0,
-                           a.stream, q, k, v, a.kv_lens, a.H, a.Skv, sl, p.chunk, p.nsplit, ws_acc,
-                           ws_ml);
+        launch_partial_d<128>(a, p, sl, ws_acc, ws_ml);
     else
-        hipLaunchKernelGGL(decode_partial_kernel<64>, dim3((unsigned)units), dim3(256), 0,
-                           a.stream, q, k, v, a.kv_lens, a.H, a.Skv, sl, p.chunk, p.nsplit, ws_acc,
-                           ws_ml);
+        launch_partial_d<64>(a, p, sl, ws_acc, ws_ml);
     e = hipGetLastError();
     if (t) t->end(kDecodePartialBf16, a.stream);
     if (e != hipSuccess) return e;

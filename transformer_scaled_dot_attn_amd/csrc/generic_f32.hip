@@ -7,7 +7,9 @@
 // accumulator once (the online-softmax recurrence), so the score matrix is
 // never materialised ("Scaled dot-product attention with masking", section
 // "The memory problem").  Keys past the valid length are never read; rows
-// past the valid query count are written as zeros.
+// past the valid query count are written as zeros.  With grouped key/value
+// heads, query head h reads K/V head h / (H / Hkv) ("Attention from First
+// Principles", section "MHA, GQA, MQA -- the KV cache lever").
 #include "device_common.h"
 #include "launch.h"
 
@@ -21,8 +23,8 @@ constexpr int kKeys = 32;   // keys per LDS tile
 template <int DP>  // d rounded up to 16, 32, 64 or 128
 __global__ __launch_bounds__(64) void generic_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ out, const int32_t* __restrict__ kv_lens, int H, int Sq, int Skv, int d,
-    float scale_log2, int causal) {
+    float* __restrict__ out, const int32_t* __restrict__ kv_lens, int H, int Hkv, int Sq, int Skv,
+    int d, float scale_log2, int causal) {
     __shared__ float ks[kKeys][DP];
     __shared__ float vs[kKeys][DP];
 
@@ -55,8 +57,9 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
     }
     float m = -INFINITY, l = 0.0f;
 
-    const float* kb = k + (size_t)bh * Skv * d;
-    const float* vb = v + (size_t)bh * Skv * d;
+    const int bk = b * Hkv + (bh - b * H) / (H / Hkv);  // this head's K/V head
+    const float* kb = k + (size_t)bk * Skv * d;
+    const float* vb = v + (size_t)bk * Skv * d;
     for (int j0 = 0; j0 < kv_hi; j0 += kKeys) {
         const int nk = min(kKeys, kv_hi - j0);
         __syncthreads();
@@ -127,16 +130,16 @@ hipError_t launch_generic_f32(const LaunchArgs& a) {
     if (t) t->begin(kGenericF32, a.stream);
     if (a.d <= 16)
         hipLaunchKernelGGL(generic_f32_kernel<16>, grid, block, 0, a.stream, q, k, v, o, a.kv_lens,
-                           a.H, a.Sq, a.Skv, a.d, sl, a.causal);
+                           a.H, a.Hkv, a.Sq, a.Skv, a.d, sl, a.causal);
     else if (a.d <= 32)
         hipLaunchKernelGGL(generic_f32_kernel<32>, grid, block, 0, a.stream, q, k, v, o, a.kv_lens,
-                           a.H, a.Sq, a.Skv, a.d, sl, a.causal);
+                           a.H, a.Hkv, a.Sq, a.Skv, a.d, sl, a.causal);
     else if (a.d <= 64)
         hipLaunchKernelGGL(generic_f32_kernel<64>, grid, block, 0, a.stream, q, k, v, o, a.kv_lens,
-                           a.H, a.Sq, a.Skv, a.d, sl, a.causal);
+                           a.H, a.Hkv, a.Sq, a.Skv, a.d, sl, a.causal);
     else
         hipLaunchKernelGGL(generic_f32_kernel<128>, grid, block, 0, a.stream, q, k, v, o,
-                           a.kv_lens, a.H, a.Sq, a.Skv, a.d, sl, a.causal);
+                           a.kv_lens, a.H, a.Hkv, a.Sq, a.Skv, a.d, sl, a.causal);
     hipError_t e = hipGetLastError();
     if (t) t->end(kGenericF32, a.stream);
     return e;

@@ -11,7 +11,7 @@ struct LaunchArgs {
     const void* k;
     const void* v;
     void* out;
-    int B, H, Sq, Skv, d;
+    int B, H, Hkv, Sq, Skv, d;  // Hkv key/value heads; query head h reads K/V head h / (H / Hkv)
     float scale;
     int causal;
     const int32_t* kv_lens;
@@ -25,8 +25,9 @@ struct DecodePlan {
     int chunk;
     int nsplit;
 };
-DecodePlan decode_plan(int B, int H, int Skv);
-size_t decode_workspace_bytes(int B, int H, int Skv, int d);
+DecodePlan decode_plan(int B, int H, int Hkv, int Skv);
+size_t decode_workspace_bytes(int B, int H, int Hkv, int Skv, int d);
+int decode_heads_per_block(int H, int Hkv);  // query heads one decode block serves
 
 // Profiling hook: the front end brackets each launch when timing is on.
 struct KernelTimer {

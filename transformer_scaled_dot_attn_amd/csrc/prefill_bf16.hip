@@ -45,9 +45,14 @@
 // exactly zero weight).  Key rows >= L_b are never loaded (the LDS rows are
 // zero-filled instead), and query rows >= n_b are written as zeros.
 //
-// Order.  Block ids are mapped heaviest query tile first, and consecutive
-// ids walk the (b, h) pairs, so the tiles of one head land on one XCD (ids
-// are dealt round-robin over the 8 XCDs) and share its L2.
+// Order.  Block ids are mapped heaviest query tile first; within a query
+// tile rank the (b, h) pairs are laid out so that each XCD (ids are dealt
+// round-robin over the 8 XCDs) runs a contiguous range of heads: every tile
+// of a head, and the query heads that share one K/V head, use one L2.
+//
+// Grouped key/value heads (GQA / MQA): query head h reads K/V head
+// h / (H / Hkv) ("Attention from First Principles", section "MHA, GQA, MQA
+// -- the KV cache lever"); nothing else changes.
 #include "device_common.h"
 #include "launch.h"
 
@@ -92,7 +97,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
-    const int32_t* __restrict__ kv_lens, int BH, int H, int Sq, int Skv, float scale_log2,
+    const int32_t* __restrict__ kv_lens, int BH, int H, int Hkv, int Sq, int Skv, float scale_log2,
     int causal, int nqt) {
     using S = Shape<D>;
     __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][S::kTileK];
@@ -105,8 +110,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 
     const int bid = blockIdx.x;
     const int qt = nqt - 1 - bid / BH;
-    const int bh = bid - (bid / BH) * BH;
+    const int jb = bid - (bid / BH) * BH;
+    // Blocks are dealt to the 8 XCDs round-robin by id.  With BH a multiple
+    // of 8, XCD x runs the contiguous (b, h) pairs x*BH/8 .. (x+1)*BH/8 - 1,
+    // so every query tile of a head, and the query heads that share a K/V
+    // head, meet in one L2.
+    const int bh = (BH & 7) == 0 ? (jb & 7) * (BH >> 3) + (jb >> 3) : jb;
     const int b = bh / H;
+    const int bk = b * Hkv + (bh - b * H) / (H / Hkv);  // this head's K/V head
     const int L = valid_length(kv_lens, b, Skv);
     const int n = Sq < L ? Sq : L;
     const int off = L - n;
@@ -156,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // are never read.  K runs two tiles ahead of the scores, V one tile.
     const int st_row = tid / S::kChunks;
     const int st_col = (tid % S::kChunks) * 8;
-    const size_t head_off = (size_t)bh * Skv * D + st_col;
+    const size_t head_off = (size_t)bk * Skv * D + st_col;
     u32x4 kreg[S::kPerThread], vreg[S::kPerThread];
     bool kok[S::kPerThread], vok[S::kPerThread];
     auto fetch = [&](const uint16_t* __restrict__ src, int tile, u32x4 (&dst)[S::kPerThread],
@@ -456,10 +467,10 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
     if (t) t->begin(kPrefillBf16, a.stream);
     if (a.d == 128)
         hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(kThreads), 0, a.stream, q, k, v, o,
-                           a.kv_lens, BH, a.H, a.Sq, a.Skv, sl, a.causal, nqt);
+                           a.kv_lens, BH, a.H, a.Hkv, a.Sq, a.Skv, sl, a.causal, nqt);
     else
         hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(kThreads), 0, a.stream, q, k, v, o,
-                           a.kv_lens, BH, a.H, a.Sq, a.Skv, sl, a.causal, nqt);
+                           a.kv_lens, BH, a.H, a.Hkv, a.Sq, a.Skv, sl, a.causal, nqt);
     hipError_t e = hipGetLastError();
     if (t) t->end(kPrefillBf16, a.stream);
     return e;

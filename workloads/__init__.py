@@ -42,6 +42,11 @@ class Workload:
     seed: int
     kv_len_range: Optional[tuple] = None   # (lo, hi) inclusive, or None
     description: str = ""
+    Hkv: Optional[int] = None              # key/value heads (None: H, multi-head)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H if self.Hkv is None else self.Hkv
 
     @property
     def scale(self) -> float:
@@ -67,6 +72,17 @@ WORKLOADS = {
         Workload("decode8192_bf16", 64, 32, 1, 8192, 128, "bf16", False, 5, (512, 8192),
                  description="decode, one query against a KV cache of capacity 8192, "
                              "lengths U[512,8192]"),
+        # Grouped K/V heads at the page's Llama-3-8B shape, 32 query heads and
+        # 8 K/V heads ("Attention from First Principles", section 6), and MQA
+        # (one K/V head): the h_kv in {1, 8, 32} sweep of its Exercise F.
+        Workload("gqa_prefill2048_bf16", 2, 32, 2048, 2048, 128, "bf16", True, 6, Hkv=8,
+                 description="causal GQA prefill, 32 query heads over 8 K/V heads, S=2048"),
+        Workload("gqa_decode8192_bf16", 64, 32, 1, 8192, 128, "bf16", False, 7, (512, 8192),
+                 Hkv=8, description="GQA decode, 32 query heads over 8 K/V heads, capacity "
+                                    "8192, lengths U[512,8192]"),
+        Workload("mqa_decode8192_bf16", 64, 32, 1, 8192, 128, "bf16", False, 8, (512, 8192),
+                 Hkv=1, description="MQA decode, 32 query heads over one K/V head, capacity "
+                                    "8192, lengths U[512,8192]"),
     ]
 }
 
@@ -110,15 +126,20 @@ def _valid_rows(w: Workload, lens: Optional[np.ndarray], b: int, tensor: str) ->
 def make_tensor(w: Workload, tensor: str, lens: Optional[np.ndarray] = None,
                 pairs: Optional[Iterable[tuple]] = None, pad_fill: float = 0.0) -> np.ndarray:
     """Draw one of q/k/v.  Returns float32 [B,H,S,d] for "f32" workloads and
-    uint16 bf16 bits for "bf16".  With ``pairs`` (an iterable of (b, h)), only
-    those slices are drawn and the result is [len(pairs), 1, S, d]."""
+    uint16 bf16 bits for "bf16" (k and v have the workload's K/V head count).
+    With ``pairs`` (an iterable of (b, h) query heads), only those slices are
+    drawn -- for k and v, the slice of each pair's K/V head h // (H // H_kv)
+    -- and the result is [len(pairs), 1, S, d]."""
     S = w.Sq if tensor == "q" else w.Skv
+    heads = w.H if tensor == "q" else w.kv_heads
+    group = w.H // w.kv_heads
     out_dtype = np.float32 if w.dtype == "f32" else np.uint16
     if pairs is None:
-        sel = [(b, h) for b in range(w.B) for h in range(w.H)]
-        shape = (w.B, w.H, S, w.d)
+        sel = [(b, h) for b in range(w.B) for h in range(heads)]
+        shape = (w.B, heads, S, w.d)
     else:
-        sel = list(pairs)
+        # pairs name query heads; key/value slices are those of their K/V head
+        sel = [(b, h if tensor == "q" else h // group) for b, h in pairs]
         shape = (len(sel), 1, S, w.d)
     if w.dtype == "f32":
         fill = np.float32(pad_fill)
@@ -150,14 +171,17 @@ def make_inputs(w: Workload, pairs: Optional[Sequence[tuple]] = None,
 
 
 def random_problem(seed: int, B: int, H: int, Sq: int, Skv: int, d: int, dtype: str = "f32",
-                   kv_lens: Optional[Sequence[int]] = None, dv: Optional[int] = None) -> dict:
+                   kv_lens: Optional[Sequence[int]] = None, dv: Optional[int] = None,
+                   Hkv: Optional[int] = None) -> dict:
     """A small ad-hoc problem with every row drawn (pad rows included): used by
-    tests that sweep many shapes.  dtype "f64", "f32" or "bf16" (uint16 bits)."""
+    tests that sweep many shapes.  dtype "f64", "f32" or "bf16" (uint16 bits);
+    k and v have Hkv heads (default H)."""
     rng = np.random.default_rng(np.random.SeedSequence([seed, 99]))
     dv = d if dv is None else dv
+    Hkv = H if Hkv is None else Hkv
     q = rng.standard_normal((B, H, Sq, d), dtype=np.float32)
-    k = rng.standard_normal((B, H, Skv, d), dtype=np.float32)
-    v = rng.standard_normal((B, H, Skv, dv), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, Skv, d), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, Skv, dv), dtype=np.float32)
     if dtype == "bf16":
         q, k, v = bf16_bits(q), bf16_bits(k), bf16_bits(v)
     elif dtype == "f64":
@@ -206,12 +230,15 @@ def device_inputs(w: Workload, device="cuda", pad_fill: float = 0.0) -> dict:
     lens = kv_lens_for(w)
     tdtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
     res = {}
+    group = w.H // w.kv_heads
     for name, S in (("q", w.Sq), ("k", w.Skv), ("v", w.Skv)):
-        t = torch.empty((w.B, w.H, S, w.d), dtype=tdtype, device=device)
+        heads = w.H if name == "q" else w.kv_heads
+        t = torch.empty((w.B, heads, S, w.d), dtype=tdtype, device=device)
         for b in range(w.B):
-            part = make_tensor(w, name, lens, pairs=[(b, h) for h in range(w.H)],
-                               pad_fill=pad_fill)
-            t[b].copy_(to_torch(part.reshape(w.H, S, w.d), device))
+            # one query head per K/V head selects that K/V head's slice
+            pairs = [(b, h * (1 if name == "q" else group)) for h in range(heads)]
+            part = make_tensor(w, name, lens, pairs=pairs, pad_fill=pad_fill)
+            t[b].copy_(to_torch(part.reshape(heads, S, w.d), device))
         res[name] = t
     res["kv_lens"] = None if lens is None else torch.from_numpy(lens).to(device)
     res["kv_lens_host"] = lens
