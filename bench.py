@@ -54,10 +54,76 @@ def prefill_flops(w, lens=None) -> float:
 
 
 def decode_bytes(w, lens) -> float:
-    """Bytes the decode must move: valid K and V rows, q, out, kv_lens."""
-    kv = 2 * 2 * w.d * w.H * int(sum(int(min(max(int(x), 0), w.Skv)) for x in lens))
+    """Bytes the decode must move: valid K and V rows (of the K/V heads),
+    q, out, kv_lens."""
+    kv = 2 * 2 * w.d * w.kv_heads * int(sum(int(min(max(int(x), 0), w.Skv)) for x in lens))
     qo = 2 * (2 * w.B * w.H * w.d)
     return float(kv + qo + 4 * w.B)
+
+
+def decode_flops(w, lens) -> float:
+    """4*d flops per (query head, valid key) pair."""
+    return 4.0 * w.d * w.H * float(sum(int(min(max(int(x), 0), w.Skv)) for x in lens))
+
+
+def timed_calls(attn, fn, steps, warmup, kernels):
+    """Run fn warmup + steps times; the average HIP-event duration (ms) of
+    each named library kernel over the timed calls."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    attn.profile_enable(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    prof = attn.profile_read()
+    attn.profile_enable(False)
+    return {k: (prof[k][1] / prof[k][0] if prof[k][0] else float("nan")) for k in kernels}
+
+
+def gqa_decode_sweep(attn, W, dev, steps, warmup):
+    """Decode at 32, 8 and 1 K/V heads for 32 query heads (the page's
+    Exercise F): bytes moved fall by H / H_kv while the flops stay, so the
+    measured intensity should track H / H_kv."""
+    import torch
+    rows = []
+    for name in ("decode8192_bf16", "gqa_decode8192_bf16", "mqa_decode8192_bf16"):
+        w = W.WORKLOADS[name]
+        x = W.device_inputs(w, dev)
+        out = torch.empty_like(x["q"])
+        fn = lambda: attn.fwd(x["q"], x["k"], x["v"], out, causal=w.causal,
+                              kv_lens=x["kv_lens"], scale=x["scale"])
+        t = timed_calls(attn, fn, steps, warmup, ("decode_bf16_partial", "decode_bf16_combine"))
+        ms = t["decode_bf16_partial"] + t["decode_bf16_combine"]
+        lens = x["kv_lens_host"]
+        nbytes, flops = decode_bytes(w, lens), decode_flops(w, lens)
+        rows.append({"workload": name, "H": w.H, "H_kv": w.kv_heads, "ms_per_call": ms,
+                     "GB/s": nbytes / (ms * 1e-3) / 1e9, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+                     "intensity_flop_per_byte": flops / nbytes,
+                     "partial_avg_launch_ms": t["decode_bf16_partial"]})
+        del x, out
+        torch.cuda.empty_cache()
+    return rows
+
+
+def prefill_sweep(attn, W, dev, steps, warmup):
+    """Causal prefill, B=1, H=32, d=128, over S = 128 .. 8192: TFLOP/s by S
+    (the page's Exercise D: work grows as S^2, so time should too once the
+    GPU is full)."""
+    import torch
+    rows = []
+    for S in (128, 256, 512, 1024, 2048, 4096, 8192):
+        w = W.Workload(f"prefill{S}_sweep", 1, 32, S, S, 128, "bf16", True, 100 + S)
+        x = W.device_inputs(w, dev)
+        out = torch.empty_like(x["q"])
+        fn = lambda: attn.fwd(x["q"], x["k"], x["v"], out, causal=True, scale=x["scale"])
+        ms = timed_calls(attn, fn, steps, warmup, ("prefill_bf16_mfma",))["prefill_bf16_mfma"]
+        flops = prefill_flops(w)
+        rows.append({"S": S, "avg_launch_ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12})
+        del x, out
+        torch.cuda.empty_cache()
+    return rows
 
 
 def profiled_traffic(kernel: str, workload: str):
@@ -94,9 +160,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--parts", default="prefill,decode",
-                    help="comma list of prefill, decode, copy (default prefill,decode); "
-                         "copy adds a plain 1 GiB device-to-device copy per step, the "
-                         "known-size kernel that scales the HBM byte counters")
+                    help="comma list of prefill, decode, copy, gqa, sweep (default "
+                         "prefill,decode); copy adds a plain 1 GiB device-to-device copy per "
+                         "step, the known-size kernel that scales the HBM byte counters; gqa "
+                         "measures decode at 32, 8 and 1 K/V heads for 32 query heads; sweep "
+                         "measures causal prefill over S = 128 .. 8192 (both reported beside "
+                         "the step, under their own keys)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="oracle threads for the CPU baseline (default min(16, cores))")
@@ -230,6 +299,13 @@ def main():
         result["value"] = result["decode"]["value"]
         result["unit"] = "GB/s"
         result["roofline"] = result["decode"]["roofline"]
+
+    if "gqa" in parts:
+        print("[bench] grouped-head decode sweep", file=sys.stderr, flush=True)
+        result["gqa_decode"] = gqa_decode_sweep(attn, W, dev, args.steps, args.warmup)
+    if "sweep" in parts:
+        print("[bench] prefill S sweep", file=sys.stderr, flush=True)
+        result["prefill_sweep"] = prefill_sweep(attn, W, dev, args.steps, args.warmup)
 
     if not args.no_cpu_baseline and "prefill" in parts:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
