@@ -83,9 +83,9 @@ def timed_calls(attn, fn, steps, warmup, kernels):
 
 
 def gqa_decode_sweep(attn, W, dev, steps, warmup):
-    """Decode at 32, 8 and 1 K/V heads for 32 query heads (the page's
-    Exercise F): bytes moved fall by H / H_kv while the flops stay, so the
-    measured intensity should track H / H_kv."""
+    """Decode at 32, 8 and 1 K/V heads for 32 query heads ("Attention from
+    First Principles", section 10, exercise F): bytes moved fall by H / H_kv
+    while the flops stay, so the intensity is H / H_kv."""
     import torch
     rows = []
     for name in ("decode8192_bf16", "gqa_decode8192_bf16", "mqa_decode8192_bf16"):
@@ -109,8 +109,8 @@ def gqa_decode_sweep(attn, W, dev, steps, warmup):
 
 def prefill_sweep(attn, W, dev, steps, warmup):
     """Causal prefill, B=1, H=32, d=128, over S = 128 .. 8192: TFLOP/s by S
-    (the page's Exercise D: work grows as S^2, so time should too once the
-    GPU is full)."""
+    ("Attention from First Principles", section 10, exercise D: work grows
+    as S^2, so time should too once the GPU is full)."""
     import torch
     rows = []
     for S in (128, 256, 512, 1024, 2048, 4096, 8192):

@@ -72,9 +72,10 @@ WORKLOADS = {
         Workload("decode8192_bf16", 64, 32, 1, 8192, 128, "bf16", False, 5, (512, 8192),
                  description="decode, one query against a KV cache of capacity 8192, "
                              "lengths U[512,8192]"),
-        # Grouped K/V heads at the page's Llama-3-8B shape, 32 query heads and
-        # 8 K/V heads ("Attention from First Principles", section 6), and MQA
-        # (one K/V head): the h_kv in {1, 8, 32} sweep of its Exercise F.
+        # Grouped K/V heads at the GQA(8) shape of the Llama-3-8B example, 32
+        # query heads and 8 K/V heads ("Attention from First Principles",
+        # section 7), and MQA (one K/V head): the h_kv in {1, 8, 32} sweep of
+        # that page's section 10, exercise F.
         Workload("gqa_prefill2048_bf16", 2, 32, 2048, 2048, 128, "bf16", True, 6, Hkv=8,
                  description="causal GQA prefill, 32 query heads over 8 K/V heads, S=2048"),
         Workload("gqa_decode8192_bf16", 64, 32, 1, 8192, 128, "bf16", False, 7, (512, 8192),
