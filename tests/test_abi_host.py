@@ -118,7 +118,7 @@ def test_gqa_workspace_sizes():
     # one partial per query head and split, whatever the K/V head count
     for Hkv in (1, 8, 32):
         w = lib.attn_workspace_bytes_gqa(64, 32, Hkv, 1, 8192, 128, BF16)
-        assert w >= 64 * 32 * (8192 // 128) * (128 + 2) * 4 and w % 256 == 0
+        assert w >= 64 * 32 * (8192 // 1024) * (128 + 2) * 4 and w % 256 == 0
         assert attn.workspace_bytes(64, 32, 1, 8192, 128, BF16, kv_heads=Hkv) == w
     assert lib.attn_workspace_bytes_gqa(64, 32, 32, 1, 8192, 128, BF16) == \
         attn.workspace_bytes(64, 32, 1, 8192, 128, BF16)
