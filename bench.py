@@ -118,9 +118,12 @@ def prefill_sweep(attn, W, dev, steps, warmup):
         x = W.device_inputs(w, dev)
         out = torch.empty_like(x["q"])
         fn = lambda: attn.fwd(x["q"], x["k"], x["v"], out, causal=True, scale=x["scale"])
-        ms = timed_calls(attn, fn, steps, warmup, ("prefill_bf16_mfma",))["prefill_bf16_mfma"]
+        t = timed_calls(attn, fn, steps, warmup, ("prefill_bf16_mfma", "prefill_bf16_combine"))
+        comb = t["prefill_bf16_combine"]
+        ms = t["prefill_bf16_mfma"] + (0.0 if math.isnan(comb) else comb)
         flops = prefill_flops(w)
-        rows.append({"S": S, "avg_launch_ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12})
+        rows.append({"S": S, "ms_per_call": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+                     "key_splits": attn.workspace_bytes(1, 32, S, S, 128, attn.BF16) > 0})
         del x, out
         torch.cuda.empty_cache()
     return rows

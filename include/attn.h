@@ -109,6 +109,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int 
 /*
  * attn_workspace_bytes -- device bytes attn_fwd_ws needs for this problem
  * (0 when the chosen kernel needs none).  Returns 0 for invalid arguments.
+ * Decode needs one fp32 (m, l, acc[d]) partial per query head and key split;
+ * prefill needs one per query row and key split only when a short query
+ * chunk against a long cache leaves CUs idle (fewer than 256 query tiles of
+ * 256 rows) and the key range is split.
  */
 size_t attn_workspace_bytes(int B, int H, int Sq, int Skv, int d, int dtype);
 

@@ -123,13 +123,27 @@ def test_gqa_workspace_sizes():
     assert lib.attn_workspace_bytes_gqa(64, 32, 32, 1, 8192, 128, BF16) == \
         attn.workspace_bytes(64, 32, 1, 8192, 128, BF16)
     assert lib.attn_workspace_bytes_gqa(64, 32, 5, 1, 8192, 128, BF16) == 0
-    assert lib.attn_workspace_bytes_gqa(1, 32, 8, 2048, 2048, 128, BF16) == 0
+    assert lib.attn_workspace_bytes_gqa(2, 32, 8, 4096, 4096, 128, BF16) == 0
+
+
+def test_prefill_split_workspace():
+    # a grid of at least 2 blocks per CU needs no splits and no workspace
+    assert attn.workspace_bytes(1, 32, 4096, 4096, 128, BF16) == 0
+    assert attn.workspace_bytes(4, 32, 1024, 1024, 128, BF16) == 0
+    # a short query chunk against a long cache splits the key range: one
+    # (m, l, acc[d]) partial per query row and split
+    w = attn.workspace_bytes(1, 32, 512, 4096, 128, BF16)
+    assert w >= 1 * 32 * 512 * 2 * (128 + 2) * 4 and w % 256 == 0
+    assert attn.workspace_bytes(1, 32, 256, 8192, 64, BF16, kv_heads=8) > 0
+    # at most 16 splits, each of at least 8 key tiles
+    assert attn.workspace_bytes(1, 1, 2, 64, 128, BF16) == 0
+    assert attn.workspace_bytes(1, 1, 2, 100000, 128, BF16) <= 16 * 2 * (128 + 2) * 4 + 512
 
 
 def test_profile_names():
     names = attn.profile_names()
     assert names == ["prefill_bf16_mfma", "decode_bf16_partial", "decode_bf16_combine",
-                     "generic_f32"]
+                     "generic_f32", "prefill_bf16_combine"]
 
 
 def test_python_layer_rejects_bad_tensors():

@@ -162,3 +162,46 @@ def test_workload_decode8192_sampled():
     lens = W.kv_lens_for(w)
     bs = [int(np.argmin(lens)), int(np.argmax(lens)), 0, 17, 40, 63]
     _sampled(w, [(b, h) for b in bs for h in (0, 11, 31)])
+
+
+# ------------------------------------------- chunked prefill (1 < Sq < Skv)
+def test_chunked_prefill_matches_full_prefill():
+    """Cached vs uncached at scale: the last c rows of a causal prefill over S
+    tokens equal a prefill of those c queries against the full S-key cache
+    (bottom-right alignment).  The short chunk runs with its key range split
+    over several blocks and merged, the full prefill without, so they agree
+    to rounding; both are checked against the oracle on sampled heads."""
+    import torch
+    B, H, S, d = 1, 32, 2048, 128
+    w = W.Workload("chunk_check", B, H, S, S, d, "bf16", True, 77)
+    x = W.device_inputs(w)
+    full = attn.fwd(x["q"], x["k"], x["v"], causal=True, scale=x["scale"])
+    for c in (512, 100, 2):
+        _say("chunked prefill, chunk", c, "plan workspace",
+             attn.workspace_bytes(B, H, c, S, d, attn.BF16))
+        qc = x["q"][:, :, S - c:].contiguous()
+        part = attn.fwd(qc, x["k"], x["v"], causal=True, scale=x["scale"])
+        torch.cuda.synchronize()
+        got, ref = W.from_torch(part), W.from_torch(full[:, :, S - c:])
+        assert np.max(np.abs(got - ref)) <= BF16_TOL, c
+        sub = W.make_inputs(w, pairs=[(0, 0), (0, 21)])
+        oref = oracle.attention(sub["q"][:, :, S - c:], sub["k"], sub["v"], sub["scale"], True)
+        assert_matches(got[0, [0, 21]][:, None], oref, BF16_TOL, what=f"chunk {c}")
+
+
+CHUNK_CASES = [
+    # seed, B, H, Sq, Skv, d, causal, kv_lens: few query tiles against long caches
+    (61, 1, 4, 300, 3000, 128, 1, None),
+    (62, 2, 2, 2, 5000, 64, 1, [5000, 2047]),
+    (63, 1, 8, 64, 4096, 128, 0, None),
+    (64, 3, 1, 257, 2600, 128, 1, [2600, 300, 0]),
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=lambda c: f"s{c[0]}")
+def test_split_prefill_shapes(case):
+    seed, B, H, Sq, Skv, d, causal, lens = case
+    _say("split prefill case", case, "workspace", attn.workspace_bytes(B, H, Sq, Skv, d, attn.BF16))
+    assert attn.workspace_bytes(B, H, Sq, Skv, d, attn.BF16) > 0
+    prob = W.random_problem(seed, B, H, Sq, Skv, d, "bf16", lens)
+    check_problem(prob, causal, BF16_TOL, f"split prefill {case}")

@@ -216,8 +216,11 @@ const char* attn_kernel_for(int Sq, int Skv, int d, int dtype) {
 size_t attn_workspace_bytes_gqa(int B, int H, int Hkv, int Sq, int Skv, int d, int dtype) {
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
     if (check_shape(B, H, Hkv, Sq, Skv, d) != ATTN_OK) return 0;
-    if (choose_path(Sq, d, dtype) != kPathDecode) return 0;
-    return decode_workspace_bytes(B, H, Hkv, Skv, d);
+    switch (choose_path(Sq, d, dtype)) {
+        case kPathDecode: return decode_workspace_bytes(B, H, Hkv, Skv, d);
+        case kPathPrefill: return prefill_workspace_bytes(B, H, Sq, Skv, d);
+        default: return 0;
+    }
 }
 
 size_t attn_workspace_bytes(int B, int H, int Sq, int Skv, int d, int dtype) {
@@ -317,6 +320,7 @@ const char* attn_profile_name(int kernel) {
         case kDecodePartialBf16: return "decode_bf16_partial";
         case kDecodeCombineBf16: return "decode_bf16_combine";
         case kGenericF32: return "generic_f32";
+        case kPrefillCombineBf16: return "prefill_bf16_combine";
         default: return nullptr;
     }
 }

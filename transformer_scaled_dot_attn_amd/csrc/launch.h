@@ -29,6 +29,15 @@ DecodePlan decode_plan(int B, int H, int Hkv, int Skv);
 size_t decode_workspace_bytes(int B, int H, int Hkv, int Skv, int d);
 int decode_heads_per_block(int H, int Hkv);  // query heads one decode block serves
 
+// Prefill plan: key-range splits per query tile (1 = none, no workspace).
+struct PrefillPlan {
+    int nsplit;
+};
+PrefillPlan prefill_plan(int B, int H, int Sq, int Skv);
+size_t prefill_workspace_bytes(int B, int H, int Sq, int Skv, int d);
+
+inline size_t round_up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 // Profiling hook: the front end brackets each launch when timing is on.
 struct KernelTimer {
     virtual void begin(int kernel, hipStream_t s) = 0;
@@ -38,7 +47,7 @@ struct KernelTimer {
 KernelTimer* active_timer();  // nullptr when timing is off
 
 enum KernelId { kPrefillBf16 = 0, kDecodePartialBf16 = 1, kDecodeCombineBf16 = 2, kGenericF32 = 3,
-                kNumKernels = 4 };
+                kPrefillCombineBf16 = 4, kNumKernels = 5 };
 
 hipError_t launch_generic_f32(const LaunchArgs& a);
 hipError_t launch_prefill_bf16(const LaunchArgs& a);

@@ -53,6 +53,8 @@
 // Grouped key/value heads (GQA / MQA): query head h reads K/V head
 // h / (H / Hkv) ("Attention from First Principles", section "MHA, GQA, MQA
 // -- the KV cache lever"); nothing else changes.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
     const int32_t* __restrict__ kv_lens, int BH, int H, int Hkv, int Sq, int Skv, float scale_log2,
-    int causal, int nqt) {
+    int causal, int nqt, int nsplit, float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
     using S = Shape<D>;
     __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][S::kTileK];
     __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][S::kTileV];
@@ -109,8 +111,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int half = lane >> 5;
 
     const int bid = blockIdx.x;
-    const int qt = nqt - 1 - bid / BH;
-    const int jb = bid - (bid / BH) * BH;
+    const int qt = nqt - 1 - bid / (BH * nsplit);
+    const int rem = bid - (bid / (BH * nsplit)) * (BH * nsplit);
+    const int split = rem / BH;  // key-range split of this query tile
+    const int jb = rem - split * BH;
     // Blocks are dealt to the 8 XCDs round-robin by id.  With BH a multiple
     // of 8, XCD x runs the contiguous (b, h) pairs x*BH/8 .. (x+1)*BH/8 - 1,
     // so every query tile of a head, and the query heads that share a K/V
@@ -125,7 +129,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 
     uint16_t* obase = out + (size_t)bh * Sq * D;
     if (q0 >= n) {
-        // every row of this tile is padding: write zeros
+        // every row of this tile is padding: write zeros (split 0 does it;
+        // the split combine writes zeros for these rows itself)
+        if (nsplit > 1) return;
         const int rows = min(kBM, Sq - q0);
         const u32x4 z = {0, 0, 0, 0};
         for (int e = tid; e < rows * S::kChunks; e += kThreads)
@@ -133,15 +139,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         return;
     }
 
-    // keys the whole block may see, and this wave's limits
+    // keys the whole query tile may see, this block's split of them, and
+    // this wave's limits: tiles t0 <= t < t1 of the block, t < t1w of the wave
     const int kv_hi = causal ? min(L, off + min(q0 + kBM, n)) : L;
-    const int ntiles = (kv_hi + kBN - 1) / kBN;
+    const int ntiles_q = (kv_hi + kBN - 1) / kBN;
+    const int per_split = (ntiles_q + nsplit - 1) / nsplit;
+    const int t0 = min(ntiles_q, split * per_split);
+    const int t1 = min(ntiles_q, t0 + per_split);
     const int qw = q0 + wave * 32;
     const bool wave_live = qw < n;
     const int p_lo = off + qw;
     const int p_hi = off + min(qw + 32, n) - 1;
     const int kv_hi_w = wave_live ? (causal ? min(L, p_hi + 1) : L) : 0;
-    const int ntiles_w = (kv_hi_w + kBN - 1) / kBN;  // tiles this wave computes
+    const int t1w = min(t1, (kv_hi_w + kBN - 1) / kBN);  // this wave computes t0 <= t < t1w
     const int kfull_w = causal ? min(L, p_lo + 1) : L;
 
     // this lane's query
@@ -393,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // a branch the compiler's wait counts stay exact (each stash waits only
     // for its own loads).
     auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-        const bool pipe = t + 1 < ntiles_w;  // this wave scores tile t+1
+        const bool pipe = t + 1 < t1w;  // this wave scores tile t+1
         fetch(k, t + 2, kreg, kok);
         // S^T(t+1) under which P(t) is formed
         if (pipe) score(t + 1, sn, &sc);
@@ -403,7 +413,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
             // P(t) V(t) under which the maximum of S^T(t+1) is found
             const float mx = mix(t, &sn);
             reference(mx);
-        } else if (t < ntiles_w) {
+        } else if (t < t1w) {
             weigh(sc);
             mix(t, nullptr);
         }
@@ -412,24 +422,50 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         __syncthreads();
     };
 
-    // prologue: K(0), V(0), K(1) staged; S^T(0) scored and its reference set
-    fetch(k, 0, kreg, kok);
-    fetch(v, 0, vreg, vok);
-    stash_k(0);
-    stash_v(0);
-    fetch(k, 1, kreg, kok);
-    stash_k(1);
+    // prologue: K(t0), V(t0), K(t0+1) staged; S^T(t0) scored and its
+    // reference set
+    fetch(k, t0, kreg, kok);
+    fetch(v, t0, vreg, vok);
+    stash_k(t0);
+    stash_v(t0);
+    fetch(k, t0 + 1, kreg, kok);
+    stash_k(t0 + 1);
     __syncthreads();
-    if (ntiles_w > 0) {
-        score(0, s0, nullptr);
-        mask(0, s0);
+    if (t0 < t1w) {
+        score(t0, s0, nullptr);
+        mask(t0, s0);
         reference(scan(s0));
     }
-    __syncthreads();  // K(0) is read by every wave before K(2) replaces it
+    __syncthreads();  // K(t0) is read by every wave before K(t0+2) replaces it
 
-    for (int t = 0; t < ntiles; t += 2) {
+    for (int t = t0; t < t1; t += 2) {
         step(t, s0, s1);
-        if (t + 1 < ntiles) step(t + 1, s1, s0);
+        if (t + 1 < t1) step(t + 1, s1, s0);
+    }
+
+    if (nsplit > 1) {
+        // ---- split epilogue: this split's (m, l, acc) of every live row, the
+        // reference in exp2 units (-inf with l = 0 when the split saw none of
+        // the row's keys); the combine kernel merges the splits.
+        if (q_live) {
+            const size_t unit = ((size_t)bh * Sq + qi) * nsplit + split;
+            const float l_tot = halves_sum(l_run);
+            float* arow = ws_acc + unit * D;
+#pragma unroll
+            for (int db = 0; db < S::kDBlocks; ++db)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int d0 = db * 32 + 8 * rg + 4 * half;
+                    const f32x4 w4 = {oacc[db][4 * rg], oacc[db][4 * rg + 1], oacc[db][4 * rg + 2],
+                                      oacc[db][4 * rg + 3]};
+                    *reinterpret_cast<f32x4*>(arow + d0) = w4;
+                }
+            if (half == 0) {
+                ws_ml[unit * 2] = m_run == -INFINITY ? -INFINITY : m_run * scale_log2;
+                ws_ml[unit * 2 + 1] = l_tot;
+            }
+        }
+        return;
     }
 
     // ---- epilogue: out = acc / l, rows past n_b are zero
@@ -452,27 +488,126 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     }
 }
 
+// Merge of the key-range splits of each query row (log-sum-exp rule, as at
+// decode): M = max_s m_s, l = sum_s l_s 2^(m_s - M),
+// out = (sum_s acc_s 2^(m_s - M)) / l; padded rows are written as zeros.
+// Each thread merges 4 consecutive columns of one row with 16-byte loads;
+// a block covers 256 / (D/4) rows.
+constexpr int kMaxSplit = 16;
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_combine_kernel(
+    const int32_t* __restrict__ kv_lens, int H, int Sq, int Skv, int nsplit, size_t nrows,
+    const float* __restrict__ ws_acc, const float* __restrict__ ws_ml, uint16_t* __restrict__ out) {
+    constexpr int TPR = D / 4;  // threads per row
+    constexpr int ROWS = 256 / TPR;
+    const int tid = threadIdx.x;
+    const int c = (tid % TPR) * 4;
+    const size_t row = (size_t)blockIdx.x * ROWS + tid / TPR;  // (b*H + h)*Sq + i
+    if (row >= nrows) return;
+    const int bh = (int)(row / Sq);
+    const int i = (int)(row - (size_t)bh * Sq);
+    const int L = valid_length(kv_lens, bh / H, Skv);
+    const int n = Sq < L ? Sq : L;
+    u32x2 res = {0, 0};
+    if (i < n) {
+        const float* ml = ws_ml + row * nsplit * 2;
+        float w[kMaxSplit];
+        float M = -INFINITY;
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplit; ++sp)
+            if (sp < nsplit) M = fmaxf(M, ml[2 * sp]);
+        float lt = 0.0f;
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplit; ++sp) {
+            w[sp] = 0.0f;
+            if (sp < nsplit) {
+                const float m = ml[2 * sp];
+                w[sp] = m == -INFINITY ? 0.0f : fast_exp2(m - M);
+                lt = fmaf(ml[2 * sp + 1], w[sp], lt);
+            }
+        }
+        const float* ac = ws_acc + row * nsplit * D + c;
+        f32x4 at = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplit; ++sp)
+            if (sp < nsplit) {
+                const f32x4 a4 = *reinterpret_cast<const f32x4*>(ac + (size_t)sp * D);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) at[e] = fmaf(a4[e], w[sp], at[e]);
+            }
+        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+        res[0] = pack_bf16(at[0] * inv, at[1] * inv);
+        res[1] = pack_bf16(at[2] * inv, at[3] * inv);
+    }
+    *reinterpret_cast<u32x2*>(out + row * D + c) = res;
+}
+
 }  // namespace
+
+PrefillPlan prefill_plan(int B, int H, int Sq, int Skv) {
+    // Each query tile is one block.  When that leaves CUs idle (short query
+    // chunks against a long cache), the key range of every query tile is
+    // split over about one block per CU in all, each split at least 16 key
+    // tiles, and the splits are merged by a second kernel.  Measured on
+    // 1-4 x 32 heads: 512 queries against 4096 keys 117 -> 64 us (4 splits),
+    // 256 against 8192 214 -> 66 us (8 splits); grids of 256 blocks or more
+    // are faster unsplit, the merge costing more than the idle CUs.
+    const long blocks = (long)((Sq + kBM - 1) / kBM) * B * H;
+    const long tiles = (Skv + kBN - 1) / kBN;
+    long nsplit = 256 / blocks;
+    nsplit = std::min({nsplit, tiles / 16, (long)kMaxSplit});
+    return PrefillPlan{(int)std::max(1L, nsplit)};
+}
+
+size_t prefill_workspace_bytes(int B, int H, int Sq, int Skv, int d) {
+    const PrefillPlan p = prefill_plan(B, H, Sq, Skv);
+    if (p.nsplit == 1) return 0;
+    const size_t units = (size_t)B * H * Sq * p.nsplit;
+    return round_up256(units * d * sizeof(float)) + round_up256(units * 2 * sizeof(float));
+}
 
 hipError_t launch_prefill_bf16(const LaunchArgs& a) {
     const int nqt = (a.Sq + kBM - 1) / kBM;
     const int BH = a.B * a.H;
-    const dim3 grid((unsigned)((long)nqt * BH));
+    const PrefillPlan p = prefill_plan(a.B, a.H, a.Sq, a.Skv);
+    const dim3 grid((unsigned)((long)nqt * BH * p.nsplit));
     const uint16_t* q = static_cast<const uint16_t*>(a.q);
     const uint16_t* k = static_cast<const uint16_t*>(a.k);
     const uint16_t* v = static_cast<const uint16_t*>(a.v);
     uint16_t* o = static_cast<uint16_t*>(a.out);
+    float* ws_acc = nullptr;
+    float* ws_ml = nullptr;
+    if (p.nsplit > 1) {
+        const size_t units = (size_t)BH * a.Sq * p.nsplit;
+        ws_acc = static_cast<float*>(a.workspace);
+        ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
+                                         round_up256(units * a.d * sizeof(float)));
+    }
     const float sl = a.scale * kLog2e;
     KernelTimer* t = active_timer();
     if (t) t->begin(kPrefillBf16, a.stream);
     if (a.d == 128)
         hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(kThreads), 0, a.stream, q, k, v, o,
-                           a.kv_lens, BH, a.H, a.Hkv, a.Sq, a.Skv, sl, a.causal, nqt);
+                           a.kv_lens, BH, a.H, a.Hkv, a.Sq, a.Skv, sl, a.causal, nqt, p.nsplit,
+                           ws_acc, ws_ml);
     else
         hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(kThreads), 0, a.stream, q, k, v, o,
-                           a.kv_lens, BH, a.H, a.Hkv, a.Sq, a.Skv, sl, a.causal, nqt);
+                           a.kv_lens, BH, a.H, a.Hkv, a.Sq, a.Skv, sl, a.causal, nqt, p.nsplit,
+                           ws_acc, ws_ml);
     hipError_t e = hipGetLastError();
     if (t) t->end(kPrefillBf16, a.stream);
+    if (e != hipSuccess || p.nsplit == 1) return e;
+    if (t) t->begin(kPrefillCombineBf16, a.stream);
+    const size_t rows = (size_t)BH * a.Sq;
+    if (a.d == 128)
+        hipLaunchKernelGGL(prefill_combine_kernel<128>, dim3((unsigned)((rows + 7) / 8)), dim3(256),
+                           0, a.stream, a.kv_lens, a.H, a.Sq, a.Skv, p.nsplit, rows, ws_acc, ws_ml, o);
+    else
+        hipLaunchKernelGGL(prefill_combine_kernel<64>, dim3((unsigned)((rows + 15) / 16)), dim3(256),
+                           0, a.stream, a.kv_lens, a.H, a.Sq, a.Skv, p.nsplit, rows, ws_acc, ws_ml, o);
+    e = hipGetLastError();
+    if (t) t->end(kPrefillCombineBf16, a.stream);
     return e;
 }
 
