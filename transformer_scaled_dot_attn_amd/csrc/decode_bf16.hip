@@ -3,23 +3,25 @@
 // Decode reads the whole valid cache and does little arithmetic per byte
 // ("Attention from First Principles", section 6: a matrix-vector product
 // whose intensity is about 1 for multi-head attention), so this path is
-// built for HBM bandwidth, not for the matrix cores:
-//   * partial kernel: one block per (b, K/V head, group of HB query heads,
-//     split of `chunk` keys).  With grouped key/value heads (GQA / MQA:
-//     query head h reads K/V head h / (H / H_kv), "Attention from First
-//     Principles", section "MHA, GQA, MQA -- the KV cache lever") the block
-//     scores each K/V row against all HB query heads it serves, so K and V
-//     are read once per group instead of once per query head -- the rise in
-//     decode intensity to H / H_kv that the same page's section 6 derives.
-//     Each key
-//     row (d bf16 = 2d bytes) is read by d/8 lanes with one 16-byte load
-//     each, so every wave-wide load covers whole contiguous rows.  Logits use
-//     v_dot2 on the raw bf16 pairs (exact products, fp32 sums), reduced over
-//     the row's lanes with DPP.  K and V are read once, with non-temporal
-//     loads; each lane keeps two steps of 4 rows in flight.  Each lane group keeps a running maximum m,
-//     normaliser l and an fp32 accumulator for its 8 columns (the online
-//     softmax recurrence); the block merges its groups in LDS and writes one
-//     (m, l, acc[d]) partial.  Keys past the valid length are never loaded.
+// built for HBM bandwidth.  With grouped key/value heads (GQA / MQA: query
+// head h reads K/V head h / (H / H_kv), same page, section "MHA, GQA, MQA --
+// the KV cache lever") each K/V row serves H / H_kv query heads, the rise in
+// decode intensity that section 6 derives, and the kernels read it once per
+// group of query heads:
+//   * vector partial kernel (multi-head, and 2 query heads per K/V head):
+//     one block per (b, K/V head, group of HB query heads, split of `chunk`
+//     keys).  Each key row (d bf16 = 2d bytes) is read by d/8 lanes with one
+//     16-byte load each, so every wave-wide load covers whole contiguous
+//     rows.  Logits use v_dot2 on the raw bf16 pairs (exact products, fp32
+//     sums), reduced over the row's lanes with DPP, once per served head.  K
+//     and V are read once, with non-temporal loads; each lane keeps two steps
+//     of 4 rows in flight.  Each lane group keeps a running maximum m,
+//     normaliser l and an fp32 accumulator for its 8 columns per head (the
+//     online softmax recurrence); the block merges its groups in LDS and
+//     writes one (m, l, acc[d]) partial per head.  Keys past the valid
+//     length are never loaded.
+//   * matrix-core partial kernel (4 or more query heads per K/V head): the
+//     served heads are the columns of 32x32 MFMA tiles (below).
 //   * combine kernel: per (b, h), merges the partials with the log-sum-exp
 //     rule  M = max m_s,  l = sum l_s 2^(m_s - M),
 //     out = (sum acc_s 2^(m_s - M)) / l, and rounds to bf16.  L_b = 0 gives 0.
@@ -178,6 +180,194 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     }
 }
 
+// Matrix-core partial kernel for grouped K/V heads: one wavefront per (b,
+// K/V head, group of up to 32 query heads, split of `chunk` keys).  The
+// query heads a K/V head serves are the 32 columns of one MFMA tile (heads
+// past the group are zero columns), so per 32-key tile the wave computes
+// S^T = K Q^T with 8 (d/16) v_mfma_f32_32x32x16_bf16 -- K rows loaded from
+// memory straight into the A-operand layout, Q^T held as the B operand --
+// and O^T += V^T P^T with 8 (d/16) more, V^T read through
+// ds_read_b64_tr_b16 from the tile staged in LDS.  In both accumulators a
+// lane owns one query head, so the online softmax is lane-local plus one
+// half swap, as in the prefill kernel.  The matrix cores have ample headroom
+// (16 MFMAs per 16 KiB of K+V), so with grouped heads decode stays bound by
+// the bytes of K and V, read once per group of up to 32 query heads.
+template <int D>
+__global__ __launch_bounds__(64, 2) void decode_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ kv_lens, int H, int Hkv,
+    int Skv, float scale_log2, int chunk, int nsplit, int hgroups, float* __restrict__ ws_acc,
+    float* __restrict__ ws_ml) {
+    constexpr int kKSteps = D / 16;       // MFMA k-steps of K Q^T
+    constexpr int kDBlocks = D / 32;      // 32-row blocks of O^T
+    constexpr int kStrideV = D + 16;      // padded LDS row of V (elements)
+    constexpr int kChunks = D / 8;        // 16-byte chunks per row
+    constexpr int kVRows = 64 / kChunks;  // V rows per wave-wide load
+    constexpr int kVLoads = 32 / kVRows;  // wave-wide loads per 32-row V tile
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v[32 * kStrideV];
+
+    const int lane = threadIdx.x;
+    const int half = lane >> 5;
+    const int unit = blockIdx.x;
+    const int split = unit % nsplit;
+    const int g = unit / nsplit;
+    const int hgrp = g % hgroups;
+    const int bk = g / hgroups;                // b * Hkv + K/V head
+    const int b = bk / Hkv;
+    const int group = H / Hkv;
+    const int h0 = (bk - b * Hkv) * group + hgrp * 32;  // first query head served
+    const int nh = min(32, group - hgrp * 32);          // query heads served
+    const int L = valid_length(kv_lens, b, Skv);
+    const int k0 = split * chunk;
+    if (k0 >= L) return;  // the combine kernel reads only splits below L
+    const int k1 = min(k0 + chunk, L);
+
+    // Q^T fragments (B operand): lane l holds features 16*ks + 8*(l/32) .. +7
+    // of query head h0 + l%32 (zero past the group).
+    const int jh = lane & 31;
+    const bool live = jh < nh;
+    u32x4 qf[kKSteps];
+    {
+        const uint16_t* qrow = q + ((size_t)b * H + h0 + (live ? jh : 0)) * D + half * 8;
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks)
+            qf[ks] = live ? ldg16(qrow + ks * 16) : u32x4{0, 0, 0, 0};
+    }
+    const uint16_t* kb = k + (size_t)bk * Skv * D;
+    const uint16_t* vb = v + (size_t)bk * Skv * D;
+
+    // K tile rows in A-operand order (row = lane % 32, features
+    // 16*ks + 8*(lane/32) ..), V tile rows whole (kVRows rows per load).
+    // Rows at or past k1 are redirected to row k0 (valid; logits masked).
+    // A K load instruction covers 32 bytes of each of 32 rows, so K goes
+    // through the vector cache (the other 3/4 of each line are the next
+    // three loads): streaming (non-temporal) K loads measured 1.4x slower.
+    u32x4 kr[kKSteps], vr[kVLoads];
+    auto load_k = [&](int t0) {
+        const int row = t0 + jh;
+        const uint16_t* src = kb + (size_t)(row < k1 ? row : k0) * D + half * 8;
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) kr[ks] = ldg16(src + ks * 16);
+    };
+    auto load_v = [&](int t0) {
+#pragma unroll
+        for (int c = 0; c < kVLoads; ++c) {
+            const int row = t0 + c * kVRows + lane / kChunks;
+            vr[c] = ldg16_stream(vb + (size_t)(row < k1 ? row : k0) * D + (lane % kChunks) * 8);
+        }
+    };
+    //  V^T operand via ds_read_b64_tr_b16 (the prefill kernel's mapping):
+    //  within each 16-lane group, source lane i reads features col0 + 4*(i%4)
+    //  .. +3 of key row key0 + i/4; lanes of the second half take keys 4..7
+    //  (and 12..15) of each 16-key step, matching their P^T fragment.
+    const int n16 = lane & 15;
+    const int v_rd = (4 * half + (n16 >> 2)) * kStrideV + 16 * ((lane >> 4) & 1) + 4 * (n16 & 3);
+
+    f32x16 oacc[kDBlocks];
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    load_k(k0);
+    load_v(k0);
+    for (int t0 = k0; t0 < k1; t0 += 32) {
+        // V(t0) to LDS; the next tile's V loads reuse its registers
+#pragma unroll
+        for (int c = 0; c < kVLoads; ++c)
+            *reinterpret_cast<u32x4*>(lds_v + (c * kVRows + lane / kChunks) * kStrideV +
+                                      (lane % kChunks) * 8) = vr[c];
+        __syncthreads();
+        const bool next = t0 + 32 < k1;
+        if (next) load_v(t0 + 32);
+
+        // S^T = K Q^T for 32 keys x 32 heads
+        f32x16 sacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, kr[ks]), __builtin_bit_cast(bf16x8, qf[ks]), sacc, 0, 0,
+                0);
+        if (next) load_k(t0 + 32);
+        if (t0 + 32 > k1) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = t0 + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (j >= k1) sacc[r] = -INFINITY;
+            }
+        }
+        // online softmax, lazy per-lane reference (as the prefill kernel)
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+        mx = halves_max(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const bool grow = (m_new - m_run) * scale_log2 > 8.0f;  // true if m_run = -inf
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float alpha = grow ? fast_exp2((m_run - m_new) * scale_log2) : 1.0f;
+            m_run = grow ? m_new : m_run;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        const float mc = m_run == -INFINITY ? 0.0f : m_run * scale_log2;
+        u32x4 pf[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float a0 = fast_exp2(fmaf(sacc[8 * h2 + 2 * i], scale_log2, -mc));
+                const float a1 = fast_exp2(fmaf(sacc[8 * h2 + 2 * i + 1], scale_log2, -mc));
+                pf[h2][i] = pack_bf16(a0, a1);
+                l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pf[h2][i]),
+                                                        as_bf16x2(0x3F803F80u), l_run, false);
+            }
+        // O^T += V^T P^T, output blocks innermost
+#pragma unroll
+        for (int st = 0; st < 2 * kDBlocks; ++st) {
+            const int db = st % kDBlocks, kk = st / kDBlocks;
+            const uint16_t* a1 = lds_v + v_rd + kk * 16 * kStrideV + db * 32;
+            const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TSDA_LDS i16x4*)(a1));
+            const i16x4 x1 =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((TSDA_LDS i16x4*)(a1 + 8 * kStrideV));
+            u32x4 a;
+            a[0] = (uint32_t)(uint16_t)x0[0] | ((uint32_t)(uint16_t)x0[1] << 16);
+            a[1] = (uint32_t)(uint16_t)x0[2] | ((uint32_t)(uint16_t)x0[3] << 16);
+            a[2] = (uint32_t)(uint16_t)x1[0] | ((uint32_t)(uint16_t)x1[1] << 16);
+            a[3] = (uint32_t)(uint16_t)x1[2] | ((uint32_t)(uint16_t)x1[3] << 16);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, pf[kk]), oacc[db], 0, 0,
+                0);
+        }
+        __syncthreads();  // the V tile is read before the next one is stored
+    }
+
+    // one partial per served query head: (m, l) in exp2 units and acc[D]
+    const float l_tot = halves_sum(l_run);
+    if (live) {
+        const size_t uq = ((size_t)b * H + h0 + jh) * nsplit + split;
+        float* arow = ws_acc + uq * D;
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int d0 = db * 32 + 8 * rg + 4 * half;
+                const f32x4 w4 = {oacc[db][4 * rg], oacc[db][4 * rg + 1], oacc[db][4 * rg + 2],
+                                  oacc[db][4 * rg + 3]};
+                *reinterpret_cast<f32x4*>(arow + d0) = w4;
+            }
+        if (half == 0) {
+            ws_ml[uq * 2] = m_run * scale_log2;
+            ws_ml[uq * 2 + 1] = l_tot;
+        }
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(2 * D) void decode_combine_kernel(
     const int32_t* __restrict__ kv_lens, int H, int Skv, int chunk, int nsplit,
@@ -238,23 +428,34 @@ int decode_heads_per_block(int H, int Hkv) {
 }
 
 DecodePlan decode_plan(int B, int H, int Hkv, int Skv) {
+    const int group = H / Hkv;
+    if (group >= 4) {
+        // Matrix-core kernel, one wave per (b, K/V head, 32 query heads,
+        // split).  Splits of 512 keys measured best at 8 and at 1 K/V heads
+        // (64 to 1024 tried); smaller problems split finer, down to 64 keys,
+        // until there are 1024 waves.
+        const int hgroups = (group + 31) / 32;
+        const long pairs = (long)B * Hkv * hgroups;
+        int chunk = 512;
+        while (chunk > 64 && pairs * ((Skv + chunk - 1) / chunk) < 1024) chunk /= 2;
+        return DecodePlan{chunk, (Skv + chunk - 1) / chunk, hgroups};
+    }
     // Multi-head: splits of 128 keys (64 KiB of K+V at d = 128) measured
     // fastest on the ragged decode workload: many short units spread the
     // reads of the valid prefixes of all caches evenly over the memory
     // system.  Smaller problems split finer so the grid still fills the GPU.
-    // A block serving several query heads does several times the vector work
-    // per row and merges one partial per head at its end, so it takes the
-    // longest split (up to 1024 keys) that still leaves 8 blocks per CU:
-    // 1024 measured 1.25x faster than 128 at 8 K/V heads.
+    // A block serving two query heads does twice the vector work per row and
+    // merges one partial per head at its end, so it takes the longest split
+    // (up to 1024 keys) that still leaves 8 blocks per CU.
     const int hb = decode_heads_per_block(H, Hkv);
-    const long groups = (long)B * Hkv * (H / Hkv / hb);
+    const long groups = (long)B * Hkv * (group / hb);
     int chunk = 128;
     if (hb > 1) {
         while (chunk < 1024 && groups * ((Skv + 2 * chunk - 1) / (2 * chunk)) >= 2048) chunk *= 2;
     } else if (groups * ((Skv + chunk - 1) / chunk) < 8192) {
         chunk = 64;
     }
-    return DecodePlan{chunk, (Skv + chunk - 1) / chunk};
+    return DecodePlan{chunk, (Skv + chunk - 1) / chunk, 0};
 }
 
 size_t decode_workspace_bytes(int B, int H, int Hkv, int Skv, int d) {
@@ -299,10 +500,24 @@ hipError_t launch_decode_bf16(const LaunchArgs& a) {
     KernelTimer* t = active_timer();
     hipError_t e;
     if (t) t->begin(kDecodePartialBf16, a.stream);
-    if (a.d == 128)
+    if (p.hgroups > 0) {
+        const unsigned blocks = (unsigned)((size_t)a.B * a.Hkv * p.hgroups * p.nsplit);
+        const uint16_t* q = static_cast<const uint16_t*>(a.q);
+        const uint16_t* k = static_cast<const uint16_t*>(a.k);
+        const uint16_t* v = static_cast<const uint16_t*>(a.v);
+        if (a.d == 128)
+            hipLaunchKernelGGL(decode_mfma_kernel<128>, dim3(blocks), dim3(64), 0, a.stream, q, k, v,
+                               a.kv_lens, a.H, a.Hkv, a.Skv, sl, p.chunk, p.nsplit, p.hgroups,
+                               ws_acc, ws_ml);
+        else
+            hipLaunchKernelGGL(decode_mfma_kernel<64>, dim3(blocks), dim3(64), 0, a.stream, q, k, v,
+                               a.kv_lens, a.H, a.Hkv, a.Skv, sl, p.chunk, p.nsplit, p.hgroups,
+                               ws_acc, ws_ml);
+    } else if (a.d == 128) {
         launch_partial_d<128>(a, p, sl, ws_acc, ws_ml);
-    else
+    } else {
         launch_partial_d<64>(a, p, sl, ws_acc, ws_ml);
+    }
     e = hipGetLastError();
     if (t) t->end(kDecodePartialBf16, a.stream);
     if (e != hipSuccess) return e;

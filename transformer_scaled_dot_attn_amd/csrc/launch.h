@@ -20,10 +20,13 @@ struct LaunchArgs {
     size_t workspace_bytes;
 };
 
-// Decode split plan: keys per split and number of splits per (b, h).
+// Decode split plan: keys per split, number of splits per (b, h), and for
+// grouped heads (H / Hkv >= 4) the matrix-core kernel's groups of 32 query
+// heads per K/V head (0: the vector kernel).
 struct DecodePlan {
     int chunk;
     int nsplit;
+    int hgroups;
 };
 DecodePlan decode_plan(int B, int H, int Hkv, int Skv);
 size_t decode_workspace_bytes(int B, int H, int Hkv, int Skv, int d);
