@@ -82,13 +82,14 @@ def timed_calls(attn, fn, steps, warmup, kernels):
     return {k: (prof[k][1] / prof[k][0] if prof[k][0] else float("nan")) for k in kernels}
 
 
-def gqa_decode_sweep(attn, W, dev, steps, warmup):
+def gqa_decode_sweep(attn, W, dev, steps, warmup,
+                     names=("decode8192_bf16", "gqa_decode8192_bf16", "mqa_decode8192_bf16")):
     """Decode at 32, 8 and 1 K/V heads for 32 query heads ("Attention from
     First Principles", section 10, exercise F): bytes moved fall by H / H_kv
     while the flops stay, so the intensity is H / H_kv."""
     import torch
     rows = []
-    for name in ("decode8192_bf16", "gqa_decode8192_bf16", "mqa_decode8192_bf16"):
+    for name in names:
         w = W.WORKLOADS[name]
         x = W.device_inputs(w, dev)
         out = torch.empty_like(x["q"])
@@ -98,10 +99,19 @@ def gqa_decode_sweep(attn, W, dev, steps, warmup):
         ms = t["decode_bf16_partial"] + t["decode_bf16_combine"]
         lens = x["kv_lens_host"]
         nbytes, flops = decode_bytes(w, lens), decode_flops(w, lens)
+        p_ms = t["decode_bf16_partial"]
+        kv_bytes = nbytes - 2 * 2 * w.B * w.H * w.d  # what the partial kernel reads
+        kernel = "decode_bf16_partial" if w.H // w.kv_heads < 4 else "decode_bf16_mfma"
         rows.append({"workload": name, "H": w.H, "H_kv": w.kv_heads, "ms_per_call": ms,
                      "GB/s": nbytes / (ms * 1e-3) / 1e9, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
                      "intensity_flop_per_byte": flops / nbytes,
-                     "partial_avg_launch_ms": t["decode_bf16_partial"]})
+                     "roofline": {"kernel": kernel, "bound": "hbm",
+                                  "achieved": kv_bytes / (p_ms * 1e-3) / 1e9,
+                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": kv_bytes / (p_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                  "traffic": profiled_traffic(kernel, name),
+                                  "algorithmic_bytes_per_launch": kv_bytes,
+                                  "avg_launch_ms": p_ms}})
         del x, out
         torch.cuda.empty_cache()
     return rows
@@ -163,8 +173,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--parts", default="prefill,decode",
-                    help="comma list of prefill, decode, copy, gqa, sweep (default "
-                         "prefill,decode); copy adds a plain 1 GiB device-to-device copy per "
+                    help="comma list of prefill, decode, copy, gqa, gqa8, sweep (default "
+                         "prefill,decode); gqa8 is the 8-K/V-head decode alone; copy adds a plain 1 GiB device-to-device copy per "
                          "step, the known-size kernel that scales the HBM byte counters; gqa "
                          "measures decode at 32, 8 and 1 K/V heads for 32 query heads; sweep "
                          "measures causal prefill over S = 128 .. 8192 (both reported beside "
@@ -306,6 +316,9 @@ def main():
     if "gqa" in parts:
         print("[bench] grouped-head decode sweep", file=sys.stderr, flush=True)
         result["gqa_decode"] = gqa_decode_sweep(attn, W, dev, args.steps, args.warmup)
+    elif "gqa8" in parts:
+        result["gqa_decode"] = gqa_decode_sweep(attn, W, dev, args.steps, args.warmup,
+                                                names=("gqa_decode8192_bf16",))
     if "sweep" in parts:
         print("[bench] prefill S sweep", file=sys.stderr, flush=True)
         result["prefill_sweep"] = prefill_sweep(attn, W, dev, args.steps, args.warmup)
