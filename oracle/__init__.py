@@ -57,6 +57,12 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_attn_fwd_weights_gqa.argtypes = [p, p, p, i, p, p, i, i, i, i, i, i, i, d, i, p,
                                                 i]
     lib.oracle_attn_fwd_weights_gqa.restype = i
+    ll = ctypes.c_longlong
+    lib.oracle_attn_fwd_mask.argtypes = [p, p, p, i, p, i, i, i, i, i, i, i, d, i, p, p, ll, ll, i]
+    lib.oracle_attn_fwd_mask.restype = i
+    lib.oracle_attn_fwd_weights_mask.argtypes = [p, p, p, i, p, p, i, i, i, i, i, i, i, d, i, p, p,
+                                                 ll, ll, i]
+    lib.oracle_attn_fwd_weights_mask.restype = i
     lib.oracle_default_threads.argtypes = []
     lib.oracle_default_threads.restype = i
     return lib
@@ -83,7 +89,8 @@ def default_threads() -> int:
     return load().oracle_default_threads()
 
 
-def attention(q, k, v, scale, causal, kv_lens=None, *, weights=False, nthreads=0, lib=None):
+def attention(q, k, v, scale, causal, kv_lens=None, *, mask=None, weights=False, nthreads=0,
+              lib=None):
     """Reference attention forward.
 
     q: [B,H,Sq,d], k: [B,Hkv,Skv,d], v: [B,Hkv,Skv,dv] numpy arrays of one
@@ -92,6 +99,9 @@ def attention(q, k, v, scale, causal, kv_lens=None, *, weights=False, nthreads=0
     query heads (query head h reads key/value head h // (H // Hkv)).
     scale: the multiplier of QK^T (a float; pass float32 values widened).
     kv_lens: None or int array [B] of valid lengths (clamped to [0, Skv]).
+    mask: None or an array broadcastable to [B,H,Sq,Skv]; nonzero where query
+    row i of (b, h) may see key j (combined with the causal and length rules
+    by logical AND).  It is expanded to the full [B,H,Sq,Skv] bytes here.
     Returns out [B,H,Sq,dv] float64, and with weights=True also the weight
     tensor [B,H,Sq,Skv].
     """
@@ -121,6 +131,24 @@ def attention(q, k, v, scale, causal, kv_lens=None, *, weights=False, nthreads=0
         lens_ptr = lens_arr.ctypes.data
     out = np.empty((B, H, Sq, dv), dtype=np.float64)
     code = DTYPE_CODES[q.dtype]
+    if mask is not None:
+        m = np.ascontiguousarray(np.broadcast_to(np.asarray(mask) != 0, (B, H, Sq, Skv)),
+                                 dtype=np.uint8)
+        sb, sh = H * Sq * Skv, Sq * Skv
+        if weights:
+            w = np.empty((B, H, Sq, Skv), dtype=np.float64)
+            rc = lib.oracle_attn_fwd_weights_mask(
+                q.ctypes.data, k.ctypes.data, v.ctypes.data, code, out.ctypes.data, w.ctypes.data,
+                B, H, Hkv, Sq, Skv, d, dv, float(scale), int(bool(causal)), lens_ptr,
+                m.ctypes.data, sb, sh, int(nthreads))
+        else:
+            rc = lib.oracle_attn_fwd_mask(
+                q.ctypes.data, k.ctypes.data, v.ctypes.data, code, out.ctypes.data, B, H, Hkv, Sq,
+                Skv, d, dv, float(scale), int(bool(causal)), lens_ptr, m.ctypes.data, sb, sh,
+                int(nthreads))
+        if rc != 0:
+            raise ValueError(f"oracle error {rc}: {ERRORS.get(rc, 'unknown')}")
+        return (out, w) if weights else out
     if weights:
         w = np.empty((B, H, Sq, Skv), dtype=np.float64)
         rc = lib.oracle_attn_fwd_weights_gqa(q.ctypes.data, k.ctypes.data, v.ctypes.data, code,

@@ -32,6 +32,13 @@
  *   - the softmax subtracts the row maximum before exponentiating, the stable
  *     form that page's Part 7 (debugging) asks for.
  *
+ * Explicit allowed-mask: an optional byte array, nonzero where query row i
+ * of (b, h) may see key j (the True-means-allowed boolean mask of "Attention
+ * from Scratch", KubeDojo module 1.4.3, Part 3), combined with the causal
+ * and length rules by logical AND as that part combines its causal and
+ * padding masks.  Element (b, h, i, j) is mask[b*sb + h*sh + i*Skv + j];
+ * a stride of 0 broadcasts over that axis.
+ *
  * Grouped heads (GQA / MQA): with H_kv key/value heads for H query heads
  * (H a multiple of H_kv), query head h reads key/value head h / (H / H_kv).
  * That is the grouping of "Attention from First Principles", section "MHA,
@@ -75,6 +82,8 @@ typedef struct {
     double scale;
     int causal;
     const int32_t* kv_lens;
+    const uint8_t* mask;  /* optional allowed-mask, see above */
+    long long mask_sb, mask_sh;
     int next_pair;    /* work counter, guarded by mu */
     pthread_mutex_t mu;
 } job_t;
@@ -87,9 +96,11 @@ static int valid_len(const job_t* J, int b) {
     return (int)L;
 }
 
-/* Mask M: is key j visible to the query at absolute position p? */
-static int key_visible(const job_t* J, int j, int p, int L) {
+/* Mask M: is key j visible to query row i (absolute position p) of (b, h)? */
+static int key_visible(const job_t* J, int b, int h, int i, int j, int p, int L) {
     if (j >= L) return 0;          /* padding: past the valid length */
+    if (J->mask && !J->mask[b * J->mask_sb + h * J->mask_sh + (long long)i * J->Skv + j])
+        return 0;                  /* the caller's allowed-mask */
     if (!J->causal) return 1;
     return j <= p;                 /* causal: M_pj = 0 iff j <= p */
 }
@@ -124,7 +135,7 @@ static void one_row(const job_t* J, int b, int h, int i, double* out_row, double
     double m = -INFINITY;
     int any = 0;
     for (int j = 0; j < Skv; ++j) {
-        if (!key_visible(J, j, p, L)) continue;
+        if (!key_visible(J, b, h, i, j, p, L)) continue;
         s[j] = score(J, qrow, kbase, j);
         if (s[j] > m) m = s[j];
         any = 1;
@@ -134,11 +145,11 @@ static void one_row(const job_t* J, int b, int h, int i, double* out_row, double
     /* softmax normaliser over the visible keys */
     double l = 0.0;
     for (int j = 0; j < Skv; ++j)
-        if (key_visible(J, j, p, L)) l += exp(s[j] - m);
+        if (key_visible(J, b, h, i, j, p, L)) l += exp(s[j] - m);
 
     /* weighted mixture of value rows */
     for (int j = 0; j < Skv; ++j) {
-        if (!key_visible(J, j, p, L)) continue;
+        if (!key_visible(J, b, h, i, j, p, L)) continue;
         const double w = exp(s[j] - m) / l;
         if (w_row) w_row[j] = w;
         for (int c = 0; c < dv; ++c)
@@ -215,6 +226,40 @@ int oracle_attn_fwd_gqa(const void* q, const void* k, const void* v, int dtype, 
     J.q = q; J.k = k; J.v = v; J.dtype = dtype; J.out = out; J.weights = NULL;
     J.B = B; J.H = H; J.Hkv = Hkv; J.Sq = Sq; J.Skv = Skv; J.d = d; J.dv = dv;
     J.scale = scale; J.causal = causal ? 1 : 0; J.kv_lens = kv_lens;
+    return run(&J, nthreads);
+}
+
+/* As oracle_attn_fwd_gqa, with an allowed-mask (NULL: none) whose element
+   (b, h, i, j) is mask[b*mask_sb + h*mask_sh + i*Skv + j], nonzero = allowed.
+   Negative strides return 2 (bad shape). */
+int oracle_attn_fwd_mask(const void* q, const void* k, const void* v, int dtype, double* out,
+                         int B, int H, int Hkv, int Sq, int Skv, int d, int dv, double scale,
+                         int causal, const int32_t* kv_lens, const uint8_t* mask,
+                         long long mask_sb, long long mask_sh, int nthreads) {
+    if (mask_sb < 0 || mask_sh < 0) return OR_E_SHAPE;
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.dtype = dtype; J.out = out; J.weights = NULL;
+    J.B = B; J.H = H; J.Hkv = Hkv; J.Sq = Sq; J.Skv = Skv; J.d = d; J.dv = dv;
+    J.scale = scale; J.causal = causal ? 1 : 0; J.kv_lens = kv_lens;
+    J.mask = mask; J.mask_sb = mask_sb; J.mask_sh = mask_sh;
+    return run(&J, nthreads);
+}
+
+/* As oracle_attn_fwd_mask, and also the weight tensor [B,H,Sq,Skv]. */
+int oracle_attn_fwd_weights_mask(const void* q, const void* k, const void* v, int dtype,
+                                 double* out, double* weights, int B, int H, int Hkv, int Sq,
+                                 int Skv, int d, int dv, double scale, int causal,
+                                 const int32_t* kv_lens, const uint8_t* mask, long long mask_sb,
+                                 long long mask_sh, int nthreads) {
+    if (!weights) return OR_E_NULL;
+    if (mask_sb < 0 || mask_sh < 0) return OR_E_SHAPE;
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.dtype = dtype; J.out = out; J.weights = weights;
+    J.B = B; J.H = H; J.Hkv = Hkv; J.Sq = Sq; J.Skv = Skv; J.d = d; J.dv = dv;
+    J.scale = scale; J.causal = causal ? 1 : 0; J.kv_lens = kv_lens;
+    J.mask = mask; J.mask_sb = mask_sb; J.mask_sh = mask_sh;
     return run(&J, nthreads);
 }
 

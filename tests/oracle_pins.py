@@ -273,6 +273,108 @@ def pin_grouped_heads_match_expansion(attn):
             assert np.all(out[b][:, pad] == 0.0)
 
 
+def _random_mask(seed, shape, density=0.6):
+    return np.random.default_rng(np.random.SeedSequence([seed, 11])).random(shape) < density
+
+
+def pin_mask_of_the_rules_equals_the_rules(attn):
+    """An allowed-mask that spells out the causal rule ("Self-Attention",
+    section "Causal Masking", bottom-right aligned) with the causal flag off
+    gives exactly the causal result, and an all-true mask exactly the
+    unmasked one: the explicit mask and the built-in rules are one AND
+    ("Attention from Scratch", KubeDojo module 1.4.3, Part 3)."""
+    for ci, (B, H, Sq, Skv, d, causal, lens) in enumerate(_mixed_cases()):
+        q, k, v = _rand(ci, B, H, Sq, d), _rand(ci + 50, B, H, Skv, d), _rand(ci + 90, B, H, Skv, d)
+        ref = attn(q, k, v, 0.6, 1, lens)
+        full = np.zeros((B, 1, Sq, Skv), dtype=bool)
+        for b in range(B):
+            L = Skv if lens is None else min(lens[b], Skv)
+            allowed, _ = _visible(Sq, Skv, 1, L)
+            full[b, 0] = allowed
+        assert np.array_equal(attn(q, k, v, 0.6, 0, lens, mask=full), ref), f"case {ci}"
+        assert np.array_equal(attn(q, k, v, 0.6, 1, lens, mask=full), ref), f"case {ci} both"
+        ones = np.ones((1, 1, 1, Skv), dtype=np.uint8)
+        assert np.array_equal(attn(q, k, v, 0.6, causal, lens, mask=ones),
+                              attn(q, k, v, 0.6, causal, lens)), f"case {ci} all-true"
+
+
+def pin_key_padding_mask_equals_lengths(attn):
+    """A key-padding mask [B,1,1,Skv] (the padding mask of "Attention from
+    Scratch", Part 3, broadcast over heads and queries) equals the valid
+    lengths on every query row they both compute (rows i < L_b of a square
+    problem, where the bottom-right offset is 0)."""
+    B, H, S, d = 3, 2, 6, 3
+    q, k, v = _rand(40, B, H, S, d), _rand(41, B, H, S, d), _rand(42, B, H, S, d)
+    lens = [6, 4, 1]
+    kp = (np.arange(S)[None, :] < np.array(lens)[:, None])[:, None, None, :]
+    for causal in (0, 1):
+        by_len = attn(q, k, v, 0.8, causal, lens)
+        by_mask = attn(q, k, v, 0.8, causal, mask=kp)
+        for b in range(B):
+            assert np.array_equal(by_mask[b, :, :lens[b]], by_len[b, :, :lens[b]]), (causal, b)
+
+
+def pin_mask_single_allowed_key(attn):
+    """A row allowed exactly one key puts all its weight there: the output is
+    that key's value row exactly (softmax over one logit is 1), and a row
+    allowed no key is exactly zero."""
+    B, H, Sq, Skv, d = 2, 2, 4, 6, 3
+    q, k, v = _rand(43, B, H, Sq, d), _rand(44, B, H, Skv, d), _rand(45, B, H, Skv, d)
+    pick = np.random.default_rng(5).integers(0, Skv, size=(B, H, Sq))
+    m = np.zeros((B, H, Sq, Skv), dtype=np.uint8)
+    for b in range(B):
+        for h in range(H):
+            for i in range(Sq):
+                m[b, h, i, pick[b, h, i]] = 7  # any nonzero byte allows
+    m[1, 0, 2, :] = 0
+    out, w = attn(q, k, v, 0.9, 0, mask=m, weights=True)
+    for b in range(B):
+        for h in range(H):
+            for i in range(Sq):
+                if b == 1 and h == 0 and i == 2:
+                    assert np.all(out[b, h, i] == 0.0) and np.all(w[b, h, i] == 0.0)
+                    continue
+                assert np.array_equal(out[b, h, i], v[b, h, pick[b, h, i]]), (b, h, i)
+                assert w[b, h, i, pick[b, h, i]] == 1.0
+
+
+def pin_mask_matches_torch_sdpa(attn):
+    """Random allowed-masks in every broadcast shape, with the causal rule,
+    valid lengths and grouped heads, against torch's CPU
+    scaled_dot_product_attention in float64 given the AND of the mask and the
+    rules (an independent routine).  Rows with no allowed key (where torch
+    returns NaN) are exactly zero here, and every disallowed weight is 0."""
+    import torch
+    import torch.nn.functional as F
+    B, H, Hkv, Sq, Skv, d = 2, 4, 2, 5, 7, 3
+    lens = [7, 5]
+    for ci, shape in enumerate([(B, H, Sq, Skv), (B, 1, Sq, Skv), (1, H, Sq, Skv),
+                                (B, H, 1, Skv), (1, 1, Sq, Skv)]):
+        m = _random_mask(ci, shape)
+        causal = ci % 2
+        q = _rand(100 + ci, B, H, Sq, d)
+        k, v = _rand(110 + ci, B, Hkv, Skv, d), _rand(120 + ci, B, Hkv, Skv, d)
+        out, w = attn(q, k, v, 0.7, causal, lens, mask=m, weights=True)
+        mm = np.broadcast_to(m, (B, H, Sq, Skv))
+        ke = torch.from_numpy(k).repeat_interleave(H // Hkv, dim=1)
+        ve = torch.from_numpy(v).repeat_interleave(H // Hkv, dim=1)
+        for b in range(B):
+            rule, pad = _visible(Sq, Skv, causal, lens[b])
+            for h in range(H):
+                allowed = mm[b, h] & rule
+                assert np.all(w[b, h][~allowed] == 0.0), (ci, b, h)
+                rows = np.nonzero(allowed.any(axis=1))[0]
+                empty = np.nonzero(~allowed.any(axis=1))[0]
+                assert np.all(out[b, h, empty] == 0.0), (ci, b, h)
+                if len(rows) == 0:
+                    continue
+                ref = F.scaled_dot_product_attention(
+                    torch.from_numpy(q[b, h, rows]), ke[b, h], ve[b, h],
+                    attn_mask=torch.from_numpy(np.ascontiguousarray(allowed[rows])),
+                    scale=0.7).numpy()
+                assert np.allclose(out[b, h, rows], ref, rtol=0, atol=1e-12), (ci, b, h)
+
+
 ALL_PINS = [
     pin_p2_causal_example,
     pin_p3_unmasked_example,
@@ -288,6 +390,10 @@ ALL_PINS = [
     pin_low_precision_inputs_widen_exactly,
     pin_length_clamp,
     pin_grouped_heads_match_expansion,
+    pin_mask_of_the_rules_equals_the_rules,
+    pin_key_padding_mask_equals_lengths,
+    pin_mask_single_allowed_key,
+    pin_mask_matches_torch_sdpa,
 ]
 
 

@@ -33,8 +33,13 @@ MUTANTS = {
     "not_normalised": [("exp(s[j] - m) / l;", "exp(s[j] - m);", 1)],
     "max_not_subtracted": [("exp(s[j] - m)", "exp(s[j])", 2)],
     "max_not_tracked": [("if (s[j] > m) m = s[j];", "", 1)],
-    "mask_after_softmax": [("if (key_visible(J, j, p, L)) l += exp(s[j] - m);",
+    "mask_after_softmax": [("if (key_visible(J, b, h, i, j, p, L)) l += exp(s[j] - m);",
                             "l += exp(score(J, qrow, kbase, j) - m);", 1)],
+    "allowed_mask_ignored": [("if (J->mask && !J->mask[", "if (0 && !J->mask[", 1)],
+    "allowed_mask_inverted": [("if (J->mask && !J->mask[", "if (J->mask && J->mask[", 1)],
+    "allowed_mask_row_reversed": [("(long long)i * J->Skv + j]", "(long long)(J->Sq - 1 - i) * J->Skv + j]", 1)],
+    "allowed_mask_batch_ignored": [("[b * J->mask_sb + h * J->mask_sh", "[h * J->mask_sh", 1)],
+    "allowed_mask_head_ignored": [("[b * J->mask_sb + h * J->mask_sh", "[b * J->mask_sb", 1)],
     "kv_head_modulo": [("const int hk = h / (J->H / J->Hkv);", "const int hk = h % J->Hkv;", 1)],
     "kv_base_strides_query_heads": [("((size_t)b * J->Hkv + hk) * (size_t)Skv * J->d;",
                                      "((size_t)b * J->H + hk) * (size_t)Skv * J->d;", 1)],
