@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 typedef enum {
     ATTN_OK = 0,
@@ -72,9 +72,9 @@ typedef enum {
     ATTN_E_SHAPE = 2,       /* a size <= 0, Sq > Skv, H % H_kv != 0, or sizes overflow */
     ATTN_E_UNSUPPORTED = 3, /* valid request outside the kernels' support matrix */
     ATTN_E_DTYPE = 4,       /* dtype is not an attn_dtype value */
-    ATTN_E_ALIGN = 5,       /* a base pointer is not 16-byte aligned */
+    ATTN_E_ALIGN = 5,       /* a base pointer is not 16-byte aligned (mask: 4 bytes) */
     ATTN_E_WORKSPACE = 6,   /* caller workspace smaller than attn_workspace_bytes() */
-    ATTN_E_ARG = 7,         /* scale is not finite */
+    ATTN_E_ARG = 7,         /* scale is not finite and > 0 */
     ATTN_E_LAUNCH = 8,      /* a HIP call or kernel launch failed */
     ATTN_E_NOMEM = 9        /* the library could not allocate its workspace */
 } attn_status;
@@ -96,7 +96,8 @@ typedef enum {
 /*
  * attn_fwd -- out = softmax(scale * Q K^T + M) V, arguments as above.
  * scale: the logit multiplier, normally 1/sqrt(d) ("Self-Attention",
- * section "Why divide by sqrt(d_k)?").  causal: 0 or nonzero.
+ * section "Why divide by sqrt(d_k)?"); it must be finite and > 0, the only
+ * values the pages use (else ATTN_E_ARG).  causal: 0 or nonzero.
  * Temporary memory comes from a library-owned workspace on the current
  * device, grown on demand (the call that grows it synchronizes the device
  * first).  Calls that use the library workspace must not run concurrently
@@ -150,6 +151,46 @@ int attn_fwd_gqa_ws(const void* q, const void* k, const void* v, void* out, int 
 /* The host-side checks of attn_fwd_gqa alone (as attn_validate). */
 int attn_validate_gqa(const void* q, const void* k, const void* v, void* out, int B, int H,
                       int H_kv, int Sq, int Skv, int d, float scale, int causal, int dtype);
+
+/*
+ * attn_fwd_mask -- attn_fwd_gqa with an explicit allowed-mask ANDed into M:
+ * query row i of (b, h) sees key j only if the causal and length rules above
+ * allow it AND mask byte (b, h, i, j) is nonzero (the boolean allowed-mask,
+ * True = may attend, of "Attention from Scratch", KubeDojo module 1.4.3,
+ * Part 3, which combines its causal and padding masks by logical AND; a
+ * torch.bool tensor's bytes are such a mask).  It covers key-padding masks
+ * of padded cross-attention sources, left padding, per-row query lengths
+ * (hide every key of a padded row), and arbitrary patterns.  A row that sees
+ * no key, or a padded row (i >= n_b), is written as 0.
+ *
+ *   mask      DEVICE bytes; byte (b, h, i, j) is
+ *             mask[b*mask_sb + h*mask_sh + i*mask_si + j], i indexing the
+ *             Sq query rows as given (before the bottom-right offset).  A
+ *             stride of 0 broadcasts that axis ([B,1,1,Skv] key padding:
+ *             mask_sh = mask_si = 0).  NULL: no mask (attn_fwd_gqa_ws).
+ *   mask_s*   strides in bytes, >= 0 (else ATTN_E_SHAPE).
+ *   Rows are read as 4-byte words: mask must be 4-byte aligned and the
+ *   strides multiples of 4 (else ATTN_E_ALIGN), and each row must be
+ *   readable up to Skv rounded up to a multiple of 4 (the bytes past Skv are
+ *   ignored).  A dense [B,H,Sq,Skv] mask with Skv a multiple of 4 meets all
+ *   of this; otherwise pad its rows.  32 * mask_si + Skv must stay below
+ *   2^32 (else ATTN_E_UNSUPPORTED).  The mask is only read.
+ *   workspace NULL: the library-owned workspace, as attn_fwd_gqa; else a
+ *             caller buffer as for attn_fwd_gqa_ws (attn_workspace_bytes_gqa
+ *             gives its size; a mask changes nothing there).
+ * The masked kernels are separate instantiations: calls with mask == NULL
+ * run exactly the unmasked code.
+ */
+int attn_fwd_mask(const void* q, const void* k, const void* v, void* out, int B, int H, int H_kv,
+                  int Sq, int Skv, int d, float scale, int causal, const int32_t* kv_lens,
+                  const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int64_t mask_si,
+                  int dtype, void* stream, void* workspace, size_t workspace_bytes);
+
+/* The host-side checks of attn_fwd_mask alone (as attn_validate). */
+int attn_validate_mask(const void* q, const void* k, const void* v, void* out, int B, int H,
+                       int H_kv, int Sq, int Skv, int d, float scale, int causal,
+                       const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int64_t mask_si,
+                       int dtype);
 
 /*
  * attn_validate -- the host-side checks of attn_fwd alone: returns what

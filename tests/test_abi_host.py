@@ -62,6 +62,7 @@ def test_validate_accepts_supported_requests():
     (dict(Skv=0), attn.E_SHAPE), (dict(d=0), attn.E_SHAPE), (dict(Sq=5, Skv=4), attn.E_SHAPE),
     (dict(B=1 << 20, H=1 << 10, Sq=1, Skv=1 << 16, d=128), attn.E_SHAPE),
     (dict(scale=float("inf")), attn.E_ARG), (dict(scale=float("nan")), attn.E_ARG),
+    (dict(scale=0.0), attn.E_ARG), (dict(scale=-0.125), attn.E_ARG),
     (dict(q=A + 8), attn.E_ALIGN), (dict(out=A + 2), attn.E_ALIGN),
     (dict(d=32), attn.E_UNSUPPORTED), (dict(d=96), attn.E_UNSUPPORTED),
     (dict(d=256), attn.E_UNSUPPORTED), (dict(dtype=F32, d=129), attn.E_UNSUPPORTED),
@@ -159,3 +160,31 @@ def test_python_layer_rejects_bad_tensors():
     k2 = torch.zeros(1, 2, 4, 64)
     with pytest.raises(ValueError):
         attn.fwd(q3, k2, k2)
+
+
+def vm(mask=A, sb=0, sh=0, si=0, B=2, H=4, Hkv=2, Sq=8, Skv=64, d=128, dtype=BF16, scale=0.125):
+    return attn.validate_mask(A, A, A, A, B, H, Hkv, Sq, Skv, d, scale, 1, mask, sb, sh, si, dtype)
+
+
+def test_validate_mask():
+    # NULL mask: the attn_validate_gqa checks alone
+    assert vm(mask=None) == attn.OK
+    assert vm(sb=4 * 8 * 64, sh=8 * 64, si=64) == attn.OK          # dense [B,H,Sq,Skv]
+    assert vm(sb=8 * 64, sh=0, si=64) == attn.OK                    # [B,1,Sq,Skv]
+    assert vm(sb=64, sh=0, si=0) == attn.OK                         # key padding [B,1,1,Skv]
+    assert vm(Sq=1, sb=68, sh=0, si=0, Skv=65) == attn.OK           # padded rows
+    assert vm(dtype=F32, d=40, si=64) == attn.OK
+    # word-aligned base and strides
+    assert vm(mask=A + 2) == attn.E_ALIGN
+    assert vm(si=65) == attn.E_ALIGN
+    assert vm(sb=66) == attn.E_ALIGN
+    assert vm(sh=6) == attn.E_ALIGN
+    # negative strides, overflowing extents
+    assert vm(si=-64) == attn.E_SHAPE
+    assert vm(sb=-4) == attn.E_SHAPE
+    assert vm(B=2, sb=1 << 62) == attn.E_SHAPE
+    assert vm(si=1 << 27) == attn.E_UNSUPPORTED and vm(si=(1 << 27) - 64) == attn.OK
+    # the shared checks come first
+    assert vm(B=0, mask=A + 1) == attn.E_SHAPE
+    assert vm(scale=0.0) == attn.E_ARG
+    assert vm(Hkv=3) == attn.E_SHAPE

@@ -1,0 +1,172 @@
+"""Explicit allowed-masks on the GPU against the CPU oracle.
+
+The mask (True = may attend) is ANDed with the causal and length rules
+("Attention from Scratch", KubeDojo module 1.4.3, Part 3).  Every kernel
+family -- bf16 prefill (with and without key-range splits), the vector and
+matrix-core decode kernels, the fp32 kernel -- runs masks in every broadcast
+shape on ragged sizes (Skv not a multiple of the tiles, nor of 4) and is
+compared element by element with the oracle; rows with no allowed key must
+be exactly zero.  An all-true mask must give the unmasked result bit for bit,
+and a mask spelling out the causal rule must reproduce the causal result.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import transformer_scaled_dot_attn_amd as attn
+import workloads as W
+from gpu_util import BF16_TOL, F32_TOL, assert_matches, gpu_run
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+CASES = [
+    # seed, dtype, B, H, Hkv, Sq, Skv, d, causal, kv_lens, mask shape (None = full), density
+    (71, "bf16", 2, 4, 4, 300, 300, 128, 1, [300, 170], "b1qk", 0.7),
+    (72, "bf16", 1, 2, 2, 129, 262, 64, 0, None, "1hqk", 0.5),
+    (73, "bf16", 2, 4, 2, 256, 512, 128, 1, None, "bh1k", 0.8),
+    (74, "bf16", 1, 2, 2, 200, 2602, 128, 1, [2602], "11qk", 0.3),   # key-range splits
+    (75, "bf16", 2, 4, 4, 65, 131, 64, 0, [131, 40], "bhqk", 0.05),  # many empty rows
+    (76, "bf16", 3, 4, 4, 1, 700, 128, 0, [700, 333, 0], "bh1k", 0.5),  # vector decode
+    (77, "bf16", 2, 8, 4, 1, 1031, 64, 0, [1031, 500], "b11k", 0.6),  # 2 heads per block
+    (78, "bf16", 2, 16, 2, 1, 1100, 128, 0, [1100, 900], "bh1k", 0.4),  # matrix-core decode
+    (79, "bf16", 1, 32, 1, 1, 2049, 128, 0, None, "b11k", 0.02),
+    (80, "f32", 2, 3, 3, 70, 90, 40, 1, [90, 50], "bhqk", 0.6),
+    (81, "f32", 1, 4, 2, 1, 150, 128, 0, None, "1h1k", 0.5),
+]
+
+_SHAPES = {"bhqk": "BHQK", "b1qk": "B1QK", "1hqk": "1HQK", "bh1k": "BH1K", "11qk": "11QK",
+           "b11k": "B11K", "1h1k": "1H1K"}
+
+
+def _mask_shape(code, B, H, Sq, Skv):
+    dims = {"B": B, "H": H, "Q": Sq, "K": Skv, "1": 1}
+    return tuple(dims[c] for c in _SHAPES[code])
+
+
+def _run_case(case, mask):
+    seed, dt, B, H, Hkv, Sq, Skv, d, causal, lens = case[:10]
+    prob = W.random_problem(seed, B, H, Sq, Skv, d, dt, lens, Hkv=Hkv)
+    q, k, v = prob["q"], prob["k"], prob["v"]
+    got, _ = gpu_run(q, k, v, prob["scale"], causal, lens,
+                     mask=None if mask is None else W.mask_to_torch(mask))
+    clamped = None if lens is None else np.clip(lens, 0, Skv)
+    return got, prob, clamped
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}")
+def test_mask_matches_oracle(case):
+    seed, dt, B, H, Hkv, Sq, Skv, d, causal, lens, shape, density = case
+    _say(f"mask case s{seed}: {dt} B{B} H{H}/{Hkv} Sq{Sq} Skv{Skv} d{d} causal{causal} {shape}")
+    mask = W.random_mask(seed, _mask_shape(shape, B, H, Sq, Skv), density)
+    if shape == "bhqk" and Sq > 3:
+        mask[0, 0, 3, :] = False  # one row with no allowed key
+    got, prob, clamped = _run_case(case, mask)
+    ref = oracle.attention(prob["q"], prob["k"], prob["v"], prob["scale"], causal, clamped,
+                           mask=mask)
+    tol = F32_TOL if dt == "f32" else BF16_TOL
+    assert_matches(got, ref, tol, clamped, Skv, f"s{seed}")
+    # rows the oracle gives no visible key are exactly zero on the GPU too
+    empty = np.all(ref == 0.0, axis=-1)
+    assert np.all(got[empty] == 0.0), f"s{seed}: rows without an allowed key are not zero"
+    if shape == "bhqk" and Sq > 3:
+        assert np.all(got[0, 0, 3] == 0.0)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}")
+def test_all_true_mask_is_bitwise_unmasked(case):
+    seed, dt, B, H, Hkv, Sq, Skv, d, causal, lens = case[:10]
+    _say(f"all-true mask s{seed}")
+    ones = np.ones((1, 1, 1, Skv), dtype=bool)
+    with_mask, _, _ = _run_case(case, ones)
+    without, _, _ = _run_case(case, None)
+    assert np.array_equal(with_mask, without), f"s{seed}: all-true mask changed the result"
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_causal_rule_as_mask(dt, d):
+    """A [1,1,S,S] lower-triangular mask with causal off gives the causal result
+    (equal values; the masked run also visits the tiles past the diagonal)."""
+    import torch
+    B, H, S = 2, 4, 333
+    _say(f"causal-as-mask {dt} d{d}")
+    prob = W.random_problem(90 + d, B, H, S, S, d, dt)
+    tri = np.tril(np.ones((S, S), dtype=bool))[None, None]
+    a, ta = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], 1)
+    b, tb = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], 0, mask=W.mask_to_torch(tri))
+    assert torch.equal(ta, tb), f"max diff {np.abs(a - b).max()}"
+
+
+def test_mask_layout_errors():
+    import torch
+    B, H, S, d = 1, 2, 90, 64
+    prob = W.random_problem(95, B, H, S, S, d, "bf16")
+    q, k, v = (W.to_torch(prob[x]) for x in ("q", "k", "v"))
+    dense = torch.ones((B, 1, S, S), dtype=torch.bool, device="cuda")  # rows of 90 bytes
+    with pytest.raises((ValueError, attn.AttnError)):
+        attn.fwd(q, k, v, mask=dense)
+    wrong = torch.ones((B, 1, S, S + 1), dtype=torch.bool, device="cuda")
+    with pytest.raises(ValueError):
+        attn.fwd(q, k, v, mask=wrong)
+    ok = W.mask_to_torch(np.ones((B, 1, S, S), dtype=bool))
+    out = attn.fwd(q, k, v, mask=ok)
+    ref = attn.fwd(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+def test_mask_decode_split_fully_hidden():
+    """Decode with whole key splits hidden (partials with no visible key) and a
+    sequence whose every key is hidden (output 0), on both decode kernels."""
+    for H, Hkv in ((8, 8), (16, 2)):
+        B, Skv, d = 2, 3000, 128
+        _say(f"decode hidden splits H{H}/{Hkv}")
+        prob = W.random_problem(96 + H, B, H, 1, Skv, d, "bf16", Hkv=Hkv)
+        starts, ends = [1700, 0], [2999, 0]
+        mask = W.key_padding_mask(starts, ends, Skv)
+        got, _ = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], 0,
+                         mask=W.mask_to_torch(mask))
+        ref = oracle.attention(prob["q"], prob["k"], prob["v"], prob["scale"], 0, mask=mask)
+        assert_matches(got, ref, BF16_TOL, what=f"H{H}/{Hkv}")
+        assert np.all(got[1] == 0.0)
+
+
+def _sampled_mask_check(w, mask_np, pairs):
+    """Run workload w in full with mask_np on the GPU (its benchmark launch
+    configuration); compare the (b, h) slices with the oracle."""
+    import torch
+    _say("workload", w.name, "with mask", mask_np.shape, "pairs", pairs)
+    x = W.device_inputs(w)
+    out = attn.fwd(x["q"], x["k"], x["v"], causal=w.causal, kv_lens=x["kv_lens"],
+                   scale=x["scale"], mask=W.mask_to_torch(mask_np))
+    torch.cuda.synchronize()
+    sub = W.make_inputs(w, pairs=pairs)
+    # the mask rows of each sampled slice, stacked like the slices
+    m = np.broadcast_to(mask_np, (w.B, w.H, mask_np.shape[2], w.Skv))
+    m_sub = np.stack([m[b, h] for b, h in pairs])[:, None]
+    ref = oracle.attention(sub["q"], sub["k"], sub["v"], sub["scale"], w.causal, sub["kv_lens"],
+                           mask=m_sub)
+    got = np.stack([W.from_torch(out[b, h]) for b, h in pairs])[:, None]
+    return assert_matches(got, ref, BF16_TOL, sub["kv_lens"], w.Skv, w.name)
+
+
+def test_prefill4096_random_mask_sampled():
+    """The 4096-token causal prefill in its benchmark launch configuration,
+    with a random [1,1,S,S] mask (every tile cut), sampled heads vs the oracle."""
+    w = W.WORKLOADS["prefill4096_bf16"]
+    _say("prefill4096 random mask")
+    mask = W.random_mask(97, (1, 1, w.Sq, w.Skv), 0.5)
+    _sampled_mask_check(w, mask, [(0, 0), (0, 31)])
+
+
+def test_decode8192_key_padding_sampled():
+    w = W.WORKLOADS["gqa_decode8192_bf16"]
+    _say("gqa decode8192 key padding")
+    rng = np.random.default_rng(98)
+    starts = rng.integers(0, 400, size=w.B)
+    mask = W.key_padding_mask(starts, np.full(w.B, w.Skv), w.Skv)
+    _sampled_mask_check(w, mask, [(0, 0), (5, 13), (63, 31)])

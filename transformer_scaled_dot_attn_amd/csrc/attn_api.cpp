@@ -127,10 +127,29 @@ EventTimer* g_timer = nullptr;
 bool g_timing_on = false;
 std::mutex g_timer_mu;
 
+// Allowed-mask layout checks: strides >= 0 and multiples of 4, base 4-byte
+// aligned, every byte offset a kernel may touch representable.
+int check_mask(const uint8_t* mask, int64_t sb, int64_t sh, int64_t si, int B, int H, int Sq,
+               int Skv) {
+    if (mask == nullptr) return ATTN_OK;
+    if (sb < 0 || sh < 0 || si < 0) return ATTN_E_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(mask) & 3u) != 0 || (sb & 3) || (sh & 3) || (si & 3))
+        return ATTN_E_ALIGN;
+    const long double last = (long double)sb * (B - 1) + (long double)sh * (H - 1) +
+                             (long double)si * (Sq - 1) + (long double)Skv + 3;
+    if (last > (long double)(INT64_MAX / 2)) return ATTN_E_SHAPE;
+    // the prefill kernel addresses a wave's 32 rows as 32-bit offsets
+    if ((long double)si * 32 + Skv + 4 > (long double)UINT32_MAX) return ATTN_E_UNSUPPORTED;
+    return ATTN_OK;
+}
+
 int run(const void* q, const void* k, const void* v, void* out, int B, int H, int Hkv, int Sq,
         int Skv, int d, float scale, int causal, const int32_t* kv_lens, int dtype, void* stream,
-        void* workspace, size_t workspace_bytes, bool library_ws) {
+        void* workspace, size_t workspace_bytes, bool library_ws, const uint8_t* mask = nullptr,
+        int64_t msb = 0, int64_t msh = 0, int64_t msi = 0) {
     int st = attn_validate_gqa(q, k, v, out, B, H, Hkv, Sq, Skv, d, scale, causal, dtype);
+    if (st != ATTN_OK) return st;
+    st = check_mask(mask, msb, msh, msi, B, H, Sq, Skv);
     if (st != ATTN_OK) return st;
     const Path path = choose_path(Sq, d, dtype);
     const size_t need = attn_workspace_bytes_gqa(B, H, Hkv, Sq, Skv, d, dtype);
@@ -163,7 +182,8 @@ int run(const void* q, const void* k, const void* v, void* out, int B, int H, in
         if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_E_ALIGN;
     }
     LaunchArgs a{q, k, v, out, B, H, Hkv, Sq, Skv, d, scale, causal ? 1 : 0, kv_lens,
-                 static_cast<hipStream_t>(stream), workspace, workspace_bytes};
+                 static_cast<hipStream_t>(stream), workspace, workspace_bytes, mask, msb, msh,
+                 msi};
     hipError_t e = hipSuccess;
     switch (path) {
         case kPathGenericF32: e = launch_generic_f32(a); break;
@@ -191,7 +211,9 @@ int attn_validate_gqa(const void* q, const void* k, const void* v, void* out, in
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_E_DTYPE;
     int st = check_shape(B, H, Hkv, Sq, Skv, d);
     if (st != ATTN_OK) return st;
-    if (!std::isfinite(scale)) return ATTN_E_ARG;
+    // the kernels track the maximum of the raw logits and hide keys with
+    // -inf logits, both of which assume a positive multiplier
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return ATTN_E_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_E_ALIGN;
     if (choose_path(Sq, d, dtype) == kPathNone) return ATTN_E_UNSUPPORTED;
     return ATTN_OK;
@@ -242,6 +264,23 @@ int attn_fwd_gqa_ws(const void* q, const void* k, const void* v, void* out, int 
                workspace, workspace_bytes, false);
 }
 
+int attn_validate_mask(const void* q, const void* k, const void* v, void* out, int B, int H,
+                       int Hkv, int Sq, int Skv, int d, float scale, int causal,
+                       const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int64_t mask_si,
+                       int dtype) {
+    int st = attn_validate_gqa(q, k, v, out, B, H, Hkv, Sq, Skv, d, scale, causal, dtype);
+    if (st != ATTN_OK) return st;
+    return check_mask(mask, mask_sb, mask_sh, mask_si, B, H, Sq, Skv);
+}
+
+int attn_fwd_mask(const void* q, const void* k, const void* v, void* out, int B, int H, int Hkv,
+                  int Sq, int Skv, int d, float scale, int causal, const int32_t* kv_lens,
+                  const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int64_t mask_si,
+                  int dtype, void* stream, void* workspace, size_t workspace_bytes) {
+    return run(q, k, v, out, B, H, Hkv, Sq, Skv, d, scale, causal, kv_lens, dtype, stream,
+               workspace, workspace_bytes, workspace == nullptr, mask, mask_sb, mask_sh, mask_si);
+}
+
 int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq,
              int Skv, int d, float scale, int causal, const int32_t* kv_lens, int dtype,
              void* stream) {
@@ -264,9 +303,11 @@ const char* attn_status_string(int status) {
             return "invalid shape (a size <= 0, Sq > Skv, H not a multiple of H_kv, or too large)";
         case ATTN_E_UNSUPPORTED: return "unsupported combination of dtype and head size";
         case ATTN_E_DTYPE: return "unknown dtype";
-        case ATTN_E_ALIGN: return "pointer not aligned (16 bytes; workspace 256 bytes)";
+        case ATTN_E_ALIGN:
+            return "pointer not aligned (16 bytes; workspace 256 bytes; mask and its strides 4 "
+                   "bytes)";
         case ATTN_E_WORKSPACE: return "workspace too small";
-        case ATTN_E_ARG: return "scale is not finite";
+        case ATTN_E_ARG: return "scale is not finite and positive";
         case ATTN_E_LAUNCH: return "HIP launch or runtime failure";
         case ATTN_E_NOMEM: return "device allocation failed";
         default: return "unknown status";

@@ -27,6 +27,11 @@
 //     out = (sum acc_s 2^(m_s - M)) / l, and rounds to bf16.  L_b = 0 gives 0.
 // Logits are kept in base 2 (scale * log2 e folded in), which leaves the
 // softmax unchanged.
+// An explicit allowed-mask (the MASK instantiations: a byte per query head
+// and key, nonzero = visible, ANDed with the length rule) is read next to
+// the K/V rows it gates; a split whose keys are all hidden leaves a partial
+// with m = -inf and l = 0, which the combine weighs as zero, and a head with
+// no visible key at all is written as 0.
 #include "device_common.h"
 #include "launch.h"
 
@@ -37,12 +42,12 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kUnroll = 4;  // key rows per lane per step (two steps in flight)
 
-template <int D, int HB>
+template <int D, int HB, bool MASK>
 __global__ __launch_bounds__(256) void decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ kv_lens, int H, int Hkv,
     int Skv, float scale_log2, int chunk, int nsplit, float* __restrict__ ws_acc,
-    float* __restrict__ ws_ml) {
+    float* __restrict__ ws_ml, const uint8_t* __restrict__ mask, long long msb, long long msh) {
     constexpr int G = D / 8;            // lanes per key row
     constexpr int KPW = 64 / G;         // key rows per wave per load
     constexpr int SLOTS = kWaves * KPW; // key rows per block per load
@@ -74,6 +79,10 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     for (int i = 0; i < HB; ++i) qw[i] = ldg16(q + ((size_t)b * H + h0 + i) * D + part * 8);
     const uint16_t* kp = k + (size_t)bk * Skv * D + part * 8;
     const uint16_t* vp = v + (size_t)bk * Skv * D + part * 8;
+    // allowed-mask bytes: lane `part` of a row group reads the byte of query
+    // head h0 + part % HB (HB <= G), and the group's lanes share them below
+    const uint8_t* mrow = nullptr;
+    if constexpr (MASK) mrow = mask + b * msb + (long long)(h0 + part % HB) * msh;
 
     float m[HB], l[HB];
     float acc[HB][8];
@@ -90,16 +99,21 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     // its logit is masked), so the next step's loads stay in flight while the
     // current step is computed.
     constexpr int kStep = SLOTS * kUnroll;
-    auto load = [&](int base, u32x4 (&kr)[kUnroll], u32x4 (&vr)[kUnroll]) {
+    auto load = [&](int base, u32x4 (&kr)[kUnroll], u32x4 (&vr)[kUnroll],
+                    uint32_t (&mk)[kUnroll]) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int j = base + u * SLOTS + slot;
-            const size_t row = (size_t)(j < k1 ? j : k0) * D;
+            const int jc = j < k1 ? j : k0;
+            const size_t row = (size_t)jc * D;
             kr[u] = ldg16_stream(kp + row);
             vr[u] = ldg16_stream(vp + row);
+            if constexpr (MASK) mk[u] = mrow[jc];
         }
     };
-    auto consume = [&](int base, const u32x4 (&kr)[kUnroll], const u32x4 (&vr)[kUnroll]) {
+    const int grp0 = lane & ~(G - 1);  // first lane of this row group
+    auto consume = [&](int base, const u32x4 (&kr)[kUnroll], const u32x4 (&vr)[kUnroll],
+                       const uint32_t (&mk)[kUnroll]) {
 #pragma unroll
         for (int i = 0; i < HB; ++i) {
             float s[kUnroll];
@@ -113,7 +127,14 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
                                                           dot, false);
                 dot = group_sum<G>(dot);
                 const int j = base + u * SLOTS + slot;
-                s[u] = j < k1 ? dot * scale_log2 : -INFINITY;
+                bool vis = j < k1;
+                if constexpr (MASK) {
+                    const uint32_t mb =
+                        HB > 1 ? (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (grp0 + i), (int)mk[u])
+                               : mk[u];
+                    vis = vis & (mb != 0);
+                }
+                s[u] = vis ? dot * scale_log2 : -INFINITY;
                 mx = fmaxf(mx, s[u]);
             }
             const float m_new = fmaxf(m[i], mx);
@@ -136,13 +157,14 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
         }
     };
     u32x4 ka[kUnroll], va[kUnroll], kb[kUnroll], vb[kUnroll];
-    load(k0, ka, va);
+    uint32_t ma[kUnroll], mb[kUnroll];
+    load(k0, ka, va, ma);
     for (int base = k0; base < k1; base += 2 * kStep) {
-        if (base + kStep < k1) load(base + kStep, kb, vb);
-        consume(base, ka, va);
+        if (base + kStep < k1) load(base + kStep, kb, vb, mb);
+        consume(base, ka, va, ma);
         if (base + kStep >= k1) break;
-        if (base + 2 * kStep < k1) load(base + 2 * kStep, ka, va);
-        consume(base + kStep, kb, vb);
+        if (base + 2 * kStep < k1) load(base + 2 * kStep, ka, va, ma);
+        consume(base + kStep, kb, vb, mb);
     }
 
     // merge the block's SLOTS row groups, one query head at a time
@@ -192,12 +214,12 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 // half swap, as in the prefill kernel.  The matrix cores have ample headroom
 // (16 MFMAs per 16 KiB of K+V), so with grouped heads decode stays bound by
 // the bytes of K and V, read once per group of up to 32 query heads.
-template <int D>
+template <int D, bool MASK>
 __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ kv_lens, int H, int Hkv,
     int Skv, float scale_log2, int chunk, int nsplit, int hgroups, float* __restrict__ ws_acc,
-    float* __restrict__ ws_ml) {
+    float* __restrict__ ws_ml, const uint8_t* __restrict__ mask, long long msb, long long msh) {
     constexpr int kKSteps = D / 16;       // MFMA k-steps of K Q^T
     constexpr int kDBlocks = D / 32;      // 32-row blocks of O^T
     constexpr int kStrideV = D + 16;      // padded LDS row of V (elements)
@@ -236,6 +258,21 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(
     const uint16_t* kb = k + (size_t)bk * Skv * D;
     const uint16_t* vb = v + (size_t)bk * Skv * D;
 
+    // allowed-mask words of this lane's query head for a 32-key tile: word g
+    // holds keys 8 g + 4 half .. +3, the keys of score elements 4 g .. +3
+    // (offsets clamped to the row's last readable word; keys past it are
+    // >= Skv >= L and hidden anyway)
+    const uint8_t* mrow = nullptr;
+    if constexpr (MASK) mrow = mask + b * msb + (long long)(h0 + (live ? jh : 0)) * msh;
+    const int mlast = mask_last_word(Skv);
+    uint32_t mw[4], mw_next[4];
+    auto load_m = [&](int t0, uint32_t (&dst)[4]) {
+        if constexpr (MASK) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) dst[g] = ldg_word(mrow + min(t0 + 8 * g + 4 * half, mlast));
+        }
+    };
+
     // K tile rows in A-operand order (row = lane % 32, features
     // 16*ks + 8*(lane/32) ..), V tile rows whole (kVRows rows per load).
     // Rows at or past k1 are redirected to row k0 (valid; logits masked).
@@ -271,6 +308,7 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(
     float m_run = -INFINITY, l_run = 0.0f;
 
     load_k(k0);
+    load_m(k0, mw);
     load_v(k0);
     for (int t0 = k0; t0 < k1; t0 += 32) {
         // V(t0) to LDS; the next tile's V loads reuse its registers
@@ -291,13 +329,29 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, kr[ks]), __builtin_bit_cast(bf16x8, qf[ks]), sacc, 0, 0,
                 0);
-        if (next) load_k(t0 + 32);
-        if (t0 + 32 > k1) {
+        if (next) {
+            load_k(t0 + 32);
+            load_m(t0 + 32, mw_next);
+        }
+        bool cut = t0 + 32 > k1;
+        if constexpr (MASK) {
+            uint32_t z = 0;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) z |= has_zero_byte(mw[g]);
+            cut = cut || __builtin_amdgcn_ballot_w64(z != 0) != 0;
+        }
+        if (cut) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int j = t0 + 8 * (r >> 2) + 4 * half + (r & 3);
-                if (j >= k1) sacc[r] = -INFINITY;
+                bool vis = j < k1;
+                if constexpr (MASK) vis = vis & byte_set(mw[r >> 2], r & 3);  // no short circuit
+                if (!vis) sacc[r] = -INFINITY;
             }
+        }
+        if constexpr (MASK) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) mw[g] = mw_next[g];
         }
         // online softmax, lazy per-lane reference (as the prefill kernel)
         float mx = -INFINITY;
@@ -396,7 +450,8 @@ __global__ __launch_bounds__(2 * D) void decode_combine_kernel(
     float lt = 0.0f, at = 0.0f;
 #pragma unroll 4
     for (int s = h2; s < nv; s += 2) {
-        const float w = fast_exp2(ml[2 * s] - M);
+        // a split whose keys are all masked has m = -inf, l = 0: weight 0
+        const float w = ml[2 * s] == -INFINITY ? 0.0f : fast_exp2(ml[2 * s] - M);
         lt = fmaf(ml[2 * s + 1], w, lt);
         at = fmaf(ac[(size_t)s * D + t], w, at);
     }
@@ -412,7 +467,7 @@ __global__ __launch_bounds__(2 * D) void decode_combine_kernel(
         const float w0 = s_m[0] == -INFINITY ? 0.0f : fast_exp2(s_m[0] - Mt);
         const float w1 = s_m[1] == -INFINITY ? 0.0f : fast_exp2(s_m[1] - Mt);
         const float l = s_l[0] * w0 + s_l[1] * w1;
-        o[t] = to_bf16((s_a[0][t] * w0 + s_a[1][t] * w1) / l);
+        o[t] = l > 0.0f ? to_bf16((s_a[0][t] * w0 + s_a[1][t] * w1) / l) : 0;  // 0: no visible key
     }
 }
 
@@ -470,10 +525,13 @@ template <int D, int HB>
 void launch_partial(const LaunchArgs& a, const DecodePlan& p, float sl, float* ws_acc,
                     float* ws_ml) {
     const size_t blocks = (size_t)a.B * a.H / HB * p.nsplit;
-    hipLaunchKernelGGL((decode_partial_kernel<D, HB>), dim3((unsigned)blocks), dim3(256), 0,
-                       a.stream, static_cast<const uint16_t*>(a.q),
-                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
-                       a.kv_lens, a.H, a.Hkv, a.Skv, sl, p.chunk, p.nsplit, ws_acc, ws_ml);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                           static_cast<const uint16_t*>(a.v), a.kv_lens, a.H, a.Hkv, a.Skv, sl,
+                           p.chunk, p.nsplit, ws_acc, ws_ml, a.mask, a.msb, a.msh);
+    };
+    a.mask ? go(decode_partial_kernel<D, HB, true>) : go(decode_partial_kernel<D, HB, false>);
 }
 
 template <int D>
@@ -505,14 +563,15 @@ hipError_t launch_decode_bf16(const LaunchArgs& a) {
         const uint16_t* q = static_cast<const uint16_t*>(a.q);
         const uint16_t* k = static_cast<const uint16_t*>(a.k);
         const uint16_t* v = static_cast<const uint16_t*>(a.v);
+        auto go = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3(blocks), dim3(64), 0, a.stream, q, k, v, a.kv_lens, a.H,
+                               a.Hkv, a.Skv, sl, p.chunk, p.nsplit, p.hgroups, ws_acc, ws_ml,
+                               a.mask, a.msb, a.msh);
+        };
         if (a.d == 128)
-            hipLaunchKernelGGL(decode_mfma_kernel<128>, dim3(blocks), dim3(64), 0, a.stream, q, k, v,
-                               a.kv_lens, a.H, a.Hkv, a.Skv, sl, p.chunk, p.nsplit, p.hgroups,
-                               ws_acc, ws_ml);
+            a.mask ? go(decode_mfma_kernel<128, true>) : go(decode_mfma_kernel<128, false>);
         else
-            hipLaunchKernelGGL(decode_mfma_kernel<64>, dim3(blocks), dim3(64), 0, a.stream, q, k, v,
-                               a.kv_lens, a.H, a.Hkv, a.Skv, sl, p.chunk, p.nsplit, p.hgroups,
-                               ws_acc, ws_ml);
+            a.mask ? go(decode_mfma_kernel<64, true>) : go(decode_mfma_kernel<64, false>);
     } else if (a.d == 128) {
         launch_partial_d<128>(a, p, sl, ws_acc, ws_ml);
     } else {

@@ -92,4 +92,18 @@ __device__ __forceinline__ u32x4 ldg16_stream(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// One 4-byte word of an allowed-mask row: keys j .. j+3, one byte each.
+__device__ __forceinline__ uint32_t ldg_word(const uint8_t* p) {
+    return *reinterpret_cast<const uint32_t*>(p);
+}
+
+// Nonzero iff some byte of w is zero, i.e. one of its four keys is hidden
+// (exact as a yes/no test: a borrow can only run past a zero byte).
+__device__ __forceinline__ uint32_t has_zero_byte(uint32_t w) {
+    return (w - 0x01010101u) & ~w & 0x80808080u;
+}
+
+// Byte e (0..3) of mask word w is nonzero: key j+e is allowed.
+__device__ __forceinline__ bool byte_set(uint32_t w, int e) { return ((w >> (8 * e)) & 0xffu) != 0; }
+
 }  // namespace tsda

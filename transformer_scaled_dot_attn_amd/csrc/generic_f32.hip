@@ -9,7 +9,10 @@
 // "The memory problem").  Keys past the valid length are never read; rows
 // past the valid query count are written as zeros.  With grouped key/value
 // heads, query head h reads K/V head h / (H / Hkv) ("Attention from First
-// Principles", section "MHA, GQA, MQA -- the KV cache lever").
+// Principles", section "MHA, GQA, MQA -- the KV cache lever").  An
+// explicit allowed-mask (MASK: a byte per query row and key, nonzero =
+// visible, ANDed with the causal and length rules) is read as eight 4-byte
+// words of the lane's row per tile; a row with no visible key is 0.
 #include "device_common.h"
 #include "launch.h"
 
@@ -20,11 +23,12 @@ namespace {
 constexpr int kRows = 64;   // query rows per block
 constexpr int kKeys = 32;   // keys per LDS tile
 
-template <int DP>  // d rounded up to 16, 32, 64 or 128
+template <int DP, bool MASK>  // DP: d rounded up to 16, 32, 64 or 128
 __global__ __launch_bounds__(64) void generic_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ out, const int32_t* __restrict__ kv_lens, int H, int Hkv, int Sq, int Skv,
-    int d, float scale_log2, int causal) {
+    int d, float scale_log2, int causal, const uint8_t* __restrict__ mask, long long msb,
+    long long msh, long long msi) {
     __shared__ float ks[kKeys][DP];
     __shared__ float vs[kKeys][DP];
 
@@ -58,6 +62,10 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
     float m = -INFINITY, l = 0.0f;
 
     const int bk = b * Hkv + (bh - b * H) / (H / Hkv);  // this head's K/V head
+    const uint8_t* mrow = nullptr;  // this lane's allowed-mask row
+    if constexpr (MASK)
+        mrow = mask + b * msb + (long long)(bh - b * H) * msh + (long long)(live ? i : 0) * msi;
+    const int mlast = mask_last_word(Skv);
     const float* kb = k + (size_t)bk * Skv * d;
     const float* vb = v + (size_t)bk * Skv * d;
     for (int j0 = 0; j0 < kv_hi; j0 += kKeys) {
@@ -79,6 +87,17 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
         }
         __syncthreads();
 
+        uint32_t mbits = ~0u;  // bit r: the mask allows key j0 + r
+        if constexpr (MASK) {
+            // words past the row's end are clamped (their keys are >= Skv >= L)
+#pragma unroll
+            for (int w = 0; w < kKeys / 4; ++w) {
+                const uint32_t word = ldg_word(mrow + min(j0 + 4 * w, mlast));
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (!byte_set(word, e)) mbits &= ~(1u << (4 * w + e));
+            }
+        }
         float s[kKeys];
         float tmax = -INFINITY;
 #pragma unroll
@@ -87,7 +106,8 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
 #pragma unroll
             for (int c = 0; c < DP; ++c) dot = fmaf(qr[c], ks[r][c], dot);
             const int j = j0 + r;
-            const bool vis = r < nk && (!causal || j <= p);
+            bool vis = r < nk && (!causal || j <= p);
+            if constexpr (MASK) vis = vis & (((mbits >> r) & 1u) != 0);  // no short circuit: keeps the loop straight-line
             s[r] = vis ? dot * scale_log2 : -INFINITY;
             tmax = fmaxf(tmax, s[r]);
         }
@@ -128,18 +148,19 @@ hipError_t launch_generic_f32(const LaunchArgs& a) {
     float* o = static_cast<float*>(a.out);
     KernelTimer* t = active_timer();
     if (t) t->begin(kGenericF32, a.stream);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, a.stream, q, k, v, o, a.kv_lens, a.H, a.Hkv, a.Sq,
+                           a.Skv, a.d, sl, a.causal, a.mask, a.msb, a.msh, a.msi);
+    };
+    const bool m = a.mask != nullptr;
     if (a.d <= 16)
-        hipLaunchKernelGGL(generic_f32_kernel<16>, grid, block, 0, a.stream, q, k, v, o, a.kv_lens,
-                           a.H, a.Hkv, a.Sq, a.Skv, a.d, sl, a.causal);
+        m ? go(generic_f32_kernel<16, true>) : go(generic_f32_kernel<16, false>);
     else if (a.d <= 32)
-        hipLaunchKernelGGL(generic_f32_kernel<32>, grid, block, 0, a.stream, q, k, v, o, a.kv_lens,
-                           a.H, a.Hkv, a.Sq, a.Skv, a.d, sl, a.causal);
+        m ? go(generic_f32_kernel<32, true>) : go(generic_f32_kernel<32, false>);
     else if (a.d <= 64)
-        hipLaunchKernelGGL(generic_f32_kernel<64>, grid, block, 0, a.stream, q, k, v, o, a.kv_lens,
-                           a.H, a.Hkv, a.Sq, a.Skv, a.d, sl, a.causal);
+        m ? go(generic_f32_kernel<64, true>) : go(generic_f32_kernel<64, false>);
     else
-        hipLaunchKernelGGL(generic_f32_kernel<128>, grid, block, 0, a.stream, q, k, v, o,
-                           a.kv_lens, a.H, a.Hkv, a.Sq, a.Skv, a.d, sl, a.causal);
+        m ? go(generic_f32_kernel<128, true>) : go(generic_f32_kernel<128, false>);
     hipError_t e = hipGetLastError();
     if (t) t->end(kGenericF32, a.stream);
     return e;

@@ -18,7 +18,15 @@ struct LaunchArgs {
     hipStream_t stream;
     void* workspace;
     size_t workspace_bytes;
+    // optional allowed-mask: byte (b, h, i, j) at mask[b*msb + h*msh + i*msi + j],
+    // nonzero = visible; 4-byte aligned, strides multiples of 4 (checked by the
+    // front end), each row readable up to Skv rounded up to 4.  nullptr: none.
+    const uint8_t* mask;
+    long long msb, msh, msi;
 };
+
+// Last 4-byte word offset of a mask row that a kernel may read.
+__host__ __device__ inline int mask_last_word(int Skv) { return ((Skv + 3) & ~3) - 4; }
 
 // Decode split plan: keys per split, number of splits per (b, h), and for
 // grouped heads (H / Hkv >= 4) the matrix-core kernel's groups of 32 query

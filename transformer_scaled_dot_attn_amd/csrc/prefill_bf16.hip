@@ -46,6 +46,17 @@
 // hold copies of row L_b - 1, whose weight there is exactly zero), and query
 // rows >= n_b are written as zeros.
 //
+// Explicit allowed-mask (the MASK instantiation).  A byte per (query row,
+// key), nonzero = visible, ANDed with the rules above (the boolean allowed-
+// mask of "Attention from Scratch", KubeDojo module 1.4.3, Part 3).  Each
+// lane reads the 32 bytes of its query row that its score registers hold,
+// as eight 4-byte words issued one iteration ahead (under the P V MFMAs);
+// at the start of the next iteration the wave parks them in a per-lane LDS
+// slot, so they hold no registers across the score MFMAs, and decides once
+// whether any of its lanes hides a key of the tile.  Only then are they read
+// back for the per-element pass.  Tile skipping still follows the causal
+// and length rules only.
+//
 // Order.  Block ids are mapped heaviest query tile first; within a query
 // tile rank the (b, h) pairs are laid out so that each XCD (ids are dealt
 // round-robin over the 8 XCDs) runs a contiguous range of heads: every tile
@@ -96,15 +107,17 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast
 // a batch of LDS reads issued ahead of the MFMAs that consume them.
 __device__ __forceinline__ void pin_schedule() { __builtin_amdgcn_sched_barrier(0); }
 
-template <int D>
+template <int D, bool MASK>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
     const int32_t* __restrict__ kv_lens, int BH, int H, int Hkv, int Sq, int Skv, float scale_log2,
-    int causal, int nqt, int nsplit, float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
+    int causal, int nqt, int nsplit, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    const uint8_t* __restrict__ allowed, long long msb, long long msh, long long msi) {
     using S = Shape<D>;
     __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][S::kTileK];
     __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][S::kTileV];
+    __shared__ u32x4 lds_m[MASK ? 2 * kThreads : 1];  // parked mask words, 32 bytes per lane
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -169,6 +182,44 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         for (int ks = 0; ks < S::kKSteps; ++ks)
             qf[ks] = q_live ? ldg16(qrow + ks * 16) : u32x4{0, 0, 0, 0};
     }
+
+    // ---- allowed-mask words of this lane's query row for one key tile:
+    // word w holds keys 32 (w/4) + 8 (w%4) + 4 half .. +3, the keys of
+    // score elements 4 (w%4) .. +3 of block w/4.  Word offsets are clamped
+    // to the row's last readable word; keys past it are >= Skv >= L and
+    // hidden by the length rule anyway.
+    u32x4 mw[2];  // in flight: word w is mw[w / 4][w % 4]
+    bool mcut = false;  // some lane of the wave hides a key of the parked tile
+    // addressed as a wave-uniform row base (row min(qw, Sq-1)) plus a 32-bit
+    // lane offset (qi - that row) * msi, below 32 * msi <= 2^32; pad lanes
+    // read the base row
+    const uint8_t* mbase = nullptr;
+    uint32_t mlane = 0;
+    if constexpr (MASK) {
+        const int r0 = __builtin_amdgcn_readfirstlane(min(qw, Sq - 1));  // uniform: SGPR base
+        mbase = allowed + b * msb + (long long)(bh - b * H) * msh + (long long)r0 * msi;
+        mlane = q_live ? (uint32_t)(qi - r0) * (uint32_t)msi : 0u;
+    }
+    const int mlast = mask_last_word(Skv);
+    auto mload = [&](int tile) {
+        if constexpr (MASK) {
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const int j = tile * kBN + 32 * (w >> 2) + 8 * (w & 3) + 4 * half;
+                mw[w >> 2][w & 3] = ldg_word(mbase + (mlane + (uint32_t)min(j, mlast)));
+            }
+        }
+    };
+    auto mpark = [&]() {
+        if constexpr (MASK) {
+            uint32_t z = 0;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) z |= has_zero_byte(mw[w >> 2][w & 3]);
+            mcut = __builtin_amdgcn_ballot_w64(z != 0) != 0;
+            lds_m[2 * tid] = mw[0];
+            lds_m[2 * tid + 1] = mw[1];
+        }
+    };
 
     // ---- tile staging: thread t moves 16-byte chunks t + 512 i of the
     // row-major tile, so consecutive threads read consecutive global bytes.
@@ -304,16 +355,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 #pragma unroll
         for (int e = 0; e < 18; ++e) pair_stage(sc, e, mc);
     };
-    // per-element mask of S^T(tile) when the tile cuts the diagonal or L
+    // per-element mask of S^T(tile) when the tile cuts the diagonal or L,
+    // or (MASK) when the allowed-mask hides a key of the tile in some lane
     auto mask = [&](int tile, f32x16 (&sn)[2]) {
         const int kbase = tile * kBN;
-        if (kbase + kBN > kfull_w) {
+        if (kbase + kBN > kfull_w || mcut) {
+            u32x4 mk[2] = {{~0u, ~0u, ~0u, ~0u}, {~0u, ~0u, ~0u, ~0u}};
+            if constexpr (MASK) {
+                mk[0] = lds_m[2 * tid];
+                mk[1] = lds_m[2 * tid + 1];
+            }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int j = kbase + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                    const bool vis = j < L && (!causal || j <= p);
+                    bool vis = j < L && (!causal || j <= p);
+                    if constexpr (MASK) vis = vis & byte_set(mk[kb][r >> 2], r & 3);  // no short circuit
                     if (!vis) sn[kb][r] = -INFINITY;
                 }
         }
@@ -402,10 +460,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // for its own loads).
     auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
         const bool pipe = t + 1 < t1w;  // this wave scores tile t+1
+        mpark();  // mask words of tile t+1
         fetch(k, t + 2, kreg);
         // S^T(t+1) under which P(t) is formed
         if (pipe) score(t + 1, sn, &sc);
         fetch(v, t + 1, vreg);
+        mload(t + 2);
         if (pipe) {
             mask(t + 1, sn);
             // P(t) V(t) under which the maximum of S^T(t+1) is found
@@ -422,6 +482,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 
     // prologue: K(t0), V(t0), K(t0+1) staged; S^T(t0) scored and its
     // reference set
+    mload(t0);
     fetch(k, t0, kreg);
     fetch(v, t0, vreg);
     stash_k(t0);
@@ -430,10 +491,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     stash_k(t0 + 1);
     __syncthreads();
     if (t0 < t1w) {
+        mpark();
         score(t0, s0, nullptr);
         mask(t0, s0);
         reference(scan(s0));
     }
+    mload(t0 + 1);
     __syncthreads();  // K(t0) is read by every wave before K(t0+2) replaces it
 
     for (int t = t0; t < t1; t += 2) {
@@ -585,14 +648,15 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
     const float sl = a.scale * kLog2e;
     KernelTimer* t = active_timer();
     if (t) t->begin(kPrefillBf16, a.stream);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, a.stream, q, k, v, o, a.kv_lens, BH, a.H,
+                           a.Hkv, a.Sq, a.Skv, sl, a.causal, nqt, p.nsplit, ws_acc, ws_ml, a.mask,
+                           a.msb, a.msh, a.msi);
+    };
     if (a.d == 128)
-        hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(kThreads), 0, a.stream, q, k, v, o,
-                           a.kv_lens, BH, a.H, a.Hkv, a.Sq, a.Skv, sl, a.causal, nqt, p.nsplit,
-                           ws_acc, ws_ml);
+        a.mask ? go(prefill_bf16_kernel<128, true>) : go(prefill_bf16_kernel<128, false>);
     else
-        hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(kThreads), 0, a.stream, q, k, v, o,
-                           a.kv_lens, BH, a.H, a.Hkv, a.Sq, a.Skv, sl, a.causal, nqt, p.nsplit,
-                           ws_acc, ws_ml);
+        a.mask ? go(prefill_bf16_kernel<64, true>) : go(prefill_bf16_kernel<64, false>);
     hipError_t e = hipGetLastError();
     if (t) t->end(kPrefillBf16, a.stream);
     if (e != hipSuccess || p.nsplit == 1) return e;

@@ -192,6 +192,34 @@ def random_problem(seed: int, B: int, H: int, Sq: int, Skv: int, d: int, dtype: 
             "scale": float(np.float32(1.0 / math.sqrt(d)))}
 
 
+# ---- allowed-masks (inputs: True = may attend) ----------------------------
+def random_mask(seed: int, shape: Sequence[int], density: float = 0.5) -> np.ndarray:
+    """Bernoulli(density) bool mask of `shape` (last axis the keys), drawn as
+    ``default_rng(SeedSequence([seed, 4])).random(shape) < density``."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 4]))
+    return rng.random(tuple(shape)) < density
+
+
+def key_padding_mask(starts: Sequence[int], ends: Sequence[int], Skv: int) -> np.ndarray:
+    """[B, 1, 1, Skv] key-padding mask: key j of sequence b is allowed iff
+    starts[b] <= j < ends[b] (left padding before starts[b], right padding
+    from ends[b]), the padding masks of a batch of unequal sources."""
+    j = np.arange(Skv)[None, :]
+    m = (j >= np.asarray(starts)[:, None]) & (j < np.asarray(ends)[:, None])
+    return m[:, None, None, :]
+
+
+def mask_to_torch(m: np.ndarray, device="cuda"):
+    """bool mask -> a torch.bool view on `device` whose rows are stored in
+    round_up(Skv, 4) bytes (the word-readable layout the library needs)."""
+    import torch
+    Skv = m.shape[-1]
+    pad = (Skv + 3) // 4 * 4
+    full = np.zeros(m.shape[:-1] + (pad,), dtype=bool)
+    full[..., :Skv] = m
+    return torch.from_numpy(full).to(device)[..., :Skv]
+
+
 # ---- moving inputs to and from a GPU (torch only moves the bits) ----------
 def to_torch(x: np.ndarray, device="cuda"):
     """float32 array -> float32 tensor; uint16 bf16 bits -> bfloat16 tensor."""
