@@ -356,24 +356,38 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         for (int e = 0; e < 18; ++e) pair_stage(sc, e, mc);
     };
     // per-element mask of S^T(tile) when the tile cuts the diagonal or L,
-    // or (MASK) when the allowed-mask hides a key of the tile in some lane
+    // or (MASK) when the allowed-mask hides a key of the tile in some lane.
+    // The rules leave keys 0 .. lim visible (lim = min(p, L - 1) causal,
+    // L - 1 otherwise), so each element costs one compare against a
+    // per-tile constant -- no short-circuit branches.
+    const int lim = causal ? min(p, L - 1) : L - 1;
     auto mask = [&](int tile, f32x16 (&sn)[2]) {
         const int kbase = tile * kBN;
-        if (kbase + kBN > kfull_w || mcut) {
-            u32x4 mk[2] = {{~0u, ~0u, ~0u, ~0u}, {~0u, ~0u, ~0u, ~0u}};
+        u32x4 mk[2] = {{~0u, ~0u, ~0u, ~0u}, {~0u, ~0u, ~0u, ~0u}};
+        if (kbase + kBN > kfull_w) {
+            // the rules cut this tile (and the allowed-mask may)
             if constexpr (MASK) {
                 mk[0] = lds_m[2 * tid];
                 mk[1] = lds_m[2 * tid + 1];
             }
+            const int rel = lim - kbase - 4 * half;  // element visible iff its offset <= rel
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int j = kbase + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                    bool vis = j < L && (!causal || j <= p);
-                    if constexpr (MASK) vis = vis & byte_set(mk[kb][r >> 2], r & 3);  // no short circuit
-                    if (!vis) sn[kb][r] = -INFINITY;
+                    bool vis = kb * 32 + 8 * (r >> 2) + (r & 3) <= rel;
+                    if constexpr (MASK) vis = vis & byte_set(mk[kb][r >> 2], r & 3);
+                    sn[kb][r] = vis ? sn[kb][r] : -INFINITY;
                 }
+        } else if (mcut) {
+            // only the allowed-mask cuts it
+            mk[0] = lds_m[2 * tid];
+            mk[1] = lds_m[2 * tid + 1];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    sn[kb][r] = byte_set(mk[kb][r >> 2], r & 3) ? sn[kb][r] : -INFINITY;
         }
     };
     // O^T += V^T(tile) P^T, output blocks innermost (consecutive MFMAs
