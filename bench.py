@@ -139,6 +139,54 @@ def prefill_sweep(attn, W, dev, steps, warmup):
     return rows
 
 
+def mask_runs(attn, W, runs, steps, warmup):
+    """The step's workloads again with explicit allowed-masks (True = may
+    attend, ANDed with the causal and length rules; "Attention from Scratch",
+    KubeDojo module 1.4.3, Part 3), against the same call unmasked.  Prefill
+    counts the causal flops of the unmasked call (the kernel computes every
+    score the rules allow, hidden or not); decode counts the K/V bytes plus
+    the mask bytes it reads."""
+    import numpy as np
+    import torch
+    rows = []
+    for kind, w, x, out in runs:
+        if kind == "prefill":
+            S = w.Skv
+            masks = [("none", None),
+                     ("key padding [1,1,1,S], first 256 keys hidden",
+                      W.key_padding_mask([256], [S], S)),
+                     ("random [1,1,S,S], density 0.5", W.random_mask(5, (1, 1, w.Sq, S), 0.5))]
+            kernels = ("prefill_bf16_mfma",)
+        else:
+            lens = x["kv_lens_host"]
+            starts = np.minimum(np.asarray(lens) // 8, 64)
+            masks = [("none", None),
+                     ("key padding [B,1,1,Skv], first min(L/8, 64) keys hidden",
+                      W.key_padding_mask(starts, np.full(w.B, w.Skv), w.Skv)),
+                     ("random [B,H,1,Skv], density 0.5",
+                      W.random_mask(6, (w.B, w.H, 1, w.Skv), 0.5))]
+            kernels = ("decode_bf16_partial", "decode_bf16_combine")
+        base = None
+        for label, m in masks:
+            tm = None if m is None else W.mask_to_torch(m)
+            fn = lambda: attn.fwd(x["q"], x["k"], x["v"], out, causal=w.causal,
+                                  kv_lens=x["kv_lens"], scale=x["scale"], mask=tm)
+            t = timed_calls(attn, fn, steps, warmup, kernels)
+            ms = sum(t.values())
+            base = ms if base is None else base
+            row = {"workload": w.name, "mask": label, "ms_per_call": ms,
+                   "time_vs_unmasked": ms / base}
+            if kind == "prefill":
+                row["TFLOP/s"] = prefill_flops(w, x["kv_lens_host"]) / (ms * 1e-3) / 1e12
+            else:
+                mbytes = 0 if m is None else int(np.prod(m.shape[:3])) * w.Skv
+                row["GB/s"] = (decode_bytes(w, x["kv_lens_host"]) + mbytes) / (ms * 1e-3) / 1e9
+            rows.append(row)
+            del tm
+        torch.cuda.empty_cache()
+    return rows
+
+
 def profiled_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 summary of this kernel
     and workload (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known
@@ -172,9 +220,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--parts", default="prefill,decode",
-                    help="comma list of prefill, decode, copy, gqa, gqa8, sweep (default "
-                         "prefill,decode); gqa8 is the 8-K/V-head decode alone; copy adds a plain 1 GiB device-to-device copy per "
+    ap.add_argument("--parts", default="prefill,decode,masks",
+                    help="comma list of prefill, decode, masks, copy, gqa, gqa8, sweep (default "
+                         "prefill,decode,masks); masks times the step's workloads again with "
+                         "allowed-masks; gqa8 is the 8-K/V-head decode alone; copy adds a plain 1 GiB device-to-device copy per "
                          "step, the known-size kernel that scales the HBM byte counters; gqa "
                          "measures decode at 32, 8 and 1 K/V heads for 32 query heads; sweep "
                          "measures causal prefill over S = 128 .. 8192 (both reported beside "
@@ -319,6 +368,9 @@ def main():
     elif "gqa8" in parts:
         result["gqa_decode"] = gqa_decode_sweep(attn, W, dev, args.steps, args.warmup,
                                                 names=("gqa_decode8192_bf16",))
+    if "masks" in parts and runs:
+        print("[bench] allowed-mask runs", file=sys.stderr, flush=True)
+        result["masks"] = mask_runs(attn, W, runs, args.steps, args.warmup)
     if "sweep" in parts:
         print("[bench] prefill S sweep", file=sys.stderr, flush=True)
         result["prefill_sweep"] = prefill_sweep(attn, W, dev, args.steps, args.warmup)

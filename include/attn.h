@@ -27,7 +27,9 @@
  *   - A padded query row, or a row with no visible key, is written as 0.
  *
  * Layout: q and out are [B][H][Sq][d], k and v are [B][H][Skv][d] (for the
- * _gqa entry points [B][H_kv][Skv][d]), all row-major, densely packed, of
+ * _gqa and _ex entry points [B][H_kv][Skv][d]; with attn_fwd_ex's value
+ * width d_v, v is [B][H_kv][Skv][d_v] and out [B][H][Sq][d_v]), all
+ * row-major, densely packed, of
  * the one element type `dtype`; out has the inputs' type.  At decode Skv is
  * the cache capacity and L_b <= Skv the filled part.  All five base
  * pointers must be 16-byte aligned.
@@ -88,9 +90,10 @@ typedef enum {
  * Support matrix (anything else valid returns ATTN_E_UNSUPPORTED -- there is
  * no silent slow fallback, the hazard "Attention from First Principles"
  * section 8 warns of):
- *   ATTN_F32 : any Sq <= Skv, 1 <= d <= 128          (VALU kernel)
- *   ATTN_BF16: Sq == 1, d in {64, 128}                (split-KV decode)
- *              Sq >= 2, d in {64, 128}                (MFMA prefill)
+ *   ATTN_F32 : any Sq <= Skv, 1 <= d, d_v <= 128     (VALU kernel)
+ *   ATTN_BF16: Sq == 1, d = d_v in {64, 128}          (split-KV decode)
+ *              Sq >= 2, d = d_v in {64, 128}          (MFMA prefill)
+ * Every path takes grouped K/V heads and an allowed-mask (attn_fwd_ex).
  */
 
 /*
@@ -153,7 +156,11 @@ int attn_validate_gqa(const void* q, const void* k, const void* v, void* out, in
                       int H_kv, int Sq, int Skv, int d, float scale, int causal, int dtype);
 
 /*
- * attn_fwd_mask -- attn_fwd_gqa with an explicit allowed-mask ANDed into M:
+ * attn_fwd_ex -- every option at once: H_kv key/value heads (as
+ * attn_fwd_gqa), a value width d_v that may differ from d (softmax(QK^T) V
+ * only needs V's rows to match K's, the d_k = 4, d_v = 2 example of
+ * "Attention from Scratch", KubeDojo module 1.4.3, Part 2; the fp32 kernel
+ * only, see the support matrix), and an explicit allowed-mask ANDed into M:
  * query row i of (b, h) sees key j only if the causal and length rules above
  * allow it AND mask byte (b, h, i, j) is nonzero (the boolean allowed-mask,
  * True = may attend, of "Attention from Scratch", KubeDojo module 1.4.3,
@@ -177,20 +184,21 @@ int attn_validate_gqa(const void* q, const void* k, const void* v, void* out, in
  *   2^32 (else ATTN_E_UNSUPPORTED).  The mask is only read.
  *   workspace NULL: the library-owned workspace, as attn_fwd_gqa; else a
  *             caller buffer as for attn_fwd_gqa_ws (attn_workspace_bytes_gqa
- *             gives its size; a mask changes nothing there).
+ *             gives its size; a mask or d_v changes nothing there).
  * The masked kernels are separate instantiations: calls with mask == NULL
  * run exactly the unmasked code.
  */
-int attn_fwd_mask(const void* q, const void* k, const void* v, void* out, int B, int H, int H_kv,
-                  int Sq, int Skv, int d, float scale, int causal, const int32_t* kv_lens,
-                  const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int64_t mask_si,
-                  int dtype, void* stream, void* workspace, size_t workspace_bytes);
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, int H, int H_kv,
+                int Sq, int Skv, int d, int d_v, float scale, int causal, const int32_t* kv_lens,
+                const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int64_t mask_si, int dtype,
+                void* stream, void* workspace, size_t workspace_bytes);
 
-/* The host-side checks of attn_fwd_mask alone (as attn_validate). */
-int attn_validate_mask(const void* q, const void* k, const void* v, void* out, int B, int H,
-                       int H_kv, int Sq, int Skv, int d, float scale, int causal,
-                       const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int64_t mask_si,
-                       int dtype);
+/* The host-side checks of attn_fwd_ex alone (as attn_validate; d_v <= 0 is
+   ATTN_E_SHAPE, a d_v the dtype's kernels do not take ATTN_E_UNSUPPORTED). */
+int attn_validate_ex(const void* q, const void* k, const void* v, void* out, int B, int H,
+                     int H_kv, int Sq, int Skv, int d, int d_v, float scale, int causal,
+                     const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int64_t mask_si,
+                     int dtype);
 
 /*
  * attn_validate -- the host-side checks of attn_fwd alone: returns what

@@ -162,8 +162,10 @@ def test_python_layer_rejects_bad_tensors():
         attn.fwd(q3, k2, k2)
 
 
-def vm(mask=A, sb=0, sh=0, si=0, B=2, H=4, Hkv=2, Sq=8, Skv=64, d=128, dtype=BF16, scale=0.125):
-    return attn.validate_mask(A, A, A, A, B, H, Hkv, Sq, Skv, d, scale, 1, mask, sb, sh, si, dtype)
+def vm(mask=A, sb=0, sh=0, si=0, B=2, H=4, Hkv=2, Sq=8, Skv=64, d=128, dtype=BF16, scale=0.125,
+       dv=None):
+    return attn.validate_ex(A, A, A, A, B, H, Hkv, Sq, Skv, d, d if dv is None else dv, scale, 1,
+                            mask, sb, sh, si, dtype)
 
 
 def test_validate_mask():
@@ -188,3 +190,15 @@ def test_validate_mask():
     assert vm(B=0, mask=A + 1) == attn.E_SHAPE
     assert vm(scale=0.0) == attn.E_ARG
     assert vm(Hkv=3) == attn.E_SHAPE
+
+
+def test_validate_value_width():
+    # d_v != d: the fp32 kernel only; d_v in 1..128
+    assert vm(mask=None, dtype=F32, d=4, dv=2) == attn.OK
+    assert vm(mask=None, dtype=F32, d=128, dv=16) == attn.OK
+    assert vm(mask=None, dtype=F32, d=20, dv=128) == attn.OK
+    assert vm(mask=None, dtype=F32, d=20, dv=129) == attn.E_UNSUPPORTED
+    assert vm(mask=None, dtype=F32, d=20, dv=0) == attn.E_SHAPE
+    assert vm(mask=None, dtype=BF16, d=128, dv=64) == attn.E_UNSUPPORTED
+    assert vm(mask=None, dtype=BF16, d=64, dv=64) == attn.OK
+    assert vm(mask=None, dtype=BF16, Sq=1, d=128, dv=128) == attn.OK

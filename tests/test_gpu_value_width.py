@@ -1,0 +1,68 @@
+"""A value width d_v different from d on the GPU (the fp32 kernel).
+
+softmax(scale Q K^T) V needs V's rows to line up with K's, not its width to
+match d ("Attention from Scratch", KubeDojo module 1.4.3, Part 2, whose
+worked example has d_k = 4 and d_v = 2).  The worked example runs at its own
+shape against the printed values and the oracle; random shapes with every
+width class on each side, with the causal rule, valid lengths, grouped heads
+and masks, are compared with the oracle; the bf16 kernels refuse d_v != d.
+"""
+import numpy as np
+import pytest
+
+import golden_io
+import oracle
+import transformer_scaled_dot_attn_amd as attn
+import workloads as W
+from gpu_util import F32_TOL, assert_matches, gpu_run
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def test_worked_example_at_its_own_shape():
+    g = golden_io.load("p3_unmasked_3tok_dk4_dv2.txt")
+    q, k, v = (g[x][None, None].astype(np.float32) for x in ("q", "k", "v"))
+    assert q.shape[-1] == 4 and v.shape[-1] == 2
+    scale = float(np.float32(g["scale"]))
+    got, _ = gpu_run(q, k, v, scale, g["causal"])
+    assert got.shape == (1, 1, 3, 2)
+    ref = oracle.attention(q, k, v, scale, g["causal"])
+    assert_matches(got, ref, F32_TOL, what="worked example")
+    oexp, otol = g["out"]
+    assert np.all(np.abs(got[0, 0] - oexp) <= otol), got[0, 0]
+
+
+CASES = [
+    # seed, B, H, Hkv, Sq, Skv, d, dv, causal, kv_lens, masked
+    (111, 1, 2, 2, 50, 50, 64, 16, 1, None, False),
+    (112, 2, 4, 2, 33, 100, 16, 128, 1, [100, 41], False),
+    (113, 1, 3, 1, 1, 300, 40, 100, 0, [250], False),
+    (114, 2, 2, 2, 70, 90, 128, 7, 0, [90, 20], True),
+    (115, 1, 2, 2, 65, 65, 3, 33, 1, None, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}")
+def test_value_width_matches_oracle(case):
+    seed, B, H, Hkv, Sq, Skv, d, dv, causal, lens, masked = case
+    _say(f"value width s{seed}: d {d} d_v {dv}")
+    prob = W.random_problem(seed, B, H, Sq, Skv, d, "f32", lens, dv=dv, Hkv=Hkv)
+    mask = W.random_mask(seed, (B, 1, Sq, Skv), 0.6) if masked else None
+    got, _ = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], causal, lens,
+                     mask=None if mask is None else W.mask_to_torch(mask))
+    assert got.shape == (B, H, Sq, dv)
+    clamped = None if lens is None else np.clip(lens, 0, Skv)
+    ref = oracle.attention(prob["q"], prob["k"], prob["v"], prob["scale"], causal, clamped,
+                           mask=mask)
+    assert_matches(got, ref, F32_TOL, clamped, Skv, f"s{seed}")
+
+
+def test_bf16_rejects_other_value_width():
+    prob = W.random_problem(116, 1, 2, 8, 8, 64, "bf16", dv=128)
+    with pytest.raises(attn.AttnError) as e:
+        gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], 1)
+    assert e.value.status == attn.E_UNSUPPORTED

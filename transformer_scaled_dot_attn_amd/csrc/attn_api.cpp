@@ -23,19 +23,21 @@ namespace {
 
 enum Path { kPathNone = -1, kPathGenericF32 = 0, kPathPrefill = 1, kPathDecode = 2 };
 
-Path choose_path(int Sq, int d, int dtype) {
-    if (dtype == ATTN_F32) return d <= 128 ? kPathGenericF32 : kPathNone;
-    if (dtype == ATTN_BF16 && (d == 64 || d == 128)) return Sq == 1 ? kPathDecode : kPathPrefill;
+Path choose_path(int Sq, int d, int dtype, int dv) {
+    if (dtype == ATTN_F32) return d <= 128 && dv <= 128 ? kPathGenericF32 : kPathNone;
+    if (dtype == ATTN_BF16 && (d == 64 || d == 128) && dv == d)
+        return Sq == 1 ? kPathDecode : kPathPrefill;
     return kPathNone;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_shape(int B, int H, int Hkv, int Sq, int Skv, int d) {
-    if (B <= 0 || H <= 0 || Sq <= 0 || Skv <= 0 || d <= 0 || Sq > Skv) return ATTN_E_SHAPE;
+int check_shape(int B, int H, int Hkv, int Sq, int Skv, int d, int dv) {
+    if (B <= 0 || H <= 0 || Sq <= 0 || Skv <= 0 || d <= 0 || dv <= 0 || Sq > Skv)
+        return ATTN_E_SHAPE;
     if (Hkv <= 0 || H % Hkv != 0) return ATTN_E_SHAPE;
     // element counts of the q/k/v tensors and the launch grids must stay in range
-    const long double kv = (long double)B * H * Skv * d;  // >= the k/v counts (Hkv <= H)
+    const long double kv = (long double)B * H * Skv * (d > dv ? d : dv);  // >= every tensor's count
     if (kv > (long double)(INT64_MAX / 8)) return ATTN_E_SHAPE;
     const long double rows = (long double)B * H * ((Sq + 63) / 64);
     if (rows > (long double)INT_MAX) return ATTN_E_SHAPE;
@@ -143,15 +145,31 @@ int check_mask(const uint8_t* mask, int64_t sb, int64_t sh, int64_t si, int B, i
     return ATTN_OK;
 }
 
+// Every host-side check of attn_fwd_ex, in the documented order.
+int validate_all(const void* q, const void* k, const void* v, void* out, int B, int H, int Hkv,
+                 int Sq, int Skv, int d, int dv, float scale, int dtype, const uint8_t* mask,
+                 int64_t msb, int64_t msh, int64_t msi) {
+    if (!q || !k || !v || !out) return ATTN_E_NULL;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_E_DTYPE;
+    int st = check_shape(B, H, Hkv, Sq, Skv, d, dv);
+    if (st != ATTN_OK) return st;
+    // the kernels track the maximum of the raw logits and hide keys with
+    // -inf logits, both of which assume a positive multiplier
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return ATTN_E_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_E_ALIGN;
+    if (choose_path(Sq, d, dtype, dv) == kPathNone) return ATTN_E_UNSUPPORTED;
+    return check_mask(mask, msb, msh, msi, B, H, Sq, Skv);
+}
+
 int run(const void* q, const void* k, const void* v, void* out, int B, int H, int Hkv, int Sq,
         int Skv, int d, float scale, int causal, const int32_t* kv_lens, int dtype, void* stream,
         void* workspace, size_t workspace_bytes, bool library_ws, const uint8_t* mask = nullptr,
-        int64_t msb = 0, int64_t msh = 0, int64_t msi = 0) {
-    int st = attn_validate_gqa(q, k, v, out, B, H, Hkv, Sq, Skv, d, scale, causal, dtype);
+        int64_t msb = 0, int64_t msh = 0, int64_t msi = 0, int dv = -1) {
+    if (dv < 0) dv = d;
+    int st = validate_all(q, k, v, out, B, H, Hkv, Sq, Skv, d, dv, scale, dtype, mask, msb, msh,
+                          msi);
     if (st != ATTN_OK) return st;
-    st = check_mask(mask, msb, msh, msi, B, H, Sq, Skv);
-    if (st != ATTN_OK) return st;
-    const Path path = choose_path(Sq, d, dtype);
+    const Path path = choose_path(Sq, d, dtype, dv);
     const size_t need = attn_workspace_bytes_gqa(B, H, Hkv, Sq, Skv, d, dtype);
     if (library_ws) {
         workspace = nullptr;
@@ -181,7 +199,7 @@ int run(const void* q, const void* k, const void* v, void* out, int B, int H, in
         if (need > 0 && (workspace == nullptr)) return ATTN_E_NULL;
         if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_E_ALIGN;
     }
-    LaunchArgs a{q, k, v, out, B, H, Hkv, Sq, Skv, d, scale, causal ? 1 : 0, kv_lens,
+    LaunchArgs a{q, k, v, out, B, H, Hkv, Sq, Skv, d, dv, scale, causal ? 1 : 0, kv_lens,
                  static_cast<hipStream_t>(stream), workspace, workspace_bytes, mask, msb, msh,
                  msi};
     hipError_t e = hipSuccess;
@@ -207,16 +225,7 @@ extern "C" {
 int attn_validate_gqa(const void* q, const void* k, const void* v, void* out, int B, int H,
                       int Hkv, int Sq, int Skv, int d, float scale, int causal, int dtype) {
     (void)causal;
-    if (!q || !k || !v || !out) return ATTN_E_NULL;
-    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_E_DTYPE;
-    int st = check_shape(B, H, Hkv, Sq, Skv, d);
-    if (st != ATTN_OK) return st;
-    // the kernels track the maximum of the raw logits and hide keys with
-    // -inf logits, both of which assume a positive multiplier
-    if (!std::isfinite(scale) || !(scale > 0.0f)) return ATTN_E_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_E_ALIGN;
-    if (choose_path(Sq, d, dtype) == kPathNone) return ATTN_E_UNSUPPORTED;
-    return ATTN_OK;
+    return validate_all(q, k, v, out, B, H, Hkv, Sq, Skv, d, d, scale, dtype, nullptr, 0, 0, 0);
 }
 
 int attn_validate(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq,
@@ -226,8 +235,8 @@ int attn_validate(const void* q, const void* k, const void* v, void* out, int B,
 
 const char* attn_kernel_for(int Sq, int Skv, int d, int dtype) {
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return nullptr;
-    if (check_shape(1, 1, 1, Sq, Skv, d) != ATTN_OK) return nullptr;
-    switch (choose_path(Sq, d, dtype)) {
+    if (check_shape(1, 1, 1, Sq, Skv, d, d) != ATTN_OK) return nullptr;
+    switch (choose_path(Sq, d, dtype, d)) {
         case kPathGenericF32: return "generic_f32";
         case kPathPrefill: return "prefill_bf16_mfma";
         case kPathDecode: return "decode_bf16_splitkv";
@@ -237,8 +246,8 @@ const char* attn_kernel_for(int Sq, int Skv, int d, int dtype) {
 
 size_t attn_workspace_bytes_gqa(int B, int H, int Hkv, int Sq, int Skv, int d, int dtype) {
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
-    if (check_shape(B, H, Hkv, Sq, Skv, d) != ATTN_OK) return 0;
-    switch (choose_path(Sq, d, dtype)) {
+    if (check_shape(B, H, Hkv, Sq, Skv, d, d) != ATTN_OK) return 0;
+    switch (choose_path(Sq, d, dtype, d)) {
         case kPathDecode: return decode_workspace_bytes(B, H, Hkv, Skv, d);
         case kPathPrefill: return prefill_workspace_bytes(B, H, Sq, Skv, d);
         default: return 0;
@@ -264,21 +273,22 @@ int attn_fwd_gqa_ws(const void* q, const void* k, const void* v, void* out, int 
                workspace, workspace_bytes, false);
 }
 
-int attn_validate_mask(const void* q, const void* k, const void* v, void* out, int B, int H,
-                       int Hkv, int Sq, int Skv, int d, float scale, int causal,
-                       const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int64_t mask_si,
-                       int dtype) {
-    int st = attn_validate_gqa(q, k, v, out, B, H, Hkv, Sq, Skv, d, scale, causal, dtype);
-    if (st != ATTN_OK) return st;
-    return check_mask(mask, mask_sb, mask_sh, mask_si, B, H, Sq, Skv);
+int attn_validate_ex(const void* q, const void* k, const void* v, void* out, int B, int H,
+                     int Hkv, int Sq, int Skv, int d, int dv, float scale, int causal,
+                     const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int64_t mask_si,
+                     int dtype) {
+    (void)causal;
+    return validate_all(q, k, v, out, B, H, Hkv, Sq, Skv, d, dv, scale, dtype, mask, mask_sb,
+                        mask_sh, mask_si);
 }
 
-int attn_fwd_mask(const void* q, const void* k, const void* v, void* out, int B, int H, int Hkv,
-                  int Sq, int Skv, int d, float scale, int causal, const int32_t* kv_lens,
-                  const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int64_t mask_si,
-                  int dtype, void* stream, void* workspace, size_t workspace_bytes) {
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, int H, int Hkv,
+                int Sq, int Skv, int d, int dv, float scale, int causal, const int32_t* kv_lens,
+                const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int64_t mask_si, int dtype,
+                void* stream, void* workspace, size_t workspace_bytes) {
     return run(q, k, v, out, B, H, Hkv, Sq, Skv, d, scale, causal, kv_lens, dtype, stream,
-               workspace, workspace_bytes, workspace == nullptr, mask, mask_sb, mask_sh, mask_si);
+               workspace, workspace_bytes, workspace == nullptr, mask, mask_sb, mask_sh, mask_si,
+               dv);
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq,
@@ -301,7 +311,8 @@ const char* attn_status_string(int status) {
         case ATTN_E_NULL: return "null pointer argument";
         case ATTN_E_SHAPE:
             return "invalid shape (a size <= 0, Sq > Skv, H not a multiple of H_kv, or too large)";
-        case ATTN_E_UNSUPPORTED: return "unsupported combination of dtype and head size";
+        case ATTN_E_UNSUPPORTED:
+            return "unsupported combination of dtype and head sizes (or mask row stride)";
         case ATTN_E_DTYPE: return "unknown dtype";
         case ATTN_E_ALIGN:
             return "pointer not aligned (16 bytes; workspace 256 bytes; mask and its strides 4 "

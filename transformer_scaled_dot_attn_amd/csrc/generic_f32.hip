@@ -1,4 +1,4 @@
-// Float32 attention forward on the vector ALUs (any d <= 128, any Sq <= Skv).
+// Float32 attention forward on the vector ALUs (any d, d_v <= 128, any Sq <= Skv).
 //
 // One wavefront per block and one query row per lane; the block's 64 query
 // rows share K/V tiles of 32 keys staged in LDS (every lane reads the same
@@ -12,7 +12,10 @@
 // Principles", section "MHA, GQA, MQA -- the KV cache lever").  An
 // explicit allowed-mask (MASK: a byte per query row and key, nonzero =
 // visible, ANDed with the causal and length rules) is read as eight 4-byte
-// words of the lane's row per tile; a row with no visible key is 0.
+// words of the lane's row per tile; a row with no visible key is 0.  The
+// value width d_v may differ from d (the d_v != d_k case of "Attention from
+// Scratch", KubeDojo module 1.4.3, Part 2): K rows have d features, V and
+// output rows d_v.
 #include "device_common.h"
 #include "launch.h"
 
@@ -23,14 +26,14 @@ namespace {
 constexpr int kRows = 64;   // query rows per block
 constexpr int kKeys = 32;   // keys per LDS tile
 
-template <int DP, bool MASK>  // DP: d rounded up to 16, 32, 64 or 128
+template <int DP, int DPV, bool MASK>  // DP, DPV: d, d_v rounded up to 16, 32, 64 or 128
 __global__ __launch_bounds__(64) void generic_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ out, const int32_t* __restrict__ kv_lens, int H, int Hkv, int Sq, int Skv,
-    int d, float scale_log2, int causal, const uint8_t* __restrict__ mask, long long msb,
+    int d, int dv, float scale_log2, int causal, const uint8_t* __restrict__ mask, long long msb,
     long long msh, long long msi) {
     __shared__ float ks[kKeys][DP];
-    __shared__ float vs[kKeys][DP];
+    __shared__ float vs[kKeys][DPV];
 
     const int lane = threadIdx.x;
     const int nqt = (Sq + kRows - 1) / kRows;
@@ -52,13 +55,12 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
     if (row0 >= n) kv_hi = 0;
 
     float qr[DP];
-    float acc[DP];
+    float acc[DPV];
     const float* qrow = q + ((size_t)bh * Sq + (live ? i : 0)) * d;
 #pragma unroll
-    for (int c = 0; c < DP; ++c) {
-        qr[c] = (live && c < d) ? qrow[c] : 0.0f;
-        acc[c] = 0.0f;
-    }
+    for (int c = 0; c < DP; ++c) qr[c] = (live && c < d) ? qrow[c] : 0.0f;
+#pragma unroll
+    for (int c = 0; c < DPV; ++c) acc[c] = 0.0f;
     float m = -INFINITY, l = 0.0f;
 
     const int bk = b * Hkv + (bh - b * H) / (H / Hkv);  // this head's K/V head
@@ -67,21 +69,28 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
         mrow = mask + b * msb + (long long)(bh - b * H) * msh + (long long)(live ? i : 0) * msi;
     const int mlast = mask_last_word(Skv);
     const float* kb = k + (size_t)bk * Skv * d;
-    const float* vb = v + (size_t)bk * Skv * d;
+    const float* vb = v + (size_t)bk * Skv * dv;
     for (int j0 = 0; j0 < kv_hi; j0 += kKeys) {
         const int nk = min(kKeys, kv_hi - j0);
         __syncthreads();
         // stage the tile: the tile is contiguous in global memory
         for (int e = lane; e < kKeys * d; e += 64) {
             const int r = e / d, c = e - r * d;
-            const bool ok = r < nk;
-            ks[r][c] = ok ? kb[(size_t)j0 * d + e] : 0.0f;
-            vs[r][c] = ok ? vb[(size_t)j0 * d + e] : 0.0f;
+            ks[r][c] = r < nk ? kb[(size_t)j0 * d + e] : 0.0f;
+        }
+        for (int e = lane; e < kKeys * dv; e += 64) {
+            const int r = e / dv, c = e - r * dv;
+            vs[r][c] = r < nk ? vb[(size_t)j0 * dv + e] : 0.0f;
         }
         if (d < DP) {
             for (int e = lane; e < kKeys * (DP - d); e += 64) {
                 const int r = e / (DP - d), c = d + e - r * (DP - d);
                 ks[r][c] = 0.0f;
+            }
+        }
+        if (dv < DPV) {
+            for (int e = lane; e < kKeys * (DPV - dv); e += 64) {
+                const int r = e / (DPV - dv), c = dv + e - r * (DPV - dv);
                 vs[r][c] = 0.0f;
             }
         }
@@ -116,24 +125,38 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
         const float alpha = fast_exp2(m - m_use);
         l *= alpha;
 #pragma unroll
-        for (int c = 0; c < DP; ++c) acc[c] *= alpha;
+        for (int c = 0; c < DPV; ++c) acc[c] *= alpha;
 #pragma unroll
         for (int r = 0; r < kKeys; ++r) {
             const float pr = fast_exp2(s[r] - m_use);
             l += pr;
 #pragma unroll
-            for (int c = 0; c < DP; ++c) acc[c] = fmaf(pr, vs[r][c], acc[c]);
+            for (int c = 0; c < DPV; ++c) acc[c] = fmaf(pr, vs[r][c], acc[c]);
         }
         m = m_new;
     }
 
     if (i < Sq) {
-        float* orow = out + ((size_t)bh * Sq + i) * d;
+        float* orow = out + ((size_t)bh * Sq + i) * dv;
         const float inv = (live && l > 0.0f) ? 1.0f / l : 0.0f;
 #pragma unroll
-        for (int c = 0; c < DP; ++c)
-            if (c < d) orow[c] = live ? acc[c] * inv : 0.0f;
+        for (int c = 0; c < DPV; ++c)
+            if (c < dv) orow[c] = live ? acc[c] * inv : 0.0f;
     }
+}
+
+// Calls go(generic_f32_kernel<16 << wd, 16 << wv, mask>) for run-time
+// width indices wd, wv in 0..3 and the mask flag.
+template <int WD = 0, int WV = 0, class Go>
+void dispatch(Go&& go, int wd, int wv, bool mask) {
+    if constexpr (WD < 3) {
+        if (wd > WD) return dispatch<WD + 1, WV>(go, wd, wv, mask);
+    }
+    if constexpr (WV < 3) {
+        if (wv > WV) return dispatch<WD, WV + 1>(go, wd, wv, mask);
+    }
+    constexpr int DP = 16 << WD, DPV = 16 << WV;
+    mask ? go(generic_f32_kernel<DP, DPV, true>) : go(generic_f32_kernel<DP, DPV, false>);
 }
 
 }  // namespace
@@ -150,17 +173,11 @@ hipError_t launch_generic_f32(const LaunchArgs& a) {
     if (t) t->begin(kGenericF32, a.stream);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, a.stream, q, k, v, o, a.kv_lens, a.H, a.Hkv, a.Sq,
-                           a.Skv, a.d, sl, a.causal, a.mask, a.msb, a.msh, a.msi);
+                           a.Skv, a.d, a.dv, sl, a.causal, a.mask, a.msb, a.msh, a.msi);
     };
-    const bool m = a.mask != nullptr;
-    if (a.d <= 16)
-        m ? go(generic_f32_kernel<16, true>) : go(generic_f32_kernel<16, false>);
-    else if (a.d <= 32)
-        m ? go(generic_f32_kernel<32, true>) : go(generic_f32_kernel<32, false>);
-    else if (a.d <= 64)
-        m ? go(generic_f32_kernel<64, true>) : go(generic_f32_kernel<64, false>);
-    else
-        m ? go(generic_f32_kernel<128, true>) : go(generic_f32_kernel<128, false>);
+    // d and d_v rounded up to 16, 32, 64 or 128 (d, d_v <= 128 is checked by the front end)
+    auto width = [](int x) { return x <= 16 ? 0 : x <= 32 ? 1 : x <= 64 ? 2 : 3; };
+    dispatch(go, width(a.d), width(a.dv), a.mask != nullptr);
     hipError_t e = hipGetLastError();
     if (t) t->end(kGenericF32, a.stream);
     return e;

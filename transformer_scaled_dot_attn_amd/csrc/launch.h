@@ -12,6 +12,7 @@ struct LaunchArgs {
     const void* v;
     void* out;
     int B, H, Hkv, Sq, Skv, d;  // Hkv key/value heads; query head h reads K/V head h / (H / Hkv)
+    int dv;                     // value / output width (== d on the bf16 paths)
     float scale;
     int causal;
     const int32_t* kv_lens;
