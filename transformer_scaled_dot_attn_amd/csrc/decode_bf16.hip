@@ -206,10 +206,14 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 // K/V head, group of up to 32 query heads, split of `chunk` keys).  The
 // query heads a K/V head serves are the 32 columns of one MFMA tile (heads
 // past the group are zero columns), so per 32-key tile the wave computes
-// S^T = K Q^T with 8 (d/16) v_mfma_f32_32x32x16_bf16 -- K rows loaded from
-// memory straight into the A-operand layout, Q^T held as the B operand --
-// and O^T += V^T P^T with 8 (d/16) more, V^T read through
-// ds_read_b64_tr_b16 from the tile staged in LDS.  In both accumulators a
+// S^T = K Q^T with 8 (d/16) v_mfma_f32_32x32x16_bf16 -- K from the tile
+// staged in LDS as the A operand, Q^T held as the B operand -- and
+// O^T += V^T P^T with 8 (d/16) more, V^T read through ds_read_b64_tr_b16
+// from the staged V tile.  K and V both arrive by whole-row, non-temporal
+// 16-byte loads (a wave-wide load covers 1 KiB of contiguous rows), issued
+// for the next tile at the top of each iteration; K loaded straight into
+// the A-operand layout instead (32 bytes of each of 32 rows per load)
+// measured 17 % slower at 8 K/V heads.  In both accumulators a
 // lane owns one query head, so the online softmax is lane-local plus one
 // half swap, as in the prefill kernel.  The matrix cores have ample headroom
 // (16 MFMAs per 16 KiB of K+V), so with grouped heads decode stays bound by
@@ -225,8 +229,12 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(
     constexpr int kStrideV = D + 16;      // padded LDS row of V (elements)
     constexpr int kChunks = D / 8;        // 16-byte chunks per row
     constexpr int kVRows = 64 / kChunks;  // V rows per wave-wide load
-    constexpr int kVLoads = 32 / kVRows;  // wave-wide loads per 32-row V tile
+    constexpr int kVLoads = 32 / kVRows;  // wave-wide loads per 32-row K or V tile
+    constexpr int kStrideK = D + 8;       // padded LDS row of K: 8 consecutive rows start in
+                                          // 8 different 16-byte bank groups (A-operand reads)
+    constexpr int kAheadK = 2;            // K operand k-steps read ahead of their MFMA
     __shared__ __attribute__((aligned(16))) uint16_t lds_v[32 * kStrideV];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k[32 * kStrideK];
 
     const int lane = threadIdx.x;
     const int half = lane >> 5;
@@ -273,26 +281,21 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(
         }
     };
 
-    // K tile rows in A-operand order (row = lane % 32, features
-    // 16*ks + 8*(lane/32) ..), V tile rows whole (kVRows rows per load).
-    // Rows at or past k1 are redirected to row k0 (valid; logits masked).
-    // A K load instruction covers 32 bytes of each of 32 rows, so K goes
-    // through the vector cache (the other 3/4 of each line are the next
-    // three loads): streaming (non-temporal) K loads measured 1.4x slower.
-    u32x4 kr[kKSteps], vr[kVLoads];
-    auto load_k = [&](int t0) {
-        const int row = t0 + jh;
-        const uint16_t* src = kb + (size_t)(row < k1 ? row : k0) * D + half * 8;
-#pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) kr[ks] = ldg16(src + ks * 16);
-    };
-    auto load_v = [&](int t0) {
+    // K and V tile rows whole (kVRows rows per load, lane%kChunks the
+    // 16-byte chunk).  Rows at or past k1 are redirected to row k0 (valid;
+    // their logits are masked).
+    u32x4 kr[kVLoads], vr[kVLoads];
+    auto load_kv = [&](int t0) {
 #pragma unroll
         for (int c = 0; c < kVLoads; ++c) {
             const int row = t0 + c * kVRows + lane / kChunks;
-            vr[c] = ldg16_stream(vb + (size_t)(row < k1 ? row : k0) * D + (lane % kChunks) * 8);
+            const size_t off = (size_t)(row < k1 ? row : k0) * D + (lane % kChunks) * 8;
+            kr[c] = ldg16_stream(kb + off);
+            vr[c] = ldg16_stream(vb + off);
         }
     };
+    // K operand of S^T from LDS: row lane%32, features 16*ks + 8*(lane/32)
+    const int k_rd = jh * kStrideK + half * 8;
     //  V^T operand via ds_read_b64_tr_b16 (the prefill kernel's mapping):
     //  within each 16-lane group, source lane i reads features col0 + 4*(i%4)
     //  .. +3 of key row key0 + i/4; lanes of the second half take keys 4..7
@@ -307,31 +310,39 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
 
-    load_k(k0);
+    load_kv(k0);
     load_m(k0, mw);
-    load_v(k0);
     for (int t0 = k0; t0 < k1; t0 += 32) {
-        // V(t0) to LDS; the next tile's V loads reuse its registers
+        // K(t0), V(t0) to LDS; the next tile's loads reuse their registers
 #pragma unroll
-        for (int c = 0; c < kVLoads; ++c)
-            *reinterpret_cast<u32x4*>(lds_v + (c * kVRows + lane / kChunks) * kStrideV +
-                                      (lane % kChunks) * 8) = vr[c];
+        for (int c = 0; c < kVLoads; ++c) {
+            const int r = c * kVRows + lane / kChunks, col = (lane % kChunks) * 8;
+            *reinterpret_cast<u32x4*>(lds_k + r * kStrideK + col) = kr[c];
+            *reinterpret_cast<u32x4*>(lds_v + r * kStrideV + col) = vr[c];
+        }
         __syncthreads();
         const bool next = t0 + 32 < k1;
-        if (next) load_v(t0 + 32);
+        if (next) {
+            load_kv(t0 + 32);
+            load_m(t0 + 32, mw_next);
+        }
 
-        // S^T = K Q^T for 32 keys x 32 heads
+        // S^T = K Q^T for 32 keys x 32 heads, K operands read kAheadK ahead
         f32x16 sacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
+        u32x4 ka[kAheadK + 1];
 #pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks)
+        for (int ks = 0; ks < kAheadK; ++ks)
+            ka[ks] = *reinterpret_cast<const u32x4*>(lds_k + k_rd + ks * 16);
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) {
+            if (ks + kAheadK < kKSteps)
+                ka[(ks + kAheadK) % (kAheadK + 1)] =
+                    *reinterpret_cast<const u32x4*>(lds_k + k_rd + (ks + kAheadK) * 16);
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, kr[ks]), __builtin_bit_cast(bf16x8, qf[ks]), sacc, 0, 0,
-                0);
-        if (next) {
-            load_k(t0 + 32);
-            load_m(t0 + 32, mw_next);
+                __builtin_bit_cast(bf16x8, ka[ks % (kAheadK + 1)]),
+                __builtin_bit_cast(bf16x8, qf[ks]), sacc, 0, 0, 0);
         }
         bool cut = t0 + 32 > k1;
         if constexpr (MASK) {
@@ -398,7 +409,7 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(
                 __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, pf[kk]), oacc[db], 0, 0,
                 0);
         }
-        __syncthreads();  // the V tile is read before the next one is stored
+        __syncthreads();  // the K and V tiles are read before the next ones are stored
     }
 
     // one partial per served query head: (m, l) in exp2 units and acc[D]
@@ -549,6 +560,10 @@ void launch_partial_d(const LaunchArgs& a, const DecodePlan& p, float sl, float*
 
 hipError_t launch_decode_bf16(const LaunchArgs& a) {
     const DecodePlan p = decode_plan(a.B, a.H, a.Hkv, a.Skv);
+    // the front end sizes the workspace; refuse rather than write through a bad one
+    if (a.workspace == nullptr ||
+        a.workspace_bytes < decode_workspace_bytes(a.B, a.H, a.Hkv, a.Skv, a.d))
+        return hipErrorInvalidValue;
     const size_t units = (size_t)a.B * a.H * p.nsplit;
     float* ws_acc = static_cast<float*>(a.workspace);
     float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +

@@ -654,6 +654,10 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
     float* ws_acc = nullptr;
     float* ws_ml = nullptr;
     if (p.nsplit > 1) {
+        // the front end sizes the workspace; refuse rather than write through a bad one
+        if (a.workspace == nullptr ||
+            a.workspace_bytes < prefill_workspace_bytes(a.B, a.H, a.Sq, a.Skv, a.d))
+            return hipErrorInvalidValue;
         const size_t units = (size_t)BH * a.Sq * p.nsplit;
         ws_acc = static_cast<float*>(a.workspace);
         ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
