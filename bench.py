@@ -83,15 +83,18 @@ def timed_calls(attn, fn, steps, warmup, kernels):
 
 
 def gqa_decode_sweep(attn, W, dev, steps, warmup,
-                     names=("decode8192_bf16", "gqa_decode8192_bf16", "mqa_decode8192_bf16")):
+                     names=("decode8192_bf16", "gqa_decode8192_bf16", "mqa_decode8192_bf16"),
+                     have=None):
     """Decode at 32, 8 and 1 K/V heads for 32 query heads ("Attention from
     First Principles", section 10, exercise F): bytes moved fall by H / H_kv
-    while the flops stay, so the intensity is H / H_kv."""
+    while the flops stay, so the intensity is H / H_kv.  `have` maps workload
+    names to device inputs already drawn (the step's), which are reused."""
     import torch
     rows = []
+    have = have or {}
     for name in names:
         w = W.WORKLOADS[name]
-        x = W.device_inputs(w, dev)
+        x = have[name] if name in have else W.device_inputs(w, dev)
         out = torch.empty_like(x["q"])
         fn = lambda: attn.fwd(x["q"], x["k"], x["v"], out, causal=w.causal,
                               kv_lens=x["kv_lens"], scale=x["scale"])
@@ -220,9 +223,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--parts", default="prefill,decode,masks",
+    ap.add_argument("--parts", default="prefill,decode,masks,gqa,sweep",
                     help="comma list of prefill, decode, masks, copy, gqa, gqa8, sweep (default "
-                         "prefill,decode,masks); masks times the step's workloads again with "
+                         "prefill,decode,masks,gqa,sweep); masks times the step's workloads again with "
                          "allowed-masks; gqa8 is the 8-K/V-head decode alone; copy adds a plain 1 GiB device-to-device copy per "
                          "step, the known-size kernel that scales the HBM byte counters; gqa "
                          "measures decode at 32, 8 and 1 K/V heads for 32 query heads; sweep "
@@ -364,7 +367,8 @@ def main():
 
     if "gqa" in parts:
         print("[bench] grouped-head decode sweep", file=sys.stderr, flush=True)
-        result["gqa_decode"] = gqa_decode_sweep(attn, W, dev, args.steps, args.warmup)
+        have = {w.name: x for kind, w, x, _ in runs if kind == "decode"}
+        result["gqa_decode"] = gqa_decode_sweep(attn, W, dev, args.steps, args.warmup, have=have)
     elif "gqa8" in parts:
         result["gqa_decode"] = gqa_decode_sweep(attn, W, dev, args.steps, args.warmup,
                                                 names=("gqa_decode8192_bf16",))
