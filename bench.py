@@ -158,7 +158,9 @@ def mask_runs(attn, W, runs, steps, warmup):
             masks = [("none", None),
                      ("key padding [1,1,1,S], first 256 keys hidden",
                       W.key_padding_mask([256], [S], S)),
-                     ("random [1,1,S,S], density 0.5", W.random_mask(5, (1, 1, w.Sq, S), 0.5))]
+                     ("random [1,1,S,S], density 0.5", W.random_mask(5, (1, 1, w.Sq, S), 0.5)),
+                     ("8 packed documents of 512 [1,1,S,S]", W.document_mask([S // 8] * 8)),
+                     ("sliding window of 256 [1,1,S,S]", W.window_mask(S, 256))]
             kernels = ("prefill_bf16_mfma",)
         else:
             lens = x["kv_lens_host"]

@@ -101,6 +101,32 @@ def test_causal_rule_as_mask(dt, d):
     assert torch.equal(ta, tb), f"max diff {np.abs(a - b).max()}"
 
 
+STRUCTURED = [
+    # name, B, H, S, d, causal, kv_lens, mask builder
+    ("left padding", 2, 4, 1000, 128, 1, [1000, 700],
+     lambda S: W.key_padding_mask([300, 130], [S, S], S)),
+    ("documents", 1, 4, 1000, 128, 1, None, lambda S: W.document_mask([200, 577, 223])),
+    ("documents d64", 1, 2, 777, 64, 0, None, lambda S: W.document_mask([64, 1, 300, 412])),
+    ("sliding window", 1, 4, 1200, 128, 1, None, lambda S: W.window_mask(S, 130)),
+    ("window split", 1, 2, 4500, 128, 0, None, lambda S: W.window_mask(S, 70)),
+]
+
+
+@pytest.mark.parametrize("case", STRUCTURED, ids=lambda c: c[0].replace(" ", "_"))
+def test_structured_masks_skip_hidden_tiles(case):
+    """Masks that hide whole tiles from whole waves (those waves skip them)."""
+    name, B, H, S, d, causal, lens, build = case
+    _say(f"structured mask {name}: B{B} H{H} S{S} d{d} causal{causal}")
+    prob = W.random_problem(sum(map(ord, name)), B, H, S, S, d, "bf16", lens)
+    mask = build(S)
+    got, _ = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], causal, lens,
+                     mask=W.mask_to_torch(mask))
+    ref = oracle.attention(prob["q"], prob["k"], prob["v"], prob["scale"], causal, lens,
+                           mask=mask)
+    assert_matches(got, ref, BF16_TOL, lens, S, name)
+    assert np.all(got[np.all(ref == 0.0, axis=-1)] == 0.0)
+
+
 def test_mask_layout_errors():
     import torch
     B, H, S, d = 1, 2, 90, 64

@@ -54,8 +54,11 @@
 // at the start of the next iteration the wave parks them in a per-lane LDS
 // slot, so they hold no registers across the score MFMAs, and decides once
 // whether any of its lanes hides a key of the tile.  Only then are they read
-// back for the per-element pass.  Tile skipping still follows the causal
-// and length rules only.
+// back for the per-element pass.  A tile that the mask hides entirely from
+// every live row of a wave is skipped by that wave (its weights would all be
+// exactly zero and its maximum -inf), so structured masks -- left padding,
+// packed documents, sliding windows -- cost only the tiles they open; the
+// block still stages every tile its rules reach.
 //
 // Order.  Block ids are mapped heaviest query tile first; within a query
 // tile rank the (b, h) pairs are laid out so that each XCD (ids are dealt
@@ -189,7 +192,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // to the row's last readable word; keys past it are >= Skv >= L and
     // hidden by the length rule anyway.
     u32x4 mw[2];  // in flight: word w is mw[w / 4][w % 4]
-    bool mcut = false;  // some lane of the wave hides a key of the parked tile
+    bool mcut = false;   // some lane of the wave hides a key of the parked tile
+    bool mnone = false;  // no live lane of the wave sees a key of the parked tile
     // addressed as a wave-uniform row base (row min(qw, Sq-1)) plus a 32-bit
     // lane offset (qi - that row) * msi, below 32 * msi <= 2^32; pad lanes
     // read the base row
@@ -212,10 +216,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     };
     auto mpark = [&]() {
         if constexpr (MASK) {
-            uint32_t z = 0;
+            uint32_t z = 0, nz = 0;
 #pragma unroll
-            for (int w = 0; w < 8; ++w) z |= has_zero_byte(mw[w >> 2][w & 3]);
+            for (int w = 0; w < 8; ++w) {
+                z |= has_zero_byte(mw[w >> 2][w & 3]);
+                nz |= mw[w >> 2][w & 3];
+            }
             mcut = __builtin_amdgcn_ballot_w64(z != 0) != 0;
+            mnone = __builtin_amdgcn_ballot_w64(q_live && nz != 0) == 0;
             lds_m[2 * tid] = mw[0];
             lds_m[2 * tid + 1] = mw[1];
         }
@@ -494,6 +502,38 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         __syncthreads();
     };
 
+    // The masked step: as `step`, but a wave skips the tiles its mask words
+    // show fully hidden.  `have` says whether the wave holds the scores of
+    // tile t (it skipped tile t otherwise); the four cases chain the score of
+    // the next computed tile to the weights of the last one exactly as the
+    // prologue, the pipelined step and the wave's last tile do.
+    bool have = false;
+    auto step_m = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+        mpark();  // mask words of tile t+1
+        const bool next = t + 1 < t1w && !mnone;  // this wave computes tile t+1
+        fetch(k, t + 2, kreg);
+        if (next) {
+            if (have) score(t + 1, sn, &sc);
+            else score(t + 1, sn, nullptr);
+        }
+        fetch(v, t + 1, vreg);
+        mload(t + 2);
+        if (next) mask(t + 1, sn);
+        if (have && next) {
+            const float mx = mix(t, &sn);
+            reference(mx);
+        } else if (have) {
+            weigh(sc);
+            mix(t, nullptr);
+        } else if (next) {
+            reference(scan(sn));
+        }
+        have = next;
+        stash_k(t + 2);
+        stash_v(t + 1);
+        __syncthreads();
+    };
+
     // prologue: K(t0), V(t0), K(t0+1) staged; S^T(t0) scored and its
     // reference set
     mload(t0);
@@ -504,8 +544,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     fetch(k, t0 + 1, kreg);
     stash_k(t0 + 1);
     __syncthreads();
-    if (t0 < t1w) {
+    if constexpr (MASK) {
         mpark();
+        have = t0 < t1w && !mnone;
+        if (have) {
+            score(t0, s0, nullptr);
+            mask(t0, s0);
+            reference(scan(s0));
+        }
+    } else if (t0 < t1w) {
         score(t0, s0, nullptr);
         mask(t0, s0);
         reference(scan(s0));
@@ -513,9 +560,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     mload(t0 + 1);
     __syncthreads();  // K(t0) is read by every wave before K(t0+2) replaces it
 
-    for (int t = t0; t < t1; t += 2) {
-        step(t, s0, s1);
-        if (t + 1 < t1) step(t + 1, s1, s0);
+    if constexpr (MASK) {
+        for (int t = t0; t < t1; t += 2) {
+            step_m(t, s0, s1);
+            if (t + 1 < t1) step_m(t + 1, s1, s0);
+        }
+    } else {
+        for (int t = t0; t < t1; t += 2) {
+            step(t, s0, s1);
+            if (t + 1 < t1) step(t + 1, s1, s0);
+        }
     }
 
     if (nsplit > 1) {

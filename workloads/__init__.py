@@ -209,6 +209,20 @@ def key_padding_mask(starts: Sequence[int], ends: Sequence[int], Skv: int) -> np
     return m[:, None, None, :]
 
 
+def document_mask(doc_lens: Sequence[int]) -> np.ndarray:
+    """[1, 1, S, S] mask of packed documents: row i may see key j iff both lie
+    in the same document (consecutive runs of the given lengths, S their sum)."""
+    doc = np.repeat(np.arange(len(doc_lens)), doc_lens)
+    return (doc[:, None] == doc[None, :])[None, None]
+
+
+def window_mask(S: int, width: int) -> np.ndarray:
+    """[1, 1, S, S] sliding-window mask: row i may see keys i - width < j <= i + width
+    (the causal flag then keeps the keys up to i)."""
+    i = np.arange(S)
+    return (np.abs(i[:, None] - i[None, :]) < width)[None, None]
+
+
 def mask_to_torch(m: np.ndarray, device="cuda"):
     """bool mask -> a torch.bool view on `device` whose rows are stored in
     round_up(Skv, 4) bytes (the word-readable layout the library needs)."""
