@@ -183,8 +183,11 @@ int attn_validate_gqa(const void* q, const void* k, const void* v, void* out, in
  *   of this; otherwise pad its rows.  32 * mask_si + Skv must stay below
  *   2^32 (else ATTN_E_UNSUPPORTED).  The mask is only read.
  *   workspace NULL: the library-owned workspace, as attn_fwd_gqa; else a
- *             caller buffer as for attn_fwd_gqa_ws (attn_workspace_bytes_gqa
- *             gives its size; a mask or d_v changes nothing there).
+ *             caller buffer as for attn_fwd_gqa_ws, of attn_workspace_bytes_ex
+ *             bytes (a masked bf16 prefill needs a little more: one byte per
+ *             query tile and key tile, which it uses to skip key tiles the
+ *             mask hides from a whole query tile when the mask is shared by
+ *             all heads).
  * The masked kernels are separate instantiations: calls with mask == NULL
  * run exactly the unmasked code.
  */
@@ -192,6 +195,11 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, i
                 int Sq, int Skv, int d, int d_v, float scale, int causal, const int32_t* kv_lens,
                 const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int64_t mask_si, int dtype,
                 void* stream, void* workspace, size_t workspace_bytes);
+
+/* Device bytes attn_fwd_ex needs as caller workspace (masked != 0 when a
+   mask is passed); 0 also for invalid arguments. */
+size_t attn_workspace_bytes_ex(int B, int H, int H_kv, int Sq, int Skv, int d, int d_v, int dtype,
+                               int masked);
 
 /* The host-side checks of attn_fwd_ex alone (as attn_validate; d_v <= 0 is
    ATTN_E_SHAPE, a d_v the dtype's kernels do not take ATTN_E_UNSUPPORTED). */

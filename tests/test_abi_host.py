@@ -144,7 +144,7 @@ def test_prefill_split_workspace():
 def test_profile_names():
     names = attn.profile_names()
     assert names == ["prefill_bf16_mfma", "decode_bf16_partial", "decode_bf16_combine",
-                     "generic_f32", "prefill_bf16_combine"]
+                     "generic_f32", "prefill_bf16_combine", "prefill_mask_tiles"]
 
 
 def test_python_layer_rejects_bad_tensors():
@@ -202,3 +202,20 @@ def test_validate_value_width():
     assert vm(mask=None, dtype=BF16, d=128, dv=64) == attn.E_UNSUPPORTED
     assert vm(mask=None, dtype=BF16, d=64, dv=64) == attn.OK
     assert vm(mask=None, dtype=BF16, Sq=1, d=128, dv=128) == attn.OK
+
+
+def test_masked_prefill_workspace():
+    # key-tile marks: one byte per (batch, query tile, key tile), after any split partials
+    base = attn.workspace_bytes(2, 32, 4096, 4096, 128, BF16)
+    masked = attn.workspace_bytes(2, 32, 4096, 4096, 128, BF16, masked=True)
+    assert base == 0 and masked >= 2 * 16 * 64 and masked % 256 == 0
+    split = attn.workspace_bytes(1, 2, 300, 8000, 128, BF16)
+    assert split > 0
+    assert attn.workspace_bytes(1, 2, 300, 8000, 128, BF16, masked=True) >= split + 2 * 125
+    # decode and fp32: a mask needs nothing more
+    assert attn.workspace_bytes(4, 8, 1, 5000, 128, BF16, masked=True) == \
+        attn.workspace_bytes(4, 8, 1, 5000, 128, BF16)
+    assert attn.workspace_bytes(1, 2, 64, 64, 32, F32, masked=True) == 0
+    # beyond the list size the marks are not used
+    assert attn.workspace_bytes(1, 1, 64, 200000, 128, BF16, masked=True) == \
+        attn.workspace_bytes(1, 1, 64, 200000, 128, BF16)

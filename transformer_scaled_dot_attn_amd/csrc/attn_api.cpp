@@ -170,7 +170,7 @@ int run(const void* q, const void* k, const void* v, void* out, int B, int H, in
                           msi);
     if (st != ATTN_OK) return st;
     const Path path = choose_path(Sq, d, dtype, dv);
-    const size_t need = attn_workspace_bytes_gqa(B, H, Hkv, Sq, Skv, d, dtype);
+    const size_t need = attn_workspace_bytes_ex(B, H, Hkv, Sq, Skv, d, dv, dtype, mask != nullptr);
     if (library_ws) {
         workspace = nullptr;
         if (need > 0) {
@@ -250,6 +250,19 @@ size_t attn_workspace_bytes_gqa(int B, int H, int Hkv, int Sq, int Skv, int d, i
     switch (choose_path(Sq, d, dtype, d)) {
         case kPathDecode: return decode_workspace_bytes(B, H, Hkv, Skv, d);
         case kPathPrefill: return prefill_workspace_bytes(B, H, Sq, Skv, d);
+        default: return 0;
+    }
+}
+
+size_t attn_workspace_bytes_ex(int B, int H, int Hkv, int Sq, int Skv, int d, int dv, int dtype,
+                               int masked) {
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
+    if (check_shape(B, H, Hkv, Sq, Skv, d, dv) != ATTN_OK) return 0;
+    switch (choose_path(Sq, d, dtype, dv)) {
+        case kPathDecode: return decode_workspace_bytes(B, H, Hkv, Skv, d);
+        case kPathPrefill:
+            return prefill_workspace_bytes(B, H, Sq, Skv, d) +
+                   (masked ? prefill_mask_workspace_bytes(B, Sq, Skv) : 0);
         default: return 0;
     }
 }
@@ -373,6 +386,7 @@ const char* attn_profile_name(int kernel) {
         case kDecodeCombineBf16: return "decode_bf16_combine";
         case kGenericF32: return "generic_f32";
         case kPrefillCombineBf16: return "prefill_bf16_combine";
+        case kPrefillMaskTiles: return "prefill_mask_tiles";
         default: return nullptr;
     }
 }

@@ -47,6 +47,8 @@ struct PrefillPlan {
 };
 PrefillPlan prefill_plan(int B, int H, int Sq, int Skv);
 size_t prefill_workspace_bytes(int B, int H, int Sq, int Skv, int d);
+// extra bytes a masked prefill needs for its key-tile marks (after the above)
+size_t prefill_mask_workspace_bytes(int B, int Sq, int Skv);
 
 inline size_t round_up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -59,7 +61,7 @@ struct KernelTimer {
 KernelTimer* active_timer();  // nullptr when timing is off
 
 enum KernelId { kPrefillBf16 = 0, kDecodePartialBf16 = 1, kDecodeCombineBf16 = 2, kGenericF32 = 3,
-                kPrefillCombineBf16 = 4, kNumKernels = 5 };
+                kPrefillCombineBf16 = 4, kPrefillMaskTiles = 5, kNumKernels = 6 };
 
 hipError_t launch_generic_f32(const LaunchArgs& a);
 hipError_t launch_prefill_bf16(const LaunchArgs& a);

@@ -56,9 +56,14 @@
 // whether any of its lanes hides a key of the tile.  Only then are they read
 // back for the per-element pass.  A tile that the mask hides entirely from
 // every live row of a wave is skipped by that wave (its weights would all be
-// exactly zero and its maximum -inf), so structured masks -- left padding,
-// packed documents, sliding windows -- cost only the tiles they open; the
-// block still stages every tile its rules reach.
+// exactly zero and its maximum -inf).  For a mask shared by all heads, a
+// small kernel first reads it once (prefill_mask_tiles_kernel) and marks,
+// per query tile and key tile, whether any row of the query tile may see a
+// key of the key tile; each block compacts its query tile's marks into an
+// ascending list of key tiles and stages and walks only those, so
+// structured masks -- left padding, packed documents, sliding windows --
+// cost only the tiles they open.  The loop then runs over list positions:
+// LDS ring slots follow the position, key offsets and masks the listed tile.
 //
 // Order.  Block ids are mapped heaviest query tile first; within a query
 // tile rank the (b, h) pairs are laid out so that each XCD (ids are dealt
@@ -82,6 +87,7 @@ constexpr int kBN = 64;    // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
+constexpr int kMaxListTiles = 2048;   // key tiles a block's tile list may hold (Skv <= 131072)
 
 template <int D>
 struct Shape {
@@ -116,11 +122,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
     const int32_t* __restrict__ kv_lens, int BH, int H, int Hkv, int Sq, int Skv, float scale_log2,
     int causal, int nqt, int nsplit, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
-    const uint8_t* __restrict__ allowed, long long msb, long long msh, long long msi) {
+    const uint8_t* __restrict__ allowed, long long msb, long long msh, long long msi,
+    const uint8_t* __restrict__ tmap, int nkt) {
     using S = Shape<D>;
     __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][S::kTileK];
     __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][S::kTileV];
     __shared__ u32x4 lds_m[MASK ? 2 * kThreads : 1];  // parked mask words, 32 bytes per lane
+    __shared__ int lds_tl[MASK ? kMaxListTiles : 1];  // this query tile's listed key tiles
+    __shared__ int lds_tn;                            // their number
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -170,6 +179,45 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int kv_hi_w = wave_live ? (causal ? min(L, p_hi + 1) : L) : 0;
     const int t1w = min(t1, (kv_hi_w + kBN - 1) / kBN);  // this wave computes t0 <= t < t1w
     const int kfull_w = causal ? min(L, p_lo + 1) : L;
+    const int tw = (kv_hi_w + kBN - 1) / kBN;  // key tiles this wave's rules reach
+
+    // Masked calls walk list positions pp0 <= pos < pp1 of the key tiles the
+    // mask opens to this query tile (all tiles when no list is given);
+    // tix(pos) is the key tile at a position (positions past the list map to
+    // its last tile, a valid one, for the staging run-ahead).
+    int pp0 = t0, pp1 = t1;
+    bool listed = false;
+    int lcount = 0;
+    if constexpr (MASK) {
+        if (tmap != nullptr) {  // the mask is shared by all heads (msh == 0)
+            listed = true;
+            const uint8_t* tm = tmap + ((size_t)(msb != 0 ? b : 0) * nqt + qt) * nkt;
+            if (wave == 0) {
+                // compact the marks of key tiles 0 .. ntiles_q-1 in ascending
+                // order: 64 tiles per round, a lane each, ballot and prefix count
+                int base = 0;
+                for (int k0 = 0; k0 < ntiles_q; k0 += 64) {
+                    const int kt = k0 + lane;
+                    const bool on = kt < ntiles_q && tm[min(kt, nkt - 1)] != 0;
+                    const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
+                    if (on) lds_tl[base + __builtin_popcountll(bal & ((1ull << lane) - 1))] = kt;
+                    base += __builtin_popcountll(bal);
+                }
+                if (lane == 0) lds_tn = base;
+            }
+            __syncthreads();
+            lcount = lds_tn;
+            const int per = (lcount + nsplit - 1) / nsplit;
+            pp0 = min(lcount, split * per);
+            pp1 = min(lcount, pp0 + per);
+        }
+    }
+    auto tix = [&](int pos) -> int {
+        if constexpr (MASK) {
+            if (listed) return lcount > 0 ? lds_tl[min(pos, lcount - 1)] : 0;
+        }
+        return pos;
+    };
 
     // this lane's query
     const int qi = qw + (lane & 31);
@@ -508,17 +556,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // the next computed tile to the weights of the last one exactly as the
     // prologue, the pipelined step and the wave's last tile do.
     bool have = false;
-    auto step_m = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-        mpark();  // mask words of tile t+1
-        const bool next = t + 1 < t1w && !mnone;  // this wave computes tile t+1
-        fetch(k, t + 2, kreg);
+    auto step_m = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {  // t: list position
+        mpark();  // mask words of position t+1
+        const bool next = t + 1 < pp1 && tix(t + 1) < tw && !mnone;  // this wave computes t+1
+        fetch(k, tix(t + 2), kreg);
         if (next) {
             if (have) score(t + 1, sn, &sc);
             else score(t + 1, sn, nullptr);
         }
-        fetch(v, t + 1, vreg);
-        mload(t + 2);
-        if (next) mask(t + 1, sn);
+        fetch(v, tix(t + 1), vreg);
+        mload(tix(t + 2));
+        if (next) mask(tix(t + 1), sn);
         if (have && next) {
             const float mx = mix(t, &sn);
             reference(mx);
@@ -536,20 +584,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 
     // prologue: K(t0), V(t0), K(t0+1) staged; S^T(t0) scored and its
     // reference set
-    mload(t0);
-    fetch(k, t0, kreg);
-    fetch(v, t0, vreg);
-    stash_k(t0);
-    stash_v(t0);
-    fetch(k, t0 + 1, kreg);
-    stash_k(t0 + 1);
+    mload(tix(pp0));
+    fetch(k, tix(pp0), kreg);
+    fetch(v, tix(pp0), vreg);
+    stash_k(pp0);
+    stash_v(pp0);
+    fetch(k, tix(pp0 + 1), kreg);
+    stash_k(pp0 + 1);
     __syncthreads();
     if constexpr (MASK) {
         mpark();
-        have = t0 < t1w && !mnone;
+        have = pp0 < pp1 && tix(pp0) < tw && !mnone;
         if (have) {
-            score(t0, s0, nullptr);
-            mask(t0, s0);
+            score(pp0, s0, nullptr);
+            mask(tix(pp0), s0);
             reference(scan(s0));
         }
     } else if (t0 < t1w) {
@@ -557,13 +605,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         mask(t0, s0);
         reference(scan(s0));
     }
-    mload(t0 + 1);
+    mload(tix(pp0 + 1));
     __syncthreads();  // K(t0) is read by every wave before K(t0+2) replaces it
 
     if constexpr (MASK) {
-        for (int t = t0; t < t1; t += 2) {
+        for (int t = pp0; t < pp1; t += 2) {
             step_m(t, s0, s1);
-            if (t + 1 < t1) step_m(t + 1, s1, s0);
+            if (t + 1 < pp1) step_m(t + 1, s1, s0);
         }
     } else {
         for (int t = t0; t < t1; t += 2) {
@@ -614,6 +662,45 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                 }
                 *reinterpret_cast<u32x2*>(orow + d0) = w;
             }
+    }
+}
+
+// Tile marks of an allowed-mask shared by all heads: one workgroup per
+// (mask batch, query tile, key tile), one row per thread, writes 1 if any of
+// the query tile's rows allows a key of the key tile, else 0.  Key tiles past
+// the last key a causal row of the tile can reach are marked 0 unread (the
+// prefill never visits them).
+__global__ __launch_bounds__(kBM) void prefill_mask_tiles_kernel(
+    const uint8_t* __restrict__ mask, long long msb, long long msi, int Sq, int Skv, int nqt,
+    int nkt, int causal, uint8_t* __restrict__ tmap) {
+    const int kt = blockIdx.x % nkt;
+    const int qt = (blockIdx.x / nkt) % nqt;
+    const int bm = blockIdx.x / (nkt * nqt);
+    const int q0 = qt * kBM;
+    __shared__ int flags[kBM / 64];
+    if (causal) {
+        // row i sits at position <= Skv - Sq + i (reading of the rules)
+        const int hi = Skv - Sq + min(q0 + kBM, Sq);
+        if (kt * kBN >= hi) {
+            if (threadIdx.x == 0) tmap[blockIdx.x] = 0;
+            return;
+        }
+    }
+    const int row = q0 + (int)threadIdx.x;
+    uint32_t any = 0;
+    if (row < Sq) {
+        const uint8_t* mrow = mask + bm * msb + (long long)row * msi;
+        const int mlast = mask_last_word(Skv);
+#pragma unroll
+        for (int w = 0; w < kBN / 4; ++w) any |= ldg_word(mrow + min(kt * kBN + 4 * w, mlast));
+    }
+    const bool wv = __builtin_amdgcn_ballot_w64(any != 0) != 0;
+    if ((threadIdx.x & 63) == 0) flags[threadIdx.x >> 6] = wv;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int f = 0;
+        for (int w = 0; w < kBM / 64; ++w) f |= flags[w];
+        tmap[blockIdx.x] = f ? 1 : 0;
     }
 }
 
@@ -696,6 +783,14 @@ size_t prefill_workspace_bytes(int B, int H, int Sq, int Skv, int d) {
     return round_up256(units * d * sizeof(float)) + round_up256(units * 2 * sizeof(float));
 }
 
+size_t prefill_mask_workspace_bytes(int B, int Sq, int Skv) {
+    // tile marks of a mask shared by all heads, one byte per (mask batch,
+    // query tile, key tile), after the split partials; none past the list size
+    const size_t nkt = (Skv + kBN - 1) / kBN;
+    if (nkt > (size_t)kMaxListTiles) return 0;
+    return round_up256((size_t)B * ((Sq + kBM - 1) / kBM) * nkt);
+}
+
 hipError_t launch_prefill_bf16(const LaunchArgs& a) {
     const int nqt = (a.Sq + kBM - 1) / kBM;
     const int BH = a.B * a.H;
@@ -707,11 +802,15 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
     uint16_t* o = static_cast<uint16_t*>(a.out);
     float* ws_acc = nullptr;
     float* ws_ml = nullptr;
+    const size_t ws_split = prefill_workspace_bytes(a.B, a.H, a.Sq, a.Skv, a.d);
+    // a mask shared by all heads gets key-tile lists (marks after the partials)
+    const int nkt = (a.Skv + kBN - 1) / kBN;
+    const size_t ws_marks = a.mask && a.msh == 0 ? prefill_mask_workspace_bytes(a.B, a.Sq, a.Skv) : 0;
+    if (ws_split + ws_marks > 0 &&
+        (a.workspace == nullptr || a.workspace_bytes < ws_split + ws_marks))
+        return hipErrorInvalidValue;  // the front end sizes it; never write through a bad one
+    uint8_t* tmap = ws_marks ? static_cast<uint8_t*>(a.workspace) + ws_split : nullptr;
     if (p.nsplit > 1) {
-        // the front end sizes the workspace; refuse rather than write through a bad one
-        if (a.workspace == nullptr ||
-            a.workspace_bytes < prefill_workspace_bytes(a.B, a.H, a.Sq, a.Skv, a.d))
-            return hipErrorInvalidValue;
         const size_t units = (size_t)BH * a.Sq * p.nsplit;
         ws_acc = static_cast<float*>(a.workspace);
         ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
@@ -719,11 +818,21 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
     }
     const float sl = a.scale * kLog2e;
     KernelTimer* t = active_timer();
+    if (tmap) {
+        const int Bm = a.msb != 0 ? a.B : 1;
+        if (t) t->begin(kPrefillMaskTiles, a.stream);
+        hipLaunchKernelGGL(prefill_mask_tiles_kernel, dim3((unsigned)((long)Bm * nqt * nkt)),
+                           dim3(kBM), 0, a.stream, a.mask, a.msb, a.msi, a.Sq, a.Skv, nqt, nkt,
+                           a.causal, tmap);
+        hipError_t e = hipGetLastError();
+        if (t) t->end(kPrefillMaskTiles, a.stream);
+        if (e != hipSuccess) return e;
+    }
     if (t) t->begin(kPrefillBf16, a.stream);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, a.stream, q, k, v, o, a.kv_lens, BH, a.H,
                            a.Hkv, a.Sq, a.Skv, sl, a.causal, nqt, p.nsplit, ws_acc, ws_ml, a.mask,
-                           a.msb, a.msh, a.msi);
+                           a.msb, a.msh, a.msi, tmap, nkt);
     };
     if (a.d == 128)
         a.mask ? go(prefill_bf16_kernel<128, true>) : go(prefill_bf16_kernel<128, false>);
