@@ -146,9 +146,9 @@ def mask_runs(attn, W, runs, steps, warmup):
     """The step's workloads again with explicit allowed-masks (True = may
     attend, ANDed with the causal and length rules; "Attention from Scratch",
     KubeDojo module 1.4.3, Part 3), against the same call unmasked.  Prefill
-    counts the causal flops of the unmasked call (the kernel computes every
-    score the rules allow, hidden or not); decode counts the K/V bytes plus
-    the mask bytes it reads."""
+    counts 4*d flops per visible (query, key) pair -- allowed by the mask and
+    by the causal rule -- the algorithmic work; decode counts the K/V bytes
+    plus the mask bytes it reads."""
     import numpy as np
     import torch
     rows = []
@@ -182,7 +182,14 @@ def mask_runs(attn, W, runs, steps, warmup):
             row = {"workload": w.name, "mask": label, "ms_per_call": ms,
                    "time_vs_unmasked": ms / base}
             if kind == "prefill":
-                row["TFLOP/s"] = prefill_flops(w, x["kv_lens_host"]) / (ms * 1e-3) / 1e12
+                if m is None:
+                    flops = prefill_flops(w, x["kv_lens_host"])
+                else:  # the step's prefill has B = 1 and no lengths; masks here are [1,1,*,S]
+                    rule = np.tril(np.ones((w.Sq, w.Skv), dtype=bool), w.Skv - w.Sq)
+                    vis = np.broadcast_to(m[0, 0], (w.Sq, w.Skv)) & (rule if w.causal else True)
+                    flops = 4.0 * w.d * w.H * w.B * float(np.count_nonzero(vis))
+                row["visible_pairs_share"] = flops / prefill_flops(w, x["kv_lens_host"])
+                row["TFLOP/s"] = flops / (ms * 1e-3) / 1e12
             else:
                 mbytes = 0 if m is None else int(np.prod(m.shape[:3])) * w.Skv
                 row["GB/s"] = (decode_bytes(w, x["kv_lens_host"]) + mbytes) / (ms * 1e-3) / 1e9
