@@ -181,6 +181,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int kfull_w = causal ? min(L, p_lo + 1) : L;
     const int tw = (kv_hi_w + kBN - 1) / kBN;  // key tiles this wave's rules reach
 
+    // this lane's query
+    const int qi = qw + (lane & 31);
+    const int p = off + qi;
+    const bool q_live = qi < n;
+
+    // Q^T fragments: B operand of S^T = K Q^T.  Lane l holds 8 consecutive
+    // features 16*ks + 8*(l/32) .. +7 of query (l%32).  Issued before the
+    // key-tile list is built, so their latency overlaps it.
+    u32x4 qf[S::kKSteps];
+    {
+        const uint16_t* qrow = q + ((size_t)bh * Sq + (q_live ? qi : 0)) * D + half * 8;
+#pragma unroll
+        for (int ks = 0; ks < S::kKSteps; ++ks)
+            qf[ks] = q_live ? ldg16(qrow + ks * 16) : u32x4{0, 0, 0, 0};
+    }
+
+
     // Masked calls walk list positions pp0 <= pos < pp1 of the key tiles the
     // mask opens to this query tile (all tiles when no list is given);
     // tix(pos) is the key tile at a position (positions past the list map to
@@ -218,21 +235,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         }
         return pos;
     };
-
-    // this lane's query
-    const int qi = qw + (lane & 31);
-    const int p = off + qi;
-    const bool q_live = qi < n;
-
-    // Q^T fragments: B operand of S^T = K Q^T.  Lane l holds 8 consecutive
-    // features 16*ks + 8*(l/32) .. +7 of query (l%32).
-    u32x4 qf[S::kKSteps];
-    {
-        const uint16_t* qrow = q + ((size_t)bh * Sq + (q_live ? qi : 0)) * D + half * 8;
-#pragma unroll
-        for (int ks = 0; ks < S::kKSteps; ++ks)
-            qf[ks] = q_live ? ldg16(qrow + ks * 16) : u32x4{0, 0, 0, 0};
-    }
 
     // ---- allowed-mask words of this lane's query row for one key tile:
     // word w holds keys 32 (w/4) + 8 (w%4) + 4 half .. +3, the keys of
