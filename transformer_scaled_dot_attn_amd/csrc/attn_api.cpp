@@ -8,6 +8,7 @@
 // and bottlenecks are opposite (same page, sections 6 and 8).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -125,8 +126,10 @@ class EventTimer final : public KernelTimer {
     std::vector<hipEvent_t> pool_;
 };
 
-EventTimer* g_timer = nullptr;
-bool g_timing_on = false;
+// Launches read these without the lock: the timer is created once (under it)
+// and never freed, and the switch is a flag.
+std::atomic<EventTimer*> g_timer{nullptr};
+std::atomic<bool> g_timing_on{false};
 std::mutex g_timer_mu;
 
 // Allowed-mask layout checks: strides >= 0 and multiples of 4, base 4-byte
@@ -214,7 +217,10 @@ int run(const void* q, const void* k, const void* v, void* out, int B, int H, in
 
 }  // namespace
 
-KernelTimer* active_timer() { return g_timing_on ? g_timer : nullptr; }
+KernelTimer* active_timer() {
+    return g_timing_on.load(std::memory_order_acquire) ? g_timer.load(std::memory_order_acquire)
+                                                       : nullptr;
+}
 
 }  // namespace tsda
 
@@ -356,27 +362,28 @@ void attn_release(void) {
 
 int attn_profile_enable(int on) {
     std::lock_guard<std::mutex> g(g_timer_mu);
-    if (!g_timer) g_timer = new EventTimer();
-    g_timer->reset();
-    g_timing_on = on != 0;
+    if (!g_timer.load()) g_timer.store(new EventTimer(), std::memory_order_release);
+    g_timer.load()->reset();
+    g_timing_on.store(on != 0, std::memory_order_release);
     return ATTN_OK;
 }
 
 int attn_profile_reset(void) {
     std::lock_guard<std::mutex> g(g_timer_mu);
-    if (g_timer) g_timer->reset();
+    if (EventTimer* tm = g_timer.load()) tm->reset();
     return ATTN_OK;
 }
 
 int attn_profile_read(int kernel, long* launches, double* total_ms) {
     if (kernel < 0 || kernel >= kNumKernels) return ATTN_E_ARG;
     std::lock_guard<std::mutex> g(g_timer_mu);
-    if (!g_timer) {
+    EventTimer* tm = g_timer.load();
+    if (!tm) {
         if (launches) *launches = 0;
         if (total_ms) *total_ms = 0.0;
         return ATTN_OK;
     }
-    return g_timer->read(kernel, launches, total_ms);
+    return tm->read(kernel, launches, total_ms);
 }
 
 const char* attn_profile_name(int kernel) {
