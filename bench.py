@@ -147,8 +147,8 @@ def mask_runs(attn, W, runs, steps, warmup):
     attend, ANDed with the causal and length rules; "Attention from Scratch",
     KubeDojo module 1.4.3, Part 3), against the same call unmasked.  Prefill
     counts 4*d flops per visible (query, key) pair -- allowed by the mask and
-    by the causal rule -- the algorithmic work; decode counts the K/V bytes
-    plus the mask bytes it reads."""
+    by the causal rule -- the algorithmic work; decode counts the bytes of the
+    K/V rows some query head of their group may see, plus q, out and the mask."""
     import numpy as np
     import torch
     rows = []
@@ -164,9 +164,9 @@ def mask_runs(attn, W, runs, steps, warmup):
             kernels = ("prefill_bf16_mfma", "prefill_mask_tiles")
         else:
             lens = x["kv_lens_host"]
-            starts = np.minimum(np.asarray(lens) // 8, 64)
+            starts = np.asarray(lens) // 2
             masks = [("none", None),
-                     ("key padding [B,1,1,Skv], first min(L/8, 64) keys hidden",
+                     ("left padding [B,1,1,Skv], first half of each sequence hidden",
                       W.key_padding_mask(starts, np.full(w.B, w.Skv), w.Skv)),
                      ("random [B,H,1,Skv], density 0.5",
                       W.random_mask(6, (w.B, w.H, 1, w.Skv), 0.5))]
@@ -191,8 +191,19 @@ def mask_runs(attn, W, runs, steps, warmup):
                 row["visible_pairs_share"] = flops / prefill_flops(w, x["kv_lens_host"])
                 row["TFLOP/s"] = flops / (ms * 1e-3) / 1e12
             else:
-                mbytes = 0 if m is None else int(np.prod(m.shape[:3])) * w.Skv
-                row["GB/s"] = (decode_bytes(w, x["kv_lens_host"]) + mbytes) / (ms * 1e-3) / 1e9
+                nbytes = decode_bytes(w, x["kv_lens_host"])
+                if m is not None:
+                    # algorithmic bytes: the K/V rows some query head of the group may see
+                    lens = np.asarray(x["kv_lens_host"])
+                    seen = np.broadcast_to(m[:, :, 0, :], (w.B, w.H, w.Skv)) & \
+                        (np.arange(w.Skv)[None, None, :] < lens[:, None, None])
+                    rows = seen.reshape(w.B, w.kv_heads, w.H // w.kv_heads, w.Skv).any(axis=2)
+                    nbytes += 2 * 2 * w.d * float(np.count_nonzero(rows)) \
+                        - 2 * 2 * w.d * w.kv_heads * float(lens.clip(0, w.Skv).sum()) \
+                        + int(np.prod(m.shape[:3])) * w.Skv
+                    row["visible_kv_rows_share"] = float(np.count_nonzero(rows)) / float(
+                        w.kv_heads * lens.clip(0, w.Skv).sum())
+                row["GB/s"] = nbytes / (ms * 1e-3) / 1e9
             rows.append(row)
             del tm
         torch.cuda.empty_cache()

@@ -31,7 +31,9 @@
 // and key, nonzero = visible, ANDed with the length rule) is read next to
 // the K/V rows it gates; a split whose keys are all hidden leaves a partial
 // with m = -inf and l = 0, which the combine weighs as zero, and a head with
-// no visible key at all is written as 0.
+// no visible key at all is written as 0.  A split the mask hides entirely
+// from every head it serves writes that empty partial without reading its
+// K/V rows (a left-padded cache then streams only its visible keys).
 #include "device_common.h"
 #include "launch.h"
 
@@ -82,7 +84,27 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     // allowed-mask bytes: lane `part` of a row group reads the byte of query
     // head h0 + part % HB (HB <= G), and the group's lanes share them below
     const uint8_t* mrow = nullptr;
-    if constexpr (MASK) mrow = mask + b * msb + (long long)(h0 + part % HB) * msh;
+    if constexpr (MASK) {
+        mrow = mask + b * msb + (long long)(h0 + part % HB) * msh;
+        // does any served head see any key of the split?
+        const int nk = k1 - k0;
+        int vis = 0;
+        for (int e = tid; e < HB * nk; e += 256) {
+            const int i = e / nk;
+            vis |= mask[b * msb + (long long)(h0 + i) * msh + k0 + (e - i * nk)];
+        }
+        if (!__syncthreads_or(vis)) {
+            for (int e = tid; e < HB * D; e += 256) {
+                const size_t uq = ((size_t)b * H + h0 + e / D) * nsplit + split;
+                ws_acc[uq * D + e % D] = 0.0f;
+                if (e % D == 0) {
+                    ws_ml[uq * 2] = -INFINITY;
+                    ws_ml[uq * 2 + 1] = 0.0f;
+                }
+            }
+            return;
+        }
+    }
 
     float m[HB], l[HB];
     float acc[HB][8];
@@ -273,6 +295,30 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(
     const uint8_t* mrow = nullptr;
     if constexpr (MASK) mrow = mask + b * msb + (long long)(h0 + (live ? jh : 0)) * msh;
     const int mlast = mask_last_word(Skv);
+    if constexpr (MASK) {
+        if (msh == 0) {
+            // a mask shared by all heads: does it open any key of the split?
+            // (lane l checks the words at 4 l, 4 (l + 64), ...; keys >= k1 are
+            // excluded byte by byte)
+            uint32_t vis = 0;
+            for (int j = k0 + 4 * lane; j < k1; j += 256) {
+                const uint32_t wd = ldg_word(mask + b * msb + min(j, mlast));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vis |= (j + e < k1) & byte_set(wd, e);
+            }
+            if (__builtin_amdgcn_ballot_w64(vis != 0) == 0) {
+                if (live) {
+                    const size_t uq = ((size_t)b * H + h0 + jh) * nsplit + split;
+                    for (int c = half; c < D; c += 2) ws_acc[uq * D + c] = 0.0f;
+                    if (half == 0) {
+                        ws_ml[uq * 2] = -INFINITY;
+                        ws_ml[uq * 2 + 1] = 0.0f;
+                    }
+                }
+                return;
+            }
+        }
+    }
     uint32_t mw[4], mw_next[4];
     auto load_m = [&](int t0, uint32_t (&dst)[4]) {
         if constexpr (MASK) {
