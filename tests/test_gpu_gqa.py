@@ -6,7 +6,11 @@ element with the oracle; prefill and fp32 results must also equal, bit for
 bit, the multi-head call on K and V expanded with repeat_interleave (the
 kernels' per-head arithmetic does not depend on where a head's K/V lives).
 The full-size grouped workloads run in the benchmark's launch configuration
-and are compared on sampled (batch, head) slices.
+and are compared on sampled (batch, head) slices.  Grouped bf16 decode
+without a mask runs the stream kernel, whose wave shares cross pair and batch
+boundaries; its edge cases (empty caches, more than 64 batch items, fewer
+tiles than one wave's floor, two head groups per K/V head) have cases of
+their own.
 """
 import numpy as np
 import pytest
@@ -58,6 +62,52 @@ def test_gqa_shapes(case):
         assert np.array_equal(got, exp), f"gqa {case}: differs from the expanded MHA call"
     else:
         assert_matches(got, exp, BF16_TOL, clamped, Skv, f"gqa {case} vs expanded")
+
+
+# Stream decode (bf16, Sq = 1, 4 or more query heads per K/V head, no mask):
+# a fixed grid of waves shares all key tiles of all (batch item, K/V head,
+# head group) pairs equally, at least 16 tiles of 32 keys per wave.
+STREAM = [
+    # name, B, H, Hkv, Skv, d, lengths (None: all Skv; "rand:seed": drawn in [0, Skv])
+    ("one key", 1, 4, 1, 1, 128, None),
+    ("one tile each", 3, 8, 2, 32, 128, [32, 1, 31]),
+    ("fewer tiles than the floor", 2, 16, 4, 200, 64, [200, 0]),
+    ("short and empty caches, B 70", 70, 16, 2, 300, 128, "rand:61"),
+    ("B 200 groups of 4", 200, 8, 2, 600, 128, "rand:62"),
+    ("tile edges", 6, 32, 8, 1100, 128, [1024, 1025, 1023, 992, 33, 64]),
+    ("64 heads per K/V head", 3, 64, 1, 1500, 128, [1500, 31, 0]),
+    ("48 heads per K/V head", 2, 48, 1, 2500, 128, [2500, 1999]),
+    ("d 64 long", 5, 16, 4, 4000, 64, "rand:63"),
+    ("every cache empty", 3, 8, 2, 500, 128, [0, 0, 0]),
+]
+
+
+def _stream_lens(spec, B, Skv):
+    if spec is None or not isinstance(spec, str):
+        return spec
+    rng = np.random.default_rng(int(spec.split(":")[1]))
+    lens = rng.integers(0, Skv + 1, size=B)
+    lens[rng.random(B) < 0.2] = 0  # runs of empty caches
+    return [int(x) for x in lens]
+
+
+@pytest.mark.parametrize("case", STREAM, ids=lambda c: c[0].replace(" ", "_"))
+def test_stream_decode_matches_oracle(case):
+    name, B, H, Hkv, Skv, d, spec = case
+    lens = _stream_lens(spec, B, Skv)
+    _say(f"stream decode {name}: B{B} H{H}/{Hkv} Skv{Skv} d{d}")
+    prob = W.random_problem(sum(map(ord, name)), B, H, 1, Skv, d, "bf16", lens, Hkv=Hkv)
+    got, t1 = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], 0, lens)
+    ref = oracle.attention(prob["q"], prob["k"], prob["v"], prob["scale"], 0, lens)
+    assert_matches(got, ref, BF16_TOL, lens, Skv, name)
+    if lens is not None:
+        for b, L in enumerate(lens):
+            if L == 0:
+                assert np.all(got[b] == 0.0), f"{name}: empty cache {b} not zero"
+    # a fixed schedule: the same call gives the same bits
+    _, t2 = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], 0, lens)
+    import torch
+    assert torch.equal(t1, t2)
 
 
 def test_gqa_rejects_uneven_groups():

@@ -30,8 +30,10 @@ struct LaunchArgs {
 __host__ __device__ inline int mask_last_word(int Skv) { return ((Skv + 3) & ~3) - 4; }
 
 // Decode split plan: keys per split, number of splits per (b, h), and for
-// grouped heads (H / Hkv >= 4) the matrix-core kernel's groups of 32 query
-// heads per K/V head (0: the vector kernel).
+// grouped heads (H / Hkv >= 4) the matrix-core kernels' groups of 32 query
+// heads per K/V head (0: the vector kernel).  Grouped heads without an
+// allowed-mask use the stream kernel, which sizes its own grid; the plan's
+// split fields then serve only the workspace bound.
 struct DecodePlan {
     int chunk;
     int nsplit;
