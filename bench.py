@@ -197,11 +197,11 @@ def mask_runs(attn, W, runs, steps, warmup):
                     lens = np.asarray(x["kv_lens_host"])
                     seen = np.broadcast_to(m[:, :, 0, :], (w.B, w.H, w.Skv)) & \
                         (np.arange(w.Skv)[None, None, :] < lens[:, None, None])
-                    rows = seen.reshape(w.B, w.kv_heads, w.H // w.kv_heads, w.Skv).any(axis=2)
-                    nbytes += 2 * 2 * w.d * float(np.count_nonzero(rows)) \
+                    kv_seen = seen.reshape(w.B, w.kv_heads, w.H // w.kv_heads, w.Skv).any(axis=2)
+                    nbytes += 2 * 2 * w.d * float(np.count_nonzero(kv_seen)) \
                         - 2 * 2 * w.d * w.kv_heads * float(lens.clip(0, w.Skv).sum()) \
                         + int(np.prod(m.shape[:3])) * w.Skv
-                    row["visible_kv_rows_share"] = float(np.count_nonzero(rows)) / float(
+                    row["visible_kv_rows_share"] = float(np.count_nonzero(kv_seen)) / float(
                         w.kv_heads * lens.clip(0, w.Skv).sum())
                 row["GB/s"] = nbytes / (ms * 1e-3) / 1e9
             rows.append(row)

@@ -1,0 +1,91 @@
+"""Host-side bookkeeping of bench.py, run on the CPU with the kernel launches
+and their timing replaced by stubs: the masked-run rows (visible-pair flops,
+visible K/V-row bytes) and the grouped-decode rows are assembled without a
+GPU, so an error there shows up before a GPU run."""
+import math
+import types
+
+import numpy as np
+
+import bench
+import workloads as W
+
+
+class _Attn:
+    BF16 = 1
+
+    def fwd(self, *a, **kw):
+        return None
+
+
+def _stub_timing(monkeypatch):
+    calls = []
+
+    def timed(attn, fn, steps, warmup, kernels):
+        fn()
+        calls.append(kernels)
+        # the second kernel of a masked prefill (the tile-mark pre-pass) is
+        # absent from an unmasked call, as on the GPU
+        return {k: (math.nan if k == "prefill_mask_tiles" and len(calls) == 1 else 1.0)
+                for k in kernels}
+
+    monkeypatch.setattr(bench, "timed_calls", timed)
+    return calls
+
+
+def _host_workloads():
+    # mask_to_torch would upload; the bookkeeping only needs the array
+    names = {k: getattr(W, k) for k in dir(W) if not k.startswith("__")}
+    names["mask_to_torch"] = lambda m, device="cuda": m
+    return types.SimpleNamespace(**names)
+
+
+def _inputs(w):
+    lens = W.kv_lens_for(w)
+    return {"q": None, "k": None, "v": None, "scale": 1.0 / math.sqrt(w.d),
+            "kv_lens": None if lens is None else np.asarray(lens, dtype=np.int32),
+            "kv_lens_host": None if lens is None else [int(x) for x in lens]}
+
+
+def test_mask_rows(monkeypatch):
+    calls = _stub_timing(monkeypatch)
+    runs = []
+    for kind, name in (("prefill", "prefill4096_bf16"), ("decode", "decode8192_bf16"),
+                       ("decode", "gqa_decode8192_bf16")):
+        w = W.WORKLOADS[name]
+        runs.append((kind, w, _inputs(w), None))
+    rows = bench.mask_runs(_Attn(), _host_workloads(), runs, steps=1, warmup=0)
+    assert len(rows) == 5 + 3 + 3 and len(calls) == len(rows)
+    for r in rows:
+        assert r["ms_per_call"] > 0 and math.isfinite(r["time_vs_unmasked"])
+    pre = [r for r in rows if r["workload"] == "prefill4096_bf16"]
+    assert pre[0]["mask"] == "none" and pre[0]["visible_pairs_share"] == 1.0
+    for r in pre[1:]:
+        assert 0.0 < r["visible_pairs_share"] < 1.0 and r["TFLOP/s"] > 0
+    # documents of 512 and a window of 256 open about an eighth of the causal pairs
+    assert 0.10 < pre[3]["visible_pairs_share"] < 0.15
+    assert 0.10 < pre[4]["visible_pairs_share"] < 0.15
+    for name in ("decode8192_bf16", "gqa_decode8192_bf16"):
+        dec = [r for r in rows if r["workload"] == name]
+        assert "visible_kv_rows_share" not in dec[0]
+        # the left half of every sequence hidden: about half of the rows
+        assert 0.45 < dec[1]["visible_kv_rows_share"] < 0.55
+        assert dec[1]["GB/s"] < dec[0]["GB/s"]
+        # random [B,H,1,S] masks: a K/V row is seen if any query head of its group sees it
+        g = W.WORKLOADS[name].H // W.WORKLOADS[name].kv_heads
+        assert abs(dec[2]["visible_kv_rows_share"] - (1.0 - 0.5 ** g)) < 0.02
+
+
+def test_grouped_decode_rows(monkeypatch):
+    _stub_timing(monkeypatch)
+    w = W.WORKLOADS["decode8192_bf16"]
+    have = {w.name: _inputs(w)}
+    import torch
+    monkeypatch.setattr(W, "device_inputs", lambda w, dev="cuda", **kw: _inputs(w))
+    monkeypatch.setattr(torch, "empty_like", lambda x: None)
+    rows = bench.gqa_decode_sweep(_Attn(), W, "cpu", 1, 0, have=have)
+    by = {r["H_kv"]: r for r in rows}
+    assert set(by) >= {32, 8, 1}
+    for hkv, r in by.items():
+        assert abs(r["intensity_flop_per_byte"] - 32 / hkv) < 0.05 * 32 / hkv
+        assert r["roofline"]["bound"] == "hbm" and r["roofline"]["frac"] > 0
