@@ -79,15 +79,15 @@ def test_mask_matches_oracle(case):
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}")
 def test_all_true_mask_is_bitwise_unmasked(case):
-    """Bit for bit, except bf16 decode with 4 or more query heads per K/V head:
-    unmasked it runs the stream kernel, whose partials cut the keys elsewhere
-    than the masked split kernel's, so the two agree to rounding only."""
+    """Bit for bit, except bf16 decode: unmasked it runs the stream kernel,
+    whose partials cut the keys elsewhere than the masked split kernels', so
+    the two agree to rounding only."""
     seed, dt, B, H, Hkv, Sq, Skv, d, causal, lens = case[:10]
     _say(f"all-true mask s{seed}")
     ones = np.ones((1, 1, 1, Skv), dtype=bool)
     with_mask, _, _ = _run_case(case, ones)
     without, _, _ = _run_case(case, None)
-    if dt == "bf16" and Sq == 1 and H // Hkv >= 4:
+    if dt == "bf16" and Sq == 1:
         clamped = None if lens is None else np.clip(lens, 0, Skv)
         assert_matches(with_mask, without, BF16_TOL, clamped, Skv, f"s{seed} masked vs stream")
     else:

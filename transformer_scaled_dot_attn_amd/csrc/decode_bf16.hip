@@ -8,22 +8,28 @@
 // the KV cache lever") each K/V row serves H / H_kv query heads, the rise in
 // decode intensity that section 6 derives, and the kernels read it once per
 // group of query heads:
-//   * vector partial kernel (multi-head, and 2 query heads per K/V head):
-//     one block per (b, K/V head, group of HB query heads, split of `chunk`
-//     keys).  Each key row (d bf16 = 2d bytes) is read by d/8 lanes with one
-//     16-byte load each, so every wave-wide load covers whole contiguous
-//     rows.  Logits use v_dot2 on the raw bf16 pairs (exact products, fp32
-//     sums), reduced over the row's lanes with DPP, once per served head.  K
-//     and V are read once, with non-temporal loads; each lane keeps two steps
-//     of 4 rows in flight.  Each lane group keeps a running maximum m,
-//     normaliser l and an fp32 accumulator for its 8 columns per head (the
-//     online softmax recurrence); the block merges its groups in LDS and
-//     writes one (m, l, acc[d]) partial per head.  Keys past the valid
-//     length are never loaded.
-//   * matrix-core partial kernels (4 or more query heads per K/V head): the
-//     served heads are the columns of 32x32 MFMA tiles; a fixed grid of
-//     waves shares all key tiles equally, or, with an allowed-mask, one wave
-//     per split (below).
+//   * stream kernel (every call without an allowed-mask): the query heads a
+//     K/V head serves are the columns of 32x32 MFMA tiles (one live column
+//     for multi-head attention: the loop is bound by K/V bytes either way),
+//     and a fixed grid of waves shares all key tiles of all caches equally
+//     (below).
+//   * split kernels (calls with an allowed-mask), one unit per split of
+//     `chunk` keys, so that a split the mask hides from every head it serves
+//     writes an empty partial without reading its K/V rows:
+//       - vector kernel (1 or 2 query heads per K/V head): one block per
+//         (b, K/V head, group of HB query heads, split).  Each key row
+//         (d bf16 = 2d bytes) is read by d/8 lanes with one 16-byte load
+//         each, so every wave-wide load covers whole contiguous rows.
+//         Logits use v_dot2 on the raw bf16 pairs (exact products, fp32
+//         sums), reduced over the row's lanes with DPP, once per served head.
+//         K and V are read once, with non-temporal loads; each lane keeps two
+//         steps of 4 rows in flight.  Each lane group keeps a running maximum
+//         m, normaliser l and an fp32 accumulator for its 8 columns per head
+//         (the online softmax recurrence); the block merges its groups in LDS
+//         and writes one (m, l, acc[d]) partial per head.  Keys past the
+//         valid length are never loaded.
+//       - matrix-core split kernel (4 or more query heads per K/V head): the
+//         stream kernel's loop over one split.
 //   * combine kernels: per (b, h), merge the partials with the log-sum-exp
 //     rule  M = max m_s,  l = sum l_s 2^(m_s - M),
 //     out = (sum acc_s 2^(m_s - M)) / l, and round to bf16.  L_b = 0 gives 0.
@@ -241,22 +247,26 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 // rows per load) measured 17 % slower at 8 K/V heads.  In both accumulators a
 // lane owns one query head, so the online softmax is lane-local plus one half
 // swap, as in the prefill kernel.  The matrix cores have ample headroom (16
-// MFMAs per 16 KiB of K+V): with grouped heads decode stays bound by the
-// bytes of K and V, read once per group of up to 32 query heads.  A copy of
-// the loop with its arithmetic removed runs no faster, so how the grid meets
-// memory decides the speed.  Two kernels drive the loop:
-//   * stream kernel (no allowed-mask): a fixed grid of as many waves as the
-//     GPU holds at once.  The (b, K/V head, head group) pairs, each cut into
-//     ceil(L_b / 32) key tiles, are laid end to end and wave w takes the w-th
-//     equal share of that sequence, crossing pair boundaries as it goes and
-//     writing one partial per pair it touches (the stream-K decomposition of
-//     Osama et al., 2023, applied to the key axis).  Every wave streams the
-//     same bytes, so ragged lengths leave no part-filled last round of
-//     waves; fixed 512-key splits measured 20-25 % slower at 4 and 8 query
-//     heads per K/V head on lengths U[512, 8192].
-//   * split kernel (allowed-mask): one wave per (b, K/V head, head group,
-//     split of `chunk` keys), so that a split the mask hides from every head
-//     skips its K/V reads.
+// MFMAs per 16 KiB of K+V): decode stays bound by the bytes of K and V,
+// read once per group of up to 32 query heads.  A copy of the loop with its
+// arithmetic removed runs no faster, so how the grid meets memory decides the
+// speed.  Two kernels drive the loop:
+//   * stream kernel (no allowed-mask, any number of query heads per K/V
+//     head): a fixed grid of as many waves as the GPU holds at once.  The
+//     (b, K/V head, head group) pairs, each cut into ceil(L_b / 32) key
+//     tiles, are laid end to end and wave w takes the w-th equal share of
+//     that sequence, crossing pair boundaries as it goes and writing one
+//     partial per pair it touches (the stream-K decomposition of Osama et
+//     al., 2023, applied to the key axis).  Every wave streams the same
+//     bytes, so ragged lengths leave no part-filled last round of waves.  On
+//     lengths U[512, 8192] (B = 64, H = 32), fixed splits measured 12 %
+//     slower at 32 K/V heads (the vector kernel), 29 % at 16 and 20-25 % at
+//     4 and 8 (the split kernel); with short caches in a large capacity
+//     (lengths U[16, 512] of 8192) the vector kernel's grid of mostly empty
+//     splits took 4.8x as long.
+//   * split kernel (allowed-mask, 4 or more query heads per K/V head): one
+//     wave per (b, K/V head, head group, split of `chunk` keys), so that a
+//     split the mask hides from every head skips its K/V reads.
 template <int D>
 struct MfmaDecode {
     static constexpr int kKSteps = D / 16;      // MFMA k-steps of K Q^T
@@ -554,8 +564,10 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
 // Stream kernel: wave w of the grid's W waves takes tiles [w T' / W',
 // (w+1) T' / W') of the T' key tiles of all pairs laid end to end, pair
 // p = (b * H_kv + K/V head) * hgroups + head group holding tiles
-// ceil(L_b / 32) of them, where W' = min(W, max(1, T' / min_tiles)) (waves
-// past W' exit).  The partial of pair p computed by wave w goes to slot
+// ceil(L_b / 32) of them, where W' = min(W, max(T' / min_tiles,
+// min(T', min_waves))) (waves past W' exit): shares of at least min_tiles
+// tiles, unless that leaves fewer than min_waves waves, then down to one tile
+// per wave.  The partial of pair p computed by wave w goes to slot
 // w + p (distinct: along the sequence each new segment raises the wave or the
 // pair index), head row jh of it; span[2p] and span[2p+1] receive the waves
 // that hold the pair's first and last tile, so the combine reads slots
@@ -564,8 +576,8 @@ template <int D>
 __global__ __launch_bounds__(64, 2) void decode_mfma_stream_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ kv_lens, int B, int H, int Hkv,
-    int Skv, float scale_log2, int hgroups, int min_tiles, float* __restrict__ ws_acc,
-    float* __restrict__ ws_ml, int* __restrict__ span) {
+    int Skv, float scale_log2, int hgroups, int min_tiles, int min_waves,
+    float* __restrict__ ws_acc, float* __restrict__ ws_ml, int* __restrict__ span) {
     using C = MfmaDecode<D>;
     __shared__ __attribute__((aligned(16))) uint16_t lds_v[32 * C::kStrideV];
     __shared__ __attribute__((aligned(16))) uint16_t lds_k[32 * C::kStrideK];
@@ -590,7 +602,8 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_stream_kernel(
     }
     const uint32_t inc = wave_incl_scan(mine);
     const long long T = (long long)(uint32_t)__builtin_amdgcn_readlane((int)inc, 63) * G;
-    const long long nw = min((long long)gridDim.x, max(1LL, T / min_tiles));
+    const long long nw =
+        min((long long)gridDim.x, max(T / min_tiles, min(T, (long long)min_waves)));
     if (w >= nw) return;
     const long long s = w * T / nw, e = (w + 1) * T / nw;  // this wave's tiles
     if (s >= e) return;
@@ -785,10 +798,10 @@ DecodePlan decode_plan(int B, int H, int Hkv, int Skv) {
         while (chunk > 64 && pairs * ((Skv + chunk - 1) / chunk) < 1024) chunk /= 2;
         return DecodePlan{chunk, (Skv + chunk - 1) / chunk, hgroups};
     }
-    // Multi-head: splits of 128 keys (64 KiB of K+V at d = 128) measured
-    // fastest on the ragged decode workload: many short units spread the
-    // reads of the valid prefixes of all caches evenly over the memory
-    // system.  Smaller problems split finer so the grid still fills the GPU.
+    // Vector split kernel (with an allowed-mask): splits of 128 keys (64 KiB
+    // of K+V at d = 128) measured fastest on the ragged decode workload: many
+    // short units spread the reads of the valid prefixes of all caches evenly
+    // over the memory system.  Smaller problems split finer so the grid still fills the GPU.
     // A block serving two query heads does twice the vector work per row and
     // merges one partial per head at its end, so it takes the longest split
     // (up to 1024 keys) that still leaves 8 blocks per CU.
@@ -805,21 +818,24 @@ DecodePlan decode_plan(int B, int H, int Hkv, int Skv) {
 
 namespace {
 
-// Stream kernel (grouped heads, no allowed-mask): every wave takes at least
-// kStreamMinTiles key tiles (512 keys), so that its partials -- one K+V tile's
-// bytes when a K/V head serves 32 query heads -- stay a small share of what
-// it streams (a floor of 8 measured 20 % slower at 1 and 2 K/V heads, 32 no
-// faster at 4 and 8).
-constexpr int kStreamMinTiles = 16;
-// Most stream waves ever launched (workspace bound): 256 compute units with
-// 16 resident waves each, the d = 64 kernel's occupancy.
-constexpr long kStreamMaxWaves = 4096;
+// Stream kernel (every bf16 decode without an allowed-mask).  Shares of a
+// wave: at least 16 key tiles when a partial holds 16 or more query heads
+// (its bytes then come near a K+V tile's), else 4; but never fewer waves than
+// a quarter of those the GPU holds, down to one tile each, so that short
+// caches still spread over the chip.  Measured (B = 64, H = 32, d = 128):
+// lengths U[512, 8192] at 1 and 2 K/V heads, floors of 8 are 20-25 % slower
+// than 16 and 32; lengths U[16, 512] in caches of 8192, floors of 16 are
+// 25-100 % slower than 2-4 at 1, 8 and 32 K/V heads.
+int stream_min_tiles(int H, int Hkv) { return std::min(32, H / Hkv) >= 16 ? 16 : 4; }
+// Most stream waves launched on a d = 128 or d = 64 decode (workspace bound):
+// 256 compute units with 8 or 16 resident waves.
+long stream_max_waves(int d) { return d == 128 ? 2048 : 4096; }
 
-// Waves the stream kernel can use on this problem: the tiles of caches all
-// Skv long over the per-wave floor, within kStreamMaxWaves.
-long stream_wave_cap(int B, int Hkv, int hgroups, int Skv) {
+// Waves the stream kernel can use on this problem: at most one per key tile
+// of caches all Skv long.
+long stream_wave_cap(int B, int Hkv, int hgroups, int Skv, int d) {
     const long tmax = (long)B * Hkv * hgroups * ((Skv + 31) / 32);
-    return std::min(kStreamMaxWaves, std::max(1L, tmax / kStreamMinTiles));
+    return std::min(stream_max_waves(d), std::max(1L, tmax));
 }
 
 // Stream workspace: partial slots (wave + pair, at most cap + pairs) of nhs
@@ -830,7 +846,7 @@ struct StreamLayout {
 StreamLayout stream_layout(int B, int H, int Hkv, int Skv, int d) {
     const int group = H / Hkv, hg = (group + 31) / 32, nhs = std::min(32, group);
     const size_t pairs = (size_t)B * Hkv * hg;
-    const size_t rows = ((size_t)stream_wave_cap(B, Hkv, hg, Skv) + pairs) * nhs;
+    const size_t rows = ((size_t)stream_wave_cap(B, Hkv, hg, Skv, d) + pairs) * nhs;
     StreamLayout l;
     l.ml = round256(rows * d * sizeof(float));
     l.span = l.ml + round256(rows * 2 * sizeof(float));
@@ -864,7 +880,7 @@ int stream_resident_waves(int d) {
         (void)hipGetLastError();  // a failed query leaves no error for the launches
         per = d == 128 ? 8 : 16;
     }
-    const int waves = (int)std::min((long)cus * per, kStreamMaxWaves);
+    const int waves = (int)std::min((long)cus * per, stream_max_waves(d));
     if (cached) cache[dev][di].store(waves, std::memory_order_relaxed);
     return waves;
 }
@@ -875,8 +891,7 @@ size_t decode_workspace_bytes(int B, int H, int Hkv, int Skv, int d) {
     const DecodePlan p = decode_plan(B, H, Hkv, Skv);
     const size_t units = (size_t)B * H * p.nsplit;  // one partial per query head and split
     const size_t split = round256(units * d * sizeof(float)) + round256(units * 2 * sizeof(float));
-    if (p.hgroups == 0) return split;
-    // grouped heads: the split kernel with an allowed-mask, else the stream kernel
+    // split kernels with an allowed-mask, else the stream kernel
     return std::max(split, stream_layout(B, H, Hkv, Skv, d).total);
 }
 
@@ -922,26 +937,30 @@ hipError_t launch_decode_bf16(const LaunchArgs& a) {
     const float sl = a.scale * kLog2e;
     KernelTimer* t = active_timer();
     hipError_t e;
-    if (p.hgroups > 0 && a.mask == nullptr) {
+    if (a.mask == nullptr) {
+        const int hgroups = (a.H / a.Hkv + 31) / 32;
         const StreamLayout l = stream_layout(a.B, a.H, a.Hkv, a.Skv, a.d);
         char* ws = static_cast<char*>(a.workspace);
         float* acc = reinterpret_cast<float*>(ws);
         float* ml = reinterpret_cast<float*>(ws + l.ml);
         int* span = reinterpret_cast<int*>(ws + l.span);
-        const int waves = (int)std::min((long)stream_resident_waves(a.d),
-                                        stream_wave_cap(a.B, a.Hkv, p.hgroups, a.Skv));
+        const int resident = stream_resident_waves(a.d);
+        const int waves =
+            (int)std::min((long)resident, stream_wave_cap(a.B, a.Hkv, hgroups, a.Skv, a.d));
+        const int min_tiles = stream_min_tiles(a.H, a.Hkv);
+        const int min_waves = std::max(1, resident / 4);
         const uint16_t* q = static_cast<const uint16_t*>(a.q);
         const uint16_t* k = static_cast<const uint16_t*>(a.k);
         const uint16_t* v = static_cast<const uint16_t*>(a.v);
         if (t) t->begin(kDecodePartialBf16, a.stream);
         if (a.d == 128)
             hipLaunchKernelGGL(decode_mfma_stream_kernel<128>, dim3(waves), dim3(64), 0, a.stream,
-                               q, k, v, a.kv_lens, a.B, a.H, a.Hkv, a.Skv, sl, p.hgroups,
-                               kStreamMinTiles, acc, ml, span);
+                               q, k, v, a.kv_lens, a.B, a.H, a.Hkv, a.Skv, sl, hgroups,
+                               min_tiles, min_waves, acc, ml, span);
         else
             hipLaunchKernelGGL(decode_mfma_stream_kernel<64>, dim3(waves), dim3(64), 0, a.stream,
-                               q, k, v, a.kv_lens, a.B, a.H, a.Hkv, a.Skv, sl, p.hgroups,
-                               kStreamMinTiles, acc, ml, span);
+                               q, k, v, a.kv_lens, a.B, a.H, a.Hkv, a.Skv, sl, hgroups,
+                               min_tiles, min_waves, acc, ml, span);
         e = hipGetLastError();
         if (t) t->end(kDecodePartialBf16, a.stream);
         if (e != hipSuccess) return e;
@@ -949,11 +968,11 @@ hipError_t launch_decode_bf16(const LaunchArgs& a) {
         const unsigned pairs = (unsigned)((size_t)a.B * a.H);
         if (a.d == 128)
             hipLaunchKernelGGL(decode_combine_stream_kernel<128>, dim3(pairs), dim3(256), 0,
-                               a.stream, a.kv_lens, a.H, a.Hkv, a.Skv, p.hgroups, acc, ml, span,
+                               a.stream, a.kv_lens, a.H, a.Hkv, a.Skv, hgroups, acc, ml, span,
                                o);
         else
             hipLaunchKernelGGL(decode_combine_stream_kernel<64>, dim3(pairs), dim3(128), 0,
-                               a.stream, a.kv_lens, a.H, a.Hkv, a.Skv, p.hgroups, acc, ml, span,
+                               a.stream, a.kv_lens, a.H, a.Hkv, a.Skv, hgroups, acc, ml, span,
                                o);
         e = hipGetLastError();
         if (t) t->end(kDecodeCombineBf16, a.stream);

@@ -29,11 +29,11 @@ struct LaunchArgs {
 // Last 4-byte word offset of a mask row that a kernel may read.
 __host__ __device__ inline int mask_last_word(int Skv) { return ((Skv + 3) & ~3) - 4; }
 
-// Decode split plan: keys per split, number of splits per (b, h), and for
-// grouped heads (H / Hkv >= 4) the matrix-core kernels' groups of 32 query
-// heads per K/V head (0: the vector kernel).  Grouped heads without an
-// allowed-mask use the stream kernel, which sizes its own grid; the plan's
-// split fields then serve only the workspace bound.
+// Decode split plan of the kernels that serve calls with an allowed-mask:
+// keys per split, number of splits per (b, h), and for grouped heads
+// (H / Hkv >= 4) the matrix-core split kernel's groups of 32 query heads per
+// K/V head (0: the vector kernel).  Calls without a mask run the stream
+// kernel, which sizes its own grid.
 struct DecodePlan {
     int chunk;
     int nsplit;
