@@ -104,7 +104,7 @@ def gqa_decode_sweep(attn, W, dev, steps, warmup,
         nbytes, flops = decode_bytes(w, lens), decode_flops(w, lens)
         p_ms = t["decode_bf16_partial"]
         kv_bytes = nbytes - 2 * 2 * w.B * w.H * w.d  # what the partial kernel reads
-        kernel = "decode_bf16_partial" if w.H // w.kv_heads < 4 else "decode_bf16_mfma"
+        kernel = "decode_bf16_partial"  # the stream kernel, at every K/V head count
         rows.append({"workload": name, "H": w.H, "H_kv": w.kv_heads, "ms_per_call": ms,
                      "GB/s": nbytes / (ms * 1e-3) / 1e9, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
                      "intensity_flop_per_byte": flops / nbytes,
