@@ -79,6 +79,8 @@ STREAM = [
     ("48 heads per K/V head", 2, 48, 1, 2500, 128, [2500, 1999]),
     ("d 64 long", 5, 16, 4, 4000, 64, "rand:63"),
     ("every cache empty", 3, 8, 2, 500, 128, [0, 0, 0]),
+    ("B 1030, 17 batch items per lane", 1030, 8, 2, 100, 128, "rand:64"),
+    ("B 4500 multi-head, 71 per lane", 4500, 2, 2, 40, 64, "rand:65"),
 ]
 
 

@@ -590,16 +590,13 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_stream_kernel(
     const int nhs = min(32, group);  // head rows per partial slot
 
     // tiles per pair of batch item b: ceil(L_b / 32).  Lane l sums the items
-    // l*per .. l*per+per-1 and a wave scan gives it the tiles before them.
+    // l*per .. l*per+per-1 (independent loads, issued together) and a wave
+    // scan gives it the tiles before them.
     const int per = (B + 63) / 64;
     const int b_lo = min(lane * per, B), b_hi = min(b_lo + per, B);
     uint32_t mine = 0;
-    int l_first = 0;
-    for (int bb = b_lo; bb < b_hi; ++bb) {
-        const int Lb = valid_length(kv_lens, bb, Skv);
-        if (bb == b_lo) l_first = Lb;
-        mine += (uint32_t)(Lb + 31) >> 5;
-    }
+#pragma unroll 8
+    for (int bb = b_lo; bb < b_hi; ++bb) mine += (uint32_t)(valid_length(kv_lens, bb, Skv) + 31) >> 5;
     const uint32_t inc = wave_incl_scan(mine);
     const long long T = (long long)(uint32_t)__builtin_amdgcn_readlane((int)inc, 63) * G;
     const long long nw =
@@ -608,20 +605,33 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_stream_kernel(
     const long long s = w * T / nw, e = (w + 1) * T / nw;  // this wave's tiles
     if (s >= e) return;
 
-    // the batch item b holding tile s, and `base`, the first tile of its pairs
+    // the batch item b holding tile s, and `base`, the first tile of its
+    // pairs: first the lane whose items hold it, then, one item per lane, a
+    // second scan over that lane's items
     const uint64_t hit = __builtin_amdgcn_ballot_w64(
         mine > 0 && (long long)(inc - mine) * G <= s && s < (long long)inc * G);
     if (hit == 0) return;  // unreachable: s < T
     const int src = __builtin_ctzll(hit);
-    int b = __builtin_amdgcn_readlane(b_lo, src);
-    const int b_end = __builtin_amdgcn_readlane(b_hi, src);
+    const int b_first = __builtin_amdgcn_readlane(b_lo, src);
+    const int cnt = __builtin_amdgcn_readlane(b_hi, src) - b_first;
     long long base = (long long)(uint32_t)__builtin_amdgcn_readlane((int)(inc - mine), src) * G;
-    int L = __builtin_amdgcn_readlane(l_first, src);
-    while (s >= base + (long long)((L + 31) >> 5) * G) {
-        base += (long long)((L + 31) >> 5) * G;
-        if (++b >= b_end) return;  // unreachable
-        L = valid_length(kv_lens, b, Skv);
+    int b = -1, L = 0;
+    for (int c = 0; c < cnt; c += 64) {
+        const int Lb = c + lane < cnt ? valid_length(kv_lens, b_first + c + lane, Skv) : 0;
+        const uint32_t n = (uint32_t)(Lb + 31) >> 5;
+        const uint32_t inc2 = wave_incl_scan(n);
+        const uint64_t hit2 = __builtin_amdgcn_ballot_w64(
+            n > 0 && base + (long long)(inc2 - n) * G <= s && s < base + (long long)inc2 * G);
+        if (hit2 != 0) {
+            const int src2 = __builtin_ctzll(hit2);
+            b = b_first + c + src2;
+            L = __builtin_amdgcn_readlane(Lb, src2);
+            base += (long long)(uint32_t)__builtin_amdgcn_readlane((int)(inc2 - n), src2) * G;
+            break;
+        }
+        base += (long long)(uint32_t)__builtin_amdgcn_readlane((int)inc2, 63) * G;
     }
+    if (b < 0) return;  // unreachable
     int nb = (L + 31) >> 5;
     int j = (int)((s - base) / nb);               // pair within batch item b
     int t = (int)(s - base - (long long)j * nb);  // tile within the pair
