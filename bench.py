@@ -170,7 +170,7 @@ def mask_runs(attn, W, runs, steps, warmup):
                       W.key_padding_mask(starts, np.full(w.B, w.Skv), w.Skv)),
                      ("random [B,H,1,Skv], density 0.5",
                       W.random_mask(6, (w.B, w.H, 1, w.Skv), 0.5))]
-            kernels = ("decode_bf16_partial", "decode_bf16_combine")
+            kernels = ("decode_bf16_partial", "decode_bf16_combine", "decode_mask_tiles")
         base = None
         for label, m in masks:
             tm = None if m is None else W.mask_to_torch(m)

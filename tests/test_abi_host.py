@@ -87,13 +87,30 @@ def test_kernel_choice():
     assert attn.kernel_for(5, 4, 64, BF16) is None
 
 
+def _stream_rows(B, H, Hkv, Skv, d):
+    """Partial rows of the stream decode: one slot per (wave, pair) segment,
+    at most (2048 waves at d = 128, 4096 at d = 64, and no more than tiles)
+    + pairs slots, of min(32, H / H_kv) head rows each."""
+    group = H // Hkv
+    pairs = B * Hkv * ((group + 31) // 32)
+    waves = min(2048 if d == 128 else 4096, max(1, pairs * ((Skv + 31) // 32)))
+    return (waves + pairs) * min(32, group), pairs
+
+
 def test_workspace_sizes():
-    # decode needs (m, l, acc[d]) partials; the other kernels need none
+    # decode needs (m, l, acc[d]) partials and two wave indices per pair;
+    # the other kernels need none here
     assert attn.workspace_bytes(1, 32, 4096, 4096, 128, BF16) == 0
     assert attn.workspace_bytes(1, 1, 64, 64, 16, F32) == 0
     w = attn.workspace_bytes(64, 32, 1, 8192, 128, BF16)
-    assert w >= 64 * 32 * (8192 // 512) * (128 + 2) * 4
+    rows, pairs = _stream_rows(64, 32, 32, 8192, 128)
+    assert w >= rows * (128 + 2) * 4 + pairs * 2 * 4
+    assert w <= rows * (128 + 2) * 4 + pairs * 2 * 4 + 3 * 256
     assert w % 256 == 0
+    # a short problem needs few slots
+    small = attn.workspace_bytes(1, 4, 1, 40, 64, BF16)
+    rows, pairs = _stream_rows(1, 4, 4, 40, 64)
+    assert rows == 8 + 4 and small <= 3 * 256 + rows * 66 * 4
     assert attn.workspace_bytes(0, 32, 1, 8192, 128, BF16) == 0
 
 
@@ -116,10 +133,12 @@ def test_validate_gqa():
 
 def test_gqa_workspace_sizes():
     lib = attn.library()
-    # one partial per query head and split, whatever the K/V head count
+    # one partial per (wave, pair) segment, min(32, H / H_kv) head rows each
     for Hkv in (1, 8, 32):
         w = lib.attn_workspace_bytes_gqa(64, 32, Hkv, 1, 8192, 128, BF16)
-        assert w >= 64 * 32 * (8192 // 1024) * (128 + 2) * 4 and w % 256 == 0
+        rows, pairs = _stream_rows(64, 32, Hkv, 8192, 128)
+        assert rows * (128 + 2) * 4 + pairs * 8 <= w <= rows * (128 + 2) * 4 + pairs * 8 + 768
+        assert w % 256 == 0
         assert attn.workspace_bytes(64, 32, 1, 8192, 128, BF16, kv_heads=Hkv) == w
     assert lib.attn_workspace_bytes_gqa(64, 32, 32, 1, 8192, 128, BF16) == \
         attn.workspace_bytes(64, 32, 1, 8192, 128, BF16)
@@ -144,7 +163,8 @@ def test_prefill_split_workspace():
 def test_profile_names():
     names = attn.profile_names()
     assert names == ["prefill_bf16_mfma", "decode_bf16_partial", "decode_bf16_combine",
-                     "generic_f32", "prefill_bf16_combine", "prefill_mask_tiles"]
+                     "generic_f32", "prefill_bf16_combine", "prefill_mask_tiles",
+                     "decode_mask_tiles"]
 
 
 def test_python_layer_rejects_bad_tensors():
@@ -212,9 +232,11 @@ def test_masked_prefill_workspace():
     split = attn.workspace_bytes(1, 2, 300, 8000, 128, BF16)
     assert split > 0
     assert attn.workspace_bytes(1, 2, 300, 8000, 128, BF16, masked=True) >= split + 2 * 125
-    # decode and fp32: a mask needs nothing more
-    assert attn.workspace_bytes(4, 8, 1, 5000, 128, BF16, masked=True) == \
-        attn.workspace_bytes(4, 8, 1, 5000, 128, BF16)
+    # decode: a visible-tile count and a list of up to ceil(Skv / 32) tiles per pair
+    dec = attn.workspace_bytes(4, 8, 1, 5000, 128, BF16)
+    dec_m = attn.workspace_bytes(4, 8, 1, 5000, 128, BF16, masked=True)
+    assert dec_m - dec >= 32 * 4 + 32 * 157 * 4 and dec_m - dec <= 32 * 4 + 32 * 157 * 4 + 512
+    # fp32: a mask needs nothing
     assert attn.workspace_bytes(1, 2, 64, 64, 32, F32, masked=True) == 0
     # beyond the list size the marks are not used
     assert attn.workspace_bytes(1, 1, 64, 200000, 128, BF16, masked=True) == \

@@ -13,9 +13,10 @@ import workloads as W
 
 class _Attn:
     BF16 = 1
+    masked = False
 
     def fwd(self, *a, **kw):
-        return None
+        _Attn.masked = kw.get("mask") is not None
 
 
 def _stub_timing(monkeypatch):
@@ -24,9 +25,8 @@ def _stub_timing(monkeypatch):
     def timed(attn, fn, steps, warmup, kernels):
         fn()
         calls.append(kernels)
-        # the second kernel of a masked prefill (the tile-mark pre-pass) is
-        # absent from an unmasked call, as on the GPU
-        return {k: (math.nan if k == "prefill_mask_tiles" and len(calls) == 1 else 1.0)
+        # the mask pre-passes are absent from an unmasked call, as on the GPU
+        return {k: (math.nan if k.endswith("_mask_tiles") and not _Attn.masked else 1.0)
                 for k in kernels}
 
     monkeypatch.setattr(bench, "timed_calls", timed)

@@ -203,3 +203,35 @@ def test_decode8192_key_padding_sampled():
     starts = rng.integers(0, 400, size=w.B)
     mask = W.key_padding_mask(starts, np.full(w.B, w.Skv), w.Skv)
     _sampled_mask_check(w, mask, [(0, 0), (5, 13), (63, 31)])
+
+
+def test_decode8192_random_head_mask_sampled():
+    """Multi-head decode over the full workload with a per-head random mask:
+    wave shares of listed tiles run past 128 entries, so the tile lists roll
+    over in chunks of 64."""
+    w = W.WORKLOADS["decode8192_bf16"]
+    _say("decode8192 random per-head mask")
+    mask = W.random_mask(99, (w.B, w.H, 1, w.Skv), 0.5)
+    _sampled_mask_check(w, mask, [(0, 0), (7, 31), (40, 5), (63, 17)])
+
+
+def test_decode_sparse_visible_windows():
+    """Long caches where a few windows far apart are visible (listed tiles
+    far apart), per head and shared, one sequence with nothing visible."""
+    B, H, Hkv, Skv, d = 3, 8, 2, 20000, 128
+    for shared in (False, True):
+        _say(f"sparse windows shared={shared}")
+        prob = W.random_problem(131 + shared, B, H, 1, Skv, d, "bf16", [20000, 17001, 9000],
+                                Hkv=Hkv)
+        mask = np.zeros((B, 1 if shared else H, 1, Skv), dtype=bool)
+        for b in range(B - 1):
+            for hh in range(mask.shape[1]):
+                for lo in (37 + 101 * hh, 5000 + 7 * hh, 16990):
+                    mask[b, hh, 0, lo:lo + 45] = True
+        got, _ = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], 0,
+                         [20000, 17001, 9000], mask=W.mask_to_torch(mask))
+        ref = oracle.attention(prob["q"], prob["k"], prob["v"], prob["scale"], 0,
+                               [20000, 17001, 9000], mask=mask)
+        assert_matches(got, ref, BF16_TOL, what=f"sparse shared={shared}")
+        assert np.all(got[B - 1] == 0.0)
+

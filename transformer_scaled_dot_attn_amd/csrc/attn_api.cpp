@@ -265,7 +265,9 @@ size_t attn_workspace_bytes_ex(int B, int H, int Hkv, int Sq, int Skv, int d, in
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
     if (check_shape(B, H, Hkv, Sq, Skv, d, dv) != ATTN_OK) return 0;
     switch (choose_path(Sq, d, dtype, dv)) {
-        case kPathDecode: return decode_workspace_bytes(B, H, Hkv, Skv, d);
+        case kPathDecode:
+            return decode_workspace_bytes(B, H, Hkv, Skv, d) +
+                   (masked ? decode_mask_workspace_bytes(B, H, Hkv, Skv, d) : 0);
         case kPathPrefill:
             return prefill_workspace_bytes(B, H, Sq, Skv, d) +
                    (masked ? prefill_mask_workspace_bytes(B, Sq, Skv) : 0);
@@ -394,6 +396,7 @@ const char* attn_profile_name(int kernel) {
         case kGenericF32: return "generic_f32";
         case kPrefillCombineBf16: return "prefill_bf16_combine";
         case kPrefillMaskTiles: return "prefill_mask_tiles";
+        case kDecodeMaskTiles: return "decode_mask_tiles";
         default: return nullptr;
     }
 }

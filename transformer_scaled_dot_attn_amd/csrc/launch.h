@@ -29,19 +29,11 @@ struct LaunchArgs {
 // Last 4-byte word offset of a mask row that a kernel may read.
 __host__ __device__ inline int mask_last_word(int Skv) { return ((Skv + 3) & ~3) - 4; }
 
-// Decode split plan of the kernels that serve calls with an allowed-mask:
-// keys per split, number of splits per (b, h), and for grouped heads
-// (H / Hkv >= 4) the matrix-core split kernel's groups of 32 query heads per
-// K/V head (0: the vector kernel).  Calls without a mask run the stream
-// kernel, which sizes its own grid.
-struct DecodePlan {
-    int chunk;
-    int nsplit;
-    int hgroups;
-};
-DecodePlan decode_plan(int B, int H, int Hkv, int Skv);
+// Decode workspace: the stream kernel's partials and pair spans; with an
+// allowed-mask, plus decode_mask_workspace_bytes for the pairs' visible-tile
+// counts and lists.
 size_t decode_workspace_bytes(int B, int H, int Hkv, int Skv, int d);
-int decode_heads_per_block(int H, int Hkv);  // query heads one decode block serves
+size_t decode_mask_workspace_bytes(int B, int H, int Hkv, int Skv, int d);
 
 // Prefill plan: key-range splits per query tile (1 = none, no workspace).
 struct PrefillPlan {
@@ -63,7 +55,8 @@ struct KernelTimer {
 KernelTimer* active_timer();  // nullptr when timing is off
 
 enum KernelId { kPrefillBf16 = 0, kDecodePartialBf16 = 1, kDecodeCombineBf16 = 2, kGenericF32 = 3,
-                kPrefillCombineBf16 = 4, kPrefillMaskTiles = 5, kNumKernels = 6 };
+                kPrefillCombineBf16 = 4, kPrefillMaskTiles = 5, kDecodeMaskTiles = 6,
+                kNumKernels = 7 };
 
 hipError_t launch_generic_f32(const LaunchArgs& a);
 hipError_t launch_prefill_bf16(const LaunchArgs& a);
