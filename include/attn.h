@@ -113,8 +113,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int 
 /*
  * attn_workspace_bytes -- device bytes attn_fwd_ws needs for this problem
  * (0 when the chosen kernel needs none).  Returns 0 for invalid arguments.
- * Decode needs one fp32 (m, l, acc[d]) partial per query head and key split;
- * prefill needs one per query row and key split only when a short query
+ * Decode needs fp32 (m, l, acc[d]) partials: one per served query head for
+ * each (wave, cache) segment of its fixed grid of waves (at most as many
+ * waves as the GPU holds, plus one segment per cache), and two wave indices
+ * per cache; prefill needs one per query row and key split only when a short query
  * chunk against a long cache leaves CUs idle (fewer than 256 query tiles of
  * 256 rows) and the key range is split.
  */
@@ -135,7 +137,7 @@ int attn_fwd_ws(const void* q, const void* k, const void* v, void* out, int B, i
  * attn_fwd_gqa -- attn_fwd with H_kv key/value heads (layout and head
  * grouping above; k and v are [B][H_kv][Skv][d]).  H_kv must divide H, else
  * ATTN_E_SHAPE.  The decode kernel reads each K/V row once for all the query
- * heads it serves (up to 8 per pass), so decode bytes fall by up to H / H_kv.
+ * heads it serves (up to 32 per pass), so decode bytes fall by up to H / H_kv.
  * Other arguments, ownership and errors as attn_fwd.
  */
 int attn_fwd_gqa(const void* q, const void* k, const void* v, void* out, int B, int H, int H_kv,
@@ -197,7 +199,9 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, i
                 void* stream, void* workspace, size_t workspace_bytes);
 
 /* Device bytes attn_fwd_ex needs as caller workspace (masked != 0 when a
-   mask is passed); 0 also for invalid arguments. */
+   mask is passed: a masked prefill adds key-tile marks, a masked decode a
+   visible-tile count and list per (b, K/V head) cache); 0 also for invalid
+   arguments. */
 size_t attn_workspace_bytes_ex(int B, int H, int H_kv, int Sq, int Skv, int d, int d_v, int dtype,
                                int masked);
 
