@@ -67,8 +67,10 @@
 //
 // Order.  Block ids are mapped heaviest query tile first; within a query
 // tile rank the (b, h) pairs are laid out so that each XCD (ids are dealt
-// round-robin over the 8 XCDs) runs a contiguous range of heads: every tile
-// of a head, and the query heads that share one K/V head, use one L2.
+// round-robin over the 8 XCDs) runs whole heads -- every tile of a head, and
+// the query heads that share one K/V head, use one L2 -- with the (b, K/V
+// head) units dealt to the XCDs in turn, so that every XCD holds heads of
+// every batch item and ragged lengths load the XCDs evenly.
 //
 // Grouped key/value heads (GQA / MQA): query head h reads K/V head
 // h / (H / Hkv) ("Attention from First Principles", section "MHA, GQA, MQA
@@ -141,29 +143,45 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int rem = bid - (bid / (BH * nsplit)) * (BH * nsplit);
     const int split = rem / BH;  // key-range split of this query tile
     const int jb = rem - split * BH;
-    // Blocks are dealt to the 8 XCDs round-robin by id.  With BH a multiple
-    // of 8, XCD x runs the contiguous (b, h) pairs x*BH/8 .. (x+1)*BH/8 - 1,
-    // so every query tile of a head, and the query heads that share a K/V
-    // head, meet in one L2.
-    const int bh = (BH & 7) == 0 ? (jb & 7) * (BH >> 3) + (jb >> 3) : jb;
+    // Blocks are dealt to the 8 XCDs round-robin by id.  When the (b, K/V
+    // head) units, each with the g = H / Hkv query heads that share it, number
+    // a multiple of 8, unit u runs on XCD u mod 8: every query tile of a head,
+    // and the heads of one K/V group, meet in one L2, and each XCD holds heads
+    // of every batch item, so ragged lengths load the XCDs evenly.  Otherwise,
+    // with BH a multiple of 8, XCD x runs the contiguous (b, h) pairs
+    // x*BH/8 .. (x+1)*BH/8 - 1.
+    const int g = H / Hkv;
+    const int units = BH / g;
+    int bh = jb;
+    if ((units & 7) == 0) {
+        const int i = jb >> 3;
+        bh = ((jb & 7) + 8 * (i / g)) * g + i % g;
+    } else if ((BH & 7) == 0) {
+        bh = (jb & 7) * (BH >> 3) + (jb >> 3);
+    }
     const int b = bh / H;
     const int bk = b * Hkv + (bh - b * H) / (H / Hkv);  // this head's K/V head
     const int L = valid_length(kv_lens, b, Skv);
     const int n = Sq < L ? Sq : L;
     const int off = L - n;
-    const int q0 = qt * kBM;
+    // Query tile rows.  Without a mask the tiles end at the last valid row
+    // (q0 = n - (nqt - qt) kBM; rows below 0 are dead), so a sequence's partly
+    // filled tile is its first one, whose rows see the fewest keys; the pad
+    // rows n .. Sq-1 are zeroed by the blocks of the tiling from row 0 (block
+    // qt: rows qt kBM .. qt kBM + kBM - 1).  With a mask the tiles start at
+    // row 0, as the key-tile marks do.
+    const int qz = qt * kBM;
+    const int q0 = MASK ? qz : n - (nqt - qt) * kBM;
 
     uint16_t* obase = out + (size_t)bh * Sq * D;
-    if (q0 >= n) {
-        // every row of this tile is padding: write zeros (split 0 does it;
-        // the split combine writes zeros for these rows itself)
-        if (nsplit > 1) return;
-        const int rows = min(kBM, Sq - q0);
+    // pad rows are zero (without splits; the split combine zeroes them itself)
+    const int z0 = max(qz, n), z1 = min(qz + kBM, Sq);
+    if (nsplit == 1 && z0 < z1 && (!MASK || q0 >= n)) {
         const u32x4 z = {0, 0, 0, 0};
-        for (int e = tid; e < rows * S::kChunks; e += kThreads)
-            *reinterpret_cast<u32x4*>(obase + (size_t)q0 * D + e * 8) = z;
-        return;
+        for (int e = tid; e < (z1 - z0) * S::kChunks; e += kThreads)
+            *reinterpret_cast<u32x4*>(obase + (size_t)z0 * D + e * 8) = z;
     }
+    if (q0 >= n || q0 + kBM <= 0) return;  // no valid row in this tile
 
     // keys the whole query tile may see, this block's split of them, and
     // this wave's limits: tiles t0 <= t < t1 of the block, t < t1w of the wave
@@ -173,7 +191,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int t0 = min(ntiles_q, split * per_split);
     const int t1 = min(ntiles_q, t0 + per_split);
     const int qw = q0 + wave * 32;
-    const bool wave_live = qw < n;
+    const bool wave_live = qw < n && qw + 32 > 0;
     const int p_lo = off + qw;
     const int p_hi = off + min(qw + 32, n) - 1;
     const int kv_hi_w = wave_live ? (causal ? min(L, p_hi + 1) : L) : 0;
@@ -184,7 +202,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // this lane's query
     const int qi = qw + (lane & 31);
     const int p = off + qi;
-    const bool q_live = qi < n;
+    const bool q_live = qi >= 0 && qi < n;
 
     // Q^T fragments: B operand of S^T = K Q^T.  Lane l holds 8 consecutive
     // features 16*ks + 8*(l/32) .. +7 of query (l%32).  Issued before the
@@ -647,8 +665,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         return;
     }
 
-    // ---- epilogue: out = acc / l, rows past n_b are zero
-    if (qi < Sq) {
+    // ---- epilogue: out = acc / l; with a mask this tile's rows past n_b are
+    // zero too (without one the pad rows were zeroed above)
+    if (MASK ? qi < Sq : q_live) {
         const float l_tot = halves_sum(l_run);
         const float inv = (q_live && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
         uint16_t* orow = obase + (size_t)qi * D;
