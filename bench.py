@@ -142,6 +142,31 @@ def prefill_sweep(attn, W, dev, steps, warmup):
     return rows
 
 
+def prefill_configs(attn, W, dev, steps, warmup,
+                    names=("mha768_bf16", "padded2048_bf16", "gqa_prefill2048_bf16")):
+    """The other bf16 prefill workloads (d_model 768 at S = 512; causal with
+    right padding, lengths U[256, 2048]; grouped K/V heads at S = 2048),
+    each timed on its own: TFLOP/s of 4*d flops per visible pair."""
+    import torch
+    rows = []
+    for name in names:
+        w = W.WORKLOADS[name]
+        x = W.device_inputs(w, dev)
+        out = torch.empty_like(x["q"])
+        fn = lambda: attn.fwd(x["q"], x["k"], x["v"], out, causal=w.causal,
+                              kv_lens=x["kv_lens"], scale=x["scale"])
+        t = timed_calls(attn, fn, steps, warmup, ("prefill_bf16_mfma", "prefill_bf16_combine"))
+        ms = sum(v for v in t.values() if not math.isnan(v))  # the combine runs only with splits
+        flops = prefill_flops(w, x["kv_lens_host"])
+        tflops = flops / (ms * 1e-3) / 1e12
+        rows.append({"workload": name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "S": w.Sq,
+                     "d": w.d, "ms_per_call": ms, "TFLOP/s": tflops,
+                     "frac": tflops / PEAK_BF16_TFLOPS, "flop_per_call": flops})
+        del x, out
+        torch.cuda.empty_cache()
+    return rows
+
+
 def mask_runs(attn, W, runs, steps, warmup):
     """The step's workloads again with explicit allowed-masks (True = may
     attend, ANDed with the causal and length rules; "Attention from Scratch",
@@ -243,9 +268,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--parts", default="prefill,decode,masks,gqa,sweep",
-                    help="comma list of prefill, decode, masks, copy, gqa, gqa8, sweep (default "
-                         "prefill,decode,masks,gqa,sweep); masks times the step's workloads again with "
+    ap.add_argument("--parts", default="prefill,decode,masks,gqa,configs,sweep",
+                    help="comma list of prefill, decode, masks, copy, gqa, gqa8, configs, sweep "
+                         "(default prefill,decode,masks,gqa,configs,sweep); configs times the other "
+                         "bf16 prefill workloads; masks times the step's workloads again with "
                          "allowed-masks; gqa8 is the 8-K/V-head decode alone; copy adds a plain 1 GiB device-to-device copy per "
                          "step, the known-size kernel that scales the HBM byte counters; gqa "
                          "measures decode at 32, 8 and 1 K/V heads for 32 query heads; sweep "
@@ -395,6 +421,9 @@ def main():
     if "masks" in parts and runs:
         print("[bench] allowed-mask runs", file=sys.stderr, flush=True)
         result["masks"] = mask_runs(attn, W, runs, args.steps, args.warmup)
+    if "configs" in parts:
+        print("[bench] other prefill workloads", file=sys.stderr, flush=True)
+        result["prefill_configs"] = prefill_configs(attn, W, dev, args.steps, args.warmup)
     if "sweep" in parts:
         print("[bench] prefill S sweep", file=sys.stderr, flush=True)
         result["prefill_sweep"] = prefill_sweep(attn, W, dev, args.steps, args.warmup)

@@ -89,3 +89,22 @@ def test_grouped_decode_rows(monkeypatch):
     for hkv, r in by.items():
         assert abs(r["intensity_flop_per_byte"] - 32 / hkv) < 0.05 * 32 / hkv
         assert r["roofline"]["bound"] == "hbm" and r["roofline"]["frac"] > 0
+
+
+def test_prefill_config_rows(monkeypatch):
+    _stub_timing(monkeypatch)
+    import torch
+    monkeypatch.setattr(W, "device_inputs", lambda w, dev="cuda", **kw: _inputs(w))
+    monkeypatch.setattr(torch, "empty_like", lambda x: None)
+    rows = bench.prefill_configs(_Attn(), W, "cpu", 1, 0)
+    by = {r["workload"]: r for r in rows}
+    # C2: 4 d flops per causal pair of 4 x 12 sequences of 512
+    assert by["mha768_bf16"]["flop_per_call"] == 4 * 64 * 48 * 512 * 513 / 2
+    # C4: the drawn lengths set the visible pairs, below the unpadded count
+    pad = by["padded2048_bf16"]
+    full = 4 * 128 * 8 * 32 * 2048 * 2049 / 2
+    assert 0.2 * full < pad["flop_per_call"] < full
+    for r in rows:
+        # the stub times the prefill and the split-combine kernel at 1 ms each
+        assert r["ms_per_call"] == 2.0 and r["frac"] == r["TFLOP/s"] / bench.PEAK_BF16_TFLOPS
+
