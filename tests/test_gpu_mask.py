@@ -235,3 +235,20 @@ def test_decode_sparse_visible_windows():
         assert_matches(got, ref, BF16_TOL, what=f"sparse shared={shared}")
         assert np.all(got[B - 1] == 0.0)
 
+
+
+def test_decode_mask_past_one_prepass_chunk():
+    """A masked decode over more than 65536 keys: the visible-tile pre-pass
+    flags tiles in LDS chunks of 2048 tiles, so its lists span two chunks."""
+    B, H, Hkv, Skv, d = 2, 4, 2, 70000, 128
+    lens = [70000, 66001]
+    for shape in ((B, H, 1, Skv), (B, 1, 1, Skv)):
+        _say(f"decode 70000 keys, mask {shape}")
+        prob = W.random_problem(141 + len(shape), B, H, 1, Skv, d, "bf16", lens, Hkv=Hkv)
+        mask = W.random_mask(141, shape, 0.02)
+        mask[..., 65530:65560] = True  # keys both sides of the chunk edge
+        got, _ = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], 0, lens,
+                         mask=W.mask_to_torch(mask))
+        ref = oracle.attention(prob["q"], prob["k"], prob["v"], prob["scale"], 0, lens,
+                               mask=mask)
+        assert_matches(got, ref, BF16_TOL, what=f"70000 keys {shape}")
