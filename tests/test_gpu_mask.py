@@ -2,12 +2,14 @@
 
 The mask (True = may attend) is ANDed with the causal and length rules
 ("Attention from Scratch", KubeDojo module 1.4.3, Part 3).  Every kernel
-family -- bf16 prefill (with and without key-range splits), the vector and
-matrix-core decode kernels, the fp32 kernel -- runs masks in every broadcast
-shape on ragged sizes (Skv not a multiple of the tiles, nor of 4) and is
-compared element by element with the oracle; rows with no allowed key must
-be exactly zero.  An all-true mask must give the unmasked result bit for bit,
-and a mask spelling out the causal rule must reproduce the causal result.
+family -- bf16 prefill (with and without key-range splits), the decode
+stream kernel over its visible-tile lists (one and several query heads per
+K/V head), the fp32 kernel -- runs masks in every broadcast shape on ragged
+sizes (Skv not a multiple of the tiles, nor of 4) and is compared element by
+element with the oracle; rows with no allowed key must be exactly zero.  An
+all-true mask must give the unmasked result bit for bit (decode: to
+rounding), and a mask spelling out the causal rule must reproduce the causal
+result.
 """
 import numpy as np
 import pytest
@@ -79,9 +81,9 @@ def test_mask_matches_oracle(case):
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}")
 def test_all_true_mask_is_bitwise_unmasked(case):
-    """Bit for bit, except bf16 decode: unmasked it runs the stream kernel,
-    whose partials cut the keys elsewhere than the masked split kernels', so
-    the two agree to rounding only."""
+    """Bit for bit, except bf16 decode: the masked stream kernel can hold a
+    different number of resident waves than the unmasked one (d = 64), and so
+    cut its shares of the keys elsewhere; the two agree to rounding."""
     seed, dt, B, H, Hkv, Sq, Skv, d, causal, lens = case[:10]
     _say(f"all-true mask s{seed}")
     ones = np.ones((1, 1, 1, Skv), dtype=bool)
