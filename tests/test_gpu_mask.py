@@ -33,9 +33,9 @@ CASES = [
     (73, "bf16", 2, 4, 2, 256, 512, 128, 1, None, "bh1k", 0.8),
     (74, "bf16", 1, 2, 2, 200, 2602, 128, 1, [2602], "11qk", 0.3),   # key-range splits
     (75, "bf16", 2, 4, 4, 65, 131, 64, 0, [131, 40], "bhqk", 0.05),  # many empty rows
-    (76, "bf16", 3, 4, 4, 1, 700, 128, 0, [700, 333, 0], "bh1k", 0.5),  # vector decode
-    (77, "bf16", 2, 8, 4, 1, 1031, 64, 0, [1031, 500], "b11k", 0.6),  # 2 heads per block
-    (78, "bf16", 2, 16, 2, 1, 1100, 128, 0, [1100, 900], "bh1k", 0.4),  # matrix-core decode
+    (76, "bf16", 3, 4, 4, 1, 700, 128, 0, [700, 333, 0], "bh1k", 0.5),  # decode, one head per K/V head
+    (77, "bf16", 2, 8, 4, 1, 1031, 64, 0, [1031, 500], "b11k", 0.6),  # decode, 2 heads per K/V head
+    (78, "bf16", 2, 16, 2, 1, 1100, 128, 0, [1100, 900], "bh1k", 0.4),  # decode, 8 heads per K/V head
     (79, "bf16", 1, 32, 1, 1, 2049, 128, 0, None, "b11k", 0.02),
     (80, "f32", 2, 3, 3, 70, 90, 40, 1, [90, 50], "bhqk", 0.6),
     (81, "f32", 1, 4, 2, 1, 150, 128, 0, None, "1h1k", 0.5),
@@ -155,8 +155,9 @@ def test_mask_layout_errors():
 
 
 def test_mask_decode_split_fully_hidden():
-    """Decode with whole key splits hidden (partials with no visible key) and a
-    sequence whose every key is hidden (output 0), on both decode kernels."""
+    """Decode with long key ranges hidden (no tile listed there) and a
+    sequence whose every key is hidden (no tile listed at all: output 0), at
+    one and at 8 query heads per K/V head."""
     for H, Hkv in ((8, 8), (16, 2)):
         B, Skv, d = 2, 3000, 128
         _say(f"decode hidden splits H{H}/{Hkv}")
