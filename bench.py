@@ -266,8 +266,10 @@ def profiled_traffic(kernel: str, workload: str):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # 20 warm-up steps (~17 ms): the first ~15 steps after a cold start run
+    # through a power-management transient (prefill 150 -> 190 -> 150 us)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--parts", default="prefill,decode,masks,gqa,configs,sweep",
                     help="comma list of prefill, decode, masks, copy, gqa, gqa8, configs, sweep "
                          "(default prefill,decode,masks,gqa,configs,sweep); configs times the other "
