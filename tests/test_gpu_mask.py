@@ -255,3 +255,32 @@ def test_decode_mask_past_one_prepass_chunk():
         ref = oracle.attention(prob["q"], prob["k"], prob["v"], prob["scale"], 0, lens,
                                mask=mask)
         assert_matches(got, ref, BF16_TOL, what=f"70000 keys {shape}")
+
+
+def test_masked_decode_caller_workspace():
+    """A masked decode with a caller workspace of workspace_bytes(masked=True)
+    gives the bits of the library-owned one; one sized for the unmasked call
+    (no room for the visible-tile lists) is refused."""
+    import torch
+    B, H, Hkv, Skv, d = 3, 8, 2, 3000, 128
+    lens = [3000, 17, 2000]
+    prob = W.random_problem(151, B, H, 1, Skv, d, "bf16", lens, Hkv=Hkv)
+    q, k, v = (W.to_torch(prob[x]) for x in ("q", "k", "v"))
+    tl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    mask = W.mask_to_torch(W.random_mask(151, (B, H, 1, Skv), 0.3))
+    ref = attn.fwd(q, k, v, causal=False, kv_lens=tl, mask=mask)
+    need = attn.workspace_bytes(B, H, 1, Skv, d, attn.BF16, kv_heads=Hkv, masked=True)
+    plain = attn.workspace_bytes(B, H, 1, Skv, d, attn.BF16, kv_heads=Hkv)
+    assert need > plain
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = attn.fwd(q, k, v, causal=False, kv_lens=tl, mask=mask, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    with pytest.raises(attn.AttnError) as e:
+        attn.fwd(q, k, v, causal=False, kv_lens=tl, mask=mask, workspace=ws[:plain])
+    assert e.value.status == attn.E_WORKSPACE
+    # the unmasked call runs in the smaller buffer
+    out2 = attn.fwd(q, k, v, causal=False, kv_lens=tl, workspace=ws[:plain])
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16),
+                       attn.fwd(q, k, v, causal=False, kv_lens=tl).view(torch.int16))
