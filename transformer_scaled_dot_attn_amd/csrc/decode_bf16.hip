@@ -535,83 +535,90 @@ __global__ __launch_bounds__(64, 2) void decode_stream_kernel(
     }
 }
 
-// Final step of a combine block of 2 D threads: thread (h2, t) holds the
-// merge (M, lt, at) of half h2 of the partials for column t; the halves are
-// merged in LDS and column t of the output row o is written (0 when no key
-// was visible: l = 0).
-template <int D>
-__device__ __forceinline__ void merge_halves(float M, float lt, float at, uint16_t* __restrict__ o) {
-    __shared__ float s_m[2], s_l[2];
-    __shared__ float s_a[2][D];
-    const int t = threadIdx.x % D;
-    const int h2 = threadIdx.x / D;
-    if (t == 0) {
-        s_m[h2] = M;
-        s_l[h2] = lt;
-    }
-    s_a[h2][t] = at;
-    __syncthreads();
-    if (h2 == 0) {
-        // a half with no partial has M = -inf and contributes nothing
-        const float Mt = fmaxf(s_m[0], s_m[1]);
-        const float w0 = s_m[0] == -INFINITY ? 0.0f : fast_exp2(s_m[0] - Mt);
-        const float w1 = s_m[1] == -INFINITY ? 0.0f : fast_exp2(s_m[1] - Mt);
-        const float l = s_l[0] * w0 + s_l[1] * w1;
-        o[t] = l > 0.0f ? to_bf16((s_a[0][t] * w0 + s_a[1][t] * w1) / l) : 0;  // 0: no visible key
-    }
-}
-
 // Combine: per (b, h), merges the partials of the head's pair, slots
-// span[2p] + p .. span[2p+1] + p (head row h mod 32 of the pair's group), each
-// half of the block taking every other slot, four at a time with one running
-// maximum.  A pair with no tile (L_b = 0, or with a mask no listed tile:
-// counts[p] = 0) wrote no partial; its heads are 0.
+// span[2p] + p .. span[2p+1] + p (head row h mod 32 of the pair's group).  The
+// block's 256 threads form kG groups of D/4 threads, each thread holding 4
+// columns (16-byte loads); group g takes every kG-th slot, kU at a time with
+// one running maximum, and the groups are merged in LDS.  A pair with no tile
+// (L_b = 0, or with a mask no listed tile: counts[p] = 0) wrote no partial;
+// its heads are 0, as is a head with no visible key (l = 0).
 template <int D>
-__global__ __launch_bounds__(2 * D) void decode_combine_kernel(
+__global__ __launch_bounds__(256) void decode_combine_kernel(
     const int32_t* __restrict__ kv_lens, int H, int Hkv, int Skv, int hgroups,
     const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
     const int* __restrict__ span, const int* __restrict__ counts, uint16_t* __restrict__ out) {
+    constexpr int kC = D / 4;     // threads per partial row
+    constexpr int kG = 256 / kC;  // groups of slots: 8 at d = 128, 16 at d = 64
+    constexpr int kU = 4;         // slots per group per step
+    __shared__ float s_m[kG], s_l[kG];
+    __shared__ __attribute__((aligned(16))) float s_a[kG][D];
     const int bh = blockIdx.x;
     const int b = bh / H, h = bh - b * H;
-    const int t = threadIdx.x % D;
-    const int h2 = threadIdx.x / D;
+    const int tid = threadIdx.x;
+    const int g = tid / kC, c = (tid % kC) * 4;
     const int group = H / Hkv, nhs = min(32, group);
     const int kvh = h / group, r = h - kvh * group;
     const long long pr = ((long long)b * Hkv + kvh) * hgroups + r / 32;
     const int hh = r % 32;
     uint16_t* o = out + (size_t)bh * D;
+    // the span is read with the length (unused when the pair has no tile)
+    const int w0 = span[2 * pr], w1 = span[2 * pr + 1];
     if (valid_length(kv_lens, b, Skv) == 0 || (counts != nullptr && counts[pr] == 0)) {
-        if (h2 == 0) o[t] = 0;
+        if (tid < kC) *reinterpret_cast<u32x2*>(o + c) = u32x2{0, 0};
         return;
     }
-    const int w0 = span[2 * pr], w1 = span[2 * pr + 1];
-    float M = -INFINITY, lt = 0.0f, at = 0.0f;
-    for (int w = w0 + h2; w <= w1; w += 8) {
-        float mv[4], lv[4], av[4];
+    float M = -INFINITY, lt = 0.0f;
+    f32x4 at = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int w = w0 + g; w <= w1; w += kG * kU) {
+        float mv[kU], lv[kU];
+        f32x4 av[kU];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ww = w + 2 * i;
+        for (int i = 0; i < kU; ++i) {
+            const int ww = w + kG * i;
             const bool ok = ww <= w1;
             const size_t u = (size_t)((ww + pr) * nhs + hh);
             mv[i] = ok ? ws_ml[u * 2] : -INFINITY;
             lv[i] = ok ? ws_ml[u * 2 + 1] : 0.0f;
-            av[i] = ok ? ws_acc[u * D + t] : 0.0f;
+            av[i] = ok ? *reinterpret_cast<const f32x4*>(ws_acc + u * D + c)
+                       : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
         float Mn = M;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Mn = fmaxf(Mn, mv[i]);
+        for (int i = 0; i < kU; ++i) Mn = fmaxf(Mn, mv[i]);
         const float f = M == -INFINITY ? 0.0f : fast_exp2(M - Mn);
         lt *= f;
         at *= f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kU; ++i) {
             const float wt = mv[i] == -INFINITY ? 0.0f : fast_exp2(mv[i] - Mn);
             lt = fmaf(lv[i], wt, lt);
-            at = fmaf(av[i], wt, at);
+            at += av[i] * wt;
         }
         M = Mn;
     }
-    merge_halves<D>(M, lt, at, o);
+    if (c == 0) {
+        s_m[g] = M;
+        s_l[g] = lt;
+    }
+    *reinterpret_cast<f32x4*>(&s_a[g][c]) = at;
+    __syncthreads();
+    if (tid < kC) {
+        // a group with no slot has M = -inf and contributes nothing
+        float Mt = -INFINITY;
+#pragma unroll
+        for (int gg = 0; gg < kG; ++gg) Mt = fmaxf(Mt, s_m[gg]);
+        float l = 0.0f;
+        f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int gg = 0; gg < kG; ++gg) {
+            const float wt = s_m[gg] == -INFINITY ? 0.0f : fast_exp2(s_m[gg] - Mt);
+            l = fmaf(s_l[gg], wt, l);
+            a += *reinterpret_cast<const f32x4*>(&s_a[gg][c]) * wt;
+        }
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;  // 0: no visible key
+        const u32x2 wv = {pack_bf16(a[0] * inv, a[1] * inv), pack_bf16(a[2] * inv, a[3] * inv)};
+        *reinterpret_cast<u32x2*>(o + c) = wv;
+    }
 }
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -755,7 +762,7 @@ hipError_t launch_decode_bf16(const LaunchArgs& a) {
         hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(heads), dim3(256), 0, a.stream,
                            a.kv_lens, a.H, a.Hkv, a.Skv, hgroups, acc, ml, span, counts, o);
     else
-        hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(heads), dim3(128), 0, a.stream,
+        hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(heads), dim3(256), 0, a.stream,
                            a.kv_lens, a.H, a.Hkv, a.Skv, hgroups, acc, ml, span, counts, o);
     e = hipGetLastError();
     if (t) t->end(kDecodeCombineBf16, a.stream);
