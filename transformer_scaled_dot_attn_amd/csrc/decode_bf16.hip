@@ -623,14 +623,15 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Shares of a wave: at least 16 key tiles when a partial holds 16 or more
+// Shares of a wave: at least 32 key tiles when a partial holds 16 or more
 // query heads (its bytes then come near a K+V tile's), else 4; but never
 // fewer waves than a quarter of those the GPU holds, down to one tile each,
 // so that short caches still spread over the chip.  Measured (B = 64,
-// H = 32, d = 128): lengths U[512, 8192] at 1 and 2 K/V heads, floors of 8
-// are 20-25 % slower than 16 and 32; lengths U[16, 512] in caches of 8192,
-// floors of 16 are 25-100 % slower than 2-4 at 1, 8 and 32 K/V heads.
-int stream_min_tiles(int H, int Hkv) { return std::min(32, H / Hkv) >= 16 ? 16 : 4; }
+// H = 32, d = 128, capacity 8192): at 1 and 2 K/V heads, floors of 32 beat
+// 16 by 4-8 % (fewer partials to write and merge) and floors of 8 lose
+// 10-25 %, while 256 waves lose 23 %; with lengths U[16, 512], floors of 16
+// are 25-100 % slower than 2-4 at 1, 8 and 32 K/V heads.
+int stream_min_tiles(int H, int Hkv) { return std::min(32, H / Hkv) >= 16 ? 32 : 4; }
 // Most stream waves launched on a d = 128 or d = 64 decode (workspace bound):
 // 256 compute units with 8 or 16 resident waves.
 long stream_max_waves(int d) { return d == 128 ? 2048 : 4096; }
