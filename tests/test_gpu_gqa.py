@@ -81,6 +81,10 @@ STREAM = [
     ("every cache empty", 3, 8, 2, 500, 128, [0, 0, 0]),
     ("B 1030, 17 batch items per lane", 1030, 8, 2, 100, 128, "rand:64"),
     ("B 4500 multi-head, 71 per lane", 4500, 2, 2, 40, 64, "rand:65"),
+    # hundreds of partials per (b, K/V head): the combine's groups take
+    # several rounds of slots, with a ragged last round
+    ("one long cache, 8 K/V heads", 1, 32, 8, 32768, 128, None),
+    ("one long cache d 64", 1, 16, 2, 40000, 64, [39999]),
 ]
 
 
