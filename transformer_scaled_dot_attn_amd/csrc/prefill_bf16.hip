@@ -729,10 +729,12 @@ __global__ __launch_bounds__(kBM) void prefill_mask_tiles_kernel(
 // decode): M = max_s m_s, l = sum_s l_s 2^(m_s - M),
 // out = (sum_s acc_s 2^(m_s - M)) / l; padded rows are written as zeros.
 // Each thread merges 4 consecutive columns of one row with 16-byte loads;
-// a block covers 256 / (D/4) rows.
+// a block covers 256 / (D/4) rows.  A thread issues the loads of all its
+// splits before any arithmetic (one memory round trip); NS >= nsplit bounds
+// the register arrays that hold them.
 constexpr int kMaxSplit = 16;
 
-template <int D>
+template <int D, int NS>
 __global__ __launch_bounds__(256) void prefill_combine_kernel(
     const int32_t* __restrict__ kv_lens, int H, int Sq, int Skv, int nsplit, size_t nrows,
     const float* __restrict__ ws_acc, const float* __restrict__ ws_ml, uint16_t* __restrict__ out) {
@@ -748,31 +750,32 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(
     const int n = Sq < L ? Sq : L;
     u32x2 res = {0, 0};
     if (i < n) {
+        // every split's (m, l) and accumulator columns are loaded up front:
+        // one memory round trip per row
         const float* ml = ws_ml + row * nsplit * 2;
-        float w[kMaxSplit];
+        const float* ac = ws_acc + row * nsplit * D + c;
+        float mv[NS], lv[NS];
+        f32x4 av[NS];
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp) {
+            const bool ok = sp < nsplit;
+            mv[sp] = ok ? ml[2 * sp] : -INFINITY;
+            lv[sp] = ok ? ml[2 * sp + 1] : 0.0f;
+            av[sp] = ok ? *reinterpret_cast<const f32x4*>(ac + (size_t)sp * D)
+                        : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
         float M = -INFINITY;
 #pragma unroll
-        for (int sp = 0; sp < kMaxSplit; ++sp)
-            if (sp < nsplit) M = fmaxf(M, ml[2 * sp]);
+        for (int sp = 0; sp < NS; ++sp) M = fmaxf(M, mv[sp]);
         float lt = 0.0f;
-#pragma unroll
-        for (int sp = 0; sp < kMaxSplit; ++sp) {
-            w[sp] = 0.0f;
-            if (sp < nsplit) {
-                const float m = ml[2 * sp];
-                w[sp] = m == -INFINITY ? 0.0f : fast_exp2(m - M);
-                lt = fmaf(ml[2 * sp + 1], w[sp], lt);
-            }
-        }
-        const float* ac = ws_acc + row * nsplit * D + c;
         f32x4 at = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int sp = 0; sp < kMaxSplit; ++sp)
-            if (sp < nsplit) {
-                const f32x4 a4 = *reinterpret_cast<const f32x4*>(ac + (size_t)sp * D);
+        for (int sp = 0; sp < NS; ++sp) {
+            const float w = mv[sp] == -INFINITY ? 0.0f : fast_exp2(mv[sp] - M);
+            lt = fmaf(lv[sp], w, lt);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) at[e] = fmaf(a4[e], w[sp], at[e]);
-            }
+            for (int e = 0; e < 4; ++e) at[e] = fmaf(av[sp][e], w, at[e]);
+        }
         const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
         res[0] = pack_bf16(at[0] * inv, at[1] * inv);
         res[1] = pack_bf16(at[2] * inv, at[3] * inv);
@@ -864,12 +867,19 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
     if (e != hipSuccess || p.nsplit == 1) return e;
     if (t) t->begin(kPrefillCombineBf16, a.stream);
     const size_t rows = (size_t)BH * a.Sq;
+    // a bound of 4 splits where it suffices: its register arrays keep twice
+    // the waves resident of the 16-split form
+    auto merge = [&](auto kern, int rows_per_block) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
+                           dim3(256), 0, a.stream, a.kv_lens, a.H, a.Sq, a.Skv, p.nsplit, rows, ws_acc,
+                           ws_ml, o);
+    };
     if (a.d == 128)
-        hipLaunchKernelGGL(prefill_combine_kernel<128>, dim3((unsigned)((rows + 7) / 8)), dim3(256),
-                           0, a.stream, a.kv_lens, a.H, a.Sq, a.Skv, p.nsplit, rows, ws_acc, ws_ml, o);
+        p.nsplit <= 4 ? merge(prefill_combine_kernel<128, 4>, 8)
+                      : merge(prefill_combine_kernel<128, kMaxSplit>, 8);
     else
-        hipLaunchKernelGGL(prefill_combine_kernel<64>, dim3((unsigned)((rows + 15) / 16)), dim3(256),
-                           0, a.stream, a.kv_lens, a.H, a.Sq, a.Skv, p.nsplit, rows, ws_acc, ws_ml, o);
+        p.nsplit <= 4 ? merge(prefill_combine_kernel<64, 4>, 16)
+                      : merge(prefill_combine_kernel<64, kMaxSplit>, 16);
     e = hipGetLastError();
     if (t) t->end(kPrefillCombineBf16, a.stream);
     return e;
