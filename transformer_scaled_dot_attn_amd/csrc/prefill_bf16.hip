@@ -687,8 +687,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 }
 
 // Tile marks of an allowed-mask shared by all heads: one workgroup per
-// (mask batch, query tile, key tile), one row per thread, writes 1 if any of
-// the query tile's rows allows a key of the key tile, else 0.  Key tiles past
+// (mask batch, query tile, key tile), writes 1 if any of the query tile's
+// rows allows a key of the key tile, else 0.  Each wave reads 64 rows; lane
+// l reads 4-byte word l mod 16 of every 4th row from l / 16, so each load
+// instruction covers 4 whole 64-byte row segments.  Key tiles past
 // the last key a causal row of the tile can reach are marked 0 unread (the
 // prefill never visits them).
 __global__ __launch_bounds__(kBM) void prefill_mask_tiles_kernel(
@@ -707,13 +709,15 @@ __global__ __launch_bounds__(kBM) void prefill_mask_tiles_kernel(
             return;
         }
     }
-    const int row = q0 + (int)threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int r0 = q0 + (int)(threadIdx.x >> 6) * 64 + (lane >> 4);
+    const int col = min(kt * kBN + 4 * (lane & 15), mask_last_word(Skv));
+    const uint8_t* mtile = mask + bm * msb + col;
     uint32_t any = 0;
-    if (row < Sq) {
-        const uint8_t* mrow = mask + bm * msb + (long long)row * msi;
-        const int mlast = mask_last_word(Skv);
 #pragma unroll
-        for (int w = 0; w < kBN / 4; ++w) any |= ldg_word(mrow + min(kt * kBN + 4 * w, mlast));
+    for (int it = 0; it < 16; ++it) {
+        const int row = r0 + 4 * it;
+        if (row < Sq) any |= ldg_word(mtile + (long long)row * msi);
     }
     const bool wv = __builtin_amdgcn_ballot_w64(any != 0) != 0;
     if ((threadIdx.x & 63) == 0) flags[threadIdx.x >> 6] = wv;
