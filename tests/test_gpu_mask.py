@@ -110,6 +110,20 @@ def test_causal_rule_as_mask(dt, d):
     assert torch.equal(ta, tb), f"max diff {np.abs(a - b).max()}"
 
 
+def _edge_mask(S):
+    """Row i sees key 100 only, except row 255, which sees only key 63 (the
+    last byte of the last row of query tile 0 in key tile 0), and row 511,
+    which sees only key S - 1 (query tile 1's ragged last key tile): each of
+    those two (query tile, key tile) blocks is visible through one byte."""
+    m = np.zeros((S, S), dtype=bool)
+    m[:, 100] = True
+    m[255, 100] = False
+    m[255, 63] = True
+    m[511, 100] = False
+    m[511, S - 1] = True
+    return m[None, None]
+
+
 STRUCTURED = [
     # name, B, H, S, d, causal, kv_lens, mask builder
     ("left padding", 2, 4, 1000, 128, 1, [1000, 700],
@@ -118,6 +132,7 @@ STRUCTURED = [
     ("documents d64", 1, 2, 777, 64, 0, None, lambda S: W.document_mask([64, 1, 300, 412])),
     ("sliding window", 1, 4, 1200, 128, 1, None, lambda S: W.window_mask(S, 130)),
     ("window split", 1, 2, 4500, 128, 0, None, lambda S: W.window_mask(S, 70)),
+    ("tile edges only", 1, 2, 602, 128, 0, None, _edge_mask),
 ]
 
 
