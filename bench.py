@@ -20,6 +20,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -66,9 +67,24 @@ def decode_flops(w, lens) -> float:
     return 4.0 * w.d * w.H * float(sum(int(min(max(int(x), 0), w.Skv)) for x in lens))
 
 
+def kernel_stats(attn, kernels):
+    """Per-launch HIP-event durations of the named library kernels since the
+    last profile reset: {name: {"ms": mean, "median_us", "min_us", "n"}}
+    (ms is NaN for a kernel that did not run)."""
+    res = {}
+    for k in kernels:
+        t = attn.profile_samples(k)
+        if t:
+            res[k] = {"ms": sum(t) / len(t), "median_us": 1e3 * statistics.median(t),
+                      "min_us": 1e3 * min(t), "n": len(t)}
+        else:
+            res[k] = {"ms": float("nan"), "median_us": None, "min_us": None, "n": 0}
+    return res
+
+
 def timed_calls(attn, fn, steps, warmup, kernels):
-    """Run fn warmup + steps times; the average HIP-event duration (ms) of
-    each named library kernel over the timed calls."""
+    """Run fn warmup + steps times; per-launch statistics of each named
+    library kernel over the timed calls (see kernel_stats)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -77,9 +93,17 @@ def timed_calls(attn, fn, steps, warmup, kernels):
     for _ in range(steps):
         fn()
     torch.cuda.synchronize()
-    prof = attn.profile_read()
+    st = kernel_stats(attn, kernels)
     attn.profile_enable(False)
-    return {k: (prof[k][1] / prof[k][0] if prof[k][0] else float("nan")) for k in kernels}
+    return st
+
+
+def op_stats(st, kernels):
+    """Mean ms of one call made of the named kernels (those that ran), and the
+    median and min of the per-call sums."""
+    ran = [k for k in kernels if st[k]["n"]]
+    ms = sum(st[k]["ms"] for k in ran)
+    return ms, sum(st[k]["median_us"] for k in ran), sum(st[k]["min_us"] for k in ran)
 
 
 def gqa_decode_sweep(attn, W, dev, steps, warmup,
@@ -94,18 +118,20 @@ def gqa_decode_sweep(attn, W, dev, steps, warmup,
     have = have or {}
     for name in names:
         w = W.WORKLOADS[name]
-        x = have[name] if name in have else W.device_inputs(w, dev)
+        x = have[name] if name in have else W.device_inputs(w, dev, digest=True)
         out = torch.empty_like(x["q"])
         fn = lambda: attn.fwd(x["q"], x["k"], x["v"], out, causal=w.causal,
                               kv_lens=x["kv_lens"], scale=x["scale"])
-        t = timed_calls(attn, fn, steps, warmup, ("decode_bf16_partial", "decode_bf16_combine"))
-        ms = t["decode_bf16_partial"] + t["decode_bf16_combine"]
+        kern = ("decode_bf16_partial", "decode_bf16_combine")
+        t = timed_calls(attn, fn, steps, warmup, kern)
+        ms, med, mn = op_stats(t, kern)
         lens = x["kv_lens_host"]
         nbytes, flops = decode_bytes(w, lens), decode_flops(w, lens)
-        p_ms = t["decode_bf16_partial"]
+        p_ms = t["decode_bf16_partial"]["ms"]
         kv_bytes = nbytes - 2 * 2 * w.B * w.H * w.d  # what the partial kernel reads
         kernel = "decode_bf16_partial"  # the stream kernel, at every K/V head count
         rows.append({"workload": name, "H": w.H, "H_kv": w.kv_heads, "ms_per_call": ms,
+                     "median_us": med, "min_us": mn, "sha256": x.get("sha256"),
                      "GB/s": nbytes / (ms * 1e-3) / 1e9, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
                      "intensity_flop_per_byte": flops / nbytes,
                      "roofline": {"kernel": kernel, "bound": "hbm",
@@ -131,11 +157,12 @@ def prefill_sweep(attn, W, dev, steps, warmup):
         x = W.device_inputs(w, dev)
         out = torch.empty_like(x["q"])
         fn = lambda: attn.fwd(x["q"], x["k"], x["v"], out, causal=True, scale=x["scale"])
-        t = timed_calls(attn, fn, steps, warmup, ("prefill_bf16_mfma", "prefill_bf16_combine"))
-        comb = t["prefill_bf16_combine"]
-        ms = t["prefill_bf16_mfma"] + (0.0 if math.isnan(comb) else comb)
+        kern = ("prefill_bf16_mfma", "prefill_bf16_combine")
+        t = timed_calls(attn, fn, steps, warmup, kern)
+        ms, med, mn = op_stats(t, kern)  # the combine runs only with key splits
         flops = prefill_flops(w)
-        rows.append({"S": S, "ms_per_call": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+        rows.append({"S": S, "ms_per_call": ms, "median_us": med, "min_us": mn,
+                     "TFLOP/s": flops / (ms * 1e-3) / 1e12,
                      "key_splits": attn.workspace_bytes(1, 32, S, S, 128, attn.BF16) > 0})
         del x, out
         torch.cuda.empty_cache()
@@ -151,16 +178,18 @@ def prefill_configs(attn, W, dev, steps, warmup,
     rows = []
     for name in names:
         w = W.WORKLOADS[name]
-        x = W.device_inputs(w, dev)
+        x = W.device_inputs(w, dev, digest=True)
         out = torch.empty_like(x["q"])
         fn = lambda: attn.fwd(x["q"], x["k"], x["v"], out, causal=w.causal,
                               kv_lens=x["kv_lens"], scale=x["scale"])
-        t = timed_calls(attn, fn, steps, warmup, ("prefill_bf16_mfma", "prefill_bf16_combine"))
-        ms = sum(v for v in t.values() if not math.isnan(v))  # the combine runs only with splits
+        kern = ("prefill_bf16_mfma", "prefill_bf16_combine")
+        t = timed_calls(attn, fn, steps, warmup, kern)
+        ms, med, mn = op_stats(t, kern)  # the combine runs only with key splits
         flops = prefill_flops(w, x["kv_lens_host"])
         tflops = flops / (ms * 1e-3) / 1e12
         rows.append({"workload": name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "S": w.Sq,
-                     "d": w.d, "ms_per_call": ms, "TFLOP/s": tflops,
+                     "d": w.d, "ms_per_call": ms, "median_us": med, "min_us": mn,
+                     "sha256": x["sha256"], "TFLOP/s": tflops,
                      "frac": tflops / PEAK_BF16_TFLOPS, "flop_per_call": flops})
         del x, out
         torch.cuda.empty_cache()
@@ -202,10 +231,10 @@ def mask_runs(attn, W, runs, steps, warmup):
             fn = lambda: attn.fwd(x["q"], x["k"], x["v"], out, causal=w.causal,
                                   kv_lens=x["kv_lens"], scale=x["scale"], mask=tm)
             t = timed_calls(attn, fn, steps, warmup, kernels)
-            ms = sum(v for v in t.values() if not math.isnan(v))  # kernels a call did not launch
+            ms, med, mn = op_stats(t, kernels)  # kernels a call did not launch are left out
             base = ms if base is None else base
-            row = {"workload": w.name, "mask": label, "ms_per_call": ms,
-                   "time_vs_unmasked": ms / base}
+            row = {"workload": w.name, "mask": label, "ms_per_call": ms, "median_us": med,
+                   "min_us": mn, "time_vs_unmasked": ms / base}
             if kind == "prefill":
                 if m is None:
                     flops = prefill_flops(w, x["kv_lens_host"])
@@ -281,24 +310,78 @@ def parse():
                          "the step, under their own keys)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0,
-                    help="oracle threads for the CPU baseline (default min(16, cores))")
+                    help="oracle threads for the CPU baseline (default: every CPU the "
+                         "process may use)")
     return ap.parse_args()
 
 
+def host_cores():
+    """(logical CPUs of the host, CPUs this process may run on)."""
+    n = os.cpu_count() or 1
+    try:
+        return n, len(os.sched_getaffinity(0))
+    except AttributeError:
+        return n, n
+
+
 def cpu_baseline(threads: int):
-    """Time the oracle on the prefill workload (B=1, H=32, S=4096, d=128,
-    causal), all 32 heads, one thread per head up to `threads`."""
+    """The float64 CPU oracle (as it stands, one thread per (b, h) slice up
+    to `threads`) timed on every configuration: the tiny fp32 causal problem,
+    mha768 and prefill4096 whole, padded2048 on 4 heads of each batch item,
+    decode8192 on 2 heads of each batch item (a bounded sample: about 10 s of
+    CPU work in all).  Prefill rows give GFLOP/s of 4*d flops per visible
+    pair, the decode row GB/s of the bytes the decode reads and writes (valid
+    K/V rows, q, out, lengths).  Returns the prefill4096 row (the headline's
+    workload) with every row under "configs"."""
     import oracle
     import workloads as W
-    w = W.WORKLOADS[PREFILL]
-    x = W.make_inputs(w)
-    t0 = time.perf_counter()
-    oracle.attention(x["q"], x["k"], x["v"], x["scale"], w.causal, None, nthreads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": prefill_flops(w) / dt / 1e12, "unit": "TFLOP/s",
-            "cores": min(threads, w.B * w.H), "kind": "oracle",
-            "sample": f"all {w.H} heads of {PREFILL} (B=1, S=4096, d=128, causal), float64, "
-                      f"{dt:.2f} s wall"}
+    nproc, usable = host_cores()
+
+    def run(name, pairs=None):
+        w = W.WORKLOADS[name]
+        x = W.make_inputs(w, pairs)
+        lens = x["kv_lens"]
+        t0 = time.perf_counter()
+        oracle.attention(x["q"], x["k"], x["v"], x["scale"], w.causal, lens, nthreads=threads)
+        dt = time.perf_counter() - t0
+        slices = x["q"].shape[0] * x["q"].shape[1]
+        sub = W.Workload(name, x["q"].shape[0], x["q"].shape[1], w.Sq, w.Skv, w.d, w.dtype,
+                         w.causal, w.seed, Hkv=x["k"].shape[1])
+        row = {"workload": name, "seconds": dt, "threads": min(threads, slices),
+               "sample": "all (b, h) slices" if pairs is None else
+               f"{len(pairs)} of {w.B * w.H} (b, h) slices"}
+        if w.Sq == 1:
+            row["GB/s"] = decode_bytes(sub, lens) / dt / 1e9
+        else:
+            row["GFLOP/s"] = prefill_flops(sub, lens) / dt / 1e9
+        return row
+
+    rows = [run("tiny_f32"), run("mha768_bf16"), run(PREFILL),
+            run("padded2048_bf16", [(b, h) for b in range(8) for h in (0, 8, 16, 24)]),
+            run(DECODE, [(b, h) for b in range(64) for h in (0, 16)])]
+    head = rows[2]
+    return {"value": head["GFLOP/s"] / 1e3, "unit": "TFLOP/s", "cores": head["threads"],
+            "nproc": nproc, "usable_cpus": usable, "kind": "oracle",
+            "sample": f"all 32 heads of {PREFILL} (B=1, S=4096, d=128, causal), float64, "
+                      f"{head['seconds']:.2f} s wall on {head['threads']} threads",
+            "configs": rows}
+
+
+def sweep_slopes(rows):
+    """Exponent of time in S from the prefill sweep: log2 of the time ratio
+    of each doubling, and the least-squares slope of log time on log S over
+    S >= 1024 (exercise D of "Attention from First Principles", section 10:
+    the work grows as S^2)."""
+    pts = [(r["S"], r["ms_per_call"]) for r in rows]
+    seg = [{"from": a[0], "to": b[0], "exponent": math.log2(b[1] / a[1])}
+           for a, b in zip(pts, pts[1:])]
+    big = [(math.log2(S), math.log2(t)) for S, t in pts if S >= 1024]
+    fit = None
+    if len(big) >= 2:
+        mx = sum(x for x, _ in big) / len(big)
+        my = sum(y for _, y in big) / len(big)
+        fit = sum((x - mx) * (y - my) for x, y in big) / sum((x - mx) ** 2 for x, _ in big)
+    return {"per_doubling": seg, "fit_S_ge_1024": fit}
 
 
 def main():
@@ -323,13 +406,13 @@ def main():
     if "prefill" in parts:
         w = W.WORKLOADS[PREFILL]
         print(f"[bench] preparing {w.name}", file=sys.stderr, flush=True)
-        x = W.device_inputs(w, dev)
+        x = W.device_inputs(w, dev, digest=True)
         out = torch.empty_like(x["q"])
         runs.append(("prefill", w, x, out))
     if "decode" in parts:
         w = W.WORKLOADS[DECODE]
         print(f"[bench] preparing {w.name}", file=sys.stderr, flush=True)
-        x = W.device_inputs(w, dev)
+        x = W.device_inputs(w, dev, digest=True)
         out = torch.empty_like(x["q"])
         runs.append(("decode", w, x, out))
 
@@ -357,13 +440,13 @@ def main():
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    prof = attn.profile_read()
+    st = kernel_stats(attn, ("prefill_bf16_mfma", "decode_bf16_partial", "decode_bf16_combine"))
+    step_prefill_us = [round(1e3 * t, 1) for t in attn.profile_samples("prefill_bf16_mfma")]
     attn.profile_enable(False)
     ms_per_step = wall * 1e3 / args.steps
 
     def avg_ms(name):
-        n, ms = prof[name]
-        return ms / n if n else float("nan")
+        return st[name]["ms"]
 
     result = {
         "metric": "attn fwd TFLOP/s (causal prefill) + KV-read GB/s (decode), 1×MI355X",
@@ -381,11 +464,15 @@ def main():
             tflops = flops / (kms * 1e-3) / 1e12
             result["value"] = tflops
             result["config"]["prefill"] = cfg
+            cfg["sha256"] = x["sha256"]
             result["roofline"] = {
                 "kernel": "prefill_bf16_mfma", "bound": "mfma", "achieved": tflops,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
                 "traffic": profiled_traffic("prefill_bf16_mfma", w.name),
-                "algorithmic_flop_per_launch": flops, "avg_launch_ms": kms}
+                "algorithmic_flop_per_launch": flops, "avg_launch_ms": kms,
+                "median_us": st["prefill_bf16_mfma"]["median_us"],
+                "min_us": st["prefill_bf16_mfma"]["min_us"],
+                "launch_us": step_prefill_us}
         else:
             lens = x["kv_lens_host"]
             nbytes = decode_bytes(w, lens)
@@ -396,6 +483,7 @@ def main():
             gbs_k = kv_bytes / (p_ms * 1e-3) / 1e9
             cfg["kv_len_range"] = list(w.kv_len_range)
             cfg["sum_kv_len"] = int(np.sum(lens))
+            cfg["sha256"] = x["sha256"]
             result["config"]["decode"] = cfg
             result["decode"] = {
                 "metric": "KV-read GB/s (decode)", "value": gbs_op, "unit": "GB/s",
@@ -405,8 +493,14 @@ def main():
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs_k / PEAK_HBM_GBS,
                     "traffic": profiled_traffic("decode_bf16_partial", w.name),
                     "algorithmic_bytes_per_launch": kv_bytes,
-                    "avg_launch_ms": p_ms},
+                    "avg_launch_ms": p_ms,
+                    "median_us": st["decode_bf16_partial"]["median_us"],
+                    "min_us": st["decode_bf16_partial"]["min_us"]},
                 "combine_avg_launch_ms": c_ms,
+                "median_us": st["decode_bf16_partial"]["median_us"] +
+                (st["decode_bf16_combine"]["median_us"] or 0.0),
+                "min_us": st["decode_bf16_partial"]["min_us"] +
+                (st["decode_bf16_combine"]["min_us"] or 0.0),
             }
     if result["value"] is None and "decode" in result:
         result["value"] = result["decode"]["value"]
@@ -429,9 +523,10 @@ def main():
     if "sweep" in parts:
         print("[bench] prefill S sweep", file=sys.stderr, flush=True)
         result["prefill_sweep"] = prefill_sweep(attn, W, dev, args.steps, args.warmup)
+        result["prefill_sweep_slope"] = sweep_slopes(result["prefill_sweep"])
 
     if not args.no_cpu_baseline and "prefill" in parts:
-        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        threads = args.cpu_threads or host_cores()[1]
         print(f"[bench] cpu baseline with {threads} threads", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(threads)
     print(json.dumps(result), flush=True)

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 typedef enum {
     ATTN_OK = 0,
@@ -101,10 +101,11 @@ typedef enum {
  * scale: the logit multiplier, normally 1/sqrt(d) ("Self-Attention",
  * section "Why divide by sqrt(d_k)?"); it must be finite and > 0, the only
  * values the pages use (else ATTN_E_ARG).  causal: 0 or nonzero.
- * Temporary memory comes from a library-owned workspace on the current
- * device, grown on demand (the call that grows it synchronizes the device
- * first).  Calls that use the library workspace must not run concurrently
- * on different streams of one device; use attn_fwd_ws for that.
+ * Temporary memory comes from a library-owned workspace kept per (device,
+ * stream) pair and grown on demand; the call that grows it first waits for
+ * the earlier work on its stream.  Calls on different streams therefore
+ * never share temporary memory and may run concurrently.  attn_release
+ * frees these workspaces.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq,
              int Skv, int d, float scale, int causal, const int32_t* kv_lens, int dtype,
@@ -221,7 +222,7 @@ int attn_validate(const void* q, const void* k, const void* v, void* out, int B,
 
 /*
  * attn_kernel_for -- name of the kernel family attn_fwd would launch for
- * these sizes ("prefill_bf16_mfma", "decode_bf16_splitkv", "generic_f32"),
+ * these sizes ("prefill_bf16_mfma", "decode_bf16_stream", "generic_f32"),
  * or NULL when the request is invalid or unsupported.  Makes no HIP call.
  * The string is static.
  */
@@ -251,6 +252,10 @@ int attn_profile_enable(int on);
 int attn_profile_reset(void);
 int attn_profile_read(int kernel, long* launches, double* total_ms);
 const char* attn_profile_name(int kernel); /* NULL past the last kernel */
+/* The individual durations (milliseconds, launch order) of the first `cap`
+   recorded launches of family `kernel` go to ms[0 .. cap-1]; *launches gets
+   the number recorded since the last reset.  Synchronizes on their events. */
+int attn_profile_samples(int kernel, double* ms, long cap, long* launches);
 
 #ifdef __cplusplus
 }

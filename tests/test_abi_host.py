@@ -80,7 +80,7 @@ def test_kernel_choice():
     assert attn.kernel_for(4096, 4096, 128, BF16) == "prefill_bf16_mfma"
     assert attn.kernel_for(512, 512, 64, BF16) == "prefill_bf16_mfma"
     assert attn.kernel_for(2, 9, 64, BF16) == "prefill_bf16_mfma"
-    assert attn.kernel_for(1, 8192, 128, BF16) == "decode_bf16_splitkv"
+    assert attn.kernel_for(1, 8192, 128, BF16) == "decode_bf16_stream"
     assert attn.kernel_for(64, 64, 16, F32) == "generic_f32"
     assert attn.kernel_for(1, 64, 16, F32) == "generic_f32"
     assert attn.kernel_for(4, 4, 48, BF16) is None
@@ -241,3 +241,4 @@ def test_masked_prefill_workspace():
     # beyond the list size the marks are not used
     assert attn.workspace_bytes(1, 1, 64, 200000, 128, BF16, masked=True) == \
         attn.workspace_bytes(1, 1, 64, 200000, 128, BF16)
+

@@ -26,8 +26,12 @@ def _stub_timing(monkeypatch):
         fn()
         calls.append(kernels)
         # the mask pre-passes are absent from an unmasked call, as on the GPU
-        return {k: (math.nan if k.endswith("_mask_tiles") and not _Attn.masked else 1.0)
-                for k in kernels}
+        res = {}
+        for k in kernels:
+            ran = not (k.endswith("_mask_tiles") and not _Attn.masked)
+            res[k] = {"ms": 1.0 if ran else math.nan, "median_us": 900.0 if ran else None,
+                      "min_us": 800.0 if ran else None, "n": 3 if ran else 0}
+        return res
 
     monkeypatch.setattr(bench, "timed_calls", timed)
     return calls
@@ -44,7 +48,7 @@ def _inputs(w):
     lens = W.kv_lens_for(w)
     return {"q": None, "k": None, "v": None, "scale": 1.0 / math.sqrt(w.d),
             "kv_lens": None if lens is None else np.asarray(lens, dtype=np.int32),
-            "kv_lens_host": None if lens is None else [int(x) for x in lens]}
+            "kv_lens_host": None if lens is None else [int(x) for x in lens], "sha256": "0" * 64}
 
 
 def test_mask_rows(monkeypatch):
@@ -107,4 +111,34 @@ def test_prefill_config_rows(monkeypatch):
     for r in rows:
         # the stub times the prefill and the split-combine kernel at 1 ms each
         assert r["ms_per_call"] == 2.0 and r["frac"] == r["TFLOP/s"] / bench.PEAK_BF16_TFLOPS
+        assert r["median_us"] == 1800.0 and r["min_us"] == 1600.0 and len(r["sha256"]) == 64
+
+
+def test_sweep_slopes():
+    # time growing as S^2 from S = 1024 on gives exponents of 2 and a fit of 2
+    rows = [{"S": S, "ms_per_call": 0.01 * max(1.0, (S / 1024) ** 2)}
+            for S in (128, 256, 512, 1024, 2048, 4096, 8192)]
+    sl = bench.sweep_slopes(rows)
+    assert [round(x["exponent"], 6) for x in sl["per_doubling"]] == [0, 0, 0, 2, 2, 2]
+    assert abs(sl["fit_S_ge_1024"] - 2.0) < 1e-12
+
+
+def test_cpu_baseline_rows(monkeypatch):
+    """Every configuration gets an oracle row: GFLOP/s for prefill (visible
+    pairs of the timed slices), GB/s for decode (their K/V rows, q, out,
+    lengths); the oracle itself is stubbed here."""
+    import oracle
+    seen = []
+    monkeypatch.setattr(oracle, "attention",
+                        lambda q, k, v, scale, causal, lens, nthreads=0: seen.append(q.shape))
+    res = bench.cpu_baseline(4)
+    rows = {r["workload"]: r for r in res["configs"]}
+    assert set(rows) == {"tiny_f32", "mha768_bf16", "prefill4096_bf16", "padded2048_bf16",
+                         "decode8192_bf16"}
+    assert seen[2] == (1, 32, 4096, 128) and seen[3][:2] == (32, 1) and seen[4][:2] == (128, 1)
+    for name, r in rows.items():
+        assert r["seconds"] > 0 and r["threads"] <= 4
+        assert ("GB/s" in r) == (name == "decode8192_bf16")
+    assert res["unit"] == "TFLOP/s" and res["nproc"] >= 1 and res["cores"] == 4
+    assert res["value"] == rows["prefill4096_bf16"]["GFLOP/s"] / 1e3
 

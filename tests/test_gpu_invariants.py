@@ -147,3 +147,29 @@ def test_repeat_runs_are_bitwise_stable():
     _, a = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], 1)
     _, b = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], 1)
     assert np.array_equal(_bits(a), _bits(b))
+
+
+def test_library_workspace_per_stream():
+    """Two decodes enqueued on two streams with the library-owned workspace
+    (attn_fwd with no workspace argument) run concurrently without sharing
+    temporary memory: each gives the bits of the same call run alone."""
+    import torch
+    probs = [W.random_problem(13 + i, 4, 8, 1, 3000, 128, "bf16", [3000, 1500, 2999, 700])
+             for i in range(2)]
+    lens = torch.tensor([3000, 1500, 2999, 700], dtype=torch.int32, device="cuda")
+    xs = [[W.to_torch(p[x]) for x in ("q", "k", "v")] for p in probs]
+    alone = []
+    for q, k, v in xs:
+        alone.append(attn.fwd(q, k, v, kv_lens=lens, causal=False))
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty_like(a) for a in alone]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for rep in range(20):
+        for (q, k, v), s, o in zip(xs, streams, outs):
+            with torch.cuda.stream(s):
+                attn.fwd(q, k, v, o, kv_lens=lens, causal=False)
+    torch.cuda.synchronize()
+    for o, a in zip(outs, alone):
+        assert torch.equal(o.view(torch.int16), a.view(torch.int16))

@@ -116,7 +116,7 @@ DECODE_CASES = [
 def test_bf16_decode_shapes(case):
     seed, B, H, Sq, Skv, d, causal, lens = case
     _say("decode case", case)
-    assert attn.kernel_for(Sq, Skv, d, attn.BF16) == "decode_bf16_splitkv"
+    assert attn.kernel_for(Sq, Skv, d, attn.BF16) == "decode_bf16_stream"
     prob = W.random_problem(seed, B, H, Sq, Skv, d, "bf16", lens)
     check_problem(prob, causal, BF16_TOL, f"decode {case}")
 

@@ -47,12 +47,17 @@ int check_shape(int B, int H, int Hkv, int Sq, int Skv, int d, int dv) {
     return ATTN_OK;
 }
 
-struct DeviceWorkspace {
-    void* ptr = nullptr;
-    size_t bytes = 0;
+// Library-owned workspaces, one per (device, stream): calls on different
+// streams never share temporary memory, and calls on one stream are ordered
+// by the stream itself.
+struct StreamWorkspace {
+    int device;
+    hipStream_t stream;
+    void* ptr;
+    size_t bytes;
 };
 std::mutex g_ws_mu;
-std::vector<DeviceWorkspace> g_ws;  // indexed by device ordinal
+std::vector<StreamWorkspace> g_ws;
 
 // ---- timing -------------------------------------------------------------
 struct Record {
@@ -93,6 +98,24 @@ class EventTimer final : public KernelTimer {
         }
         if (launches) *launches = n;
         if (total_ms) *total_ms = ms;
+        return ATTN_OK;
+    }
+    // Durations (ms) of the first `cap` recorded launches of `kernel`, in
+    // launch order; *n receives the number of recorded launches.
+    int samples(int kernel, double* ms_out, long cap, long* n_out) {
+        std::lock_guard<std::mutex> g(mu_);
+        long n = 0;
+        for (const Record& r : done_) {
+            if (r.kernel != kernel) continue;
+            if (n < cap && ms_out != nullptr) {
+                if (hipEventSynchronize(r.stop) != hipSuccess) return ATTN_E_LAUNCH;
+                float t = 0.0f;
+                if (hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess) return ATTN_E_LAUNCH;
+                ms_out[n] = t;
+            }
+            ++n;
+        }
+        if (n_out) *n_out = n;
         return ATTN_OK;
     }
     void reset() {
@@ -179,23 +202,29 @@ int run(const void* q, const void* k, const void* v, void* out, int B, int H, in
         if (need > 0) {
             int dev = 0;
             if (hipGetDevice(&dev) != hipSuccess) return ATTN_E_LAUNCH;
+            const hipStream_t hs = static_cast<hipStream_t>(stream);
             std::lock_guard<std::mutex> g(g_ws_mu);
-            if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
-            DeviceWorkspace& w = g_ws[dev];
-            if (w.bytes < need) {
-                // earlier calls may still be using the old buffer
-                if (hipDeviceSynchronize() != hipSuccess) return ATTN_E_LAUNCH;
-                if (w.ptr) (void)hipFree(w.ptr);
-                w.ptr = nullptr;
-                w.bytes = 0;
-                if (hipMalloc(&w.ptr, need) != hipSuccess) {
-                    w.ptr = nullptr;
+            StreamWorkspace* w = nullptr;
+            for (StreamWorkspace& x : g_ws)
+                if (x.device == dev && x.stream == hs) w = &x;
+            if (w == nullptr) {
+                g_ws.push_back(StreamWorkspace{dev, hs, nullptr, 0});
+                w = &g_ws.back();
+            }
+            if (w->bytes < need) {
+                // earlier calls on this stream may still be using the old buffer
+                if (hipStreamSynchronize(hs) != hipSuccess) return ATTN_E_LAUNCH;
+                if (w->ptr) (void)hipFree(w->ptr);
+                w->ptr = nullptr;
+                w->bytes = 0;
+                if (hipMalloc(&w->ptr, need) != hipSuccess) {
+                    w->ptr = nullptr;
                     return ATTN_E_NOMEM;
                 }
-                w.bytes = need;
+                w->bytes = need;
             }
-            workspace = w.ptr;
-            workspace_bytes = w.bytes;
+            workspace = w->ptr;
+            workspace_bytes = w->bytes;
         }
     } else {
         if (workspace_bytes < need) return ATTN_E_WORKSPACE;
@@ -245,7 +274,7 @@ const char* attn_kernel_for(int Sq, int Skv, int d, int dtype) {
     switch (choose_path(Sq, d, dtype, d)) {
         case kPathGenericF32: return "generic_f32";
         case kPathPrefill: return "prefill_bf16_mfma";
-        case kPathDecode: return "decode_bf16_splitkv";
+        case kPathDecode: return "decode_bf16_stream";
         default: return nullptr;
     }
 }
@@ -352,13 +381,13 @@ void attn_release(void) {
     std::lock_guard<std::mutex> g(g_ws_mu);
     int cur = 0;
     const bool have_cur = hipGetDevice(&cur) == hipSuccess;
-    for (size_t dev = 0; dev < g_ws.size(); ++dev) {
-        if (g_ws[dev].ptr) {
-            (void)hipSetDevice((int)dev);
-            (void)hipFree(g_ws[dev].ptr);
+    for (StreamWorkspace& w : g_ws) {
+        if (w.ptr) {
+            (void)hipSetDevice(w.device);
+            (void)hipFree(w.ptr);
         }
-        g_ws[dev] = DeviceWorkspace{};
     }
+    g_ws.clear();
     if (have_cur) (void)hipSetDevice(cur);
 }
 
@@ -386,6 +415,17 @@ int attn_profile_read(int kernel, long* launches, double* total_ms) {
         return ATTN_OK;
     }
     return tm->read(kernel, launches, total_ms);
+}
+
+int attn_profile_samples(int kernel, double* ms, long cap, long* launches) {
+    if (kernel < 0 || kernel >= kNumKernels || cap < 0) return ATTN_E_ARG;
+    std::lock_guard<std::mutex> g(g_timer_mu);
+    EventTimer* tm = g_timer.load();
+    if (!tm) {
+        if (launches) *launches = 0;
+        return ATTN_OK;
+    }
+    return tm->samples(kernel, ms, cap, launches);
 }
 
 const char* attn_profile_name(int kernel) {

@@ -265,11 +265,15 @@ def bits_from_torch(t) -> np.ndarray:
     return t.cpu().numpy().view(np.uint32)
 
 
-def device_inputs(w: Workload, device="cuda", pad_fill: float = 0.0) -> dict:
+def device_inputs(w: Workload, device="cuda", pad_fill: float = 0.0, digest: bool = False) -> dict:
     """The workload's q, k, v as device tensors, drawn and uploaded one batch
     item at a time (bounded host memory), plus kv_lens (device int32 or None),
-    the host copy of the lengths, and scale."""
+    the host copy of the lengths, and scale.  With ``digest``, also "sha256":
+    the SHA-256 of the q, k and v bytes as uploaded (row-major [B,H,S,d], one
+    tensor after the other) followed by the int32 lengths, if any."""
+    import hashlib
     import torch
+    h = hashlib.sha256() if digest else None
     lens = kv_lens_for(w)
     tdtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
     res = {}
@@ -281,8 +285,14 @@ def device_inputs(w: Workload, device="cuda", pad_fill: float = 0.0) -> dict:
             # one query head per K/V head selects that K/V head's slice
             pairs = [(b, h * (1 if name == "q" else group)) for h in range(heads)]
             part = make_tensor(w, name, lens, pairs=pairs, pad_fill=pad_fill)
+            if h is not None:
+                h.update(memoryview(np.ascontiguousarray(part)).cast("B"))
             t[b].copy_(to_torch(part.reshape(heads, S, w.d), device))
         res[name] = t
+    if h is not None:
+        if lens is not None:
+            h.update(np.ascontiguousarray(lens, dtype=np.int32).tobytes())
+        res["sha256"] = h.hexdigest()
     res["kv_lens"] = None if lens is None else torch.from_numpy(lens).to(device)
     res["kv_lens_host"] = lens
     res["scale"] = w.scale
