@@ -78,7 +78,9 @@ typedef enum {
     ATTN_E_WORKSPACE = 6,   /* caller workspace smaller than attn_workspace_bytes() */
     ATTN_E_ARG = 7,         /* scale is not finite and > 0 */
     ATTN_E_LAUNCH = 8,      /* a HIP call or kernel launch failed */
-    ATTN_E_NOMEM = 9        /* the library could not allocate its workspace */
+    ATTN_E_NOMEM = 9,       /* the library could not allocate its workspace */
+    ATTN_E_SCRATCH = 10     /* attn_fwd_noalloc: the problem needs more temporary memory
+                               than the fixed scratch area holds */
 } attn_status;
 
 typedef enum {
@@ -212,6 +214,28 @@ int attn_validate_ex(const void* q, const void* k, const void* v, void* out, int
                      int H_kv, int Sq, int Skv, int d, int d_v, float scale, int causal,
                      const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int64_t mask_si,
                      int dtype);
+
+/*
+ * attn_fwd_noalloc -- attn_fwd_ex for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without the workspace, whose role is
+ * taken by a fixed scratch array of attn_noalloc_scratch_bytes() bytes that
+ * the library's code object holds on every device it runs on, from load until
+ * the process ends.  The call allocates and frees nothing.  A problem whose
+ * temporary memory (attn_workspace_bytes_ex) exceeds the array returns
+ * ATTN_E_SCRATCH before enqueueing anything; other errors as attn_fwd_ex.
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents: two calls whose work may overlap on one device (calls on
+ * different streams, or from different host threads) race on it and give
+ * undefined results.  Order such calls on one stream.
+ */
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, int B, int H,
+                     int H_kv, int Sq, int Skv, int d, int d_v, float scale, int causal,
+                     const int32_t* kv_lens, const uint8_t* mask, int64_t mask_sb,
+                     int64_t mask_sh, int64_t mask_si, int dtype, void* stream);
+
+/* Size in bytes of the scratch array attn_fwd_noalloc uses on each device. */
+size_t attn_noalloc_scratch_bytes(void);
 
 /*
  * attn_validate -- the host-side checks of attn_fwd alone: returns what

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     assert attn.abi_version() == attn.ABI_VERSION
-    for s in range(10):
+    for s in range(11):
         assert attn.status_string(s) and attn.status_string(s) != "unknown status"
     assert attn.status_string(99) == "unknown status"
 
@@ -242,3 +242,23 @@ def test_masked_prefill_workspace():
     assert attn.workspace_bytes(1, 1, 64, 200000, 128, BF16, masked=True) == \
         attn.workspace_bytes(1, 1, 64, 200000, 128, BF16)
 
+
+def test_noalloc_refuses_problems_beyond_the_scratch_array():
+    """attn_fwd_noalloc checks the problem's temporary memory against its
+    fixed scratch array on the host, before any HIP call: a decode whose
+    partials exceed the array is refused with ATTN_E_SCRATCH."""
+    lib = attn.library()
+    cap = attn.noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    B, H, Hkv, Skv, d = 4096, 32, 1, 8192, 128
+    assert attn.workspace_bytes(B, H, 1, Skv, d, BF16, kv_heads=Hkv) > cap
+    rc = lib.attn_fwd_noalloc(A, A, A, A, B, H, Hkv, 1, Skv, d, d, ctypes.c_float(0.088), 0,
+                              None, None, 0, 0, 0, BF16, None)
+    assert rc == attn.E_SCRATCH, attn.status_string(rc)
+    # the argument checks of attn_fwd_ex come first
+    rc = lib.attn_fwd_noalloc(A, A, A, None, B, H, Hkv, 1, Skv, d, d, ctypes.c_float(0.088), 0,
+                              None, None, 0, 0, 0, BF16, None)
+    assert rc == attn.E_NULL
+    rc = lib.attn_fwd_noalloc(A, A, A, A, B, H, 3, 1, Skv, d, d, ctypes.c_float(0.088), 0,
+                              None, None, 0, 0, 0, BF16, None)
+    assert rc == attn.E_SHAPE

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["attn_api.cpp", "generic_f32.hip", "prefill_bf16.hip", "decode_bf16.hip"]
+SOURCES = ["attn_api.cpp", "generic_f32.hip", "prefill_bf16.hip", "decode_bf16.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -246,6 +246,15 @@ int run(const void* q, const void* k, const void* v, void* out, int B, int H, in
 
 }  // namespace
 
+int run_with_workspace(const void* q, const void* k, const void* v, void* out, int B, int H,
+                       int Hkv, int Sq, int Skv, int d, int dv, float scale, int causal,
+                       const int32_t* kv_lens, const uint8_t* mask, int64_t msb, int64_t msh,
+                       int64_t msi, int dtype, void* stream, void* workspace,
+                       size_t workspace_bytes) {
+    return run(q, k, v, out, B, H, Hkv, Sq, Skv, d, scale, causal, kv_lens, dtype, stream,
+               workspace, workspace_bytes, false, mask, msb, msh, msi, dv);
+}
+
 KernelTimer* active_timer() {
     return g_timing_on.load(std::memory_order_acquire) ? g_timer.load(std::memory_order_acquire)
                                                        : nullptr;
@@ -371,6 +380,9 @@ const char* attn_status_string(int status) {
         case ATTN_E_ARG: return "scale is not finite and positive";
         case ATTN_E_LAUNCH: return "HIP launch or runtime failure";
         case ATTN_E_NOMEM: return "device allocation failed";
+        case ATTN_E_SCRATCH:
+            return "problem needs more temporary memory than the fixed scratch area "
+                   "(attn_noalloc_scratch_bytes) holds";
         default: return "unknown status";
     }
 }

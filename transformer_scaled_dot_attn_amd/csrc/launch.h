@@ -58,6 +58,13 @@ enum KernelId { kPrefillBf16 = 0, kDecodePartialBf16 = 1, kDecodeCombineBf16 = 2
                 kPrefillCombineBf16 = 4, kPrefillMaskTiles = 5, kDecodeMaskTiles = 6,
                 kNumKernels = 7 };
 
+// attn_fwd_ex on a caller-supplied workspace (checks, kernel choice, launch).
+int run_with_workspace(const void* q, const void* k, const void* v, void* out, int B, int H,
+                       int Hkv, int Sq, int Skv, int d, int dv, float scale, int causal,
+                       const int32_t* kv_lens, const uint8_t* mask, int64_t msb, int64_t msh,
+                       int64_t msi, int dtype, void* stream, void* workspace,
+                       size_t workspace_bytes);
+
 hipError_t launch_generic_f32(const LaunchArgs& a);
 hipError_t launch_prefill_bf16(const LaunchArgs& a);
 hipError_t launch_decode_bf16(const LaunchArgs& a);
