@@ -308,6 +308,8 @@ def parse():
                          "measures decode at 32, 8 and 1 K/V heads for 32 query heads; sweep "
                          "measures causal prefill over S = 128 .. 8192 (both reported beside "
                          "the step, under their own keys)")
+    ap.add_argument("--headline-first", action="store_true",
+                    help="time the step before the other parts (default: after them)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="oracle threads for the CPU baseline (default: every CPU the "
@@ -428,6 +430,33 @@ def main():
         if copy_src is not None:
             copy_dst.copy_(copy_src)
 
+    extra = {}
+
+    def secondary_parts():
+        if "gqa" in parts:
+            print("[bench] grouped-head decode sweep", file=sys.stderr, flush=True)
+            have = {w.name: x for kind, w, x, _ in runs if kind == "decode"}
+            extra["gqa_decode"] = gqa_decode_sweep(attn, W, dev, args.steps, args.warmup,
+                                                   have=have)
+        elif "gqa8" in parts:
+            extra["gqa_decode"] = gqa_decode_sweep(attn, W, dev, args.steps, args.warmup,
+                                                   names=("gqa_decode8192_bf16",))
+        if "masks" in parts and runs:
+            print("[bench] allowed-mask runs", file=sys.stderr, flush=True)
+            extra["masks"] = mask_runs(attn, W, runs, args.steps, args.warmup)
+        if "configs" in parts:
+            print("[bench] other prefill workloads", file=sys.stderr, flush=True)
+            extra["prefill_configs"] = prefill_configs(attn, W, dev, args.steps, args.warmup)
+        if "sweep" in parts:
+            print("[bench] prefill S sweep", file=sys.stderr, flush=True)
+            extra["prefill_sweep"] = prefill_sweep(attn, W, dev, args.steps, args.warmup)
+            extra["prefill_sweep_slope"] = sweep_slopes(extra["prefill_sweep"])
+
+    # The secondary measurements run first by default, so the step's timed
+    # region starts on a GPU already under load (see --headline-first).
+    if not args.headline_first:
+        secondary_parts()
+
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -507,23 +536,9 @@ def main():
         result["unit"] = "GB/s"
         result["roofline"] = result["decode"]["roofline"]
 
-    if "gqa" in parts:
-        print("[bench] grouped-head decode sweep", file=sys.stderr, flush=True)
-        have = {w.name: x for kind, w, x, _ in runs if kind == "decode"}
-        result["gqa_decode"] = gqa_decode_sweep(attn, W, dev, args.steps, args.warmup, have=have)
-    elif "gqa8" in parts:
-        result["gqa_decode"] = gqa_decode_sweep(attn, W, dev, args.steps, args.warmup,
-                                                names=("gqa_decode8192_bf16",))
-    if "masks" in parts and runs:
-        print("[bench] allowed-mask runs", file=sys.stderr, flush=True)
-        result["masks"] = mask_runs(attn, W, runs, args.steps, args.warmup)
-    if "configs" in parts:
-        print("[bench] other prefill workloads", file=sys.stderr, flush=True)
-        result["prefill_configs"] = prefill_configs(attn, W, dev, args.steps, args.warmup)
-    if "sweep" in parts:
-        print("[bench] prefill S sweep", file=sys.stderr, flush=True)
-        result["prefill_sweep"] = prefill_sweep(attn, W, dev, args.steps, args.warmup)
-        result["prefill_sweep_slope"] = sweep_slopes(result["prefill_sweep"])
+    if args.headline_first:
+        secondary_parts()
+    result.update(extra)
 
     if not args.no_cpu_baseline and "prefill" in parts:
         threads = args.cpu_threads or host_cores()[1]
