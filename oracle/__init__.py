@@ -63,6 +63,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_attn_fwd_weights_mask.argtypes = [p, p, p, i, p, p, i, i, i, i, i, i, i, d, i, p, p,
                                                  ll, ll, i]
     lib.oracle_attn_fwd_weights_mask.restype = i
+    lib.oracle_attn_fwd_ex.argtypes = [p, p, p, i, p, p, i, i, i, i, i, i, i, d, i, p, p, ll, ll,
+                                       p, ll, ll, i]
+    lib.oracle_attn_fwd_ex.restype = i
     lib.oracle_default_threads.argtypes = []
     lib.oracle_default_threads.restype = i
     return lib
@@ -89,8 +92,8 @@ def default_threads() -> int:
     return load().oracle_default_threads()
 
 
-def attention(q, k, v, scale, causal, kv_lens=None, *, mask=None, weights=False, nthreads=0,
-              lib=None):
+def attention(q, k, v, scale, causal, kv_lens=None, *, mask=None, bias=None, weights=False,
+              nthreads=0, lib=None):
     """Reference attention forward.
 
     q: [B,H,Sq,d], k: [B,Hkv,Skv,d], v: [B,Hkv,Skv,dv] numpy arrays of one
@@ -102,6 +105,8 @@ def attention(q, k, v, scale, causal, kv_lens=None, *, mask=None, weights=False,
     mask: None or an array broadcastable to [B,H,Sq,Skv]; nonzero where query
     row i of (b, h) may see key j (combined with the causal and length rules
     by logical AND).  It is expanded to the full [B,H,Sq,Skv] bytes here.
+    bias: None or an array of q's dtype broadcastable to [B,H,Sq,Skv], added
+    to the scaled logits before the softmax; -inf forbids the key.
     Returns out [B,H,Sq,dv] float64, and with weights=True also the weight
     tensor [B,H,Sq,Skv].
     """
@@ -131,6 +136,22 @@ def attention(q, k, v, scale, causal, kv_lens=None, *, mask=None, weights=False,
         lens_ptr = lens_arr.ctypes.data
     out = np.empty((B, H, Sq, dv), dtype=np.float64)
     code = DTYPE_CODES[q.dtype]
+    if bias is not None:
+        bias = np.asarray(bias)
+        if bias.dtype != q.dtype:
+            raise ValueError(f"bias must have q's dtype {q.dtype}, got {bias.dtype}")
+        bfull = np.ascontiguousarray(np.broadcast_to(bias, (B, H, Sq, Skv)))
+        m = None if mask is None else np.ascontiguousarray(
+            np.broadcast_to(np.asarray(mask) != 0, (B, H, Sq, Skv)), dtype=np.uint8)
+        w = np.empty((B, H, Sq, Skv), dtype=np.float64) if weights else None
+        rc = lib.oracle_attn_fwd_ex(
+            q.ctypes.data, k.ctypes.data, v.ctypes.data, code, out.ctypes.data,
+            None if w is None else w.ctypes.data, B, H, Hkv, Sq, Skv, d, dv, float(scale),
+            int(bool(causal)), lens_ptr, None if m is None else m.ctypes.data, H * Sq * Skv,
+            Sq * Skv, bfull.ctypes.data, H * Sq * Skv, Sq * Skv, int(nthreads))
+        if rc != 0:
+            raise ValueError(f"oracle error {rc}: {ERRORS.get(rc, 'unknown')}")
+        return (out, w) if weights else out
     if mask is not None:
         m = np.ascontiguousarray(np.broadcast_to(np.asarray(mask) != 0, (B, H, Sq, Skv)),
                                  dtype=np.uint8)

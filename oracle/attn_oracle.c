@@ -39,6 +39,14 @@
  * padding masks.  Element (b, h, i, j) is mask[b*sb + h*sh + i*Skv + j];
  * a stride of 0 broadcasts over that axis.
  *
+ * Additive bias: an optional array of the inputs' element type added to
+ * the scaled logits before the softmax, logit_ij = scale * q_i . k_j +
+ * bias_ij -- the float mask that "Attention from Scratch" (KubeDojo module
+ * 1.4.3), Part 7 describes as an additive bias, where a boolean mask only
+ * allows or forbids.  Element (b, h, i, j) is bias[b*bsb + h*bsh + i*Skv +
+ * j].  A bias of -inf forbids the key exactly as a False mask entry does
+ * (exactly zero weight; a row whose keys are all forbidden is 0).
+ *
  * Grouped heads (GQA / MQA): with H_kv key/value heads for H query heads
  * (H a multiple of H_kv), query head h reads key/value head h / (H / H_kv).
  * That is the grouping of "Attention from First Principles", section "MHA,
@@ -84,6 +92,8 @@ typedef struct {
     const int32_t* kv_lens;
     const uint8_t* mask;  /* optional allowed-mask, see above */
     long long mask_sb, mask_sh;
+    const void* bias;     /* optional additive bias (dtype elements), see above */
+    long long bias_sb, bias_sh;
     int next_pair;    /* work counter, guarded by mu */
     pthread_mutex_t mu;
 } job_t;
@@ -96,22 +106,30 @@ static int valid_len(const job_t* J, int b) {
     return (int)L;
 }
 
+/* The additive bias of (b, h, i, j), 0 without one. */
+static double bias_at(const job_t* J, int b, int h, int i, int j) {
+    if (!J->bias) return 0.0;
+    return load_elem(J->bias, J->dtype,
+                     (size_t)(b * J->bias_sb + h * J->bias_sh + (long long)i * J->Skv + j));
+}
+
 /* Mask M: is key j visible to query row i (absolute position p) of (b, h)? */
 static int key_visible(const job_t* J, int b, int h, int i, int j, int p, int L) {
     if (j >= L) return 0;          /* padding: past the valid length */
     if (J->mask && !J->mask[b * J->mask_sb + h * J->mask_sh + (long long)i * J->Skv + j])
         return 0;                  /* the caller's allowed-mask */
+    if (bias_at(J, b, h, i, j) == -INFINITY) return 0; /* a -inf bias forbids the key */
     if (!J->causal) return 1;
     return j <= p;                 /* causal: M_pj = 0 iff j <= p */
 }
 
-/* scale * (q_row . k_j), the row's logit for key j */
-static double score(const job_t* J, size_t qrow, size_t kbase, int j) {
+/* scale * (q_row . k_j) + bias, the row's logit for key j */
+static double score(const job_t* J, size_t qrow, size_t kbase, int j, double bias) {
     double acc = 0.0;
     for (int c = 0; c < J->d; ++c)
         acc += load_elem(J->q, J->dtype, qrow + c) *
                load_elem(J->k, J->dtype, kbase + (size_t)j * J->d + c);
-    return J->scale * acc;
+    return J->scale * acc + bias;
 }
 
 /* One query row: out_row[dv] and optionally w_row[Skv]; s is scratch of Skv. */
@@ -136,7 +154,7 @@ static void one_row(const job_t* J, int b, int h, int i, double* out_row, double
     int any = 0;
     for (int j = 0; j < Skv; ++j) {
         if (!key_visible(J, b, h, i, j, p, L)) continue;
-        s[j] = score(J, qrow, kbase, j);
+        s[j] = score(J, qrow, kbase, j, bias_at(J, b, h, i, j));
         if (s[j] > m) m = s[j];
         any = 1;
     }
@@ -260,6 +278,26 @@ int oracle_attn_fwd_weights_mask(const void* q, const void* k, const void* v, in
     J.B = B; J.H = H; J.Hkv = Hkv; J.Sq = Sq; J.Skv = Skv; J.d = d; J.dv = dv;
     J.scale = scale; J.causal = causal ? 1 : 0; J.kv_lens = kv_lens;
     J.mask = mask; J.mask_sb = mask_sb; J.mask_sh = mask_sh;
+    return run(&J, nthreads);
+}
+
+/* Every option at once: an allowed-mask (as oracle_attn_fwd_mask; NULL:
+   none), an additive bias of the inputs' dtype whose element (b, h, i, j) is
+   bias[b*bias_sb + h*bias_sh + i*Skv + j] (NULL: none), and optionally the
+   weight tensor (weights NULL: not returned).  Negative strides return 2. */
+int oracle_attn_fwd_ex(const void* q, const void* k, const void* v, int dtype, double* out,
+                       double* weights, int B, int H, int Hkv, int Sq, int Skv, int d, int dv,
+                       double scale, int causal, const int32_t* kv_lens, const uint8_t* mask,
+                       long long mask_sb, long long mask_sh, const void* bias, long long bias_sb,
+                       long long bias_sh, int nthreads) {
+    if (mask_sb < 0 || mask_sh < 0 || bias_sb < 0 || bias_sh < 0) return OR_E_SHAPE;
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.dtype = dtype; J.out = out; J.weights = weights;
+    J.B = B; J.H = H; J.Hkv = Hkv; J.Sq = Sq; J.Skv = Skv; J.d = d; J.dv = dv;
+    J.scale = scale; J.causal = causal ? 1 : 0; J.kv_lens = kv_lens;
+    J.mask = mask; J.mask_sb = mask_sb; J.mask_sh = mask_sh;
+    J.bias = bias; J.bias_sb = bias_sb; J.bias_sh = bias_sh;
     return run(&J, nthreads);
 }
 

@@ -375,6 +375,106 @@ def pin_mask_matches_torch_sdpa(attn):
                 assert np.allclose(out[b, h, rows], ref, rtol=0, atol=1e-12), (ci, b, h)
 
 
+def _bias_case(ci):
+    B, H, Hkv, Sq, Skv, d = 2, 4, 2, 5, 7, 3
+    q = _rand(200 + ci, B, H, Sq, d)
+    k, v = _rand(210 + ci, B, Hkv, Skv, d), _rand(220 + ci, B, Hkv, Skv, d)
+    return q, k, v, [7, 5]
+
+
+def pin_zero_bias_is_no_bias(attn):
+    """Adding a zero bias to every logit changes no bit of the output or the
+    weights (causal, padded, grouped heads, with and without a mask)."""
+    for ci in range(2):
+        q, k, v, lens = _bias_case(ci)
+        zero = np.zeros((1, 1, q.shape[2], k.shape[2]))
+        m = _random_mask(300 + ci, (q.shape[0], 1, q.shape[2], k.shape[2])) if ci else None
+        a, wa = attn(q, k, v, 0.6, 1, lens, mask=m, weights=True)
+        b, wb = attn(q, k, v, 0.6, 1, lens, mask=m, bias=zero, weights=True)
+        assert np.array_equal(a, b) and np.array_equal(wa, wb)
+
+
+def pin_neg_inf_bias_is_the_boolean_mask(attn):
+    """A bias of 0 where a boolean mask allows and -inf where it forbids is
+    that mask ("Attention from Scratch", KubeDojo module 1.4.3, Part 7: a
+    float mask is an additive bias; -inf is the forbidding value): same bits,
+    including a row with every key forbidden (exactly zero)."""
+    q, k, v, lens = _bias_case(2)
+    B, H, Sq, Skv = q.shape[0], q.shape[1], q.shape[2], k.shape[2]
+    m = _random_mask(310, (B, H, Sq, Skv))
+    m[1, 2, 0, :] = False
+    bias = np.where(m, 0.0, -np.inf)
+    for causal in (0, 1):
+        a, wa = attn(q, k, v, 0.6, causal, lens, mask=m, weights=True)
+        b, wb = attn(q, k, v, 0.6, causal, lens, bias=bias, weights=True)
+        assert np.array_equal(a, b) and np.array_equal(wa, wb), causal
+        assert np.all(b[1, 2, 0] == 0.0)
+
+
+def pin_row_constant_bias_changes_nothing(attn):
+    """softmax is unchanged by one constant added to a whole row of logits:
+    a bias that is constant along the keys (a different constant per row,
+    head and batch item, up to +-50) leaves the output unchanged."""
+    q, k, v, lens = _bias_case(3)
+    B, H, Sq, Skv = q.shape[0], q.shape[1], q.shape[2], k.shape[2]
+    c = 50.0 * (2.0 * np.random.default_rng(5).random((B, H, Sq, 1)) - 1.0)
+    base = attn(q, k, v, 0.6, 1, lens)
+    out = attn(q, k, v, 0.6, 1, lens, bias=np.broadcast_to(c, (B, H, Sq, Skv)))
+    assert np.allclose(out, base, rtol=0, atol=1e-12)
+
+
+def pin_bias_matches_torch_sdpa(attn):
+    """Random finite biases in every broadcast shape, with the causal rule,
+    valid lengths, grouped heads and a boolean mask, against torch's CPU
+    scaled_dot_product_attention in float64 given the float attn_mask
+    bias + (0 where allowed, -inf elsewhere) -- an independent routine that
+    adds a float mask to the scaled logits."""
+    import torch
+    import torch.nn.functional as F
+    for ci, shape in enumerate([(2, 4, 5, 7), (2, 1, 5, 7), (1, 4, 5, 7), (2, 4, 1, 7),
+                                (1, 1, 5, 7)]):
+        q, k, v, lens = _bias_case(10 + ci)
+        B, H, Hkv, Sq, Skv = q.shape[0], q.shape[1], k.shape[1], q.shape[2], k.shape[2]
+        bias = 3.0 * _rand(400 + ci, *shape)
+        m = _random_mask(410 + ci, (B, 1, Sq, Skv), density=0.8) if ci % 2 else None
+        causal = (ci // 2) % 2
+        out, w = attn(q, k, v, 0.7, causal, lens, mask=m, bias=bias, weights=True)
+        bb = np.broadcast_to(bias, (B, H, Sq, Skv))
+        mm = np.ones((B, H, Sq, Skv), bool) if m is None else np.broadcast_to(m, (B, H, Sq, Skv))
+        ke = torch.from_numpy(k).repeat_interleave(H // Hkv, dim=1)
+        ve = torch.from_numpy(v).repeat_interleave(H // Hkv, dim=1)
+        for b in range(B):
+            rule, pad = _visible(Sq, Skv, causal, lens[b])
+            for h in range(H):
+                allowed = mm[b, h] & rule
+                assert np.all(w[b, h][~allowed] == 0.0), (ci, b, h)
+                rows = np.nonzero(allowed.any(axis=1))[0]
+                assert np.all(out[b, h][~allowed.any(axis=1)] == 0.0), (ci, b, h)
+                if len(rows) == 0:
+                    continue
+                fm = np.where(allowed, bb[b, h], -np.inf)[rows]
+                ref = F.scaled_dot_product_attention(
+                    torch.from_numpy(q[b, h, rows]), ke[b, h], ve[b, h],
+                    attn_mask=torch.from_numpy(np.ascontiguousarray(fm)), scale=0.7).numpy()
+                assert np.allclose(out[b, h, rows], ref, rtol=0, atol=1e-12), (ci, b, h)
+
+
+def pin_low_precision_bias_widens_exactly(attn):
+    """A bfloat16 or float32 bias is its exact float64 value: the same bits
+    as the float64 call on the widened inputs."""
+    q, k, v, lens = _bias_case(20)
+    bias = 2.0 * _rand(420, 1, q.shape[1], q.shape[2], k.shape[2])
+    ref = attn(*(bf16_to_f32(bf16_bits(x)).astype(np.float64) for x in (q, k, v)), 0.5, 1, lens,
+               bias=bf16_to_f32(bf16_bits(bias)).astype(np.float64))
+    got = attn(*(bf16_bits(x) for x in (q, k, v)), 0.5, 1, lens, bias=bf16_bits(bias))
+    assert np.array_equal(got, ref)
+    ref = attn(*(x.astype(np.float32).astype(np.float64) for x in (q, k, v)), 0.5, 1, lens,
+               bias=bias.astype(np.float32).astype(np.float64))
+    got = attn(*(x.astype(np.float32) for x in (q, k, v)), 0.5, 1, lens,
+               bias=bias.astype(np.float32))
+    assert np.array_equal(got, ref)
+
+
 ALL_PINS = [
     pin_p2_causal_example,
     pin_p3_unmasked_example,
@@ -394,6 +494,11 @@ ALL_PINS = [
     pin_key_padding_mask_equals_lengths,
     pin_mask_single_allowed_key,
     pin_mask_matches_torch_sdpa,
+    pin_zero_bias_is_no_bias,
+    pin_neg_inf_bias_is_the_boolean_mask,
+    pin_row_constant_bias_changes_nothing,
+    pin_bias_matches_torch_sdpa,
+    pin_low_precision_bias_widens_exactly,
 ]
 
 

@@ -17,8 +17,8 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
 
 # name: [(original snippet, replacement, expected occurrences)]
 MUTANTS = {
-    "scale_dropped": [("return J->scale * acc;", "return acc;", 1)],
-    "scale_divides": [("return J->scale * acc;", "return acc / J->scale;", 1)],
+    "scale_dropped": [("return J->scale * acc + bias;", "return acc + bias;", 1)],
+    "scale_divides": [("return J->scale * acc + bias;", "return acc / J->scale + bias;", 1)],
     "self_not_visible": [("return j <= p;", "return j < p;", 1)],
     "sees_next_key": [("return j <= p;", "return j <= p + 1;", 1)],
     "top_left_alignment": [("const int p = (L - n) + i;", "const int p = i;", 1)],
@@ -34,12 +34,19 @@ MUTANTS = {
     "max_not_subtracted": [("exp(s[j] - m)", "exp(s[j])", 2)],
     "max_not_tracked": [("if (s[j] > m) m = s[j];", "", 1)],
     "mask_after_softmax": [("if (key_visible(J, b, h, i, j, p, L)) l += exp(s[j] - m);",
-                            "l += exp(score(J, qrow, kbase, j) - m);", 1)],
+                            "l += exp(score(J, qrow, kbase, j, 0.0) - m);", 1)],
     "allowed_mask_ignored": [("if (J->mask && !J->mask[", "if (0 && !J->mask[", 1)],
     "allowed_mask_inverted": [("if (J->mask && !J->mask[", "if (J->mask && J->mask[", 1)],
     "allowed_mask_row_reversed": [("(long long)i * J->Skv + j]", "(long long)(J->Sq - 1 - i) * J->Skv + j]", 1)],
     "allowed_mask_batch_ignored": [("[b * J->mask_sb + h * J->mask_sh", "[h * J->mask_sh", 1)],
     "allowed_mask_head_ignored": [("[b * J->mask_sb + h * J->mask_sh", "[b * J->mask_sb", 1)],
+    "bias_ignored": [("return J->scale * acc + bias;", "return J->scale * acc;", 1)],
+    "bias_scaled": [("return J->scale * acc + bias;", "return J->scale * (acc + bias);", 1)],
+    "bias_subtracted": [("return J->scale * acc + bias;", "return J->scale * acc - bias;", 1)],
+    "bias_row_reversed": [("h * J->bias_sh + (long long)i * J->Skv + j", "h * J->bias_sh + (long long)(J->Sq - 1 - i) * J->Skv + j", 1)],
+    "bias_batch_ignored": [("(size_t)(b * J->bias_sb + h * J->bias_sh", "(size_t)(h * J->bias_sh", 1)],
+    "bias_head_ignored": [("(size_t)(b * J->bias_sb + h * J->bias_sh", "(size_t)(b * J->bias_sb", 1)],
+    "neg_inf_bias_kept_visible": [("if (bias_at(J, b, h, i, j) == -INFINITY) return 0;", "", 1)],
     "kv_head_modulo": [("const int hk = h / (J->H / J->Hkv);", "const int hk = h % J->Hkv;", 1)],
     "kv_base_strides_query_heads": [("((size_t)b * J->Hkv + hk) * (size_t)Skv * J->d;",
                                      "((size_t)b * J->H + hk) * (size_t)Skv * J->d;", 1)],
