@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 typedef enum {
     ATTN_OK = 0,
@@ -76,7 +76,7 @@ typedef enum {
     ATTN_E_DTYPE = 4,       /* dtype is not an attn_dtype value */
     ATTN_E_ALIGN = 5,       /* a base pointer is not 16-byte aligned (mask: 4 bytes) */
     ATTN_E_WORKSPACE = 6,   /* caller workspace smaller than attn_workspace_bytes() */
-    ATTN_E_ARG = 7,         /* scale is not finite and > 0 */
+    ATTN_E_ARG = 7,         /* scale is not finite */
     ATTN_E_LAUNCH = 8,      /* a HIP call or kernel launch failed */
     ATTN_E_NOMEM = 9,       /* the library could not allocate its workspace */
     ATTN_E_SCRATCH = 10     /* attn_fwd_noalloc: the problem needs more temporary memory
@@ -92,17 +92,19 @@ typedef enum {
  * Support matrix (anything else valid returns ATTN_E_UNSUPPORTED -- there is
  * no silent slow fallback, the hazard "Attention from First Principles"
  * section 8 warns of):
- *   ATTN_F32 : any Sq <= Skv, 1 <= d, d_v <= 128     (VALU kernel)
- *   ATTN_BF16: Sq == 1, d = d_v in {64, 128}          (split-KV decode)
- *              Sq >= 2, d = d_v in {64, 128}          (MFMA prefill)
- * Every path takes grouped K/V heads and an allowed-mask (attn_fwd_ex).
+ *   ATTN_F32 : any Sq <= Skv, 1 <= d, d_v <= 128           (VALU kernel)
+ *   ATTN_BF16: Sq == 1, d and d_v each in {64, 128}          (split-KV decode)
+ *              Sq >= 2, d and d_v each in {64, 128}          (MFMA prefill)
+ * Every path takes grouped K/V heads, an allowed-mask (attn_fwd_ex), an
+ * additive bias (attn_fwd_bias) and any finite scale; with a bias or a scale
+ * that is not positive the bf16 paths run their general-logit kernels.
  */
 
 /*
  * attn_fwd -- out = softmax(scale * Q K^T + M) V, arguments as above.
  * scale: the logit multiplier, normally 1/sqrt(d) ("Self-Attention",
- * section "Why divide by sqrt(d_k)?"); it must be finite and > 0, the only
- * values the pages use (else ATTN_E_ARG).  causal: 0 or nonzero.
+ * section "Why divide by sqrt(d_k)?"); any finite value (else ATTN_E_ARG).
+ * causal: 0 or nonzero.
  * Temporary memory comes from a library-owned workspace kept per (device,
  * stream) pair and grown on demand; the call that grows it first waits for
  * the earlier work on its stream.  Calls on different streams therefore
@@ -161,11 +163,11 @@ int attn_validate_gqa(const void* q, const void* k, const void* v, void* out, in
                       int H_kv, int Sq, int Skv, int d, float scale, int causal, int dtype);
 
 /*
- * attn_fwd_ex -- every option at once: H_kv key/value heads (as
- * attn_fwd_gqa), a value width d_v that may differ from d (softmax(QK^T) V
- * only needs V's rows to match K's, the d_k = 4, d_v = 2 example of
- * "Attention from Scratch", KubeDojo module 1.4.3, Part 2; the fp32 kernel
- * only, see the support matrix), and an explicit allowed-mask ANDed into M:
+ * attn_fwd_ex -- H_kv key/value heads (as attn_fwd_gqa), a value width d_v
+ * that may differ from d (softmax(QK^T) V only needs V's rows to match K's,
+ * the d_k = 4, d_v = 2 example of "Attention from Scratch", KubeDojo module
+ * 1.4.3, Part 2; see the support matrix), and an explicit allowed-mask ANDed
+ * into M:
  * query row i of (b, h) sees key j only if the causal and length rules above
  * allow it AND mask byte (b, h, i, j) is nonzero (the boolean allowed-mask,
  * True = may attend, of "Attention from Scratch", KubeDojo module 1.4.3,
@@ -200,6 +202,44 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, i
                 int Sq, int Skv, int d, int d_v, float scale, int causal, const int32_t* kv_lens,
                 const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int64_t mask_si, int dtype,
                 void* stream, void* workspace, size_t workspace_bytes);
+
+/*
+ * attn_fwd_bias -- attn_fwd_ex plus an additive bias: the logit of query row
+ * i and key j of (b, h) is scale * q_i . k_j + bias(b, h, i, j), before the
+ * softmax (the float mask that "Attention from Scratch", KubeDojo module
+ * 1.4.3, Part 7 calls an additive bias, where a boolean mask only allows or
+ * forbids).  A bias of -inf hides the key exactly as a zero mask byte does;
+ * the bias is added to keys the rules and the mask leave visible.  Its
+ * entries must be finite or -inf (+inf or NaN give undefined results).
+ *
+ *   bias      DEVICE array of `dtype` elements (bf16 bias for bf16 inputs,
+ *             fp32 for fp32); element (b, h, i, j) is
+ *             bias[b*bias_sb + h*bias_sh + i*bias_si + j], i the query row as
+ *             given.  A stride of 0 broadcasts that axis.  NULL: no bias
+ *             (then this is attn_fwd_ex).
+ *   bias_s*   strides in ELEMENTS, >= 0 (else ATTN_E_SHAPE) and multiples of
+ *             4, with the base 16-byte aligned (else ATTN_E_ALIGN); rows are
+ *             read in groups of 4 elements, so each row must be readable up to
+ *             Skv rounded up to a multiple of 4.  (32 * bias_si + Skv) times
+ *             the element size must stay below 2^32 (else
+ *             ATTN_E_UNSUPPORTED).  The bias is only read.
+ * The workspace is that of attn_fwd_ex (attn_workspace_bytes_ex); the other
+ * arguments, ownership and errors are as there.  Mask checks come before
+ * bias checks.
+ */
+int attn_fwd_bias(const void* q, const void* k, const void* v, void* out, int B, int H, int H_kv,
+                  int Sq, int Skv, int d, int d_v, float scale, int causal,
+                  const int32_t* kv_lens, const uint8_t* mask, int64_t mask_sb, int64_t mask_sh,
+                  int64_t mask_si, const void* bias, int64_t bias_sb, int64_t bias_sh,
+                  int64_t bias_si, int dtype, void* stream, void* workspace,
+                  size_t workspace_bytes);
+
+/* The host-side checks of attn_fwd_bias alone (as attn_validate). */
+int attn_validate_bias(const void* q, const void* k, const void* v, void* out, int B, int H,
+                       int H_kv, int Sq, int Skv, int d, int d_v, float scale, int causal,
+                       const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int64_t mask_si,
+                       const void* bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_si,
+                       int dtype);
 
 /* Device bytes attn_fwd_ex needs as caller workspace (masked != 0 when a
    mask is passed: a masked prefill adds key-tile marks, a masked decode a

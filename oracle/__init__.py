@@ -140,7 +140,11 @@ def attention(q, k, v, scale, causal, kv_lens=None, *, mask=None, bias=None, wei
         bias = np.asarray(bias)
         if bias.dtype != q.dtype:
             raise ValueError(f"bias must have q's dtype {q.dtype}, got {bias.dtype}")
-        bfull = np.ascontiguousarray(np.broadcast_to(bias, (B, H, Sq, Skv)))
+        if bias.ndim != 4 or bias.shape[3] != Skv:
+            raise ValueError(f"bias must be 4-D [B|1, H|1, Sq|1, {Skv}]")
+        # batch and head axes of size 1 stay broadcast (stride 0); rows are expanded
+        Bb, Hb = bias.shape[0], bias.shape[1]
+        bfull = np.ascontiguousarray(np.broadcast_to(bias, (Bb, Hb, Sq, Skv)))
         m = None if mask is None else np.ascontiguousarray(
             np.broadcast_to(np.asarray(mask) != 0, (B, H, Sq, Skv)), dtype=np.uint8)
         w = np.empty((B, H, Sq, Skv), dtype=np.float64) if weights else None
@@ -148,7 +152,8 @@ def attention(q, k, v, scale, causal, kv_lens=None, *, mask=None, bias=None, wei
             q.ctypes.data, k.ctypes.data, v.ctypes.data, code, out.ctypes.data,
             None if w is None else w.ctypes.data, B, H, Hkv, Sq, Skv, d, dv, float(scale),
             int(bool(causal)), lens_ptr, None if m is None else m.ctypes.data, H * Sq * Skv,
-            Sq * Skv, bfull.ctypes.data, H * Sq * Skv, Sq * Skv, int(nthreads))
+            Sq * Skv, bfull.ctypes.data, 0 if Bb == 1 else Hb * Sq * Skv, 0 if Hb == 1 else Sq * Skv,
+            int(nthreads))
         if rc != 0:
             raise ValueError(f"oracle error {rc}: {ERRORS.get(rc, 'unknown')}")
         return (out, w) if weights else out

@@ -52,6 +52,9 @@ def test_validate_accepts_supported_requests():
     assert v(dtype=F32, d=16) == attn.OK
     assert v(dtype=F32, d=1, Sq=1, Skv=1) == attn.OK
     assert v(dtype=F32, d=128, Sq=3, Skv=7) == attn.OK
+    # any finite scale: a scale that is not positive runs the general kernels
+    assert v(scale=0.0) == attn.OK and v(scale=-0.125) == attn.OK
+    assert v(scale=-0.125, Sq=1, Skv=100) == attn.OK and v(scale=-1.0, dtype=F32, d=16) == attn.OK
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -62,7 +65,6 @@ def test_validate_accepts_supported_requests():
     (dict(Skv=0), attn.E_SHAPE), (dict(d=0), attn.E_SHAPE), (dict(Sq=5, Skv=4), attn.E_SHAPE),
     (dict(B=1 << 20, H=1 << 10, Sq=1, Skv=1 << 16, d=128), attn.E_SHAPE),
     (dict(scale=float("inf")), attn.E_ARG), (dict(scale=float("nan")), attn.E_ARG),
-    (dict(scale=0.0), attn.E_ARG), (dict(scale=-0.125), attn.E_ARG),
     (dict(q=A + 8), attn.E_ALIGN), (dict(out=A + 2), attn.E_ALIGN),
     (dict(d=32), attn.E_UNSUPPORTED), (dict(d=96), attn.E_UNSUPPORTED),
     (dict(d=256), attn.E_UNSUPPORTED), (dict(dtype=F32, d=129), attn.E_UNSUPPORTED),
@@ -208,18 +210,22 @@ def test_validate_mask():
     assert vm(si=1 << 27) == attn.E_UNSUPPORTED and vm(si=(1 << 27) - 64) == attn.OK
     # the shared checks come first
     assert vm(B=0, mask=A + 1) == attn.E_SHAPE
-    assert vm(scale=0.0) == attn.E_ARG
+    assert vm(scale=float("nan")) == attn.E_ARG
     assert vm(Hkv=3) == attn.E_SHAPE
 
 
 def test_validate_value_width():
-    # d_v != d: the fp32 kernel only; d_v in 1..128
+    # d_v != d: fp32 d_v in 1..128
     assert vm(mask=None, dtype=F32, d=4, dv=2) == attn.OK
     assert vm(mask=None, dtype=F32, d=128, dv=16) == attn.OK
     assert vm(mask=None, dtype=F32, d=20, dv=128) == attn.OK
     assert vm(mask=None, dtype=F32, d=20, dv=129) == attn.E_UNSUPPORTED
     assert vm(mask=None, dtype=F32, d=20, dv=0) == attn.E_SHAPE
-    assert vm(mask=None, dtype=BF16, d=128, dv=64) == attn.E_UNSUPPORTED
+    # bf16: d and d_v each in {64, 128}
+    assert vm(mask=None, dtype=BF16, d=128, dv=64) == attn.OK
+    assert vm(mask=None, dtype=BF16, d=64, dv=128) == attn.OK
+    assert vm(mask=None, dtype=BF16, d=64, dv=32) == attn.E_UNSUPPORTED
+    assert vm(mask=None, dtype=BF16, d=128, dv=96) == attn.E_UNSUPPORTED
     assert vm(mask=None, dtype=BF16, d=64, dv=64) == attn.OK
     assert vm(mask=None, dtype=BF16, Sq=1, d=128, dv=128) == attn.OK
 
@@ -262,3 +268,30 @@ def test_noalloc_refuses_problems_beyond_the_scratch_array():
     rc = lib.attn_fwd_noalloc(A, A, A, A, B, H, 3, 1, Skv, d, d, ctypes.c_float(0.088), 0,
                               None, None, 0, 0, 0, BF16, None)
     assert rc == attn.E_SHAPE
+
+
+def vb(bias=A, bsb=0, bsh=0, bsi=0, B=2, H=4, Hkv=2, Sq=8, Skv=64, d=128, dtype=BF16, mask=None,
+       msi=0):
+    return attn.library().attn_validate_bias(A, A, A, A, B, H, Hkv, Sq, Skv, d, d, 0.125, 1, mask,
+                                             0, 0, msi, bias, bsb, bsh, bsi, dtype)
+
+
+def test_validate_bias():
+    """Additive-bias layout checks: 16-byte base, strides >= 0 and multiples
+    of 4 elements, 32-bit row offsets for a wave's rows; a NULL bias is the
+    attn_validate_ex checks alone."""
+    assert vb(bias=None) == attn.OK
+    assert vb(bsb=4 * 8 * 64, bsh=8 * 64, bsi=64) == attn.OK       # dense [B,H,Sq,Skv]
+    assert vb(bsb=64) == attn.OK                                    # [B,1,1,Skv]
+    assert vb(Sq=1, Skv=65, bsb=68) == attn.OK                      # padded rows
+    assert vb(dtype=F32, d=16, bsi=64) == attn.OK
+    assert vb(bias=A + 8) == attn.E_ALIGN
+    assert vb(bsi=66) == attn.E_ALIGN and vb(bsh=2) == attn.E_ALIGN and vb(bsb=1) == attn.E_ALIGN
+    assert vb(bsi=-64) == attn.E_SHAPE and vb(bsh=-4) == attn.E_SHAPE
+    assert vb(B=2, bsb=1 << 62) == attn.E_SHAPE
+    # bf16 rows of 2 bytes: 32 rows of stride si must stay below 2^32 bytes
+    assert vb(bsi=1 << 26) == attn.E_UNSUPPORTED and vb(bsi=(1 << 26) - 64) == attn.OK
+    assert vb(dtype=F32, d=16, bsi=1 << 25) == attn.E_UNSUPPORTED
+    # the mask checks come first
+    assert vb(mask=A + 2, bias=A + 8) == attn.E_ALIGN
+    assert vb(mask=A, msi=65) == attn.E_ALIGN

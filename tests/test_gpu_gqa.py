@@ -18,7 +18,7 @@ import pytest
 import oracle
 import transformer_scaled_dot_attn_amd as attn
 import workloads as W
-from gpu_util import BF16_TOL, F32_TOL, assert_matches, gpu_run
+from gpu_util import BF16_TOL, F32_TOL, assert_matches, check_workload_full, gpu_run
 
 pytestmark = pytest.mark.gpu
 
@@ -129,32 +129,10 @@ def test_gqa_rejects_uneven_groups():
     assert rc == attn.E_SHAPE
 
 
-def _sampled(w, pairs):
-    import torch
-    _say("workload", w.name, "pairs", pairs)
-    x = W.device_inputs(w)
-    assert x["k"].shape[1] == w.kv_heads
-    out = attn.fwd(x["q"], x["k"], x["v"], causal=w.causal, kv_lens=x["kv_lens"],
-                   scale=x["scale"])
-    torch.cuda.synchronize()
-    sub = W.make_inputs(w, pairs=pairs)
-    ref = oracle.attention(sub["q"], sub["k"], sub["v"], sub["scale"], w.causal, sub["kv_lens"])
-    got = np.stack([W.from_torch(out[b, h]) for b, h in pairs])[:, None]
-    g = w.H // w.kv_heads
-    for idx, (b, h) in enumerate(pairs):
-        assert np.array_equal(W.bits_from_torch(x["q"][b, h]), sub["q"][idx, 0])
-        assert np.array_equal(W.bits_from_torch(x["k"][b, h // g]), sub["k"][idx, 0])
-    return assert_matches(got, ref, BF16_TOL, sub["kv_lens"], w.Skv, w.name)
-
-
-def test_workload_gqa_prefill2048_sampled():
-    w = W.WORKLOADS["gqa_prefill2048_bf16"]
-    _sampled(w, [(0, 0), (0, 3), (0, 4), (1, 17), (1, 31)])
+def test_workload_gqa_prefill2048_full():
+    check_workload_full(W.WORKLOADS["gqa_prefill2048_bf16"], say=print)
 
 
 @pytest.mark.parametrize("name", ["gqa_decode8192_bf16", "mqa_decode8192_bf16"])
-def test_workload_grouped_decode_sampled(name):
-    w = W.WORKLOADS[name]
-    lens = W.kv_lens_for(w)
-    bs = [int(np.argmin(lens)), int(np.argmax(lens)), 0, 33]
-    _sampled(w, [(b, h) for b in bs for h in (0, 3, 4, 31)])
+def test_workload_grouped_decode_full(name):
+    check_workload_full(W.WORKLOADS[name], say=print)

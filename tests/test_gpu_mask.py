@@ -17,7 +17,7 @@ import pytest
 import oracle
 import transformer_scaled_dot_attn_amd as attn
 import workloads as W
-from gpu_util import BF16_TOL, F32_TOL, assert_matches, gpu_run
+from gpu_util import BF16_TOL, F32_TOL, assert_matches, check_workload_full, gpu_run
 
 pytestmark = pytest.mark.gpu
 
@@ -186,51 +186,26 @@ def test_mask_decode_split_fully_hidden():
         assert np.all(got[1] == 0.0)
 
 
-def _sampled_mask_check(w, mask_np, pairs):
-    """Run workload w in full with mask_np on the GPU (its benchmark launch
-    configuration); compare the (b, h) slices with the oracle."""
-    import torch
-    _say("workload", w.name, "with mask", mask_np.shape, "pairs", pairs)
-    x = W.device_inputs(w)
-    out = attn.fwd(x["q"], x["k"], x["v"], causal=w.causal, kv_lens=x["kv_lens"],
-                   scale=x["scale"], mask=W.mask_to_torch(mask_np))
-    torch.cuda.synchronize()
-    sub = W.make_inputs(w, pairs=pairs)
-    # the mask rows of each sampled slice, stacked like the slices
-    m = np.broadcast_to(mask_np, (w.B, w.H, mask_np.shape[2], w.Skv))
-    m_sub = np.stack([m[b, h] for b, h in pairs])[:, None]
-    ref = oracle.attention(sub["q"], sub["k"], sub["v"], sub["scale"], w.causal, sub["kv_lens"],
-                           mask=m_sub)
-    got = np.stack([W.from_torch(out[b, h]) for b, h in pairs])[:, None]
-    return assert_matches(got, ref, BF16_TOL, sub["kv_lens"], w.Skv, w.name)
-
-
-def test_prefill4096_random_mask_sampled():
+def test_prefill4096_random_mask_full():
     """The 4096-token causal prefill in its benchmark launch configuration,
-    with a random [1,1,S,S] mask (every tile cut), sampled heads vs the oracle."""
+    with a random [1,1,S,S] mask (every tile cut), every head vs the oracle."""
     w = W.WORKLOADS["prefill4096_bf16"]
-    _say("prefill4096 random mask")
-    mask = W.random_mask(97, (1, 1, w.Sq, w.Skv), 0.5)
-    _sampled_mask_check(w, mask, [(0, 0), (0, 31)])
+    check_workload_full(w, W.random_mask(97, (1, 1, w.Sq, w.Skv), 0.5), say=print)
 
 
-def test_decode8192_key_padding_sampled():
+def test_decode8192_key_padding_full():
     w = W.WORKLOADS["gqa_decode8192_bf16"]
-    _say("gqa decode8192 key padding")
     rng = np.random.default_rng(98)
     starts = rng.integers(0, 400, size=w.B)
-    mask = W.key_padding_mask(starts, np.full(w.B, w.Skv), w.Skv)
-    _sampled_mask_check(w, mask, [(0, 0), (5, 13), (63, 31)])
+    check_workload_full(w, W.key_padding_mask(starts, np.full(w.B, w.Skv), w.Skv), say=print)
 
 
-def test_decode8192_random_head_mask_sampled():
+def test_decode8192_random_head_mask_full():
     """Multi-head decode over the full workload with a per-head random mask:
     wave shares of listed tiles run past 128 entries, so the tile lists roll
     over in chunks of 64."""
     w = W.WORKLOADS["decode8192_bf16"]
-    _say("decode8192 random per-head mask")
-    mask = W.random_mask(99, (w.B, w.H, 1, w.Skv), 0.5)
-    _sampled_mask_check(w, mask, [(0, 0), (7, 31), (40, 5), (63, 17)])
+    check_workload_full(w, W.random_mask(99, (w.B, w.H, 1, w.Skv), 0.5), say=print)
 
 
 def test_decode_sparse_visible_windows():

@@ -14,7 +14,7 @@ import golden_io
 import oracle
 import transformer_scaled_dot_attn_amd as attn
 import workloads as W
-from gpu_util import BF16_TOL, F32_TOL, assert_matches, check_problem, gpu_run
+from gpu_util import BF16_TOL, F32_TOL, assert_matches, check_workload_full, check_problem, gpu_run
 
 pytestmark = pytest.mark.gpu
 
@@ -122,46 +122,23 @@ def test_bf16_decode_shapes(case):
 
 
 # ------------------------------------------------- workloads at full size
-def _sampled(w, pairs):
-    """Run the full workload on the GPU; oracle on the chosen (b, h) slices."""
-    import torch
-    _say("workload", w.name, "pairs", pairs)
-    x = W.device_inputs(w)
-    out = attn.fwd(x["q"], x["k"], x["v"], causal=w.causal, kv_lens=x["kv_lens"],
-                   scale=x["scale"])
-    torch.cuda.synchronize()
-    sub = W.make_inputs(w, pairs=pairs)
-    ref = oracle.attention(sub["q"], sub["k"], sub["v"], sub["scale"], w.causal, sub["kv_lens"])
-    got = np.stack([W.from_torch(out[b, h]) for b, h in pairs])[:, None]
-    # the sampled slices must be the very bits the GPU consumed
-    for idx, (b, h) in enumerate(pairs):
-        assert np.array_equal(W.bits_from_torch(x["q"][b, h]), sub["q"][idx, 0])
-    return assert_matches(got, ref, BF16_TOL, sub["kv_lens"], w.Skv, w.name)
-
-
 def test_workload_mha768_full():
-    w = W.WORKLOADS["mha768_bf16"]
-    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
-    _sampled(w, pairs)
+    check_workload_full(W.WORKLOADS["mha768_bf16"], say=print)
 
 
-def test_workload_prefill4096_sampled():
-    w = W.WORKLOADS["prefill4096_bf16"]
-    _sampled(w, [(0, 0), (0, 13), (0, 31)])
+def test_workload_prefill4096_full():
+    """Every head of the 4096-token causal prefill against the oracle."""
+    check_workload_full(W.WORKLOADS["prefill4096_bf16"], say=print)
 
 
-def test_workload_padded2048_sampled():
-    w = W.WORKLOADS["padded2048_bf16"]
-    lens = W.kv_lens_for(w)
-    short = int(np.argmin(lens))
-    _sampled(w, [(short, 0), (short, 31), (0, 5), (3, 17), (int(np.argmax(lens)), 2)])
+def test_workload_padded2048_full():
+    """Every (b, h) of the padded batch (lengths U[256, 2048])."""
+    check_workload_full(W.WORKLOADS["padded2048_bf16"], say=print)
 
 
-def test_workload_decode8192_sampled():
-    w = W.WORKLOADS["decode8192_bf16"]
-    lens = W.kv_lens_for(w)
-    bs = [int(np.argmin(lens)), int(np.argmax(lens)), 0, 17, 40, 63]
-    _sampled(w, [(b, h) for b in bs for h in (0, 11, 31)])
+def test_workload_decode8192_full():
+    """Every (b, h) of the 64-sequence decode (lengths U[512, 8192])."""
+    check_workload_full(W.WORKLOADS["decode8192_bf16"], say=print)
 
 
 # ------------------------------------------- chunked prefill (1 < Sq < Skv)

@@ -1,11 +1,13 @@
-"""A value width d_v different from d on the GPU (the fp32 kernel).
+"""A value width d_v different from d on the GPU (every kernel family).
 
 softmax(scale Q K^T) V needs V's rows to line up with K's, not its width to
 match d ("Attention from Scratch", KubeDojo module 1.4.3, Part 2, whose
 worked example has d_k = 4 and d_v = 2).  The worked example runs at its own
 shape against the printed values and the oracle; random shapes with every
 width class on each side, with the causal rule, valid lengths, grouped heads
-and masks, are compared with the oracle; the bf16 kernels refuse d_v != d.
+and masks, are compared with the oracle.  The bf16 kernels take d and d_v
+each in {64, 128} (prefill, key-range splits, decode, with masks, biases and
+grouped heads) and refuse other widths.
 """
 import numpy as np
 import pytest
@@ -14,7 +16,7 @@ import golden_io
 import oracle
 import transformer_scaled_dot_attn_amd as attn
 import workloads as W
-from gpu_util import F32_TOL, assert_matches, gpu_run
+from gpu_util import BF16_TOL, F32_TOL, assert_matches, gpu_run
 
 pytestmark = pytest.mark.gpu
 
@@ -61,8 +63,41 @@ def test_value_width_matches_oracle(case):
     assert_matches(got, ref, F32_TOL, clamped, Skv, f"s{seed}")
 
 
-def test_bf16_rejects_other_value_width():
-    prob = W.random_problem(116, 1, 2, 8, 8, 64, "bf16", dv=128)
-    with pytest.raises(attn.AttnError) as e:
-        gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], 1)
-    assert e.value.status == attn.E_UNSUPPORTED
+BF16_CASES = [
+    # seed, B, H, Hkv, Sq, Skv, d, dv, causal, kv_lens, extra
+    (121, 2, 4, 2, 300, 300, 128, 64, 1, [300, 111], None),
+    (122, 1, 4, 4, 515, 515, 64, 128, 1, None, None),
+    (123, 1, 8, 8, 300, 6000, 64, 128, 1, None, None),        # key-range splits
+    (124, 1, 8, 2, 200, 5000, 128, 64, 1, None, None),
+    (125, 3, 4, 4, 1, 3000, 128, 64, 0, [3000, 17, 0], None),  # decode
+    (126, 2, 32, 1, 1, 4100, 64, 128, 0, [4100, 900], None),  # decode, MQA
+    (127, 2, 4, 2, 130, 260, 64, 128, 1, [260, 100], "mask"),
+    (128, 2, 4, 4, 1, 2000, 128, 64, 0, [2000, 500], "mask"),
+    (129, 2, 4, 2, 200, 200, 128, 64, 1, [200, 60], "bias"),
+    (130, 2, 8, 2, 1, 1500, 64, 128, 0, [1500, 70], "bias"),
+]
+
+
+@pytest.mark.parametrize("case", BF16_CASES, ids=lambda c: f"s{c[0]}")
+def test_bf16_value_width_matches_oracle(case):
+    seed, B, H, Hkv, Sq, Skv, d, dv, causal, lens, extra = case
+    _say(f"bf16 value width s{seed}: d {d} d_v {dv} {extra}")
+    prob = W.random_problem(seed, B, H, Sq, Skv, d, "bf16", lens, dv=dv, Hkv=Hkv)
+    mask = W.random_mask(seed, (B, 1, Sq, Skv), 0.6) if extra == "mask" else None
+    bias = W.random_bias(seed, (1, H, Sq, Skv), "bf16", hide=0.1) if extra == "bias" else None
+    got, _ = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], causal, lens,
+                     mask=None if mask is None else W.mask_to_torch(mask),
+                     bias=None if bias is None else W.bias_to_torch(bias))
+    assert got.shape == (B, H, Sq, dv)
+    clamped = None if lens is None else np.clip(lens, 0, Skv)
+    ref = oracle.attention(prob["q"], prob["k"], prob["v"], prob["scale"], causal, clamped,
+                           mask=mask, bias=bias)
+    assert_matches(got, ref, BF16_TOL, clamped, Skv, f"s{seed}")
+
+
+def test_bf16_rejects_other_value_widths():
+    for dv in (32, 96):
+        prob = W.random_problem(116, 1, 2, 8, 8, 64, "bf16", dv=dv)
+        with pytest.raises(attn.AttnError) as e:
+            gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], 1)
+        assert e.value.status == attn.E_UNSUPPORTED

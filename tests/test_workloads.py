@@ -62,3 +62,17 @@ def test_dot_product_variance_and_scale():
     assert abs((dots * w.scale).var() - 1) < 0.06
     s128 = W.WORKLOADS["prefill4096_bf16"].scale
     assert round(s128, 3) == 0.088 and np.float32(s128) == np.float32(1 / math.sqrt(128))
+
+
+def test_batch_item_inputs_match_whole_tensors():
+    """The per-batch-item regeneration the full-size GPU checks use gives the
+    same bits as drawing the whole tensors (grouped K/V heads, ragged lengths)."""
+    from gpu_util import batch_item_inputs
+    w = W.Workload("small_gqa", 3, 8, 20, 40, 16, "bf16", True, 5, (3, 40), Hkv=2)
+    lens = W.kv_lens_for(w)
+    full = {t: W.make_tensor(w, t, lens) for t in ("q", "k", "v")}
+    for b in range(w.B):
+        q, k, v = batch_item_inputs(w, b, lens)
+        assert np.array_equal(q[0], full["q"][b])
+        assert np.array_equal(k[0], full["k"][b])
+        assert np.array_equal(v[0], full["v"][b])

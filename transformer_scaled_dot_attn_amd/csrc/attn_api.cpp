@@ -26,7 +26,7 @@ enum Path { kPathNone = -1, kPathGenericF32 = 0, kPathPrefill = 1, kPathDecode =
 
 Path choose_path(int Sq, int d, int dtype, int dv) {
     if (dtype == ATTN_F32) return d <= 128 && dv <= 128 ? kPathGenericF32 : kPathNone;
-    if (dtype == ATTN_BF16 && (d == 64 || d == 128) && dv == d)
+    if (dtype == ATTN_BF16 && (d == 64 || d == 128) && (dv == 64 || dv == 128))
         return Sq == 1 ? kPathDecode : kPathPrefill;
     return kPathNone;
 }
@@ -171,29 +171,48 @@ int check_mask(const uint8_t* mask, int64_t sb, int64_t sh, int64_t si, int B, i
     return ATTN_OK;
 }
 
-// Every host-side check of attn_fwd_ex, in the documented order.
+// Additive-bias layout checks: strides >= 0 and multiples of 4 elements,
+// base 16-byte aligned, every element offset a kernel may touch
+// representable, and a wave's 32 rows addressable with 32-bit byte offsets.
+int check_bias(const void* bias, int64_t sb, int64_t sh, int64_t si, int B, int H, int Sq,
+               int Skv, int elem) {
+    if (bias == nullptr) return ATTN_OK;
+    if (sb < 0 || sh < 0 || si < 0) return ATTN_E_SHAPE;
+    if (!aligned16(bias) || (sb & 3) || (sh & 3) || (si & 3)) return ATTN_E_ALIGN;
+    const long double last = (long double)sb * (B - 1) + (long double)sh * (H - 1) +
+                             (long double)si * (Sq - 1) + (long double)Skv + 3;
+    if (last * elem > (long double)(INT64_MAX / 2)) return ATTN_E_SHAPE;
+    if (((long double)si * 32 + Skv + 4) * elem > (long double)UINT32_MAX)
+        return ATTN_E_UNSUPPORTED;
+    return ATTN_OK;
+}
+
+// Every host-side check of attn_fwd_bias (and so of attn_fwd_ex), in the
+// documented order.
 int validate_all(const void* q, const void* k, const void* v, void* out, int B, int H, int Hkv,
                  int Sq, int Skv, int d, int dv, float scale, int dtype, const uint8_t* mask,
-                 int64_t msb, int64_t msh, int64_t msi) {
+                 int64_t msb, int64_t msh, int64_t msi, const void* bias = nullptr,
+                 int64_t bsb = 0, int64_t bsh = 0, int64_t bsi = 0) {
     if (!q || !k || !v || !out) return ATTN_E_NULL;
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_E_DTYPE;
     int st = check_shape(B, H, Hkv, Sq, Skv, d, dv);
     if (st != ATTN_OK) return st;
-    // the kernels track the maximum of the raw logits and hide keys with
-    // -inf logits, both of which assume a positive multiplier
-    if (!std::isfinite(scale) || !(scale > 0.0f)) return ATTN_E_ARG;
+    if (!std::isfinite(scale)) return ATTN_E_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_E_ALIGN;
     if (choose_path(Sq, d, dtype, dv) == kPathNone) return ATTN_E_UNSUPPORTED;
-    return check_mask(mask, msb, msh, msi, B, H, Sq, Skv);
+    st = check_mask(mask, msb, msh, msi, B, H, Sq, Skv);
+    if (st != ATTN_OK) return st;
+    return check_bias(bias, bsb, bsh, bsi, B, H, Sq, Skv, dtype == ATTN_F32 ? 4 : 2);
 }
 
 int run(const void* q, const void* k, const void* v, void* out, int B, int H, int Hkv, int Sq,
         int Skv, int d, float scale, int causal, const int32_t* kv_lens, int dtype, void* stream,
         void* workspace, size_t workspace_bytes, bool library_ws, const uint8_t* mask = nullptr,
-        int64_t msb = 0, int64_t msh = 0, int64_t msi = 0, int dv = -1) {
+        int64_t msb = 0, int64_t msh = 0, int64_t msi = 0, int dv = -1,
+        const void* bias = nullptr, int64_t bsb = 0, int64_t bsh = 0, int64_t bsi = 0) {
     if (dv < 0) dv = d;
     int st = validate_all(q, k, v, out, B, H, Hkv, Sq, Skv, d, dv, scale, dtype, mask, msb, msh,
-                          msi);
+                          msi, bias, bsb, bsh, bsi);
     if (st != ATTN_OK) return st;
     const Path path = choose_path(Sq, d, dtype, dv);
     const size_t need = attn_workspace_bytes_ex(B, H, Hkv, Sq, Skv, d, dv, dtype, mask != nullptr);
@@ -233,7 +252,7 @@ int run(const void* q, const void* k, const void* v, void* out, int B, int H, in
     }
     LaunchArgs a{q, k, v, out, B, H, Hkv, Sq, Skv, d, dv, scale, causal ? 1 : 0, kv_lens,
                  static_cast<hipStream_t>(stream), workspace, workspace_bytes, mask, msb, msh,
-                 msi};
+                 msi, bias, bsb, bsh, bsi};
     hipError_t e = hipSuccess;
     switch (path) {
         case kPathGenericF32: e = launch_generic_f32(a); break;
@@ -292,7 +311,7 @@ size_t attn_workspace_bytes_gqa(int B, int H, int Hkv, int Sq, int Skv, int d, i
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
     if (check_shape(B, H, Hkv, Sq, Skv, d, d) != ATTN_OK) return 0;
     switch (choose_path(Sq, d, dtype, d)) {
-        case kPathDecode: return decode_workspace_bytes(B, H, Hkv, Skv, d);
+        case kPathDecode: return decode_workspace_bytes(B, H, Hkv, Skv, d, d);
         case kPathPrefill: return prefill_workspace_bytes(B, H, Sq, Skv, d);
         default: return 0;
     }
@@ -304,10 +323,10 @@ size_t attn_workspace_bytes_ex(int B, int H, int Hkv, int Sq, int Skv, int d, in
     if (check_shape(B, H, Hkv, Sq, Skv, d, dv) != ATTN_OK) return 0;
     switch (choose_path(Sq, d, dtype, dv)) {
         case kPathDecode:
-            return decode_workspace_bytes(B, H, Hkv, Skv, d) +
-                   (masked ? decode_mask_workspace_bytes(B, H, Hkv, Skv, d) : 0);
+            return decode_workspace_bytes(B, H, Hkv, Skv, d, dv) +
+                   (masked ? decode_mask_workspace_bytes(B, H, Hkv, Skv, d, dv) : 0);
         case kPathPrefill:
-            return prefill_workspace_bytes(B, H, Sq, Skv, d) +
+            return prefill_workspace_bytes(B, H, Sq, Skv, dv) +
                    (masked ? prefill_mask_workspace_bytes(B, Sq, Skv) : 0);
         default: return 0;
     }
@@ -350,6 +369,27 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, i
                dv);
 }
 
+int attn_validate_bias(const void* q, const void* k, const void* v, void* out, int B, int H,
+                       int Hkv, int Sq, int Skv, int d, int dv, float scale, int causal,
+                       const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int64_t mask_si,
+                       const void* bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_si,
+                       int dtype) {
+    (void)causal;
+    return validate_all(q, k, v, out, B, H, Hkv, Sq, Skv, d, dv, scale, dtype, mask, mask_sb,
+                        mask_sh, mask_si, bias, bias_sb, bias_sh, bias_si);
+}
+
+int attn_fwd_bias(const void* q, const void* k, const void* v, void* out, int B, int H, int Hkv,
+                  int Sq, int Skv, int d, int dv, float scale, int causal,
+                  const int32_t* kv_lens, const uint8_t* mask, int64_t mask_sb, int64_t mask_sh,
+                  int64_t mask_si, const void* bias, int64_t bias_sb, int64_t bias_sh,
+                  int64_t bias_si, int dtype, void* stream, void* workspace,
+                  size_t workspace_bytes) {
+    return run(q, k, v, out, B, H, Hkv, Sq, Skv, d, scale, causal, kv_lens, dtype, stream,
+               workspace, workspace_bytes, workspace == nullptr, mask, mask_sb, mask_sh, mask_si,
+               dv, bias, bias_sb, bias_sh, bias_si);
+}
+
 int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int Sq,
              int Skv, int d, float scale, int causal, const int32_t* kv_lens, int dtype,
              void* stream) {
@@ -375,9 +415,9 @@ const char* attn_status_string(int status) {
         case ATTN_E_DTYPE: return "unknown dtype";
         case ATTN_E_ALIGN:
             return "pointer not aligned (16 bytes; workspace 256 bytes; mask and its strides 4 "
-                   "bytes)";
+                   "bytes; bias strides 4 elements)";
         case ATTN_E_WORKSPACE: return "workspace too small";
-        case ATTN_E_ARG: return "scale is not finite and positive";
+        case ATTN_E_ARG: return "scale is not finite";
         case ATTN_E_LAUNCH: return "HIP launch or runtime failure";
         case ATTN_E_NOMEM: return "device allocation failed";
         case ATTN_E_SCRATCH:

@@ -37,6 +37,9 @@
 // in a large capacity (lengths U[16, 512] of 8192) a grid of 128-key splits,
 // almost all empty, took 4.8x as long.
 //
+// V rows and outputs may have a width DV other than the D of K (each 64 or
+// 128): Q K^T runs over D, P V over DV, and the partials hold DV columns.
+//
 // Allowed-mask (the MASK instantiations: a byte per query head and key,
 // nonzero = visible, ANDed with the length rule).  A pre-pass lists, per
 // pair, the key tiles that some served head may see; the stream kernel shares
@@ -45,6 +48,14 @@
 // A pair with no visible tile writes no partial, and its heads are written as
 // 0, as is a head whose visible tiles hold no key it may see (l = 0).
 //
+// General logits (the GEN instantiations): with an additive bias (the
+// float mask of "Attention from Scratch", KubeDojo module 1.4.3, Part 7,
+// added to each scaled logit; -inf hides the key) or a scale that is not
+// positive, each score becomes scale * s + bias before the online softmax,
+// which then tracks the maximum of those logits.  The lane's 16 bias values
+// of a tile (8-byte groups of 4 keys of its query head's row) are loaded
+// with the next tile's K/V rows; without a bias a zero array is read.
+//
 // Combine kernel: per (b, h), merges the pair's partials with the
 // log-sum-exp rule  M = max m_s,  l = sum l_s 2^(m_s - M),
 // out = (sum acc_s 2^(m_s - M)) / l, and rounds to bf16.  L_b = 0 gives 0.
@@ -52,6 +63,7 @@
 // softmax unchanged.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -94,14 +106,16 @@ __device__ __forceinline__ void mfma_load_q(const uint16_t* __restrict__ q, int 
 // key_i = k0 + 32 i; with MASK, key_i = 32 tl[i] (a list of visible tiles)
 // and mrow is the allowed-mask row of the lane's query head (words past mlast
 // never read).
-template <int D, bool MASK>
+template <int D, int DV, bool MASK, bool GEN>
 __device__ __forceinline__ void mfma_keys(const u32x4 (&qf)[D / 16], const uint16_t* __restrict__ kb,
                                           const uint16_t* __restrict__ vb, int k0, int n, int klim,
                                           const int* __restrict__ tl, float scale_log2,
                                           const uint8_t* __restrict__ mrow, int mlast,
+                                          const uint16_t* __restrict__ brow, int blast, float scale,
                                           uint16_t* lds_k, uint16_t* lds_v,
-                                          f32x16 (&oacc)[D / 32], float& m_run, float& l_run) {
-    using C = MfmaDecode<D>;
+                                          f32x16 (&oacc)[DV / 32], float& m_run, float& l_run) {
+    using C = MfmaDecode<D>;    // the key side (D features)
+    using CV = MfmaDecode<DV>;  // the value side (DV features)
     const int lane = threadIdx.x;
     const int half = lane >> 5;
     const int jh = lane & 31;
@@ -135,17 +149,44 @@ __device__ __forceinline__ void mfma_keys(const u32x4 (&qf)[D / 16], const uint1
         }
     };
 
+    // GEN: bias of this lane's query head for a 32-key tile: group g holds
+    // keys 8 g + 4 half .. +3, those of score elements 4 g .. +3 (offsets
+    // clamped to the row's last readable group, as the mask words are)
+    u32x2 bw[4], bw_next[4];
+    auto load_b = [&](int t0, u32x2 (&dst)[4]) {
+        if constexpr (GEN) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                dst[g] = *reinterpret_cast<const u32x2*>(brow + min(t0 + 8 * g + 4 * half, blast));
+        }
+    };
+
     // K and V tile rows whole (kRows rows per load, lane%kChunks the 16-byte
     // chunk).  Rows at or past klim are redirected to the tile's first row
     // (valid; their logits are masked).
-    u32x4 kr[C::kLoads], vr[C::kLoads];
+    u32x4 kr[C::kLoads], vr[CV::kLoads];
     auto load_kv = [&](int t0) {
+        if constexpr (D == DV) {  // K and V rows of one tile side by side
 #pragma unroll
-        for (int c2 = 0; c2 < C::kLoads; ++c2) {
-            const int row = t0 + c2 * C::kRows + lane / C::kChunks;
-            const size_t off = (size_t)(row < klim ? row : t0) * D + (lane % C::kChunks) * 8;
-            kr[c2] = ldg16_stream(kb + off);
-            vr[c2] = ldg16_stream(vb + off);
+            for (int c2 = 0; c2 < C::kLoads; ++c2) {
+                const int row = t0 + c2 * C::kRows + lane / C::kChunks;
+                const size_t off = (size_t)(row < klim ? row : t0) * D + (lane % C::kChunks) * 8;
+                kr[c2] = ldg16_stream(kb + off);
+                vr[c2] = ldg16_stream(vb + off);
+            }
+        } else {
+#pragma unroll
+            for (int c2 = 0; c2 < C::kLoads; ++c2) {
+                const int row = t0 + c2 * C::kRows + lane / C::kChunks;
+                kr[c2] = ldg16_stream(kb + (size_t)(row < klim ? row : t0) * D +
+                                      (lane % C::kChunks) * 8);
+            }
+#pragma unroll
+            for (int c2 = 0; c2 < CV::kLoads; ++c2) {
+                const int row = t0 + c2 * CV::kRows + lane / CV::kChunks;
+                vr[c2] = ldg16_stream(vb + (size_t)(row < klim ? row : t0) * DV +
+                                      (lane % CV::kChunks) * 8);
+            }
         }
     };
     // K operand of S^T from LDS: row lane%32, features 16*ks + 8*(lane/32)
@@ -156,10 +197,10 @@ __device__ __forceinline__ void mfma_keys(const u32x4 (&qf)[D / 16], const uint1
     //  (and 12..15) of each 16-key step, matching their P^T fragment.
     const int n16 = lane & 15;
     const int v_rd =
-        (4 * half + (n16 >> 2)) * C::kStrideV + 16 * ((lane >> 4) & 1) + 4 * (n16 & 3);
+        (4 * half + (n16 >> 2)) * CV::kStrideV + 16 * ((lane >> 4) & 1) + 4 * (n16 & 3);
 
 #pragma unroll
-    for (int db = 0; db < C::kDBlocks; ++db)
+    for (int db = 0; db < CV::kDBlocks; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
     m_run = -INFINITY;
@@ -168,13 +209,21 @@ __device__ __forceinline__ void mfma_keys(const u32x4 (&qf)[D / 16], const uint1
     int t0 = tile_key(0);
     load_kv(t0);
     load_m(t0, mw);
+    load_b(t0, bw);
     for (int i = 0; i < n; ++i) {
         // K(t0), V(t0) to LDS; the next tile's loads reuse their registers
 #pragma unroll
         for (int c2 = 0; c2 < C::kLoads; ++c2) {
             const int r = c2 * C::kRows + lane / C::kChunks, col = (lane % C::kChunks) * 8;
             *reinterpret_cast<u32x4*>(lds_k + r * C::kStrideK + col) = kr[c2];
-            *reinterpret_cast<u32x4*>(lds_v + r * C::kStrideV + col) = vr[c2];
+            if constexpr (D == DV) *reinterpret_cast<u32x4*>(lds_v + r * CV::kStrideV + col) = vr[c2];
+        }
+        if constexpr (D != DV) {
+#pragma unroll
+            for (int c2 = 0; c2 < CV::kLoads; ++c2) {
+                const int r = c2 * CV::kRows + lane / CV::kChunks, col = (lane % CV::kChunks) * 8;
+                *reinterpret_cast<u32x4*>(lds_v + r * CV::kStrideV + col) = vr[c2];
+            }
         }
         __syncthreads();
         if constexpr (MASK) {
@@ -189,6 +238,7 @@ __device__ __forceinline__ void mfma_keys(const u32x4 (&qf)[D / 16], const uint1
         if (next) {
             load_kv(t1);
             load_m(t1, mw_next);
+            load_b(t1, bw_next);
         }
 
         // S^T = K Q^T for 32 keys x 32 heads, K operands read kAheadK ahead
@@ -207,6 +257,16 @@ __device__ __forceinline__ void mfma_keys(const u32x4 (&qf)[D / 16], const uint1
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, ka[ks % (C::kAheadK + 1)]),
                 __builtin_bit_cast(bf16x8, qf[ks]), sacc, 0, 0, 0);
+        }
+        if constexpr (GEN) {
+            // logits scale * s + bias
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const uint32_t wd = bw[r >> 2][(r & 3) >> 1];
+                sacc[r] = fmaf(sacc[r], scale, (r & 1) ? bf16_hi(wd) : bf16_lo(wd));
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) bw[g] = bw_next[g];
         }
         bool cut = t0 + 32 > klim;
         if constexpr (MASK) {
@@ -240,7 +300,7 @@ __device__ __forceinline__ void mfma_keys(const u32x4 (&qf)[D / 16], const uint1
             m_run = grow ? m_new : m_run;
             l_run *= alpha;
 #pragma unroll
-            for (int db = 0; db < C::kDBlocks; ++db)
+            for (int db = 0; db < CV::kDBlocks; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
@@ -258,12 +318,12 @@ __device__ __forceinline__ void mfma_keys(const u32x4 (&qf)[D / 16], const uint1
             }
         // O^T += V^T P^T, output blocks innermost
 #pragma unroll
-        for (int st = 0; st < 2 * C::kDBlocks; ++st) {
-            const int db = st % C::kDBlocks, kk = st / C::kDBlocks;
-            const uint16_t* a1 = lds_v + v_rd + kk * 16 * C::kStrideV + db * 32;
+        for (int st = 0; st < 2 * CV::kDBlocks; ++st) {
+            const int db = st % CV::kDBlocks, kk = st / CV::kDBlocks;
+            const uint16_t* a1 = lds_v + v_rd + kk * 16 * CV::kStrideV + db * 32;
             const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TSDA_LDS i16x4*)(a1));
             const i16x4 x1 =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((TSDA_LDS i16x4*)(a1 + 8 * C::kStrideV));
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((TSDA_LDS i16x4*)(a1 + 8 * CV::kStrideV));
             u32x4 a;
             a[0] = (uint32_t)(uint16_t)x0[0] | ((uint32_t)(uint16_t)x0[1] << 16);
             a[1] = (uint32_t)(uint16_t)x0[2] | ((uint32_t)(uint16_t)x0[3] << 16);
@@ -392,16 +452,21 @@ __global__ __launch_bounds__(256) void decode_mask_tiles_kernel(
 // head row jh of it; span[2p] and span[2p+1] receive the waves that hold the
 // pair's first and last tile, so the combine reads slots span[2p] + p ..
 // span[2p+1] + p.
-template <int D, bool MASK>
+// Zero bias for GEN calls without one (read as its first 4-element group).
+__device__ __attribute__((aligned(16))) uint16_t g_zero_bias_dec[8];
+
+template <int D, int DV, bool MASK, bool GEN>
 __global__ __launch_bounds__(64, 2) void decode_stream_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ kv_lens, int B, int H, int Hkv,
     int Skv, float scale_log2, int hgroups, int min_tiles, int min_waves,
     float* __restrict__ ws_acc, float* __restrict__ ws_ml, int* __restrict__ span,
     const uint8_t* __restrict__ mask, long long msb, long long msh,
-    const int* __restrict__ counts, const int* __restrict__ lists, int ntmax) {
+    const int* __restrict__ counts, const int* __restrict__ lists, int ntmax,
+    const uint16_t* __restrict__ bias, long long bsb, long long bsh, float scale) {
     using C = MfmaDecode<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v[32 * C::kStrideV];
+    using CV = MfmaDecode<DV>;
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v[32 * CV::kStrideV];
     __shared__ __attribute__((aligned(16))) uint16_t lds_k[32 * C::kStrideK];
 
     const int lane = threadIdx.x;
@@ -491,19 +556,31 @@ __global__ __launch_bounds__(64, 2) void decode_stream_kernel(
         u32x4 qf[C::kKSteps];
         mfma_load_q<D>(q, b, H, h0, live, qf);
         const size_t kvo = ((size_t)b * Hkv + kvh) * Skv * D;
-        f32x16 oacc[C::kDBlocks];
+        const size_t vvo = ((size_t)b * Hkv + kvh) * Skv * DV;
+        f32x16 oacc[CV::kDBlocks];
         float m_run, l_run;
+        // the bias row of the lane's query head (Sq = 1: row 0), or the zero array
+        const uint16_t* brow = nullptr;
+        int blast = 0;
+        if constexpr (GEN) {
+            brow = g_zero_bias_dec;
+            if (bias != nullptr) {
+                brow = bias + b * bsb + (long long)(h0 + (live ? jh : 0)) * bsh;
+                blast = bias_last_group(Skv);
+            }
+        }
         if constexpr (MASK) {
             const uint8_t* mrow = mask + b * msb + (long long)(h0 + (live ? jh : 0)) * msh;
-            mfma_keys<D, true>(qf, k + kvo, v + kvo, 0, seg, L, lists + pr * ntmax + t,
-                               scale_log2, mrow, mlast, lds_k, lds_v, oacc, m_run, l_run);
+            mfma_keys<D, DV, true, GEN>(qf, k + kvo, v + vvo, 0, seg, L, lists + pr * ntmax + t,
+                                    scale_log2, mrow, mlast, brow, blast, scale, lds_k, lds_v,
+                                    oacc, m_run, l_run);
         } else {
-            mfma_keys<D, false>(qf, k + kvo, v + kvo, 32 * t, seg, min(32 * (t + seg), L),
-                                nullptr, scale_log2, nullptr, 0, lds_k, lds_v, oacc, m_run,
-                                l_run);
+            mfma_keys<D, DV, false, GEN>(qf, k + kvo, v + vvo, 32 * t, seg, min(32 * (t + seg), L),
+                                     nullptr, scale_log2, nullptr, 0, brow, blast, scale, lds_k,
+                                     lds_v, oacc, m_run, l_run);
         }
         const size_t uq = (size_t)(w + pr) * nhs + jh;
-        mfma_write_partial<D>(oacc, m_run, l_run, scale_log2, live, ws_acc + uq * D,
+        mfma_write_partial<DV>(oacc, m_run, l_run, scale_log2, live, ws_acc + uq * DV,
                               ws_ml + uq * 2);
         if (lane == 0) {
             if (t == 0) span[2 * pr] = w;
@@ -650,13 +727,13 @@ struct StreamLayout {
     size_t ml, span, counts, lists, total, masked_total;
     int ntmax;
 };
-StreamLayout stream_layout(int B, int H, int Hkv, int Skv, int d) {
+StreamLayout stream_layout(int B, int H, int Hkv, int Skv, int d, int dv) {
     const int group = H / Hkv, hg = (group + 31) / 32, nhs = std::min(32, group);
     const size_t pairs = (size_t)B * Hkv * hg;
     const size_t rows = ((size_t)stream_wave_cap(B, Hkv, hg, Skv, d) + pairs) * nhs;
     StreamLayout l;
     l.ntmax = (Skv + 31) / 32;
-    l.ml = round256(rows * d * sizeof(float));
+    l.ml = round256(rows * dv * sizeof(float));
     l.span = l.ml + round256(rows * 2 * sizeof(float));
     l.total = l.span + round256(pairs * 2 * sizeof(int));
     l.counts = l.total;
@@ -665,15 +742,36 @@ StreamLayout stream_layout(int B, int H, int Hkv, int Skv, int d) {
     return l;
 }
 
+// Calls go(decode_stream_kernel<D, DV, MASK, GEN>) for d, dv in {64, 128}.
+template <class Go>
+void with_stream_kernel(int d, int dv, bool masked, bool gen, Go&& go) {
+    auto pick = [&](auto dk, auto dvk) {
+        constexpr int D = decltype(dk)::value, DV = decltype(dvk)::value;
+        if (gen)
+            masked ? go(decode_stream_kernel<D, DV, true, true>)
+                   : go(decode_stream_kernel<D, DV, false, true>);
+        else
+            masked ? go(decode_stream_kernel<D, DV, true, false>)
+                   : go(decode_stream_kernel<D, DV, false, false>);
+    };
+    using I64 = std::integral_constant<int, 64>;
+    using I128 = std::integral_constant<int, 128>;
+    if (d == 128)
+        dv == 128 ? pick(I128{}, I128{}) : pick(I128{}, I64{});
+    else
+        dv == 128 ? pick(I64{}, I128{}) : pick(I64{}, I64{});
+}
+
 // Waves of the stream kernel the current device holds at once (compute
 // units x resident waves per unit), cached per device, head size and mask
-// flag (the masked d = 64 kernel holds more registers).
-int stream_resident_waves(int d, bool masked) {
+// and general-logit flags (the masked and general kernels hold more
+// registers).
+int stream_resident_waves(int d, int dv, bool masked, bool gen) {
     constexpr int kDevices = 64;
-    static std::atomic<int> cache[kDevices][4];
+    static std::atomic<int> cache[kDevices][16];
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-    const int ki = (d == 128 ? 0 : 2) + (masked ? 1 : 0);
+    const int ki = (d == 128 ? 0 : 8) + (dv == 128 ? 0 : 4) + (gen ? 2 : 0) + (masked ? 1 : 0);
     const bool cached = dev >= 0 && dev < kDevices;
     if (cached) {
         const int c = cache[dev][ki].load(std::memory_order_relaxed);
@@ -686,10 +784,8 @@ int stream_resident_waves(int d, bool masked) {
     auto query = [&](auto kern) {
         return hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, 64, 0);
     };
-    const hipError_t e = ki == 0   ? query(decode_stream_kernel<128, false>)
-                         : ki == 1 ? query(decode_stream_kernel<128, true>)
-                         : ki == 2 ? query(decode_stream_kernel<64, false>)
-                                   : query(decode_stream_kernel<64, true>);
+    hipError_t e = hipSuccess;
+    with_stream_kernel(d, dv, masked, gen, [&](auto kern) { e = query(kern); });
     if (e != hipSuccess || per <= 0) {
         (void)hipGetLastError();  // a failed query leaves no error for the launches
         per = d == 128 ? 8 : 12;
@@ -701,17 +797,17 @@ int stream_resident_waves(int d, bool masked) {
 
 }  // namespace
 
-size_t decode_workspace_bytes(int B, int H, int Hkv, int Skv, int d) {
-    return stream_layout(B, H, Hkv, Skv, d).total;
+size_t decode_workspace_bytes(int B, int H, int Hkv, int Skv, int d, int dv) {
+    return stream_layout(B, H, Hkv, Skv, d, dv).total;
 }
 
-size_t decode_mask_workspace_bytes(int B, int H, int Hkv, int Skv, int d) {
-    const StreamLayout l = stream_layout(B, H, Hkv, Skv, d);
+size_t decode_mask_workspace_bytes(int B, int H, int Hkv, int Skv, int d, int dv) {
+    const StreamLayout l = stream_layout(B, H, Hkv, Skv, d, dv);
     return l.masked_total - l.total;
 }
 
 hipError_t launch_decode_bf16(const LaunchArgs& a) {
-    const StreamLayout l = stream_layout(a.B, a.H, a.Hkv, a.Skv, a.d);
+    const StreamLayout l = stream_layout(a.B, a.H, a.Hkv, a.Skv, a.d, a.dv);
     // the front end sizes the workspace; refuse rather than write through a bad one
     if (a.workspace == nullptr || a.workspace_bytes < (a.mask ? l.masked_total : l.total))
         return hipErrorInvalidValue;
@@ -722,12 +818,14 @@ hipError_t launch_decode_bf16(const LaunchArgs& a) {
     int* span = reinterpret_cast<int*>(ws + l.span);
     int* counts = a.mask ? reinterpret_cast<int*>(ws + l.counts) : nullptr;
     int* lists = a.mask ? reinterpret_cast<int*>(ws + l.lists) : nullptr;
-    const int resident = stream_resident_waves(a.d, a.mask != nullptr);
+    // the general instantiation for a bias or a scale that is not positive
+    const bool gen = a.bias != nullptr || !(a.scale > 0.0f);
+    const int resident = stream_resident_waves(a.d, a.dv, a.mask != nullptr, gen);
     const int waves =
         (int)std::min((long)resident, stream_wave_cap(a.B, a.Hkv, hgroups, a.Skv, a.d));
     const int min_tiles = stream_min_tiles(a.H, a.Hkv);
     const int min_waves = std::max(1, resident / 4);
-    const float sl = a.scale * kLog2e;
+    const float sl = gen ? kLog2e : a.scale * kLog2e;
     const uint16_t* q = static_cast<const uint16_t*>(a.q);
     const uint16_t* k = static_cast<const uint16_t*>(a.k);
     const uint16_t* v = static_cast<const uint16_t*>(a.v);
@@ -747,19 +845,17 @@ hipError_t launch_decode_bf16(const LaunchArgs& a) {
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3(waves), dim3(64), 0, a.stream, q, k, v, a.kv_lens, a.B, a.H,
                            a.Hkv, a.Skv, sl, hgroups, min_tiles, min_waves, acc, ml, span, a.mask,
-                           a.msb, a.msh, counts, lists, l.ntmax);
+                           a.msb, a.msh, counts, lists, l.ntmax,
+                           static_cast<const uint16_t*>(a.bias), a.bsb, a.bsh, a.scale);
     };
     if (t) t->begin(kDecodePartialBf16, a.stream);
-    if (a.d == 128)
-        a.mask ? go(decode_stream_kernel<128, true>) : go(decode_stream_kernel<128, false>);
-    else
-        a.mask ? go(decode_stream_kernel<64, true>) : go(decode_stream_kernel<64, false>);
+    with_stream_kernel(a.d, a.dv, a.mask != nullptr, gen, go);
     e = hipGetLastError();
     if (t) t->end(kDecodePartialBf16, a.stream);
     if (e != hipSuccess) return e;
     if (t) t->begin(kDecodeCombineBf16, a.stream);
     const unsigned heads = (unsigned)((size_t)a.B * a.H);
-    if (a.d == 128)
+    if (a.dv == 128)
         hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(heads), dim3(256), 0, a.stream,
                            a.kv_lens, a.H, a.Hkv, a.Skv, hgroups, acc, ml, span, counts, o);
     else

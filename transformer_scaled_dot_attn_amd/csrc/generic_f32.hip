@@ -15,7 +15,10 @@
 // words of the lane's row per tile; a row with no visible key is 0.  The
 // value width d_v may differ from d (the d_v != d_k case of "Attention from
 // Scratch", KubeDojo module 1.4.3, Part 2): K rows have d features, V and
-// output rows d_v.
+// output rows d_v.  An additive bias (the float mask of that page's Part 7,
+// added to the scaled logits; -inf hides the key) is read as eight 16-byte
+// groups of the lane's row per tile.  The kernel keeps the maximum of the
+// scaled logits, so any finite scale works.
 #include "device_common.h"
 #include "launch.h"
 
@@ -31,7 +34,8 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ out, const int32_t* __restrict__ kv_lens, int H, int Hkv, int Sq, int Skv,
     int d, int dv, float scale_log2, int causal, const uint8_t* __restrict__ mask, long long msb,
-    long long msh, long long msi) {
+    long long msh, long long msi, const float* __restrict__ bias, long long bsb, long long bsh,
+    long long bsi) {
     __shared__ float ks[kKeys][DP];
     __shared__ float vs[kKeys][DPV];
 
@@ -68,6 +72,12 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
     if constexpr (MASK)
         mrow = mask + b * msb + (long long)(bh - b * H) * msh + (long long)(live ? i : 0) * msi;
     const int mlast = mask_last_word(Skv);
+    // this lane's bias row (groups past the row's end are clamped: their keys
+    // are >= Skv >= L and hidden)
+    const float* brow = nullptr;
+    if (bias != nullptr)
+        brow = bias + b * bsb + (long long)(bh - b * H) * bsh + (long long)(live ? i : 0) * bsi;
+    const int blast = bias_last_group(Skv);
     const float* kb = k + (size_t)bk * Skv * d;
     const float* vb = v + (size_t)bk * Skv * dv;
     for (int j0 = 0; j0 < kv_hi; j0 += kKeys) {
@@ -107,6 +117,14 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
                     if (!byte_set(word, e)) mbits &= ~(1u << (4 * w + e));
             }
         }
+        f32x4 bw[kKeys / 4];  // the bias of keys j0 + 4 w .. +3, times log2 e
+#pragma unroll
+        for (int w = 0; w < kKeys / 4; ++w) bw[w] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (brow != nullptr) {
+#pragma unroll
+            for (int w = 0; w < kKeys / 4; ++w)
+                bw[w] = *reinterpret_cast<const f32x4*>(brow + min(j0 + 4 * w, blast)) * kLog2e;
+        }
         float s[kKeys];
         float tmax = -INFINITY;
 #pragma unroll
@@ -117,7 +135,7 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
             const int j = j0 + r;
             bool vis = r < nk && (!causal || j <= p);
             if constexpr (MASK) vis = vis & (((mbits >> r) & 1u) != 0);  // no short circuit: keeps the loop straight-line
-            s[r] = vis ? dot * scale_log2 : -INFINITY;
+            s[r] = vis ? fmaf(dot, scale_log2, bw[r >> 2][r & 3]) : -INFINITY;
             tmax = fmaxf(tmax, s[r]);
         }
         const float m_new = fmaxf(m, tmax);
@@ -173,7 +191,8 @@ hipError_t launch_generic_f32(const LaunchArgs& a) {
     if (t) t->begin(kGenericF32, a.stream);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, a.stream, q, k, v, o, a.kv_lens, a.H, a.Hkv, a.Sq,
-                           a.Skv, a.d, a.dv, sl, a.causal, a.mask, a.msb, a.msh, a.msi);
+                           a.Skv, a.d, a.dv, sl, a.causal, a.mask, a.msb, a.msh, a.msi,
+                           static_cast<const float*>(a.bias), a.bsb, a.bsh, a.bsi);
     };
     // d and d_v rounded up to 16, 32, 64 or 128 (d, d_v <= 128 is checked by the front end)
     auto width = [](int x) { return x <= 16 ? 0 : x <= 32 ? 1 : x <= 64 ? 2 : 3; };

@@ -12,7 +12,7 @@ struct LaunchArgs {
     const void* v;
     void* out;
     int B, H, Hkv, Sq, Skv, d;  // Hkv key/value heads; query head h reads K/V head h / (H / Hkv)
-    int dv;                     // value / output width (== d on the bf16 paths)
+    int dv;                     // value / output width
     float scale;
     int causal;
     const int32_t* kv_lens;
@@ -24,7 +24,16 @@ struct LaunchArgs {
     // front end), each row readable up to Skv rounded up to 4.  nullptr: none.
     const uint8_t* mask;
     long long msb, msh, msi;
+    // optional additive bias, elements of the inputs' type: element (b, h, i,
+    // j) at bias[b*bsb + h*bsh + i*bsi + j], added to the scaled logit; -inf
+    // hides the key.  16-byte aligned, strides multiples of 4 (checked by the
+    // front end), each row readable up to Skv rounded up to 4.  nullptr: none.
+    const void* bias;
+    long long bsb, bsh, bsi;
 };
+
+// Last 4-element group offset of a bias row that a kernel may read.
+__host__ __device__ inline int bias_last_group(int Skv) { return ((Skv + 3) & ~3) - 4; }
 
 // Last 4-byte word offset of a mask row that a kernel may read.
 __host__ __device__ inline int mask_last_word(int Skv) { return ((Skv + 3) & ~3) - 4; }
@@ -32,15 +41,15 @@ __host__ __device__ inline int mask_last_word(int Skv) { return ((Skv + 3) & ~3)
 // Decode workspace: the stream kernel's partials and pair spans; with an
 // allowed-mask, plus decode_mask_workspace_bytes for the pairs' visible-tile
 // counts and lists.
-size_t decode_workspace_bytes(int B, int H, int Hkv, int Skv, int d);
-size_t decode_mask_workspace_bytes(int B, int H, int Hkv, int Skv, int d);
+size_t decode_workspace_bytes(int B, int H, int Hkv, int Skv, int d, int dv);
+size_t decode_mask_workspace_bytes(int B, int H, int Hkv, int Skv, int d, int dv);
 
 // Prefill plan: key-range splits per query tile (1 = none, no workspace).
 struct PrefillPlan {
     int nsplit;
 };
 PrefillPlan prefill_plan(int B, int H, int Sq, int Skv);
-size_t prefill_workspace_bytes(int B, int H, int Sq, int Skv, int d);
+size_t prefill_workspace_bytes(int B, int H, int Sq, int Skv, int dv);  // dv: partial width
 // extra bytes a masked prefill needs for its key-tile marks (after the above)
 size_t prefill_mask_workspace_bytes(int B, int Sq, int Skv);
 

@@ -65,6 +65,15 @@
 // cost only the tiles they open.  The loop then runs over list positions:
 // LDS ring slots follow the position, key offsets and masks the listed tile.
 //
+// General logits (the GEN instantiation).  An additive bias (the float mask
+// of "Attention from Scratch", KubeDojo module 1.4.3, Part 7: a value added
+// to each scaled logit before the softmax; -inf hides the key), or a scale
+// that is not positive: each score is rewritten as scale * s + bias before
+// the online softmax, which then tracks the maximum of those logits.  The
+// lane's 32 bias values of a tile (8-byte groups of 4 keys) are loaded two
+// tiles ahead, under the P V MFMAs, and parked in a per-lane LDS slot like
+// the mask words.  Without a bias the kernel reads a zero array instead.
+//
 // Order.  Block ids are mapped heaviest query tile first; within a query
 // tile rank the (b, h) pairs are laid out so that each XCD (ids are dealt
 // round-robin over the 8 XCDs) runs whole heads -- every tile of a head, and
@@ -75,7 +84,13 @@
 // Grouped key/value heads (GQA / MQA): query head h reads K/V head
 // h / (H / Hkv) ("Attention from First Principles", section "MHA, GQA, MQA
 // -- the KV cache lever"); nothing else changes.
+//
+// Value width.  V rows and outputs have DV features, K rows D (each 64 or
+// 128): softmax(Q K^T) V needs V's rows to line up with K's, not its width
+// to match (the d_k = 4, d_v = 2 example of "Attention from Scratch",
+// KubeDojo module 1.4.3, Part 2).  Q K^T runs over D, P V over DV.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -118,20 +133,26 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast
 // a batch of LDS reads issued ahead of the MFMAs that consume them.
 __device__ __forceinline__ void pin_schedule() { __builtin_amdgcn_sched_barrier(0); }
 
-template <int D, bool MASK>
+// Zero bias for GEN calls without one (read as its first 4-element group).
+__device__ __attribute__((aligned(16))) uint16_t g_zero_bias[8];
+
+template <int D, int DV, bool MASK, bool GEN>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
     const int32_t* __restrict__ kv_lens, int BH, int H, int Hkv, int Sq, int Skv, float scale_log2,
     int causal, int nqt, int nsplit, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     const uint8_t* __restrict__ allowed, long long msb, long long msh, long long msi,
-    const uint8_t* __restrict__ tmap, int nkt) {
-    using S = Shape<D>;
+    const uint8_t* __restrict__ tmap, int nkt, const uint16_t* __restrict__ bias, long long bsb,
+    long long bsh, long long bsi, float scale) {
+    using S = Shape<D>;    // the key side: Q K^T over D features
+    using SV = Shape<DV>;  // the value side: V rows and outputs of DV features
     __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][S::kTileK];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][S::kTileV];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][SV::kTileV];
     __shared__ u32x4 lds_m[MASK ? 2 * kThreads : 1];  // parked mask words, 32 bytes per lane
     __shared__ int lds_tl[MASK ? kMaxListTiles : 1];  // this query tile's listed key tiles
     __shared__ int lds_tn;                            // their number
+    __shared__ u32x4 lds_b[GEN ? 4 * kThreads : 1];   // parked bias, 64 bytes per lane
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -173,13 +194,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int qz = qt * kBM;
     const int q0 = MASK ? qz : n - (nqt - qt) * kBM;
 
-    uint16_t* obase = out + (size_t)bh * Sq * D;
+    uint16_t* obase = out + (size_t)bh * Sq * DV;
     // pad rows are zero (without splits; the split combine zeroes them itself)
     const int z0 = max(qz, n), z1 = min(qz + kBM, Sq);
     if (nsplit == 1 && z0 < z1 && (!MASK || q0 >= n)) {
         const u32x4 z = {0, 0, 0, 0};
-        for (int e = tid; e < (z1 - z0) * S::kChunks; e += kThreads)
-            *reinterpret_cast<u32x4*>(obase + (size_t)z0 * D + e * 8) = z;
+        for (int e = tid; e < (z1 - z0) * SV::kChunks; e += kThreads)
+            *reinterpret_cast<u32x4*>(obase + (size_t)z0 * DV + e * 8) = z;
     }
     if (q0 >= n || q0 + kBM <= 0) return;  // no valid row in this tile
 
@@ -297,6 +318,52 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         }
     };
 
+    // ---- bias of this lane's query row for one key tile (GEN): group
+    // (kb, g) holds keys 32 kb + 8 g + 4 half .. +3, those of score elements
+    // 4 g .. 4 g + 3 of block kb.  Addressed like the mask words: a
+    // wave-uniform row base plus a 32-bit lane offset; group offsets are
+    // clamped to the row's last readable group (keys past it are >= Skv >= L
+    // and hidden).  Without a bias every group reads the zero array.
+    u32x2 bw[2][4];
+    const uint8_t* bbase = nullptr;  // byte addresses: 32-bit lane offsets below 2^32
+    uint32_t blane = 0;
+    int blast = 0;
+    if constexpr (GEN) {
+        // without a mask a tile's first waves may start at a negative row
+        // (tiles end at the last valid row): the base row is clamped to 0
+        const int r0 = __builtin_amdgcn_readfirstlane(min(max(qw, 0), Sq - 1));
+        if (bias != nullptr) {
+            bbase = reinterpret_cast<const uint8_t*>(bias + b * bsb + (long long)(bh - b * H) * bsh +
+                                                     (long long)r0 * bsi);
+            blane = q_live ? 2u * (uint32_t)(qi - r0) * (uint32_t)bsi : 0u;
+            blast = bias_last_group(Skv);
+        } else {
+            bbase = reinterpret_cast<const uint8_t*>(g_zero_bias);
+        }
+    }
+    auto bload = [&](int tile) {
+        if constexpr (GEN) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int j = tile * kBN + 32 * kb + 8 * g + 4 * half;
+                    bw[kb][g] = *reinterpret_cast<const u32x2*>(
+                        bbase + (blane + 2u * (uint32_t)min(j, blast)));
+                }
+        }
+    };
+    auto bpark = [&]() {
+        if constexpr (GEN) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2)
+                    lds_b[4 * tid + 2 * kb + h2] = u32x4{bw[kb][2 * h2][0], bw[kb][2 * h2][1],
+                                                         bw[kb][2 * h2 + 1][0], bw[kb][2 * h2 + 1][1]};
+        }
+    };
+
     // ---- tile staging: thread t moves 16-byte chunks t + 512 i of the
     // row-major tile, so consecutive threads read consecutive global bytes.
     // The loads are branch-free, so they stay in flight through the compute
@@ -308,13 +375,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int st_row = tid / S::kChunks;
     const int st_col = (tid % S::kChunks) * 8;
     const size_t head_off = (size_t)bk * Skv * D + st_col;
-    u32x4 kreg[S::kPerThread], vreg[S::kPerThread];
-    auto fetch = [&](const uint16_t* __restrict__ src, int tile, u32x4 (&dst)[S::kPerThread]) {
+    const int st_row_v = tid / SV::kChunks;
+    const int st_col_v = (tid % SV::kChunks) * 8;
+    const size_t head_off_v = (size_t)bk * Skv * DV + st_col_v;
+    u32x4 kreg[S::kPerThread], vreg[SV::kPerThread];
+    auto fetch_k = [&](int tile) {
         const int kbase = tile * kBN;
 #pragma unroll
         for (int i = 0; i < S::kPerThread; ++i) {
             const int row = kbase + st_row + i * S::kRowsPerPass;
-            dst[i] = ldg16(src + head_off + (size_t)min(row, L - 1) * D);
+            kreg[i] = ldg16(k + head_off + (size_t)min(row, L - 1) * D);
+        }
+    };
+    auto fetch_v = [&](int tile) {
+        const int kbase = tile * kBN;
+#pragma unroll
+        for (int i = 0; i < SV::kPerThread; ++i) {
+            const int row = kbase + st_row_v + i * SV::kRowsPerPass;
+            vreg[i] = ldg16(v + head_off_v + (size_t)min(row, L - 1) * DV);
         }
     };
     auto stash_k = [&](int tile) {
@@ -324,10 +402,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
             *reinterpret_cast<u32x4*>(dk + i * S::kRowsPerPass * S::kStrideK) = kreg[i];
     };
     auto stash_v = [&](int tile) {
-        uint16_t* dv = lds_v[tile & 1] + st_row * S::kStrideV + st_col;
+        uint16_t* dv = lds_v[tile & 1] + st_row_v * SV::kStrideV + st_col_v;
 #pragma unroll
-        for (int i = 0; i < S::kPerThread; ++i)
-            *reinterpret_cast<u32x4*>(dv + i * S::kRowsPerPass * S::kStrideV) = vreg[i];
+        for (int i = 0; i < SV::kPerThread; ++i)
+            *reinterpret_cast<u32x4*>(dv + i * SV::kRowsPerPass * SV::kStrideV) = vreg[i];
     };
 
     // Per-lane LDS read bases (element offsets within a slot).
@@ -339,11 +417,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     //  second half take keys 4..7 (and 12..15) of each 16-key step, which
     //  matches the keys their P^T fragment holds.
     const int n16 = lane & 15;
-    const int v_rd = (4 * half + (n16 >> 2)) * S::kStrideV + 16 * ((lane >> 4) & 1) + 4 * (n16 & 3);
+    const int v_rd = (4 * half + (n16 >> 2)) * SV::kStrideV + 16 * ((lane >> 4) & 1) + 4 * (n16 & 3);
 
-    f32x16 oacc[S::kDBlocks];
+    f32x16 oacc[SV::kDBlocks];
 #pragma unroll
-    for (int db = 0; db < S::kDBlocks; ++db)
+    for (int db = 0; db < SV::kDBlocks; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
     float m_run = -INFINITY;  // reference maximum of raw logits (this lane's query)
@@ -352,7 +430,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     u32x4 pf[2][2];           // P^T fragments of the tile being mixed
 
     constexpr int kQK = 2 * S::kKSteps;       // MFMAs of S^T per tile
-    constexpr int kHalf = 2 * S::kDBlocks;    // P V MFMAs per 32-key block
+    constexpr int kHalf = 2 * SV::kDBlocks;   // P V MFMAs per 32-key block
     constexpr int kPV = 2 * kHalf;            // P V MFMAs per tile
     constexpr int kAheadK = 2;                // K operand k-steps in flight
     constexpr int kAheadV = 3;                // V operands in flight
@@ -439,6 +517,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int lim = causal ? min(p, L - 1) : L - 1;
     auto mask = [&](int tile, f32x16 (&sn)[2]) {
         const int kbase = tile * kBN;
+        if constexpr (GEN) {
+            // logits scale * s + bias (the parked bias of this tile)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const u32x4 w4 = lds_b[4 * tid + 2 * kb + h2];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int r = 8 * h2 + e;  // groups 2 h2, 2 h2 + 1: elements 8 h2 .. +7
+                        const uint32_t wd = w4[e >> 1];
+                        const float bv = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
+                        sn[kb][r] = fmaf(sn[kb][r], scale, bv);
+                    }
+                    pin_schedule();  // one 16-byte group in registers at a time
+                }
+        }
         u32x4 mk[2] = {{~0u, ~0u, ~0u, ~0u}, {~0u, ~0u, ~0u, ~0u}};
         if (kbase + kBN > kfull_w) {
             // the rules cut this tile (and the allowed-mask may)
@@ -472,11 +567,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     auto mix = [&](int tile, const f32x16 (*sn)[2]) {
         const uint16_t* vl = lds_v[tile & 1] + v_rd;
         auto vread = [&](int st, i16x4 (&dst)[2]) {
-            const int db = st % S::kDBlocks, kk = st / S::kDBlocks;  // kk = 2*kb + h2
-            const uint16_t* a1 = vl + kk * 16 * S::kStrideV + db * 32;
+            const int db = st % SV::kDBlocks, kk = st / SV::kDBlocks;  // kk = 2*kb + h2
+            const uint16_t* a1 = vl + kk * 16 * SV::kStrideV + db * 32;
             dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TSDA_LDS i16x4*)(a1));
             dst[1] =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((TSDA_LDS i16x4*)(a1 + 8 * S::kStrideV));
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((TSDA_LDS i16x4*)(a1 + 8 * SV::kStrideV));
         };
         i16x4 vr[kAheadV + 1][2];
 #pragma unroll
@@ -492,9 +587,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
             a[1] = (uint32_t)(uint16_t)src[0][2] | ((uint32_t)(uint16_t)src[0][3] << 16);
             a[2] = (uint32_t)(uint16_t)src[1][0] | ((uint32_t)(uint16_t)src[1][1] << 16);
             a[3] = (uint32_t)(uint16_t)src[1][2] | ((uint32_t)(uint16_t)src[1][3] << 16);
-            const int db = st % S::kDBlocks;
+            const int db = st % SV::kDBlocks;
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                as_bf16x8(a), as_bf16x8(pf[st / kHalf][(st % kHalf) / S::kDBlocks]), oacc[db], 0, 0,
+                as_bf16x8(a), as_bf16x8(pf[st / kHalf][(st % kHalf) / SV::kDBlocks]), oacc[db], 0, 0,
                 0);
             if (sn) {
                 constexpr int kPer = 32 / kPV;
@@ -526,7 +621,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
             m_run = grow ? m_new : m_run;
             l_run *= alpha;
 #pragma unroll
-            for (int db = 0; db < S::kDBlocks; ++db)
+            for (int db = 0; db < SV::kDBlocks; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
@@ -551,10 +646,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
         const bool pipe = t + 1 < t1w;  // this wave scores tile t+1
         mpark();  // mask words of tile t+1
-        fetch(k, t + 2, kreg);
+        bpark();  // bias of tile t+1
+        fetch_k(t + 2);
         // S^T(t+1) under which P(t) is formed
         if (pipe) score(t + 1, sn, &sc);
-        fetch(v, t + 1, vreg);
+        fetch_v(t + 1);
         mload(t + 2);
         if (pipe) {
             mask(t + 1, sn);
@@ -565,6 +661,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
             weigh(sc);
             mix(t, nullptr);
         }
+        bload(t + 2);
         stash_k(t + 2);
         stash_v(t + 1);
         __syncthreads();
@@ -578,13 +675,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     bool have = false;
     auto step_m = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {  // t: list position
         mpark();  // mask words of position t+1
+        bpark();
         const bool next = t + 1 < pp1 && tix(t + 1) < tw && !mnone;  // this wave computes t+1
-        fetch(k, tix(t + 2), kreg);
+        fetch_k(tix(t + 2));
         if (next) {
             if (have) score(t + 1, sn, &sc);
             else score(t + 1, sn, nullptr);
         }
-        fetch(v, tix(t + 1), vreg);
+        fetch_v(tix(t + 1));
         mload(tix(t + 2));
         if (next) mask(tix(t + 1), sn);
         if (have && next) {
@@ -597,6 +695,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
             reference(scan(sn));
         }
         have = next;
+        bload(tix(t + 2));
         stash_k(t + 2);
         stash_v(t + 1);
         __syncthreads();
@@ -605,13 +704,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // prologue: K(t0), V(t0), K(t0+1) staged; S^T(t0) scored and its
     // reference set
     mload(tix(pp0));
-    fetch(k, tix(pp0), kreg);
-    fetch(v, tix(pp0), vreg);
+    bload(tix(pp0));
+    fetch_k(tix(pp0));
+    fetch_v(tix(pp0));
     stash_k(pp0);
     stash_v(pp0);
-    fetch(k, tix(pp0 + 1), kreg);
+    fetch_k(tix(pp0 + 1));
     stash_k(pp0 + 1);
     __syncthreads();
+    bpark();
     if constexpr (MASK) {
         mpark();
         have = pp0 < pp1 && tix(pp0) < tw && !mnone;
@@ -626,6 +727,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         reference(scan(s0));
     }
     mload(tix(pp0 + 1));
+    bload(tix(pp0 + 1));
     __syncthreads();  // K(t0) is read by every wave before K(t0+2) replaces it
 
     if constexpr (MASK) {
@@ -647,9 +749,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         if (q_live) {
             const size_t unit = ((size_t)bh * Sq + qi) * nsplit + split;
             const float l_tot = halves_sum(l_run);
-            float* arow = ws_acc + unit * D;
+            float* arow = ws_acc + unit * DV;
 #pragma unroll
-            for (int db = 0; db < S::kDBlocks; ++db)
+            for (int db = 0; db < SV::kDBlocks; ++db)
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
                     const int d0 = db * 32 + 8 * rg + 4 * half;
@@ -670,9 +772,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     if (MASK ? qi < Sq : q_live) {
         const float l_tot = halves_sum(l_run);
         const float inv = (q_live && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
-        uint16_t* orow = obase + (size_t)qi * D;
+        uint16_t* orow = obase + (size_t)qi * DV;
 #pragma unroll
-        for (int db = 0; db < S::kDBlocks; ++db)
+        for (int db = 0; db < SV::kDBlocks; ++db)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 const int d0 = db * 32 + 8 * rg + 4 * half;
@@ -830,7 +932,7 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
     uint16_t* o = static_cast<uint16_t*>(a.out);
     float* ws_acc = nullptr;
     float* ws_ml = nullptr;
-    const size_t ws_split = prefill_workspace_bytes(a.B, a.H, a.Sq, a.Skv, a.d);
+    const size_t ws_split = prefill_workspace_bytes(a.B, a.H, a.Sq, a.Skv, a.dv);
     // a mask shared by all heads gets key-tile lists (marks after the partials)
     const int nkt = (a.Skv + kBN - 1) / kBN;
     const size_t ws_marks = a.mask && a.msh == 0 ? prefill_mask_workspace_bytes(a.B, a.Sq, a.Skv) : 0;
@@ -842,9 +944,12 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
         const size_t units = (size_t)BH * a.Sq * p.nsplit;
         ws_acc = static_cast<float*>(a.workspace);
         ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
-                                         round_up256(units * a.d * sizeof(float)));
+                                         round_up256(units * a.dv * sizeof(float)));
     }
-    const float sl = a.scale * kLog2e;
+    // the general instantiation for a bias or a scale that is not positive:
+    // it forms scale * s + bias and works in exp2 units of those logits
+    const bool gen = a.bias != nullptr || !(a.scale > 0.0f);
+    const float sl = gen ? kLog2e : a.scale * kLog2e;
     KernelTimer* t = active_timer();
     if (tmap) {
         const int Bm = a.msb != 0 ? a.B : 1;
@@ -860,12 +965,25 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, a.stream, q, k, v, o, a.kv_lens, BH, a.H,
                            a.Hkv, a.Sq, a.Skv, sl, a.causal, nqt, p.nsplit, ws_acc, ws_ml, a.mask,
-                           a.msb, a.msh, a.msi, tmap, nkt);
+                           a.msb, a.msh, a.msi, tmap, nkt, static_cast<const uint16_t*>(a.bias),
+                           a.bsb, a.bsh, a.bsi, a.scale);
     };
+    const bool m = a.mask != nullptr;
+    // instantiations for d, d_v in {64, 128}, the mask and the general logits
+    auto pick = [&](auto dk, auto dvk) {
+        constexpr int D = decltype(dk)::value, DV = decltype(dvk)::value;
+        if (gen)
+            m ? go(prefill_bf16_kernel<D, DV, true, true>) : go(prefill_bf16_kernel<D, DV, false, true>);
+        else
+            m ? go(prefill_bf16_kernel<D, DV, true, false>)
+              : go(prefill_bf16_kernel<D, DV, false, false>);
+    };
+    using I64 = std::integral_constant<int, 64>;
+    using I128 = std::integral_constant<int, 128>;
     if (a.d == 128)
-        a.mask ? go(prefill_bf16_kernel<128, true>) : go(prefill_bf16_kernel<128, false>);
+        a.dv == 128 ? pick(I128{}, I128{}) : pick(I128{}, I64{});
     else
-        a.mask ? go(prefill_bf16_kernel<64, true>) : go(prefill_bf16_kernel<64, false>);
+        a.dv == 128 ? pick(I64{}, I128{}) : pick(I64{}, I64{});
     hipError_t e = hipGetLastError();
     if (t) t->end(kPrefillBf16, a.stream);
     if (e != hipSuccess || p.nsplit == 1) return e;
@@ -878,7 +996,7 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
                            dim3(256), 0, a.stream, a.kv_lens, a.H, a.Sq, a.Skv, p.nsplit, rows, ws_acc,
                            ws_ml, o);
     };
-    if (a.d == 128)
+    if (a.dv == 128)
         p.nsplit <= 4 ? merge(prefill_combine_kernel<128, 4>, 8)
                       : merge(prefill_combine_kernel<128, kMaxSplit>, 8);
     else

@@ -234,6 +234,31 @@ def mask_to_torch(m: np.ndarray, device="cuda"):
     return torch.from_numpy(full).to(device)[..., :Skv]
 
 
+def random_bias(seed: int, shape: Sequence[int], dtype: str = "bf16", spread: float = 2.0,
+                hide: float = 0.0) -> np.ndarray:
+    """Additive bias of `shape` (last axis the keys): spread * N(0, 1) drawn
+    as ``default_rng(SeedSequence([seed, 5])).standard_normal(shape,
+    float32)``, with a fraction `hide` of the entries (drawn from the same
+    stream) set to -inf; float32, or bf16 bits (RNE)."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 5]))
+    x = spread * rng.standard_normal(tuple(shape), dtype=np.float32)
+    if hide > 0.0:
+        x[rng.random(tuple(shape)) < hide] = -np.inf
+    return x if dtype == "f32" else bf16_bits(x)
+
+
+def bias_to_torch(b: np.ndarray, device="cuda"):
+    """float32 or bf16-bit bias -> a tensor view on `device` whose rows are
+    stored in round_up(Skv, 4) elements (the 4-element groups the library
+    reads)."""
+    import torch
+    Skv = b.shape[-1]
+    pad = (Skv + 3) // 4 * 4
+    full = np.zeros(b.shape[:-1] + (pad,), dtype=b.dtype)
+    full[..., :Skv] = b
+    return to_torch(full, device)[..., :Skv]
+
+
 # ---- moving inputs to and from a GPU (torch only moves the bits) ----------
 def to_torch(x: np.ndarray, device="cuda"):
     """float32 array -> float32 tensor; uint16 bf16 bits -> bfloat16 tensor."""
