@@ -41,6 +41,20 @@ def compile_oracle(src: str = _SRC, out: str = _LIB) -> str:
     return out
 
 
+def compile_oracle_sanitized(out: str, src: str = _SRC) -> str:
+    """Compile the oracle with clang under AddressSanitizer and
+    UndefinedBehaviorSanitizer (same language and floating-point flags), for
+    the sanitizer job of the CPU tests; it needs the clang ASan runtime
+    preloaded."""
+    cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-std=c11", "-fPIC", "-shared", "-pthread",
+           "-Wall", "-Wextra", "-fno-fast-math", "-ffp-contract=off",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer", src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 def build() -> str:
     """(Re)compile the oracle library in place."""
     return compile_oracle()

@@ -67,5 +67,49 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(out_dir: str) -> str:
+    """A copy of the library whose HOST code is built with AddressSanitizer
+    and UndefinedBehaviorSanitizer (the device code is the ordinary build):
+    for running the CPU tests of the argument checks, workspace sizing and
+    kernel planning under the sanitizers.  Loading it needs the clang ASan
+    runtime preloaded (asan_runtime()).  Returns the library's path."""
+    os.makedirs(out_dir, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host",
+           "-fno-omit-frame-pointer"]
+    flags = compile_flags() + ["-Xarch_host", "-g"] + san
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        res = subprocess.run([hipcc()] + flags + ["-c", os.path.join(CSRC, src), "-o", obj],
+                             capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"compiling {src} with sanitizers failed:\n{res.stderr}")
+        return obj
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(5, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    lib = os.path.join(out_dir, "libattn_sanitized.so")
+    clangxx = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin",
+                           "clang++")
+    if not os.path.exists(clangxx):
+        clangxx = "/opt/rocm/llvm/bin/clang++"
+    res = subprocess.run([clangxx, "-shared", "-fPIC", "-fsanitize=address,undefined", "-o", lib]
+                         + objs + ["-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"linking the sanitized library failed:\n{res.stderr}")
+    return lib
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime the sanitized builds link against."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("clang AddressSanitizer runtime not found under /opt/rocm/llvm")
+    return hits[-1]
+
+
 if __name__ == "__main__":
     build(verbose=True)
