@@ -507,6 +507,7 @@ def main():
             nbytes = decode_bytes(w, lens)
             p_ms = avg_ms("decode_bf16_partial")
             c_ms = avg_ms("decode_bf16_combine")
+            c_ms = 0.0 if math.isnan(c_ms) else c_ms
             kv_bytes = nbytes - 2 * 2 * w.B * w.H * w.d  # what the partial kernel reads
             gbs_op = nbytes / ((p_ms + c_ms) * 1e-3) / 1e9
             gbs_k = kv_bytes / (p_ms * 1e-3) / 1e9
@@ -530,6 +531,7 @@ def main():
                 (st["decode_bf16_combine"]["median_us"] or 0.0),
                 "min_us": st["decode_bf16_partial"]["min_us"] +
                 (st["decode_bf16_combine"]["min_us"] or 0.0),
+                "combine_launches": st["decode_bf16_combine"]["n"],
             }
     if result["value"] is None and "decode" in result:
         result["value"] = result["decode"]["value"]

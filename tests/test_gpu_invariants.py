@@ -5,6 +5,7 @@ the method says must (or must not) matter."""
 import numpy as np
 import pytest
 
+import oracle
 import transformer_scaled_dot_attn_amd as attn
 import workloads as W
 from gpu_util import BF16_TOL, gpu_run
@@ -118,7 +119,8 @@ def test_caller_workspace_and_streams():
     lens = torch.tensor([2500, 10, 1900], dtype=torch.int32, device="cuda")
     ref = attn.fwd(q, k, v, kv_lens=lens, causal=False)
     nbytes = attn.workspace_bytes(3, 4, 1, 2500, 128, attn.BF16)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    # a caller's workspace needs no initialisation: fill it with garbage
+    ws = torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda")
     out = attn.fwd(q, k, v, kv_lens=lens, causal=False, workspace=ws)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -173,3 +175,37 @@ def test_library_workspace_per_stream():
     torch.cuda.synchronize()
     for o, a in zip(outs, alone):
         assert torch.equal(o.view(torch.int16), a.view(torch.int16))
+
+
+def test_decode_repeats_with_split_prefills_between():
+    """Repeated decodes on the library workspace give identical bits, also
+    with split prefills (whose partials share that workspace) between them."""
+    import torch
+    dec = W.random_problem(60, 6, 8, 1, 5000, 128, "bf16", [5000, 4000, 33, 0, 4999, 1200],
+                           Hkv=2)
+    pre = W.random_problem(61, 1, 8, 300, 6000, 128, "bf16")
+    dq, dk, dv = (W.to_torch(dec[x]) for x in ("q", "k", "v"))
+    pq, pk, pv = (W.to_torch(pre[x]) for x in ("q", "k", "v"))
+    lens = torch.as_tensor(np.asarray(dec["kv_lens"], np.int32)).to("cuda")
+    assert attn.workspace_bytes(1, 8, 300, 6000, 128, attn.BF16) > 0   # key-range splits
+    first = attn.fwd(dq, dk, dv, kv_lens=lens, causal=False)
+    base = _bits(first)
+    ref = oracle.attention(dec["q"], dec["k"], dec["v"], dec["scale"], 0, dec["kv_lens"])
+    assert np.abs(W.from_torch(first) - ref).max() <= BF16_TOL
+    for rep in range(6):
+        if rep % 2:
+            attn.fwd(pq, pk, pv, causal=True)
+        out = attn.fwd(dq, dk, dv, kv_lens=lens, causal=False)
+        assert np.array_equal(_bits(out), base), f"repeat {rep}"
+
+
+def test_decode_many_caches():
+    """A decode over 66560 (b, K/V head) caches of up to 33 keys, some empty."""
+    B, H, Skv, d = 1040, 64, 33, 64
+    rng = np.random.default_rng(62)
+    lens = rng.integers(0, Skv + 1, size=B).astype(np.int32)
+    prob = W.random_problem(62, B, H, 1, Skv, d, "bf16", lens)
+    got, _ = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], 0, lens)
+    ref = oracle.attention(prob["q"], prob["k"], prob["v"], prob["scale"], 0, lens)
+    from gpu_util import assert_matches
+    assert_matches(got, ref, BF16_TOL, lens, Skv, "66560 caches")
