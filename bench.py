@@ -210,6 +210,8 @@ def mask_runs(attn, W, runs, steps, warmup):
         if kind == "prefill":
             S = w.Skv
             masks = [("none", None),
+                     ("all true [1,1,1,S]", np.ones((1, 1, 1, S), dtype=bool)),
+                     ("all true [1,1,S,S]", np.ones((1, 1, w.Sq, S), dtype=bool)),
                      ("key padding [1,1,1,S], first 256 keys hidden",
                       W.key_padding_mask([256], [S], S)),
                      ("random [1,1,S,S], density 0.5", W.random_mask(5, (1, 1, w.Sq, S), 0.5)),

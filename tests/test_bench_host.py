@@ -59,16 +59,17 @@ def test_mask_rows(monkeypatch):
         w = W.WORKLOADS[name]
         runs.append((kind, w, _inputs(w), None))
     rows = bench.mask_runs(_Attn(), _host_workloads(), runs, steps=1, warmup=0)
-    assert len(rows) == 5 + 3 + 3 and len(calls) == len(rows)
+    assert len(rows) == 7 + 3 + 3 and len(calls) == len(rows)
     for r in rows:
         assert r["ms_per_call"] > 0 and math.isfinite(r["time_vs_unmasked"])
     pre = [r for r in rows if r["workload"] == "prefill4096_bf16"]
     assert pre[0]["mask"] == "none" and pre[0]["visible_pairs_share"] == 1.0
-    for r in pre[1:]:
+    assert pre[1]["visible_pairs_share"] == 1.0 and pre[2]["visible_pairs_share"] == 1.0
+    for r in pre[3:]:
         assert 0.0 < r["visible_pairs_share"] < 1.0 and r["TFLOP/s"] > 0
     # documents of 512 and a window of 256 open about an eighth of the causal pairs
-    assert 0.10 < pre[3]["visible_pairs_share"] < 0.15
-    assert 0.10 < pre[4]["visible_pairs_share"] < 0.15
+    assert 0.10 < pre[5]["visible_pairs_share"] < 0.15
+    assert 0.10 < pre[6]["visible_pairs_share"] < 0.15
     for name in ("decode8192_bf16", "gqa_decode8192_bf16"):
         dec = [r for r in rows if r["workload"] == name]
         assert "visible_kv_rows_share" not in dec[0]
