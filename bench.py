@@ -98,6 +98,41 @@ def timed_calls(attn, fn, steps, warmup, kernels):
     return st
 
 
+def timed_rounds(attn, fns, steps, warmup, kernels, rounds=5):
+    """As timed_calls for several callables, interleaved: after warming all
+    up, each of `rounds` rounds runs every callable steps / rounds times in
+    turn, so they share one clock and power history (a row measured first
+    would otherwise sit in the power transient of a cold start).  Returns
+    one kernel_stats-like dict per callable."""
+    import torch
+    for fn in fns:
+        for _ in range(warmup):
+            fn()
+    torch.cuda.synchronize()
+    per = max(1, steps // rounds)
+    samples = [{k: [] for k in kernels} for _ in fns]
+    for _ in range(rounds):
+        for i, fn in enumerate(fns):
+            attn.profile_enable(True)
+            for _ in range(per):
+                fn()
+            torch.cuda.synchronize()
+            for k in kernels:
+                samples[i][k] += attn.profile_samples(k)
+            attn.profile_enable(False)
+    out = []
+    for smp in samples:
+        res = {}
+        for k, t in smp.items():
+            if t:
+                res[k] = {"ms": sum(t) / len(t), "median_us": 1e3 * statistics.median(t),
+                          "min_us": 1e3 * min(t), "n": len(t)}
+            else:
+                res[k] = {"ms": float("nan"), "median_us": None, "min_us": None, "n": 0}
+        out.append(res)
+    return out
+
+
 def op_stats(st, kernels):
     """Mean ms of one call made of the named kernels (those that ran), and the
     median and min of the per-call sums."""
@@ -228,11 +263,12 @@ def mask_runs(attn, W, runs, steps, warmup):
                       W.random_mask(6, (w.B, w.H, 1, w.Skv), 0.5))]
             kernels = ("decode_bf16_partial", "decode_bf16_combine", "decode_mask_tiles")
         base = None
-        for label, m in masks:
-            tm = None if m is None else W.mask_to_torch(m)
-            fn = lambda: attn.fwd(x["q"], x["k"], x["v"], out, causal=w.causal,
-                                  kv_lens=x["kv_lens"], scale=x["scale"], mask=tm)
-            t = timed_calls(attn, fn, steps, warmup, kernels)
+        tms = [None if m is None else W.mask_to_torch(m) for _, m in masks]
+        fns = [(lambda tm=tm: attn.fwd(x["q"], x["k"], x["v"], out, causal=w.causal,
+                                       kv_lens=x["kv_lens"], scale=x["scale"], mask=tm))
+               for tm in tms]
+        stats = timed_rounds(attn, fns, steps, warmup, kernels)  # the masks interleaved
+        for (label, m), t in zip(masks, stats):
             ms, med, mn = op_stats(t, kernels)  # kernels a call did not launch are left out
             base = ms if base is None else base
             row = {"workload": w.name, "mask": label, "ms_per_call": ms, "median_us": med,
@@ -261,7 +297,7 @@ def mask_runs(attn, W, runs, steps, warmup):
                         w.kv_heads * lens.clip(0, w.Skv).sum())
                 row["GB/s"] = nbytes / (ms * 1e-3) / 1e9
             rows.append(row)
-            del tm
+        del tms, fns
         torch.cuda.empty_cache()
     return rows
 

@@ -33,7 +33,11 @@ def _stub_timing(monkeypatch):
                       "min_us": 800.0 if ran else None, "n": 3 if ran else 0}
         return res
 
+    def rounds(attn, fns, steps, warmup, kernels, rounds=5):
+        return [timed(attn, fn, steps, warmup, kernels) for fn in fns]
+
     monkeypatch.setattr(bench, "timed_calls", timed)
+    monkeypatch.setattr(bench, "timed_rounds", rounds)
     return calls
 
 

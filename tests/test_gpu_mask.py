@@ -151,6 +151,70 @@ def test_structured_masks_skip_hidden_tiles(case):
     assert np.all(got[np.all(ref == 0.0, axis=-1)] == 0.0)
 
 
+def _hole_mask(Sq, Skv, holes):
+    m = np.ones((1, 1, Sq, Skv), dtype=bool)
+    for i, j in holes:
+        m[0, 0, i, j] = False
+    return m
+
+
+# name, B, H, Sq, Skv, d, causal, kv_lens, mask builder, equal to the unmasked run
+WHOLE_TILES = [
+    ("all-true plane", 2, 4, 700, 700, 128, 1, [700, 555],
+     lambda B, Sq, Skv: np.ones((1, 1, Sq, Skv), dtype=bool), True),
+    ("causal rule given with the rule", 2, 2, 600, 600, 64, 1, [600, 401],
+     lambda B, Sq, Skv: np.tril(np.ones((Sq, Skv), dtype=bool))[None, None], True),
+    ("zeros only above the diagonal", 1, 2, 300, 900, 128, 1, None,
+     lambda B, Sq, Skv: _hole_mask(Sq, Skv, [(0, 601), (0, 899), (255, 856)]), True),
+    ("one hidden byte per tile", 1, 2, 520, 520, 64, 0, None,
+     lambda B, Sq, Skv: _hole_mask(Sq, Skv, [(0, 0), (255, 63), (256, 64), (519, 519), (300, 450)]),
+     False),
+    ("one hidden byte below the diagonal", 2, 2, 400, 400, 128, 1, [400, 390],
+     lambda B, Sq, Skv: _hole_mask(Sq, Skv, [(399, 5), (256, 256)]), False),
+    ("tile-aligned padding with splits", 2, 2, 200, 2602, 128, 1, [2602, 2000],
+     lambda B, Sq, Skv: W.key_padding_mask([320, 130], [Skv, Skv], Skv), False),
+    ("per-item padding, ragged", 3, 2, 333, 1030, 64, 0, [1030, 1000, 700],
+     lambda B, Sq, Skv: W.key_padding_mask([0, 64, 192], [1030, 1030, 641], Skv), False),
+]
+
+
+@pytest.mark.parametrize("case", WHOLE_TILES, ids=lambda c: c[0].replace(" ", "_"))
+def test_tiles_the_mask_opens_whole(case):
+    """Blocks whose listed key tiles are consecutive and each opened whole by
+    the mask run the unmasked loop; a single hidden byte, or a tile the mask
+    cuts, sends the block back to the per-element path.  Bytes the causal
+    rule hides anyway do not cut a tile."""
+    name, B, H, Sq, Skv, d, causal, lens, build, same = case
+    _say(f"whole-tile mask {name}: B{B} H{H} Sq{Sq} Skv{Skv} d{d} causal{causal}")
+    prob = W.random_problem(sum(map(ord, name)), B, H, Sq, Skv, d, "bf16", lens)
+    mask = build(B, Sq, Skv)
+    got, tgot = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], causal, lens,
+                        mask=W.mask_to_torch(mask))
+    ref = oracle.attention(prob["q"], prob["k"], prob["v"], prob["scale"], causal, lens,
+                           mask=mask)
+    assert_matches(got, ref, BF16_TOL, lens, Skv, name)
+    if same:
+        import torch
+        _, plain = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], causal, lens)
+        assert torch.equal(tgot, plain), f"{name}: differs from the unmasked run"
+
+
+def test_whole_tile_mask_with_bias():
+    """The general-logit kernel with an all-true mask equals the bias alone."""
+    import torch
+    Sq, Skv = 300, 700
+    prob = W.random_problem(97, 2, 4, Sq, Skv, 128, "bf16", [700, 650], Hkv=2)
+    bias = W.random_bias(98, (2, 4, Sq, Skv), "bf16", hide=0.05)
+    tq, tk, tv = (W.to_torch(prob[x]) for x in ("q", "k", "v"))
+    tl = torch.as_tensor(np.asarray([700, 650], np.int32)).to("cuda")
+    tb = W.bias_to_torch(bias)
+    a = attn.fwd(tq, tk, tv, causal=True, kv_lens=tl, scale=prob["scale"], bias=tb)
+    m = W.mask_to_torch(np.ones((2, 1, Sq, Skv), dtype=bool))
+    b = attn.fwd(tq, tk, tv, causal=True, kv_lens=tl, scale=prob["scale"], bias=tb, mask=m)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 def test_mask_layout_errors():
     import torch
     B, H, S, d = 1, 2, 90, 64

@@ -64,6 +64,11 @@
 // structured masks -- left padding, packed documents, sliding windows --
 // cost only the tiles they open.  The loop then runs over list positions:
 // LDS ring slots follow the position, key offsets and masks the listed tile.
+// The marks also tell a tile that the mask opens whole (every byte of it
+// that the causal rule leaves visible is set) from one it cuts; a block
+// whose listed tiles are consecutive and all open whole runs the loop of
+// the unmasked kernel over them and reads no mask byte, so an all-true mask
+// or one that only pads keys costs the tile pre-pass and nothing else.
 //
 // General logits (the GEN instantiation).  An additive bias (the float mask
 // of "Attention from Scratch", KubeDojo module 1.4.3, Part 7: a value added
@@ -115,14 +120,19 @@ struct Shape {
     static constexpr int kRowsPerPass = kThreads / kChunks;      // tile rows per load pass
     static_assert(kPerThread >= 1 && kPerThread * kThreads == kBN * kChunks,
                   "tile must split evenly");
-    // LDS row strides in elements.  A K row is padded by 16 bytes, so 8
-    // consecutive rows start in 8 different 16-byte bank groups of a 128-byte
-    // bank row (the K operand loads: 8 lanes per LDS cycle, 8 rows, one chunk
-    // each).  A V row is padded by 32 bytes, so the 4 rows x 2 chunks that a
-    // 16-lane group reads with one transposing load fall in 8 different bank
-    // groups.  Every LDS address is then a per-lane base plus a constant.
+    // LDS row strides in elements.  LDS reads are served 256 bytes (16
+    // groups of 16 bytes) per cycle.  A K row is padded by 16 bytes, so the
+    // 16 consecutive rows that 16 lanes read at one chunk (the K operand
+    // loads) start in 16 different 16-byte bank groups.  A V row is padded
+    // by 64 bytes (for D = 128 row r starts at group 4 r mod 16; for D = 64
+    // at 12 r mod 16), so the 4 consecutive rows x 64 bytes that 32 lanes
+    // read with one transposing load cover the 16 groups once.  (With a
+    // 32-byte pad the 4 rows start 2 groups apart and cover 10 groups:
+    // 8.5 M conflict cycles per 4096-token prefill were measured, none with
+    // the 64-byte pad.)
+    // Every LDS address is then a per-lane base plus a constant.
     static constexpr int kStrideK = D + 8;
-    static constexpr int kStrideV = D + 16;
+    static constexpr int kStrideV = D + 32;
     static constexpr int kTileK = kBN * kStrideK;
     static constexpr int kTileV = kBN * kStrideV;
 };
@@ -152,6 +162,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     __shared__ u32x4 lds_m[MASK ? 2 * kThreads : 1];  // parked mask words, 32 bytes per lane
     __shared__ int lds_tl[MASK ? kMaxListTiles : 1];  // this query tile's listed key tiles
     __shared__ int lds_tn;                            // their number
+    __shared__ int lds_tcut;                          // some listed tile is cut by the mask
     __shared__ u32x4 lds_b[GEN ? 4 * kThreads : 1];   // parked bias, 64 bytes per lane
 
     const int tid = threadIdx.x;
@@ -216,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int p_lo = off + qw;
     const int p_hi = off + min(qw + 32, n) - 1;
     const int kv_hi_w = wave_live ? (causal ? min(L, p_hi + 1) : L) : 0;
-    const int t1w = min(t1, (kv_hi_w + kBN - 1) / kBN);  // this wave computes t0 <= t < t1w
+    int t1w = min(t1, (kv_hi_w + kBN - 1) / kBN);  // this wave computes t0 <= t < t1w
     const int kfull_w = causal ? min(L, p_lo + 1) : L;
     const int tw = (kv_hi_w + kBN - 1) / kBN;  // key tiles this wave's rules reach
 
@@ -243,7 +254,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // its last tile, a valid one, for the staging run-ahead).
     int pp0 = t0, pp1 = t1;
     bool listed = false;
-    int lcount = 0;
+    bool dense = false;  // the listed tiles are consecutive and all open whole
+    int lcount = 0, tl0 = 0;
     if constexpr (MASK) {
         if (tmap != nullptr) {  // the mask is shared by all heads (msh == 0)
             listed = true;
@@ -252,17 +264,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                 // compact the marks of key tiles 0 .. ntiles_q-1 in ascending
                 // order: 64 tiles per round, a lane each, ballot and prefix count
                 int base = 0;
+                bool cut = false;
                 for (int k0 = 0; k0 < ntiles_q; k0 += 64) {
                     const int kt = k0 + lane;
-                    const bool on = kt < ntiles_q && tm[min(kt, nkt - 1)] != 0;
-                    const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
-                    if (on) lds_tl[base + __builtin_popcountll(bal & ((1ull << lane) - 1))] = kt;
+                    const int mk = kt < ntiles_q ? tm[min(kt, nkt - 1)] : 0;
+                    const uint64_t bal = __builtin_amdgcn_ballot_w64(mk != 0);
+                    cut |= __builtin_amdgcn_ballot_w64(mk == 1) != 0;
+                    if (mk != 0) lds_tl[base + __builtin_popcountll(bal & ((1ull << lane) - 1))] = kt;
                     base += __builtin_popcountll(bal);
                 }
-                if (lane == 0) lds_tn = base;
+                if (lane == 0) {
+                    lds_tn = base;
+                    lds_tcut = cut;
+                }
             }
             __syncthreads();
             lcount = lds_tn;
+            tl0 = lcount > 0 ? lds_tl[0] : 0;
+            dense = lds_tcut == 0 && lcount > 0 && lds_tl[lcount - 1] - tl0 + 1 == lcount;
             const int per = (lcount + nsplit - 1) / nsplit;
             pp0 = min(lcount, split * per);
             pp1 = min(lcount, pp0 + per);
@@ -434,6 +453,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     constexpr int kPV = 2 * kHalf;            // P V MFMAs per tile
     constexpr int kAheadK = 2;                // K operand k-steps in flight
     constexpr int kAheadV = 3;                // V operands in flight
+    // The 18 weight stages of a tile (below) are split between the MFMAs of
+    // the next tile's scores (the first kNA) and the first kHalf P V MFMAs
+    // of the tile itself (the rest), which read only the first 32-key block
+    // of P: in proportion to the MFMAs that hide them, and at least 9 ahead
+    // of P V (stage 8 packs the block's last pair).
+    constexpr int kNA = std::clamp((18 * kQK + (kQK + kHalf) / 2) / (kQK + kHalf), 9, 18);
 
     // ---- pieces of S^T(tile) = K Q^T: two 32-key blocks, chains interleaved
     auto kread = [&](const uint16_t* kl, int ks, u32x4 (&dst)[2]) {
@@ -470,8 +495,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     };
     auto ref_log2 = [&]() { return m_run == -INFINITY ? 0.0f : m_run * scale_log2; };
 
-    // S^T(tile) into sn; when sc is given, the 16 weight pairs of the tile
-    // before it are formed under these MFMAs (pairs per MFMA = 16 / kQK).
+    // S^T(tile) into sn; when sc is given, weight stages 0 .. kNA-1 of the
+    // tile before it are issued under these MFMAs.
     auto score = [&](int tile, f32x16 (&sn)[2], const f32x16 (*sc)[2]) {
         const uint16_t* kl = lds_k[tile & 1] + k_rd;
         const float mc = ref_log2();
@@ -491,16 +516,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                 sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     as_bf16x8(ka[ks % (kAheadK + 1)][kb]), as_bf16x8(qf[ks]), sn[kb], 0, 0, 0);
                 if (sc) {
-                    constexpr int kPer = 16 / kQK;
+                    const int m = 2 * ks + kb;  // MFMA index: stages kNA m / kQK .. kNA (m+1) / kQK - 1
 #pragma unroll
-                    for (int e = 0; e < kPer; ++e) pair_stage(*sc, (2 * ks + kb) * kPer + e, mc);
+                    for (int e = kNA * m / kQK; e < kNA * (m + 1) / kQK; ++e) pair_stage(*sc, e, mc);
                 }
                 pin_schedule();
             }
-        }
-        if (sc) {
-            pair_stage(*sc, 16, mc);
-            pair_stage(*sc, 17, mc);
         }
     };
     // weights of a tile with no next tile to score under them
@@ -515,7 +536,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // L - 1 otherwise), so each element costs one compare against a
     // per-tile constant -- no short-circuit branches.
     const int lim = causal ? min(p, L - 1) : L - 1;
-    auto mask = [&](int tile, f32x16 (&sn)[2]) {
+    // UM (the tag's value): the allowed-mask words are read.
+    auto mask = [&](auto um, int tile, f32x16 (&sn)[2]) {
+        constexpr bool UM = decltype(um)::value;
         const int kbase = tile * kBN;
         if constexpr (GEN) {
             // logits scale * s + bias (the parked bias of this tile)
@@ -537,7 +560,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         u32x4 mk[2] = {{~0u, ~0u, ~0u, ~0u}, {~0u, ~0u, ~0u, ~0u}};
         if (kbase + kBN > kfull_w) {
             // the rules cut this tile (and the allowed-mask may)
-            if constexpr (MASK) {
+            if constexpr (UM) {
                 mk[0] = lds_m[2 * tid];
                 mk[1] = lds_m[2 * tid + 1];
             }
@@ -547,24 +570,29 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     bool vis = kb * 32 + 8 * (r >> 2) + (r & 3) <= rel;
-                    if constexpr (MASK) vis = vis & byte_set(mk[kb][r >> 2], r & 3);
+                    if constexpr (UM) vis = vis & byte_set(mk[kb][r >> 2], r & 3);
                     sn[kb][r] = vis ? sn[kb][r] : -INFINITY;
                 }
-        } else if (mcut) {
-            // only the allowed-mask cuts it
-            mk[0] = lds_m[2 * tid];
-            mk[1] = lds_m[2 * tid + 1];
+        } else if constexpr (UM) {
+            if (mcut) {
+                // only the allowed-mask cuts it
+                mk[0] = lds_m[2 * tid];
+                mk[1] = lds_m[2 * tid + 1];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    sn[kb][r] = byte_set(mk[kb][r >> 2], r & 3) ? sn[kb][r] : -INFINITY;
+                    for (int r = 0; r < 16; ++r)
+                        sn[kb][r] = byte_set(mk[kb][r >> 2], r & 3) ? sn[kb][r] : -INFINITY;
+            }
         }
     };
     // O^T += V^T(tile) P^T, output blocks innermost (consecutive MFMAs
-    // independent); when sn is given, the maximum of the next tile's scores
-    // is scanned under these MFMAs.  Returns that maximum (lane-local).
-    auto mix = [&](int tile, const f32x16 (*sn)[2]) {
+    // independent).  When sc (the tile's scores) is given, weight stages
+    // kNA .. 17 are issued under the first kHalf MFMAs, which use only the
+    // first 32-key block of P; when sn is given, the maximum of the next
+    // tile's scores is scanned under the other kHalf.  Returns that maximum
+    // (lane-local).
+    auto mix = [&](int tile, const f32x16 (*sn)[2], const f32x16 (*sc)[2]) {
         const uint16_t* vl = lds_v[tile & 1] + v_rd;
         auto vread = [&](int st, i16x4 (&dst)[2]) {
             const int db = st % SV::kDBlocks, kk = st / SV::kDBlocks;  // kk = 2*kb + h2
@@ -577,6 +605,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 #pragma unroll
         for (int st = 0; st < kAheadV; ++st) vread(st, vr[st]);
         float mx = -INFINITY;
+        const float mc = ref_log2();
         pin_schedule();
 #pragma unroll
         for (int st = 0; st < kPV; ++st) {
@@ -591,11 +620,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 as_bf16x8(a), as_bf16x8(pf[st / kHalf][(st % kHalf) / SV::kDBlocks]), oacc[db], 0, 0,
                 0);
-            if (sn) {
-                constexpr int kPer = 32 / kPV;
+            if (sc && st < kHalf) {
+#pragma unroll
+                for (int e = kNA + (18 - kNA) * st / kHalf; e < kNA + (18 - kNA) * (st + 1) / kHalf; ++e)
+                    pair_stage(*sc, e, mc);
+            }
+            if (sn && st >= kHalf) {
+                constexpr int kPer = 32 / kHalf;
 #pragma unroll
                 for (int e = 0; e < kPer; ++e) {
-                    const int x = st * kPer + e;
+                    const int x = (st - kHalf) * kPer + e;
                     mx = fmaxf(mx, (*sn)[x >> 4][x & 15]);
                 }
             }
@@ -643,23 +677,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // clamped) into LDS slots nobody reads again, and with no load under
     // a branch the compiler's wait counts stay exact (each stash waits only
     // for its own loads).
-    auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    // No allowed-mask word is read: the unmasked kernel and the masked
+    // kernel's blocks whose listed tiles all open whole take this step.
+    auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
         const bool pipe = t + 1 < t1w;  // this wave scores tile t+1
-        mpark();  // mask words of tile t+1
         bpark();  // bias of tile t+1
         fetch_k(t + 2);
         // S^T(t+1) under which P(t) is formed
         if (pipe) score(t + 1, sn, &sc);
         fetch_v(t + 1);
-        mload(t + 2);
         if (pipe) {
-            mask(t + 1, sn);
+            mask(std::false_type{}, t + 1, sn);
             // P(t) V(t) under which the maximum of S^T(t+1) is found
-            const float mx = mix(t, &sn);
+            const float mx = mix(t, &sn, &sc);
             reference(mx);
         } else if (t < t1w) {
             weigh(sc);
-            mix(t, nullptr);
+            mix(t, nullptr, nullptr);
         }
         bload(t + 2);
         stash_k(t + 2);
@@ -673,7 +707,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // the next computed tile to the weights of the last one exactly as the
     // prologue, the pipelined step and the wave's last tile do.
     bool have = false;
-    auto step_m = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {  // t: list position
+    auto step_m = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {  // t: list position
         mpark();  // mask words of position t+1
         bpark();
         const bool next = t + 1 < pp1 && tix(t + 1) < tw && !mnone;  // this wave computes t+1
@@ -684,13 +718,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         }
         fetch_v(tix(t + 1));
         mload(tix(t + 2));
-        if (next) mask(tix(t + 1), sn);
+        if (next) mask(std::bool_constant<MASK>{}, tix(t + 1), sn);
         if (have && next) {
-            const float mx = mix(t, &sn);
+            const float mx = mix(t, &sn, &sc);
             reference(mx);
         } else if (have) {
             weigh(sc);
-            mix(t, nullptr);
+            mix(t, nullptr, nullptr);
         } else if (next) {
             reference(scan(sn));
         }
@@ -701,45 +735,70 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         __syncthreads();
     };
 
-    // prologue: K(t0), V(t0), K(t0+1) staged; S^T(t0) scored and its
-    // reference set
-    mload(tix(pp0));
-    bload(tix(pp0));
-    fetch_k(tix(pp0));
-    fetch_v(tix(pp0));
-    stash_k(pp0);
-    stash_v(pp0);
-    fetch_k(tix(pp0 + 1));
-    stash_k(pp0 + 1);
-    __syncthreads();
-    bpark();
-    if constexpr (MASK) {
+    // The unmasked walk over key tiles ta <= t < tb.  Prologue: K(ta), V(ta),
+    // K(ta+1) staged; S^T(ta) scored and its reference set.
+    auto walk = [&](int ta, int tb) __attribute__((always_inline)) {
+        bload(ta);
+        fetch_k(ta);
+        fetch_v(ta);
+        stash_k(ta);
+        stash_v(ta);
+        fetch_k(ta + 1);
+        stash_k(ta + 1);
+        __syncthreads();
+        bpark();
+        if (ta < t1w) {
+            score(ta, s0, nullptr);
+            mask(std::false_type{}, ta, s0);
+            reference(scan(s0));
+        }
+        bload(ta + 1);
+        __syncthreads();  // K(ta) is read by every wave before K(ta+2) replaces it
+        for (int t = ta; t < tb; t += 2) {
+            step(t, s0, s1);
+            if (t + 1 < tb) step(t + 1, s1, s0);
+        }
+    };
+    // The masked walk over list positions pp0 <= t < pp1, with the same
+    // prologue; the tile scored first is the first one the wave computes.
+    auto walk_m = [&]() __attribute__((always_inline)) {
+        mload(tix(pp0));
+        bload(tix(pp0));
+        fetch_k(tix(pp0));
+        fetch_v(tix(pp0));
+        stash_k(pp0);
+        stash_v(pp0);
+        fetch_k(tix(pp0 + 1));
+        stash_k(pp0 + 1);
+        __syncthreads();
+        bpark();
         mpark();
         have = pp0 < pp1 && tix(pp0) < tw && !mnone;
         if (have) {
             score(pp0, s0, nullptr);
-            mask(tix(pp0), s0);
+            mask(std::bool_constant<MASK>{}, tix(pp0), s0);
             reference(scan(s0));
         }
-    } else if (t0 < t1w) {
-        score(t0, s0, nullptr);
-        mask(t0, s0);
-        reference(scan(s0));
-    }
-    mload(tix(pp0 + 1));
-    bload(tix(pp0 + 1));
-    __syncthreads();  // K(t0) is read by every wave before K(t0+2) replaces it
-
-    if constexpr (MASK) {
+        mload(tix(pp0 + 1));
+        bload(tix(pp0 + 1));
+        __syncthreads();
         for (int t = pp0; t < pp1; t += 2) {
             step_m(t, s0, s1);
             if (t + 1 < pp1) step_m(t + 1, s1, s0);
         }
-    } else {
-        for (int t = t0; t < t1; t += 2) {
-            step(t, s0, s1);
-            if (t + 1 < t1) step(t + 1, s1, s0);
+    };
+
+    if constexpr (MASK) {
+        if (dense) {
+            // consecutive tiles, each opened whole: positions map to tiles
+            // tl0 + pos and the mask changes no logit
+            t1w = min(tl0 + pp1, tw);
+            walk(tl0 + pp0, tl0 + pp1);
+        } else {
+            walk_m();
         }
+    } else {
+        walk(t0, t1);
     }
 
     if (nsplit > 1) {
@@ -789,12 +848,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 }
 
 // Tile marks of an allowed-mask shared by all heads: one workgroup per
-// (mask batch, query tile, key tile), writes 1 if any of the query tile's
-// rows allows a key of the key tile, else 0.  Each wave reads 64 rows; lane
-// l reads 4-byte word l mod 16 of every 4th row from l / 16, so each load
-// instruction covers 4 whole 64-byte row segments.  Key tiles past
-// the last key a causal row of the tile can reach are marked 0 unread (the
-// prefill never visits them).
+// (mask batch, query tile, key tile) writes 0 if no row of the query tile
+// may see a key of the key tile, 2 if every row may see every key of it,
+// else 1.  Only the bytes that can matter count: keys below Skv, and with
+// the causal rule keys at or before the row's position (row i sits at
+// position <= Skv - Sq + i in every batch item, a bound the rules reach
+// when the item's length is Skv), so a causal mask given with the causal
+// rule still opens its tiles whole.  Each wave reads 64 rows; lane l reads
+// 4-byte word l mod 16 of every 4th row from l / 16, so each load
+// instruction covers 4 whole 64-byte row segments.  A mask with one row for
+// all queries (row stride 0) is read once per tile, as the tile's last row,
+// which sees the most keys under the causal rule.  Key tiles past the last
+// key a causal row of the tile can reach are marked 0 unread (the prefill
+// never visits them).
 __global__ __launch_bounds__(kBM) void prefill_mask_tiles_kernel(
     const uint8_t* __restrict__ mask, long long msb, long long msi, int Sq, int Skv, int nqt,
     int nkt, int causal, uint8_t* __restrict__ tmap) {
@@ -802,9 +868,8 @@ __global__ __launch_bounds__(kBM) void prefill_mask_tiles_kernel(
     const int qt = (blockIdx.x / nkt) % nqt;
     const int bm = blockIdx.x / (nkt * nqt);
     const int q0 = qt * kBM;
-    __shared__ int flags[kBM / 64];
+    __shared__ int flags[2 * (kBM / 64)];
     if (causal) {
-        // row i sits at position <= Skv - Sq + i (reading of the rules)
         const int hi = Skv - Sq + min(q0 + kBM, Sq);
         if (kt * kBN >= hi) {
             if (threadIdx.x == 0) tmap[blockIdx.x] = 0;
@@ -813,21 +878,40 @@ __global__ __launch_bounds__(kBM) void prefill_mask_tiles_kernel(
     }
     const int lane = threadIdx.x & 63;
     const int r0 = q0 + (int)(threadIdx.x >> 6) * 64 + (lane >> 4);
-    const int col = min(kt * kBN + 4 * (lane & 15), mask_last_word(Skv));
+    const int c = kt * kBN + 4 * (lane & 15);  // first key of this lane's word
+    const int col = min(c, mask_last_word(Skv));
     const uint8_t* mtile = mask + bm * msb + col;
-    uint32_t any = 0;
+    uint32_t any = 0;   // OR of the counted bytes
+    uint32_t hole = 0;  // nonzero if a counted byte is zero
+    const bool one_row = msi == 0;
+    const int last_row = min(q0 + kBM, Sq) - 1;
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
-        const int row = r0 + 4 * it;
-        if (row < Sq) any |= ldg_word(mtile + (long long)row * msi);
+        const int row = one_row ? last_row : r0 + 4 * it;
+        if (one_row ? (it == 0 && threadIdx.x < 16) : row < Sq) {
+            const uint32_t w = ldg_word(mtile + (long long)row * msi);
+            // bytes counted: keys c .. c + nb - 1 (none for a clamped word)
+            int nb = c == col ? Skv - c : 0;
+            if (causal) nb = min(nb, Skv - Sq + row - c + 1);
+            const uint32_t ign = nb >= 4 ? 0u : nb <= 0 ? ~0u : ~0u << (8 * nb);
+            any |= w & ~ign;
+            hole |= has_zero_byte(w | ign);
+        }
     }
-    const bool wv = __builtin_amdgcn_ballot_w64(any != 0) != 0;
-    if ((threadIdx.x & 63) == 0) flags[threadIdx.x >> 6] = wv;
+    const bool wa = __builtin_amdgcn_ballot_w64(any != 0) != 0;
+    const bool wh = __builtin_amdgcn_ballot_w64(hole != 0) != 0;
+    if ((threadIdx.x & 63) == 0) {
+        flags[threadIdx.x >> 6] = wa;
+        flags[kBM / 64 + (threadIdx.x >> 6)] = wh;
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
-        int f = 0;
-        for (int w = 0; w < kBM / 64; ++w) f |= flags[w];
-        tmap[blockIdx.x] = f ? 1 : 0;
+        int fa = 0, fh = 0;
+        for (int w = 0; w < kBM / 64; ++w) {
+            fa |= flags[w];
+            fh |= flags[kBM / 64 + w];
+        }
+        tmap[blockIdx.x] = fa ? (fh ? 1 : 2) : 0;
     }
 }
 
