@@ -856,9 +856,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 // when the item's length is Skv), so a causal mask given with the causal
 // rule still opens its tiles whole.  Each wave reads 64 rows; lane l reads
 // 4-byte word l mod 16 of every 4th row from l / 16, so each load
-// instruction covers 4 whole 64-byte row segments.  A mask with one row for
-// all queries (row stride 0) is read once per tile, as the tile's last row,
-// which sees the most keys under the causal rule.  Key tiles past the last
+// instruction covers 4 whole 64-byte row segments.  Key tiles past the last
 // key a causal row of the tile can reach are marked 0 unread (the prefill
 // never visits them).
 __global__ __launch_bounds__(kBM) void prefill_mask_tiles_kernel(
@@ -883,12 +881,10 @@ __global__ __launch_bounds__(kBM) void prefill_mask_tiles_kernel(
     const uint8_t* mtile = mask + bm * msb + col;
     uint32_t any = 0;   // OR of the counted bytes
     uint32_t hole = 0;  // nonzero if a counted byte is zero
-    const bool one_row = msi == 0;
-    const int last_row = min(q0 + kBM, Sq) - 1;
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
-        const int row = one_row ? last_row : r0 + 4 * it;
-        if (one_row ? (it == 0 && threadIdx.x < 16) : row < Sq) {
+        const int row = r0 + 4 * it;
+        if (row < Sq) {
             const uint32_t w = ldg_word(mtile + (long long)row * msi);
             // bytes counted: keys c .. c + nb - 1 (none for a clamped word)
             int nb = c == col ? Skv - c : 0;
@@ -912,6 +908,32 @@ __global__ __launch_bounds__(kBM) void prefill_mask_tiles_kernel(
             fh |= flags[kBM / 64 + w];
         }
         tmap[blockIdx.x] = fa ? (fh ? 1 : 2) : 0;
+    }
+}
+
+// The same marks for a mask with one row for all queries (row stride 0):
+// one wavefront per (mask batch, key tile) reads the tile's 64 bytes of the
+// row once (16 lanes, a word each) and marks every query tile.  Under the
+// causal rule a query tile counts the keys up to its last row's position
+// bound, the most any of its rows may see; tiles past it come out 0.
+__global__ __launch_bounds__(64) void prefill_mask_row_tiles_kernel(
+    const uint8_t* __restrict__ mask, long long msb, int Sq, int Skv, int nqt, int nkt,
+    int causal, uint8_t* __restrict__ tmap) {
+    const int kt = blockIdx.x % nkt;
+    const int bm = blockIdx.x / nkt;
+    const int lane = threadIdx.x;
+    const int c = kt * kBN + 4 * (lane & 15);  // first key of this lane's word
+    const int col = min(c, mask_last_word(Skv));
+    const bool reads = lane < 16;
+    const uint32_t w = reads ? ldg_word(mask + bm * msb + col) : 0u;
+    for (int qt = 0; qt < nqt; ++qt) {
+        const int last_row = min(qt * kBM + kBM, Sq) - 1;
+        int nb = c == col ? Skv - c : 0;  // bytes counted: keys c .. c + nb - 1
+        if (causal) nb = min(nb, Skv - Sq + last_row - c + 1);
+        const uint32_t ign = nb >= 4 ? 0u : nb <= 0 ? ~0u : ~0u << (8 * nb);
+        const bool wa = __builtin_amdgcn_ballot_w64(reads && (w & ~ign) != 0) != 0;
+        const bool wh = __builtin_amdgcn_ballot_w64(reads && has_zero_byte(w | ign) != 0) != 0;
+        if (lane == 0) tmap[((size_t)bm * nqt + qt) * nkt + kt] = wa ? (wh ? 1 : 2) : 0;
     }
 }
 
@@ -1038,9 +1060,14 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
     if (tmap) {
         const int Bm = a.msb != 0 ? a.B : 1;
         if (t) t->begin(kPrefillMaskTiles, a.stream);
-        hipLaunchKernelGGL(prefill_mask_tiles_kernel, dim3((unsigned)((long)Bm * nqt * nkt)),
-                           dim3(kBM), 0, a.stream, a.mask, a.msb, a.msi, a.Sq, a.Skv, nqt, nkt,
-                           a.causal, tmap);
+        if (a.msi == 0)  // one row for all queries
+            hipLaunchKernelGGL(prefill_mask_row_tiles_kernel, dim3((unsigned)((long)Bm * nkt)),
+                               dim3(64), 0, a.stream, a.mask, a.msb, a.Sq, a.Skv, nqt, nkt,
+                               a.causal, tmap);
+        else
+            hipLaunchKernelGGL(prefill_mask_tiles_kernel, dim3((unsigned)((long)Bm * nqt * nkt)),
+                               dim3(kBM), 0, a.stream, a.mask, a.msb, a.msi, a.Sq, a.Skv, nqt, nkt,
+                               a.causal, tmap);
         hipError_t e = hipGetLastError();
         if (t) t->end(kPrefillMaskTiles, a.stream);
         if (e != hipSuccess) return e;
