@@ -260,6 +260,29 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         if (tmap != nullptr) {  // the mask is shared by all heads (msh == 0)
             listed = true;
             const uint8_t* tm = tmap + ((size_t)(msb != 0 ? b : 0) * nqt + qt) * nkt;
+            // A mask with one row for all queries (msi == 0) has no pre-pass:
+            // each lane marks its key tile from the row's 64 bytes, counting
+            // the bytes the pre-pass would (keys below Skv; under the causal
+            // rule, keys up to this query tile's last row's position bound).
+            const uint8_t* mrow = allowed + b * msb;
+            const int mrow_last = mask_last_word(Skv);
+            const int qlast = min(qz + kBM, Sq) - 1;
+            auto row_mark = [&](int kt) -> int {
+                uint32_t wd[16];
+#pragma unroll
+                for (int w = 0; w < 16; ++w) wd[w] = ldg_word(mrow + min(kt * kBN + 4 * w, mrow_last));
+                uint32_t any = 0, hole = 0;
+#pragma unroll
+                for (int w = 0; w < 16; ++w) {
+                    const int c = kt * kBN + 4 * w;
+                    int nb = c <= mrow_last ? Skv - c : 0;  // bytes counted: keys c .. c + nb - 1
+                    if (causal) nb = min(nb, Skv - Sq + qlast - c + 1);
+                    const uint32_t ign = nb >= 4 ? 0u : nb <= 0 ? ~0u : ~0u << (8 * nb);
+                    any |= wd[w] & ~ign;
+                    hole |= has_zero_byte(wd[w] | ign);
+                }
+                return any != 0 ? (hole != 0 ? 1 : 2) : 0;
+            };
             if (wave == 0) {
                 // compact the marks of key tiles 0 .. ntiles_q-1 in ascending
                 // order: 64 tiles per round, a lane each, ballot and prefix count
@@ -267,7 +290,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                 bool cut = false;
                 for (int k0 = 0; k0 < ntiles_q; k0 += 64) {
                     const int kt = k0 + lane;
-                    const int mk = kt < ntiles_q ? tm[min(kt, nkt - 1)] : 0;
+                    const int mk = kt >= ntiles_q ? 0 : msi == 0 ? row_mark(kt) : tm[min(kt, nkt - 1)];
                     const uint64_t bal = __builtin_amdgcn_ballot_w64(mk != 0);
                     cut |= __builtin_amdgcn_ballot_w64(mk == 1) != 0;
                     if (mk != 0) lds_tl[base + __builtin_popcountll(bal & ((1ull << lane) - 1))] = kt;
@@ -911,32 +934,6 @@ __global__ __launch_bounds__(kBM) void prefill_mask_tiles_kernel(
     }
 }
 
-// The same marks for a mask with one row for all queries (row stride 0):
-// one wavefront per (mask batch, key tile) reads the tile's 64 bytes of the
-// row once (16 lanes, a word each) and marks every query tile.  Under the
-// causal rule a query tile counts the keys up to its last row's position
-// bound, the most any of its rows may see; tiles past it come out 0.
-__global__ __launch_bounds__(64) void prefill_mask_row_tiles_kernel(
-    const uint8_t* __restrict__ mask, long long msb, int Sq, int Skv, int nqt, int nkt,
-    int causal, uint8_t* __restrict__ tmap) {
-    const int kt = blockIdx.x % nkt;
-    const int bm = blockIdx.x / nkt;
-    const int lane = threadIdx.x;
-    const int c = kt * kBN + 4 * (lane & 15);  // first key of this lane's word
-    const int col = min(c, mask_last_word(Skv));
-    const bool reads = lane < 16;
-    const uint32_t w = reads ? ldg_word(mask + bm * msb + col) : 0u;
-    for (int qt = 0; qt < nqt; ++qt) {
-        const int last_row = min(qt * kBM + kBM, Sq) - 1;
-        int nb = c == col ? Skv - c : 0;  // bytes counted: keys c .. c + nb - 1
-        if (causal) nb = min(nb, Skv - Sq + last_row - c + 1);
-        const uint32_t ign = nb >= 4 ? 0u : nb <= 0 ? ~0u : ~0u << (8 * nb);
-        const bool wa = __builtin_amdgcn_ballot_w64(reads && (w & ~ign) != 0) != 0;
-        const bool wh = __builtin_amdgcn_ballot_w64(reads && has_zero_byte(w | ign) != 0) != 0;
-        if (lane == 0) tmap[((size_t)bm * nqt + qt) * nkt + kt] = wa ? (wh ? 1 : 2) : 0;
-    }
-}
-
 // Merge of the key-range splits of each query row (log-sum-exp rule, as at
 // decode): M = max_s m_s, l = sum_s l_s 2^(m_s - M),
 // out = (sum_s acc_s 2^(m_s - M)) / l; padded rows are written as zeros.
@@ -1057,17 +1054,12 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
     const bool gen = a.bias != nullptr || !(a.scale > 0.0f);
     const float sl = gen ? kLog2e : a.scale * kLog2e;
     KernelTimer* t = active_timer();
-    if (tmap) {
+    if (tmap && a.msi != 0) {  // a one-row mask is marked inside the prefill
         const int Bm = a.msb != 0 ? a.B : 1;
         if (t) t->begin(kPrefillMaskTiles, a.stream);
-        if (a.msi == 0)  // one row for all queries
-            hipLaunchKernelGGL(prefill_mask_row_tiles_kernel, dim3((unsigned)((long)Bm * nkt)),
-                               dim3(64), 0, a.stream, a.mask, a.msb, a.Sq, a.Skv, nqt, nkt,
-                               a.causal, tmap);
-        else
-            hipLaunchKernelGGL(prefill_mask_tiles_kernel, dim3((unsigned)((long)Bm * nqt * nkt)),
-                               dim3(kBM), 0, a.stream, a.mask, a.msb, a.msi, a.Sq, a.Skv, nqt, nkt,
-                               a.causal, tmap);
+        hipLaunchKernelGGL(prefill_mask_tiles_kernel, dim3((unsigned)((long)Bm * nqt * nkt)),
+                           dim3(kBM), 0, a.stream, a.mask, a.msb, a.msi, a.Sq, a.Skv, nqt, nkt,
+                           a.causal, tmap);
         hipError_t e = hipGetLastError();
         if (t) t->end(kPrefillMaskTiles, a.stream);
         if (e != hipSuccess) return e;
