@@ -59,10 +59,11 @@
 // exactly zero and its maximum -inf).  For a mask shared by all heads, a
 // small kernel first reads it once (prefill_mask_tiles_kernel) and marks,
 // per query tile and key tile, whether any row of the query tile may see a
-// key of the key tile; each block compacts its query tile's marks into an
-// ascending list of key tiles and stages and walks only those, so
-// structured masks -- left padding, packed documents, sliding windows --
-// cost only the tiles they open.  The loop then runs over list positions:
+// key of the key tile (a mask with one row for all queries is marked by
+// the blocks themselves, from that row); each block compacts its query
+// tile's marks into an ascending list of key tiles and stages and walks
+// only those, so structured masks -- left padding, packed documents,
+// sliding windows -- cost only the tiles they open.  The loop then runs over list positions:
 // LDS ring slots follow the position, key offsets and masks the listed tile.
 // The marks also tell a tile that the mask opens whole (every byte of it
 // that the causal rule leaves visible is set) from one it cuts; a block
