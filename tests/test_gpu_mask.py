@@ -175,6 +175,11 @@ WHOLE_TILES = [
      lambda B, Sq, Skv: W.key_padding_mask([320, 130], [Skv, Skv], Skv), False),
     ("per-item padding, ragged", 3, 2, 333, 1030, 64, 0, [1030, 1000, 700],
      lambda B, Sq, Skv: W.key_padding_mask([0, 64, 192], [1030, 1030, 641], Skv), False),
+    # one-row masks past 64 key tiles take the pre-pass instead of the blocks' own marks
+    ("long all-true row", 1, 2, 256, 5000, 64, 1, None,
+     lambda B, Sq, Skv: np.ones((1, 1, 1, Skv), dtype=bool), True),
+    ("long padding rows with splits", 2, 2, 300, 6000, 128, 1, [6000, 5000],
+     lambda B, Sq, Skv: W.key_padding_mask([640, 100], [Skv, Skv], Skv), False),
 ]
 
 

@@ -59,12 +59,13 @@
 // exactly zero and its maximum -inf).  For a mask shared by all heads, a
 // small kernel first reads it once (prefill_mask_tiles_kernel) and marks,
 // per query tile and key tile, whether any row of the query tile may see a
-// key of the key tile (a mask with one row for all queries is marked by
-// the blocks themselves, from that row); each block compacts its query
-// tile's marks into an ascending list of key tiles and stages and walks
-// only those, so structured masks -- left padding, packed documents,
-// sliding windows -- cost only the tiles they open.  The loop then runs over list positions:
-// LDS ring slots follow the position, key offsets and masks the listed tile.
+// key of the key tile (a mask with one row for all queries and at most 64
+// key tiles is marked by the blocks themselves, from that row); each block
+// compacts its query tile's marks into an ascending list of key tiles and
+// stages and walks only those, so structured masks -- left padding, packed
+// documents, sliding windows -- cost only the tiles they open.  The loop
+// then runs over list positions: LDS ring slots follow the position, key
+// offsets and masks the listed tile.
 // The marks also tell a tile that the mask opens whole (every byte of it
 // that the causal rule leaves visible is set) from one it cuts; a block
 // whose listed tiles are consecutive and all open whole runs the loop of
@@ -261,10 +262,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         if (tmap != nullptr) {  // the mask is shared by all heads (msh == 0)
             listed = true;
             const uint8_t* tm = tmap + ((size_t)(msb != 0 ? b : 0) * nqt + qt) * nkt;
-            // A mask with one row for all queries (msi == 0) has no pre-pass:
-            // each lane marks its key tile from the row's 64 bytes, counting
-            // the bytes the pre-pass would (keys below Skv; under the causal
-            // rule, keys up to this query tile's last row's position bound).
+            // A mask with one row for all queries (msi == 0) and at most 64
+            // key tiles (one round below) has no pre-pass: each lane marks its
+            // key tile from the row's 64 bytes, counting the bytes the
+            // pre-pass would (keys below Skv; under the causal rule, keys up
+            // to this query tile's last row's position bound).  Longer rows
+            // keep the pre-pass, which costs one launch instead of a memory
+            // round trip per round in every block.
+            const bool row_marks = msi == 0 && nkt <= 64;
             const uint8_t* mrow = allowed + b * msb;
             const int mrow_last = mask_last_word(Skv);
             const int qlast = min(qz + kBM, Sq) - 1;
@@ -291,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                 bool cut = false;
                 for (int k0 = 0; k0 < ntiles_q; k0 += 64) {
                     const int kt = k0 + lane;
-                    const int mk = kt >= ntiles_q ? 0 : msi == 0 ? row_mark(kt) : tm[min(kt, nkt - 1)];
+                    const int mk = kt >= ntiles_q ? 0 : row_marks ? row_mark(kt) : tm[min(kt, nkt - 1)];
                     const uint64_t bal = __builtin_amdgcn_ballot_w64(mk != 0);
                     cut |= __builtin_amdgcn_ballot_w64(mk == 1) != 0;
                     if (mk != 0) lds_tl[base + __builtin_popcountll(bal & ((1ull << lane) - 1))] = kt;
@@ -1055,7 +1060,7 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
     const bool gen = a.bias != nullptr || !(a.scale > 0.0f);
     const float sl = gen ? kLog2e : a.scale * kLog2e;
     KernelTimer* t = active_timer();
-    if (tmap && a.msi != 0) {  // a one-row mask is marked inside the prefill
+    if (tmap && !(a.msi == 0 && nkt <= 64)) {  // short one-row masks are marked in the prefill
         const int Bm = a.msb != 0 ? a.B : 1;
         if (t) t->begin(kPrefillMaskTiles, a.stream);
         hipLaunchKernelGGL(prefill_mask_tiles_kernel, dim3((unsigned)((long)Bm * nqt * nkt)),
