@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
+import transformer_scaled_dot_attn_amd as attn
 import workloads as W
 from gpu_util import BF16_TOL, F32_TOL, assert_matches, gpu_run
 
@@ -91,4 +92,67 @@ def test_random_combination(seed):
     ref = oracle.attention(prob["q"], prob["k"], prob["v"], prob["scale"], causal, clamped,
                            mask=mask)
     assert_matches(got, ref, F32_TOL if dt == "f32" else BF16_TOL, clamped, Skv, f"c{seed}")
+    assert np.all(got[np.all(ref == 0.0, axis=-1)] == 0.0), "rows without a visible key"
+
+
+def _structured(seed):
+    """A seeded structured mask case: masks that open whole tiles (all-true
+    planes or rows, key padding at or off tile edges, the causal rule given
+    as a mask, packed documents, windows), with random sizes, broadcast,
+    lengths, grouped heads, widths and sometimes a bias."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 6]))
+    B = int(rng.integers(1, 4))
+    H = int(rng.choice([2, 4, 8]))
+    Hkv = int(rng.choice([h for h in (1, 2, 4, 8) if h <= H and H % h == 0]))
+    Sq = int(rng.integers(2, 700))
+    Skv = Sq if rng.random() < 0.5 else int(rng.integers(Sq, Sq + 6000))
+    d, dv = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+    causal = int(rng.integers(0, 2))
+    lens = None if rng.random() < 0.5 else [int(x) for x in rng.integers(1, Skv + 1, size=B)]
+    kind = str(rng.choice(["true_plane", "true_row", "pad_edge", "pad_any", "tril", "docs",
+                           "window"]))
+    if kind == "true_plane":
+        mask = np.ones((1, 1, Sq, Skv), dtype=bool)
+    elif kind == "true_row":
+        mask = np.ones((B if rng.random() < 0.5 else 1, 1, 1, Skv), dtype=bool)
+    elif kind in ("pad_edge", "pad_any"):
+        hi = max(1, Skv // 2)
+        starts = rng.integers(0, hi, size=B)
+        if kind == "pad_edge":
+            starts = starts // 64 * 64
+        mask = W.key_padding_mask([int(x) for x in starts], [Skv] * B, Skv)
+    elif kind == "tril":
+        mask = np.tril(np.ones((Sq, Skv), dtype=bool), Skv - Sq)[None, None]
+    elif kind == "docs":
+        cuts = np.sort(rng.choice(np.arange(1, Skv), size=min(3, Skv - 1), replace=False))
+        mask = W.document_mask(np.diff(np.concatenate([[0], cuts, [Skv]])).tolist())
+        mask = mask[:, :, Skv - Sq:, :]
+    else:
+        mask = W.window_mask(Skv, int(rng.integers(16, 400)))[:, :, Skv - Sq:, :]
+    bias = None
+    if rng.random() < 0.25:
+        bias = W.random_bias(seed, (1, H, Sq, Skv), "bf16", hide=0.02)
+    return B, H, Hkv, Sq, Skv, d, dv, causal, lens, kind, np.ascontiguousarray(mask), bias
+
+
+@pytest.mark.parametrize("seed", range(400, 430))
+def test_random_structured_mask(seed):
+    """Structured masks through the prefill's whole-tile paths (tile lists,
+    the plain loop, marks made by the pre-pass or by the blocks) against the
+    oracle, on random shapes."""
+    import torch
+    B, H, Hkv, Sq, Skv, d, dv, causal, lens, kind, mask, bias = _structured(seed)
+    _say(f"structured {seed}: B{B} H{H}/{Hkv} Sq{Sq} Skv{Skv} d{d}/{dv} causal{causal} "
+         f"lens {lens} {kind} {mask.shape} bias {bias is not None}")
+    prob = W.random_problem(seed, B, H, Sq, Skv, d, "bf16", lens, Hkv=Hkv, dv=dv)
+    tq, tk, tv = (W.to_torch(prob[x]) for x in ("q", "k", "v"))
+    tl = None if lens is None else torch.as_tensor(np.asarray(lens, np.int32)).to("cuda")
+    out = attn.fwd(tq, tk, tv, causal=bool(causal), kv_lens=tl, scale=prob["scale"],
+                   mask=W.mask_to_torch(mask),
+                   bias=None if bias is None else W.bias_to_torch(bias))
+    torch.cuda.synchronize()
+    got = W.from_torch(out)
+    ref = oracle.attention(prob["q"], prob["k"], prob["v"], prob["scale"], causal, lens,
+                           mask=mask, bias=bias)
+    assert_matches(got, ref, BF16_TOL, lens, Skv, f"s{seed} {kind}")
     assert np.all(got[np.all(ref == 0.0, axis=-1)] == 0.0), "rows without a visible key"
