@@ -470,25 +470,36 @@ def main():
 
     extra = {}
 
+    def secondary(key, what, fn):
+        # a failing secondary measurement is reported under its key; the step
+        # and its JSON line still follow
+        print(f"[bench] {what}", file=sys.stderr, flush=True)
+        try:
+            extra[key] = fn()
+        except Exception as e:  # noqa: BLE001 -- reported, not hidden
+            print(f"[bench] {what} failed: {e!r}", file=sys.stderr, flush=True)
+            extra[key] = {"error": repr(e)}
+
     def secondary_parts():
         if "gqa" in parts:
-            print("[bench] grouped-head decode sweep", file=sys.stderr, flush=True)
             have = {w.name: x for kind, w, x, _ in runs if kind == "decode"}
-            extra["gqa_decode"] = gqa_decode_sweep(attn, W, dev, args.steps, args.warmup,
-                                                   have=have)
+            secondary("gqa_decode", "grouped-head decode sweep",
+                      lambda: gqa_decode_sweep(attn, W, dev, args.steps, args.warmup, have=have))
         elif "gqa8" in parts:
-            extra["gqa_decode"] = gqa_decode_sweep(attn, W, dev, args.steps, args.warmup,
-                                                   names=("gqa_decode8192_bf16",))
+            secondary("gqa_decode", "8-K/V-head decode",
+                      lambda: gqa_decode_sweep(attn, W, dev, args.steps, args.warmup,
+                                               names=("gqa_decode8192_bf16",)))
         if "masks" in parts and runs:
-            print("[bench] allowed-mask runs", file=sys.stderr, flush=True)
-            extra["masks"] = mask_runs(attn, W, runs, args.steps, args.warmup)
+            secondary("masks", "allowed-mask runs",
+                      lambda: mask_runs(attn, W, runs, args.steps, args.warmup))
         if "configs" in parts:
-            print("[bench] other prefill workloads", file=sys.stderr, flush=True)
-            extra["prefill_configs"] = prefill_configs(attn, W, dev, args.steps, args.warmup)
+            secondary("prefill_configs", "other prefill workloads",
+                      lambda: prefill_configs(attn, W, dev, args.steps, args.warmup))
         if "sweep" in parts:
-            print("[bench] prefill S sweep", file=sys.stderr, flush=True)
-            extra["prefill_sweep"] = prefill_sweep(attn, W, dev, args.steps, args.warmup)
-            extra["prefill_sweep_slope"] = sweep_slopes(extra["prefill_sweep"])
+            secondary("prefill_sweep", "prefill S sweep",
+                      lambda: prefill_sweep(attn, W, dev, args.steps, args.warmup))
+            if isinstance(extra.get("prefill_sweep"), list):
+                extra["prefill_sweep_slope"] = sweep_slopes(extra["prefill_sweep"])
 
     # The secondary measurements run first by default, so the step's timed
     # region starts on a GPU already under load (see --headline-first).
@@ -583,7 +594,11 @@ def main():
     if not args.no_cpu_baseline and "prefill" in parts:
         threads = args.cpu_threads or host_cores()[1]
         print(f"[bench] cpu baseline with {threads} threads", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(threads)
+        try:
+            result["cpu_baseline"] = cpu_baseline(threads)
+        except Exception as e:  # noqa: BLE001 -- reported in the line, which still prints
+            print(f"[bench] cpu baseline failed: {e!r}", file=sys.stderr, flush=True)
+            result["cpu_baseline"] = {"error": repr(e)}
     print(json.dumps(result), flush=True)
 
 
