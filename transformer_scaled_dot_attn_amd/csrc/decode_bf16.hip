@@ -162,30 +162,34 @@ __device__ __forceinline__ void mfma_keys(const u32x4 (&qf)[D / 16], const uint1
     };
 
     // K and V tile rows whole (kRows rows per load, lane%kChunks the 16-byte
-    // chunk).  Rows at or past klim are redirected to the tile's first row
-    // (valid; their logits are masked).
+    // chunk).  Rows at or past klim are clamped to row klim - 1 (valid: klim
+    // <= L; their logits are masked).  Addresses are a wave-uniform base plus
+    // a 32-bit byte offset per lane (a head's rows span less than 4 GiB), so
+    // a load costs a min and a multiply-add.
+    const char* kbase = reinterpret_cast<const char*>(kb);
+    const char* vbase = reinterpret_cast<const char*>(vb);
+    const uint32_t kcol = (uint32_t)(lane % C::kChunks) * 16u;
+    const uint32_t vcol = (uint32_t)(lane % CV::kChunks) * 16u;
     u32x4 kr[C::kLoads], vr[CV::kLoads];
     auto load_kv = [&](int t0) {
         if constexpr (D == DV) {  // K and V rows of one tile side by side
 #pragma unroll
             for (int c2 = 0; c2 < C::kLoads; ++c2) {
-                const int row = t0 + c2 * C::kRows + lane / C::kChunks;
-                const size_t off = (size_t)(row < klim ? row : t0) * D + (lane % C::kChunks) * 8;
-                kr[c2] = ldg16_stream(kb + off);
-                vr[c2] = ldg16_stream(vb + off);
+                const int row = min(t0 + c2 * C::kRows + lane / C::kChunks, klim - 1);
+                const uint32_t off = (uint32_t)row * (2u * D) + kcol;
+                kr[c2] = ldg16_stream(kbase + off);
+                vr[c2] = ldg16_stream(vbase + off);
             }
         } else {
 #pragma unroll
             for (int c2 = 0; c2 < C::kLoads; ++c2) {
-                const int row = t0 + c2 * C::kRows + lane / C::kChunks;
-                kr[c2] = ldg16_stream(kb + (size_t)(row < klim ? row : t0) * D +
-                                      (lane % C::kChunks) * 8);
+                const int row = min(t0 + c2 * C::kRows + lane / C::kChunks, klim - 1);
+                kr[c2] = ldg16_stream(kbase + ((uint32_t)row * (2u * D) + kcol));
             }
 #pragma unroll
             for (int c2 = 0; c2 < CV::kLoads; ++c2) {
-                const int row = t0 + c2 * CV::kRows + lane / CV::kChunks;
-                vr[c2] = ldg16_stream(vb + (size_t)(row < klim ? row : t0) * DV +
-                                      (lane % CV::kChunks) * 8);
+                const int row = min(t0 + c2 * CV::kRows + lane / CV::kChunks, klim - 1);
+                vr[c2] = ldg16_stream(vbase + ((uint32_t)row * (2u * DV) + vcol));
             }
         }
     };
