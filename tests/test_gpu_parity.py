@@ -102,6 +102,34 @@ def test_bf16_prefill_shapes(case):
     check_problem(prob, causal, BF16_TOL, f"prefill {case}")
 
 
+@pytest.mark.parametrize("mask_kind", [None, "padding", "per_query"])
+def test_block_height_does_not_change_rows(mask_kind):
+    """Small unsplit grids run blocks of 128 query rows, larger ones blocks of
+    256.  With 2 batch items of 1000 rows (4 tiles of 256) 16 heads make 128
+    blocks of 256 rows (run as 128-row blocks) and 17 heads make 136 (run as
+    256-row blocks).  Both match the oracle, and the first 16 heads of the
+    larger problem are bit-identical to the smaller one: a row's result does
+    not depend on the block height."""
+    import torch
+    B, S, d, lens = 2, 1000, 128, [1000, 777]
+    prob = W.random_problem(91, B, 17, S, S, d, "bf16", lens)
+    mask = None
+    if mask_kind == "padding":
+        mask = W.key_padding_mask([0, 64], [1000, 777], S)
+    elif mask_kind == "per_query":
+        mask = W.random_mask(92, (B, 1, S, S), 0.7)
+    tm = None if mask is None else W.mask_to_torch(mask)
+    _say(f"block heights, mask {mask_kind}")
+    runs = {}
+    for H in (16, 17):
+        q, k, v = (np.ascontiguousarray(prob[x][:, :H]) for x in ("q", "k", "v"))
+        got, out = gpu_run(q, k, v, prob["scale"], 1, lens, mask=tm)
+        ref = oracle.attention(q, k, v, prob["scale"], 1, lens, mask=mask)
+        assert_matches(got, ref, BF16_TOL, lens, S, f"H{H} mask {mask_kind}")
+        runs[H] = out
+    assert torch.equal(runs[17][:, :16], runs[16]), "block height changed the rows"
+
+
 # ---------------------------------------------------------- bf16 decode path
 DECODE_CASES = [
     (31, 1, 1, 1, 1, 128, 0, None),

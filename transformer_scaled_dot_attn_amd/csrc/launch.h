@@ -46,7 +46,8 @@ size_t decode_mask_workspace_bytes(int B, int H, int Hkv, int Skv, int d, int dv
 
 // Prefill plan: key-range splits per query tile (1 = none, no workspace).
 struct PrefillPlan {
-    int nsplit;
+    int nsplit;  // key-range splits per query tile (1: none)
+    int bm;      // query rows per block: 256, or 128 on small unsplit grids
 };
 PrefillPlan prefill_plan(int B, int H, int Sq, int Skv);
 size_t prefill_workspace_bytes(int B, int H, int Sq, int Skv, int dv);  // dv: partial width
@@ -66,6 +67,10 @@ KernelTimer* active_timer();  // nullptr when timing is off
 enum KernelId { kPrefillBf16 = 0, kDecodePartialBf16 = 1, kDecodeCombineBf16 = 2, kGenericF32 = 3,
                 kPrefillCombineBf16 = 4, kPrefillMaskTiles = 5, kDecodeMaskTiles = 6,
                 kNumKernels = 7 };
+
+// ATTN_OK for hipSuccess; otherwise records e as this thread's last HIP
+// error (attn_last_hip_error) and returns ATTN_E_LAUNCH.
+int launch_status(hipError_t e);
 
 // attn_fwd_ex on a caller-supplied workspace (checks, kernel choice, launch).
 int run_with_workspace(const void* q, const void* k, const void* v, void* out, int B, int H,

@@ -106,21 +106,19 @@ namespace tsda {
 
 namespace {
 
-constexpr int kBM = 256;   // query rows per block
+constexpr int kBM = 256;   // query rows per block (128 on small grids: BM below)
 constexpr int kBN = 64;    // keys per tile
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 constexpr int kMaxListTiles = 2048;   // key tiles a block's tile list may hold (Skv <= 131072)
 
-template <int D>
+template <int D, int T>  // T: threads of the block
 struct Shape {
     static constexpr int kChunks = D / 8;                        // 16-byte chunks per row
     static constexpr int kKSteps = D / 16;                       // MFMA k-steps of Q K^T
     static constexpr int kDBlocks = D / 32;                      // 32-row blocks of O^T
-    static constexpr int kPerThread = kBN * kChunks / kThreads;  // 16-byte loads per thread
-    static constexpr int kRowsPerPass = kThreads / kChunks;      // tile rows per load pass
-    static_assert(kPerThread >= 1 && kPerThread * kThreads == kBN * kChunks,
+    static constexpr int kPerThread = kBN * kChunks / T;         // 16-byte loads per thread
+    static constexpr int kRowsPerPass = T / kChunks;             // tile rows per load pass
+    static_assert(kPerThread >= 1 && kPerThread * T == kBN * kChunks,
                   "tile must split evenly");
     // LDS row strides in elements.  LDS reads are served 256 bytes (16
     // groups of 16 bytes) per cycle.  A K row is padded by 16 bytes, so the
@@ -148,8 +146,10 @@ __device__ __forceinline__ void pin_schedule() { __builtin_amdgcn_sched_barrier(
 // Zero bias for GEN calls without one (read as its first 4-element group).
 __device__ __attribute__((aligned(16))) uint16_t g_zero_bias[8];
 
-template <int D, int DV, bool MASK, bool GEN>
-__global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
+// BM: query rows per block (256, or 128 on grids that leave CUs idle); a
+// wave owns 32 of them.
+template <int D, int DV, bool MASK, bool GEN, int BM>
+__global__ __launch_bounds__(2 * BM, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
     const int32_t* __restrict__ kv_lens, int BH, int H, int Hkv, int Sq, int Skv, float scale_log2,
@@ -157,8 +157,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint8_t* __restrict__ allowed, long long msb, long long msh, long long msi,
     const uint8_t* __restrict__ tmap, int nkt, const uint16_t* __restrict__ bias, long long bsb,
     long long bsh, long long bsi, float scale) {
-    using S = Shape<D>;    // the key side: Q K^T over D features
-    using SV = Shape<DV>;  // the value side: V rows and outputs of DV features
+    constexpr int kBMb = BM;            // query rows of this block
+    constexpr int kThreads = 2 * BM;    // 64 lanes x BM / 32 waves
+    using S = Shape<D, kThreads>;    // the key side: Q K^T over D features
+    using SV = Shape<DV, kThreads>;  // the value side: V rows and outputs of DV features
     __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][S::kTileK];
     __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][SV::kTileV];
     __shared__ u32x4 lds_m[MASK ? 2 * kThreads : 1];  // parked mask words, 32 bytes per lane
@@ -199,27 +201,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int n = Sq < L ? Sq : L;
     const int off = L - n;
     // Query tile rows.  Without a mask the tiles end at the last valid row
-    // (q0 = n - (nqt - qt) kBM; rows below 0 are dead), so a sequence's partly
+    // (q0 = n - (nqt - qt) BM; rows below 0 are dead), so a sequence's partly
     // filled tile is its first one, whose rows see the fewest keys; the pad
     // rows n .. Sq-1 are zeroed by the blocks of the tiling from row 0 (block
-    // qt: rows qt kBM .. qt kBM + kBM - 1).  With a mask the tiles start at
+    // qt: rows qt BM .. qt BM + BM - 1).  With a mask the tiles start at
     // row 0, as the key-tile marks do.
-    const int qz = qt * kBM;
-    const int q0 = MASK ? qz : n - (nqt - qt) * kBM;
+    const int qz = qt * kBMb;
+    const int q0 = MASK ? qz : n - (nqt - qt) * kBMb;
 
     uint16_t* obase = out + (size_t)bh * Sq * DV;
     // pad rows are zero (without splits; the split combine zeroes them itself)
-    const int z0 = max(qz, n), z1 = min(qz + kBM, Sq);
+    const int z0 = max(qz, n), z1 = min(qz + kBMb, Sq);
     if (nsplit == 1 && z0 < z1 && (!MASK || q0 >= n)) {
         const u32x4 z = {0, 0, 0, 0};
         for (int e = tid; e < (z1 - z0) * SV::kChunks; e += kThreads)
             *reinterpret_cast<u32x4*>(obase + (size_t)z0 * DV + e * 8) = z;
     }
-    if (q0 >= n || q0 + kBM <= 0) return;  // no valid row in this tile
+    if (q0 >= n || q0 + kBMb <= 0) return;  // no valid row in this tile
 
     // keys the whole query tile may see, this block's split of them, and
     // this wave's limits: tiles t0 <= t < t1 of the block, t < t1w of the wave
-    const int kv_hi = causal ? min(L, off + min(q0 + kBM, n)) : L;
+    const int kv_hi = causal ? min(L, off + min(q0 + kBMb, n)) : L;
     const int ntiles_q = (kv_hi + kBN - 1) / kBN;
     const int per_split = (ntiles_q + nsplit - 1) / nsplit;
     const int t0 = min(ntiles_q, split * per_split);
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
             const bool row_marks = msi == 0 && nkt <= 64;
             const uint8_t* mrow = allowed + b * msb;
             const int mrow_last = mask_last_word(Skv);
-            const int qlast = min(qz + kBM, Sq) - 1;
+            const int qlast = min(qz + kBMb, Sq) - 1;
             auto row_mark = [&](int kt) -> int {
                 uint32_t wd[16];
 #pragma unroll
@@ -888,16 +890,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 // instruction covers 4 whole 64-byte row segments.  Key tiles past the last
 // key a causal row of the tile can reach are marked 0 unread (the prefill
 // never visits them).
-__global__ __launch_bounds__(kBM) void prefill_mask_tiles_kernel(
+template <int BM>  // query rows per query tile (the prefill's block)
+__global__ __launch_bounds__(BM) void prefill_mask_tiles_kernel(
     const uint8_t* __restrict__ mask, long long msb, long long msi, int Sq, int Skv, int nqt,
     int nkt, int causal, uint8_t* __restrict__ tmap) {
     const int kt = blockIdx.x % nkt;
     const int qt = (blockIdx.x / nkt) % nqt;
     const int bm = blockIdx.x / (nkt * nqt);
-    const int q0 = qt * kBM;
-    __shared__ int flags[2 * (kBM / 64)];
+    const int q0 = qt * BM;
+    __shared__ int flags[2 * (BM / 64)];
     if (causal) {
-        const int hi = Skv - Sq + min(q0 + kBM, Sq);
+        const int hi = Skv - Sq + min(q0 + BM, Sq);
         if (kt * kBN >= hi) {
             if (threadIdx.x == 0) tmap[blockIdx.x] = 0;
             return;
@@ -927,14 +930,14 @@ __global__ __launch_bounds__(kBM) void prefill_mask_tiles_kernel(
     const bool wh = __builtin_amdgcn_ballot_w64(hole != 0) != 0;
     if ((threadIdx.x & 63) == 0) {
         flags[threadIdx.x >> 6] = wa;
-        flags[kBM / 64 + (threadIdx.x >> 6)] = wh;
+        flags[BM / 64 + (threadIdx.x >> 6)] = wh;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
         int fa = 0, fh = 0;
-        for (int w = 0; w < kBM / 64; ++w) {
+        for (int w = 0; w < BM / 64; ++w) {
             fa |= flags[w];
-            fh |= flags[kBM / 64 + w];
+            fh |= flags[BM / 64 + w];
         }
         tmap[blockIdx.x] = fa ? (fh ? 1 : 2) : 0;
     }
@@ -1008,11 +1011,19 @@ PrefillPlan prefill_plan(int B, int H, int Sq, int Skv) {
     // 1-4 x 32 heads: 512 queries against 4096 keys 117 -> 64 us (4 splits),
     // 256 against 8192 214 -> 66 us (8 splits); grids of 256 blocks or more
     // are faster unsplit, the merge costing more than the idle CUs.
+    //
+    // Unsplit grids of at most 128 blocks (half the CUs or fewer) use blocks
+    // of 128 query rows instead: twice the blocks, each with four waves, so
+    // the heaviest block's walk over the keys takes less time per step.
+    // Measured (B=1, H=32, d=128, causal): S = 512 23.1 -> 20.5 us, S = 1024
+    // 36.8 -> 33.6 us; B=4, H=12, S=512, d=64: 17.0 -> 16.1 us.  Large grids
+    // lose with them (prefill4096 150 -> 234 us: one wave per SIMD).
     const long blocks = (long)((Sq + kBM - 1) / kBM) * B * H;
     const long tiles = (Skv + kBN - 1) / kBN;
     long nsplit = 256 / blocks;
-    nsplit = std::min({nsplit, tiles / 16, (long)kMaxSplit});
-    return PrefillPlan{(int)std::max(1L, nsplit)};
+    nsplit = std::max(1L, std::min({nsplit, tiles / 16, (long)kMaxSplit}));
+    const int bm = nsplit == 1 && blocks <= 128 ? 128 : kBM;
+    return PrefillPlan{(int)nsplit, bm};
 }
 
 size_t prefill_workspace_bytes(int B, int H, int Sq, int Skv, int d) {
@@ -1024,16 +1035,17 @@ size_t prefill_workspace_bytes(int B, int H, int Sq, int Skv, int d) {
 
 size_t prefill_mask_workspace_bytes(int B, int Sq, int Skv) {
     // tile marks of a mask shared by all heads, one byte per (mask batch,
-    // query tile, key tile), after the split partials; none past the list size
+    // query tile, key tile), after the split partials; none past the list
+    // size.  Sized for query tiles of 128 rows, the smaller block height.
     const size_t nkt = (Skv + kBN - 1) / kBN;
     if (nkt > (size_t)kMaxListTiles) return 0;
-    return round_up256((size_t)B * ((Sq + kBM - 1) / kBM) * nkt);
+    return round_up256((size_t)B * ((Sq + 127) / 128) * nkt);
 }
 
 hipError_t launch_prefill_bf16(const LaunchArgs& a) {
-    const int nqt = (a.Sq + kBM - 1) / kBM;
-    const int BH = a.B * a.H;
     const PrefillPlan p = prefill_plan(a.B, a.H, a.Sq, a.Skv);
+    const int nqt = (a.Sq + p.bm - 1) / p.bm;
+    const int BH = a.B * a.H;
     const dim3 grid((unsigned)((long)nqt * BH * p.nsplit));
     const uint16_t* q = static_cast<const uint16_t*>(a.q);
     const uint16_t* k = static_cast<const uint16_t*>(a.k);
@@ -1063,29 +1075,42 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
     if (tmap && !(a.msi == 0 && nkt <= 64)) {  // short one-row masks are marked in the prefill
         const int Bm = a.msb != 0 ? a.B : 1;
         if (t) t->begin(kPrefillMaskTiles, a.stream);
-        hipLaunchKernelGGL(prefill_mask_tiles_kernel, dim3((unsigned)((long)Bm * nqt * nkt)),
-                           dim3(kBM), 0, a.stream, a.mask, a.msb, a.msi, a.Sq, a.Skv, nqt, nkt,
-                           a.causal, tmap);
+        const dim3 mgrid((unsigned)((long)Bm * nqt * nkt));
+        if (p.bm == 128)
+            hipLaunchKernelGGL(prefill_mask_tiles_kernel<128>, mgrid, dim3(128), 0, a.stream,
+                               a.mask, a.msb, a.msi, a.Sq, a.Skv, nqt, nkt, a.causal, tmap);
+        else
+            hipLaunchKernelGGL(prefill_mask_tiles_kernel<kBM>, mgrid, dim3(kBM), 0, a.stream,
+                               a.mask, a.msb, a.msi, a.Sq, a.Skv, nqt, nkt, a.causal, tmap);
         hipError_t e = hipGetLastError();
         if (t) t->end(kPrefillMaskTiles, a.stream);
         if (e != hipSuccess) return e;
     }
     if (t) t->begin(kPrefillBf16, a.stream);
     auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, a.stream, q, k, v, o, a.kv_lens, BH, a.H,
+        hipLaunchKernelGGL(kern, grid, dim3(2 * p.bm), 0, a.stream, q, k, v, o, a.kv_lens, BH, a.H,
                            a.Hkv, a.Sq, a.Skv, sl, a.causal, nqt, p.nsplit, ws_acc, ws_ml, a.mask,
                            a.msb, a.msh, a.msi, tmap, nkt, static_cast<const uint16_t*>(a.bias),
                            a.bsb, a.bsh, a.bsi, a.scale);
     };
     const bool m = a.mask != nullptr;
-    // instantiations for d, d_v in {64, 128}, the mask and the general logits
-    auto pick = [&](auto dk, auto dvk) {
+    // instantiations for d, d_v in {64, 128}, the mask, the general logits
+    // and the block height
+    auto pick_bm = [&](auto dk, auto dvk, auto bmk) {
         constexpr int D = decltype(dk)::value, DV = decltype(dvk)::value;
+        constexpr int BM = decltype(bmk)::value;
         if (gen)
-            m ? go(prefill_bf16_kernel<D, DV, true, true>) : go(prefill_bf16_kernel<D, DV, false, true>);
+            m ? go(prefill_bf16_kernel<D, DV, true, true, BM>)
+              : go(prefill_bf16_kernel<D, DV, false, true, BM>);
         else
-            m ? go(prefill_bf16_kernel<D, DV, true, false>)
-              : go(prefill_bf16_kernel<D, DV, false, false>);
+            m ? go(prefill_bf16_kernel<D, DV, true, false, BM>)
+              : go(prefill_bf16_kernel<D, DV, false, false, BM>);
+    };
+    auto pick = [&](auto dk, auto dvk) {
+        if (p.bm == 128)
+            pick_bm(dk, dvk, std::integral_constant<int, 128>{});
+        else
+            pick_bm(dk, dvk, std::integral_constant<int, kBM>{});
     };
     using I64 = std::integral_constant<int, 64>;
     using I128 = std::integral_constant<int, 128>;
