@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 
 typedef enum {
     ATTN_OK = 0,
@@ -297,6 +297,15 @@ const char* attn_status_string(int status);
 
 /* ATTN_ABI_VERSION of the loaded library. */
 int attn_abi_version(void);
+
+/*
+ * attn_last_hip_error -- the hipError_t value behind the last ATTN_E_LAUNCH
+ * that a call on this thread returned (0, hipSuccess, if none has), kept per
+ * thread until the next such failure.  attn_last_hip_error_name -- the HIP
+ * runtime's name for it (static string).  Neither makes a GPU call.
+ */
+int attn_last_hip_error(void);
+const char* attn_last_hip_error_name(void);
 
 /*
  * attn_release -- frees the library-owned workspace of every device.  The

@@ -1,6 +1,7 @@
 """The C-ABI library on the host: it loads, exports every declared entry
 point, and its argument checks and kernel choice behave as documented.
 No compute call is made (none of these reach a HIP API)."""
+import ast
 import ctypes
 import math
 import os
@@ -39,6 +40,26 @@ def test_abi_version_and_status_strings():
     for s in range(11):
         assert attn.status_string(s) and attn.status_string(s) != "unknown status"
     assert attn.status_string(99) == "unknown status"
+
+
+def test_no_hip_error_recorded_before_a_launch_failure():
+    assert attn.last_hip_error() == (0, "hipSuccess")
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Loading the library before torch must not map a second HIP runtime:
+    the library binds to the one torch carries, whatever the import order."""
+    import subprocess
+    import sys
+    code = ("import transformer_scaled_dot_attn_amd as a; a.library(); import torch; "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') "
+            "if 'libamdhip64' in l}))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True,
+                         text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    maps = ast.literal_eval(out.stdout.strip().splitlines()[-1])
+    assert len(maps) == 1, maps
 
 
 def v(B=1, H=1, Sq=4, Skv=4, d=64, scale=0.125, causal=1, dtype=BF16, q=A, k=A, vv=A, out=A):

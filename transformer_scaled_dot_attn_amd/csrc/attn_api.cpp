@@ -20,6 +20,16 @@
 #include "launch.h"
 
 namespace tsda {
+
+// HIP error behind this thread's last ATTN_E_LAUNCH (hipSuccess: none yet)
+thread_local hipError_t g_last_hip = hipSuccess;
+
+int launch_status(hipError_t e) {
+    if (e == hipSuccess) return ATTN_OK;
+    g_last_hip = e;
+    return ATTN_E_LAUNCH;
+}
+
 namespace {
 
 enum Path { kPathNone = -1, kPathGenericF32 = 0, kPathPrefill = 1, kPathDecode = 2 };
@@ -90,9 +100,11 @@ class EventTimer final : public KernelTimer {
         double ms = 0.0;
         for (const Record& r : done_) {
             if (r.kernel != kernel) continue;
-            if (hipEventSynchronize(r.stop) != hipSuccess) return ATTN_E_LAUNCH;
+            if (const hipError_t e = hipEventSynchronize(r.stop); e != hipSuccess)
+                return launch_status(e);
             float t = 0.0f;
-            if (hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess) return ATTN_E_LAUNCH;
+            if (const hipError_t e = hipEventElapsedTime(&t, r.start, r.stop); e != hipSuccess)
+                return launch_status(e);
             ms += t;
             ++n;
         }
@@ -108,9 +120,11 @@ class EventTimer final : public KernelTimer {
         for (const Record& r : done_) {
             if (r.kernel != kernel) continue;
             if (n < cap && ms_out != nullptr) {
-                if (hipEventSynchronize(r.stop) != hipSuccess) return ATTN_E_LAUNCH;
+                if (const hipError_t e = hipEventSynchronize(r.stop); e != hipSuccess)
+                    return launch_status(e);
                 float t = 0.0f;
-                if (hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess) return ATTN_E_LAUNCH;
+                if (const hipError_t e = hipEventElapsedTime(&t, r.start, r.stop); e != hipSuccess)
+                    return launch_status(e);
                 ms_out[n] = t;
             }
             ++n;
@@ -220,7 +234,7 @@ int run(const void* q, const void* k, const void* v, void* out, int B, int H, in
         workspace = nullptr;
         if (need > 0) {
             int dev = 0;
-            if (hipGetDevice(&dev) != hipSuccess) return ATTN_E_LAUNCH;
+            if (const hipError_t e = hipGetDevice(&dev); e != hipSuccess) return launch_status(e);
             const hipStream_t hs = static_cast<hipStream_t>(stream);
             std::lock_guard<std::mutex> g(g_ws_mu);
             StreamWorkspace* w = nullptr;
@@ -232,7 +246,8 @@ int run(const void* q, const void* k, const void* v, void* out, int B, int H, in
             }
             if (w->bytes < need) {
                 // earlier calls on this stream may still be using the old buffer
-                if (hipStreamSynchronize(hs) != hipSuccess) return ATTN_E_LAUNCH;
+                if (const hipError_t e = hipStreamSynchronize(hs); e != hipSuccess)
+                    return launch_status(e);
                 if (w->ptr) (void)hipFree(w->ptr);
                 w->ptr = nullptr;
                 w->bytes = 0;
@@ -260,7 +275,7 @@ int run(const void* q, const void* k, const void* v, void* out, int B, int H, in
         case kPathDecode: e = launch_decode_bf16(a); break;
         default: return ATTN_E_UNSUPPORTED;
     }
-    return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+    return launch_status(e);
 }
 
 }  // namespace
@@ -428,6 +443,10 @@ const char* attn_status_string(int status) {
 }
 
 int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+int attn_last_hip_error(void) { return static_cast<int>(g_last_hip); }
+
+const char* attn_last_hip_error_name(void) { return hipGetErrorName(g_last_hip); }
 
 void attn_release(void) {
     std::lock_guard<std::mutex> g(g_ws_mu);

@@ -29,14 +29,15 @@ void* g_addr[kMaxDevices];  // device address of `scratch` on each device, once 
 // Address of the current device's copy of the array (set-up on first use).
 int scratch_address(void** out) {
     int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess) return ATTN_E_LAUNCH;
+    if (const hipError_t e = hipGetDevice(&dev); e != hipSuccess) return launch_status(e);
     if (dev < 0 || dev >= kMaxDevices) return ATTN_E_UNSUPPORTED;
     std::lock_guard<std::mutex> g(g_mu);
     if (g_addr[dev] == nullptr) {
         void* p = nullptr;
-        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
             (void)hipGetLastError();
-            return ATTN_E_LAUNCH;
+            return launch_status(e != hipSuccess ? e : hipErrorInvalidSymbol);
         }
         g_addr[dev] = p;
     }
