@@ -95,6 +95,9 @@ typedef enum {
  *   ATTN_F32 : any Sq <= Skv, 1 <= d, d_v <= 128           (VALU kernel)
  *   ATTN_BF16: Sq == 1, d and d_v each in {64, 128}          (split-KV decode)
  *              Sq >= 2, d and d_v each in {64, 128}          (MFMA prefill)
+ *              and one head's keys under 4 GiB: Skv * max(d, d_v) * 2 < 2^32
+ *              (Skv < 16777216 at 128), since rows are addressed with
+ *              32-bit byte offsets from the head's base
  * Every path takes grouped K/V heads, an allowed-mask (attn_fwd_ex), an
  * additive bias (attn_fwd_bias) and any finite scale; with a bias or a scale
  * that is not positive the bf16 paths run their general-logit kernels.

@@ -94,6 +94,17 @@ def test_validate_rejects(kw, code):
     assert v(**kw) == code
 
 
+def test_bf16_head_rows_under_4gib():
+    """The bf16 kernels address a head's K/V rows with 32-bit byte offsets:
+    Skv * max(d, d_v) * 2 must stay below 2^32."""
+    assert v(Sq=2, Skv=(1 << 24) - 1, d=128) == attn.OK
+    assert v(Sq=2, Skv=1 << 24, d=128) == attn.E_UNSUPPORTED
+    assert v(Sq=1, Skv=1 << 24, d=128) == attn.E_UNSUPPORTED
+    assert v(Sq=2, Skv=1 << 24, d=64) == attn.OK
+    assert vm(mask=None, dtype=BF16, Sq=2, Skv=1 << 24, d=64, dv=128) == attn.E_UNSUPPORTED
+    assert v(dtype=F32, Sq=2, Skv=1 << 24, d=128) == attn.OK
+
+
 def test_check_order_null_before_shape():
     assert v(q=0, B=0) == attn.E_NULL
     assert v(B=0, scale=float("nan")) == attn.E_SHAPE

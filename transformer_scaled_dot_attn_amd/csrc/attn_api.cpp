@@ -214,6 +214,9 @@ int validate_all(const void* q, const void* k, const void* v, void* out, int B, 
     if (!std::isfinite(scale)) return ATTN_E_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_E_ALIGN;
     if (choose_path(Sq, d, dtype, dv) == kPathNone) return ATTN_E_UNSUPPORTED;
+    // the bf16 kernels address a head's K and V rows with 32-bit byte offsets
+    if (dtype == ATTN_BF16 && (long double)Skv * (d > dv ? d : dv) * 2 > (long double)UINT32_MAX)
+        return ATTN_E_UNSUPPORTED;
     st = check_mask(mask, msb, msh, msi, B, H, Sq, Skv);
     if (st != ATTN_OK) return st;
     return check_bias(bias, bsb, bsh, bsi, B, H, Sq, Skv, dtype == ATTN_F32 ? 4 : 2);

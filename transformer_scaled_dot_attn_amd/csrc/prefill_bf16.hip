@@ -421,28 +421,31 @@ __global__ __launch_bounds__(2 * BM, 1) void prefill_bf16_kernel(
     // of the same head (valid, L >= 1 here), so padded rows are never read;
     // the keys it stands for are masked (-inf logits), so its copy adds an
     // exact zero to the mixture (2 % faster than zero-filling it).  K runs two
-    // tiles ahead of the scores, V one tile.
+    // tiles ahead of the scores, V one tile.  Addresses are the head's base
+    // (wave-uniform) plus a 32-bit byte offset per lane: a head's rows span
+    // less than 4 GiB (the front end refuses larger heads), so a load costs
+    // a min and a multiply-add.
     const int st_row = tid / S::kChunks;
     const int st_col = (tid % S::kChunks) * 8;
-    const size_t head_off = (size_t)bk * Skv * D + st_col;
     const int st_row_v = tid / SV::kChunks;
     const int st_col_v = (tid % SV::kChunks) * 8;
-    const size_t head_off_v = (size_t)bk * Skv * DV + st_col_v;
+    const char* khead = reinterpret_cast<const char*>(k + (size_t)bk * Skv * D);
+    const char* vhead = reinterpret_cast<const char*>(v + (size_t)bk * Skv * DV);
     u32x4 kreg[S::kPerThread], vreg[SV::kPerThread];
     auto fetch_k = [&](int tile) {
         const int kbase = tile * kBN;
 #pragma unroll
         for (int i = 0; i < S::kPerThread; ++i) {
-            const int row = kbase + st_row + i * S::kRowsPerPass;
-            kreg[i] = ldg16(k + head_off + (size_t)min(row, L - 1) * D);
+            const int row = min(kbase + st_row + i * S::kRowsPerPass, L - 1);
+            kreg[i] = ldg16(khead + ((uint32_t)row * (2u * D) + (uint32_t)st_col * 2u));
         }
     };
     auto fetch_v = [&](int tile) {
         const int kbase = tile * kBN;
 #pragma unroll
         for (int i = 0; i < SV::kPerThread; ++i) {
-            const int row = kbase + st_row_v + i * SV::kRowsPerPass;
-            vreg[i] = ldg16(v + head_off_v + (size_t)min(row, L - 1) * DV);
+            const int row = min(kbase + st_row_v + i * SV::kRowsPerPass, L - 1);
+            vreg[i] = ldg16(vhead + ((uint32_t)row * (2u * DV) + (uint32_t)st_col_v * 2u));
         }
     };
     auto stash_k = [&](int tile) {
@@ -475,6 +478,7 @@ __global__ __launch_bounds__(2 * BM, 1) void prefill_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
     float m_run = -INFINITY;  // reference maximum of raw logits (this lane's query)
+    float ref_run = 0.0f;     // m_run * scale_log2, 0 while m_run = -inf (set where m_run moves)
     float l_run = 0.0f;       // this lane's share of the normaliser
     f32x16 s0[2], s1[2];      // S^T of two consecutive tiles (two 32-key blocks each)
     u32x4 pf[2][2];           // P^T fragments of the tile being mixed
@@ -524,7 +528,7 @@ __global__ __launch_bounds__(2 * BM, 1) void prefill_bf16_kernel(
             asm volatile("" : "+v"(l_run));
         }
     };
-    auto ref_log2 = [&]() { return m_run == -INFINITY ? 0.0f : m_run * scale_log2; };
+    auto ref_log2 = [&]() { return ref_run; };
 
     // S^T(tile) into sn; when sc is given, weight stages 0 .. kNA-1 of the
     // tile before it are issued under these MFMAs.
@@ -684,6 +688,7 @@ __global__ __launch_bounds__(2 * BM, 1) void prefill_bf16_kernel(
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
             const float alpha = grow ? fast_exp2((m_run - m_new) * scale_log2) : 1.0f;
             m_run = grow ? m_new : m_run;
+            ref_run = m_run == -INFINITY ? 0.0f : m_run * scale_log2;
             l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < SV::kDBlocks; ++db)
