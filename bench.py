@@ -302,30 +302,71 @@ def mask_runs(attn, W, runs, steps, warmup):
     return rows
 
 
+def strip_comments(text: str) -> str:
+    """C/C++ source without its comments and empty lines, each line's runs of
+    blanks outside literals cut to one space and its ends trimmed (string and
+    character literals are kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            while i < n and text[i] != "\n":
+                i += 1
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in " \t":
+            if not out or out[-1] != " ":
+                out.append(" ")
+            i += 1
+        else:
+            out.append(c)
+            i += 1
+    lines = (l.strip() for l in "".join(out).split("\n"))
+    return "\n".join(l for l in lines if l)
+
+
+def kernel_code_sha256(files) -> str:
+    """SHA-256 over the named csrc files with comments removed: a profile's
+    counters stay attached to the code they measured through comment edits,
+    and detach on any change to the code itself."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        src = os.path.join(ROOT, "transformer_scaled_dot_attn_amd", "csrc", f)
+        h.update(strip_comments(open(src, encoding="utf-8").read()).encode())
+        h.update(b"\0")
+    return h.hexdigest()
+
+
 def profiled_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 summary of this kernel
     and workload (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known
-    size), or None when there is none or the kernel's sources have changed
-    since the counters were taken."""
-    import hashlib
+    size), or None when there is none or the kernel's code has changed since
+    the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.md")
     if not os.path.exists(path):
         return None
     fields = {}
     for line in open(path):
         if ":" in line and line.split(":", 1)[0] in (
-                "traffic_bytes_per_launch", "kernel_sources", "kernel_source_sha256"):
+                "traffic_bytes_per_launch", "kernel_sources", "kernel_code_sha256"):
             key, val = line.split(":", 1)
             fields[key] = val.strip()
     if len(fields) != 3:
         return None
-    h = hashlib.sha256()
-    for f in fields["kernel_sources"].split():
-        src = os.path.join(ROOT, "transformer_scaled_dot_attn_amd", "csrc", f)
-        if not os.path.exists(src):
-            return None
-        h.update(open(src, "rb").read())
-    if h.hexdigest() != fields["kernel_source_sha256"]:
+    files = fields["kernel_sources"].split()
+    csrc = os.path.join(ROOT, "transformer_scaled_dot_attn_amd", "csrc")
+    if not all(os.path.exists(os.path.join(csrc, f)) for f in files):
+        return None
+    if kernel_code_sha256(files) != fields["kernel_code_sha256"]:
         return None
     return float(fields["traffic_bytes_per_launch"])
 

@@ -147,3 +147,29 @@ def test_cpu_baseline_rows(monkeypatch):
     assert res["unit"] == "TFLOP/s" and res["nproc"] >= 1 and res["cores"] == 4
     assert res["value"] == rows["prefill4096_bf16"]["GFLOP/s"] / 1e3
 
+
+
+def test_code_digest_ignores_comments_only():
+    """The digest that ties a profile's counters to the kernel code: comment
+    and blank-line edits keep it, any change to the code changes it, and
+    comment markers inside literals are code."""
+    a = 'int f(int x) {  // twice\n    /* no */ return 2 * x;\n}\nconst char* s = "a // b";\n'
+    b = '// header\nint f(int x) {\n\n    return 2 * x;   \n}\nconst char* s = "a // b";\n'
+    c = 'int f(int x) {\n    return 3 * x;\n}\nconst char* s = "a // b";\n'
+    d = 'int f(int x) {\n    return 2 * x;\n}\nconst char* s = "a ";\n'
+    assert bench.strip_comments(a) == bench.strip_comments(b)
+    assert bench.strip_comments(a) != bench.strip_comments(c)
+    assert bench.strip_comments(a) != bench.strip_comments(d)
+    assert bench.strip_comments("x = '\"'; // q\ny = 1;") == "x = '\"';\ny = 1;"
+
+
+def test_committed_profiles_match_the_kernel_code():
+    """Every committed summary carries the digest of the code it measured;
+    bench reports its traffic only while that digest matches."""
+    import os
+    prof = os.path.join(bench.ROOT, "profiles")
+    names = [f for f in os.listdir(prof) if f.endswith(".md") and "__" in f]
+    assert names
+    for f in names:
+        kernel, workload = f[:-3].split("__")
+        assert bench.profiled_traffic(kernel, workload) is not None, f

@@ -8,7 +8,9 @@
 //
 // Block = 8 wavefronts = 256 query rows of one (b, h); wave w owns rows
 // 32w..32w+31, and two waves share each SIMD.  The block walks the keys in
-// tiles of 64, staging K and V tiles in two-slot LDS rings.
+// tiles of 64, staging K and V tiles in two-slot LDS rings.  Grids of at
+// most 128 such blocks run blocks of 4 wavefronts = 128 rows instead, so
+// twice as many CUs share the walk; a row's arithmetic is the same.
 //
 // Transposed products.  Each wave computes S^T = K Q^T (K from LDS as the A
 // operand, Q^T held in registers as the B operand).  In the accumulator of
@@ -23,9 +25,9 @@
 // one query per lane, so the online-softmax rescale is a per-lane scalar
 // multiply.
 //
-// Staging.  All 512 threads load the next K and V tiles with branch-free
-// 16-byte loads issued between compute blocks and write them to LDS at the
-// end of the iteration, one barrier per tile.
+// Staging.  All threads of the block load the next K and V tiles with
+// branch-free 16-byte loads issued between compute blocks and write them to
+// LDS at the end of the iteration, one barrier per tile.
 //
 // Software pipeline.  Within a wave the work of a tile is a chain: Q K^T on
 // the matrix cores, then the softmax on the vector ALU, then P V on the
