@@ -47,7 +47,7 @@ size_t decode_mask_workspace_bytes(int B, int H, int Hkv, int Skv, int d, int dv
 // Prefill plan: key-range splits per query tile (1 = none, no workspace).
 struct PrefillPlan {
     int nsplit;  // key-range splits per query tile (1: none)
-    int bm;      // query rows per block: 256, or 128 on small unsplit grids
+    int bm;      // query rows per block: 256, or 128 / 64 on small unsplit grids
 };
 PrefillPlan prefill_plan(int B, int H, int Sq, int Skv);
 size_t prefill_workspace_bytes(int B, int H, int Sq, int Skv, int dv);  // dv: partial width

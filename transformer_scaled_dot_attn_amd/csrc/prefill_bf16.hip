@@ -9,8 +9,9 @@
 // Block = 8 wavefronts = 256 query rows of one (b, h); wave w owns rows
 // 32w..32w+31, and two waves share each SIMD.  The block walks the keys in
 // tiles of 64, staging K and V tiles in two-slot LDS rings.  Grids of at
-// most 128 such blocks run blocks of 4 wavefronts = 128 rows instead, so
-// twice as many CUs share the walk; a row's arithmetic is the same.
+// most 128 such blocks run blocks of 4 wavefronts = 128 rows instead, and
+// grids of at most 64 blocks of 2 wavefronts = 64 rows, so more CUs share
+// the walk; a row's arithmetic is the same at every block height.
 //
 // Transposed products.  Each wave computes S^T = K Q^T (K from LDS as the A
 // operand, Q^T held in registers as the B operand).  In the accumulator of
@@ -108,7 +109,7 @@ namespace tsda {
 
 namespace {
 
-constexpr int kBM = 256;   // query rows per block (128 on small grids: BM below)
+constexpr int kBM = 256;   // query rows per block (128 or 64 on small grids: BM below)
 constexpr int kBN = 64;    // keys per tile
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 constexpr int kMaxListTiles = 2048;   // key tiles a block's tile list may hold (Skv <= 131072)
@@ -148,8 +149,8 @@ __device__ __forceinline__ void pin_schedule() { __builtin_amdgcn_sched_barrier(
 // Zero bias for GEN calls without one (read as its first 4-element group).
 __device__ __attribute__((aligned(16))) uint16_t g_zero_bias[8];
 
-// BM: query rows per block (256, or 128 on grids that leave CUs idle); a
-// wave owns 32 of them.
+// BM: query rows per block (256, or 128 or 64 on grids that leave CUs
+// idle); a wave owns 32 of them.
 template <int D, int DV, bool MASK, bool GEN, int BM>
 __global__ __launch_bounds__(2 * BM, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -1023,13 +1024,16 @@ PrefillPlan prefill_plan(int B, int H, int Sq, int Skv) {
     // of 128 query rows instead: twice the blocks, each with four waves, so
     // the heaviest block's walk over the keys takes less time per step.
     // Measured (B=1, H=32, d=128, causal): S = 512 23.1 -> 20.5 us, S = 1024
-    // 36.8 -> 33.6 us; B=4, H=12, S=512, d=64: 17.0 -> 16.1 us.  Large grids
-    // lose with them (prefill4096 150 -> 234 us: one wave per SIMD).
+    // 36.8 -> 33.6 us; B=4, H=12, S=512, d=64: 17.0 -> 16.1 us.  Grids of at
+    // most 64 such blocks use blocks of 64 rows (two waves), still one block
+    // per CU at most: S = 128, 256, 512 at H = 32 11.3 -> 10.2, 14.1 -> 13.0,
+    // 20.0 -> 19.1 us against 128-row blocks.  Large grids lose with smaller
+    // blocks (prefill4096 150 -> 234 us with 128 rows: one wave per SIMD).
     const long blocks = (long)((Sq + kBM - 1) / kBM) * B * H;
     const long tiles = (Skv + kBN - 1) / kBN;
     long nsplit = 256 / blocks;
     nsplit = std::max(1L, std::min({nsplit, tiles / 16, (long)kMaxSplit}));
-    const int bm = nsplit == 1 && blocks <= 128 ? 128 : kBM;
+    const int bm = nsplit > 1 ? kBM : 4 * blocks <= 256 ? 64 : blocks <= 128 ? 128 : kBM;
     return PrefillPlan{(int)nsplit, bm};
 }
 
@@ -1043,10 +1047,10 @@ size_t prefill_workspace_bytes(int B, int H, int Sq, int Skv, int d) {
 size_t prefill_mask_workspace_bytes(int B, int Sq, int Skv) {
     // tile marks of a mask shared by all heads, one byte per (mask batch,
     // query tile, key tile), after the split partials; none past the list
-    // size.  Sized for query tiles of 128 rows, the smaller block height.
+    // size.  Sized for query tiles of 64 rows, the smallest block height.
     const size_t nkt = (Skv + kBN - 1) / kBN;
     if (nkt > (size_t)kMaxListTiles) return 0;
-    return round_up256((size_t)B * ((Sq + 127) / 128) * nkt);
+    return round_up256((size_t)B * ((Sq + 63) / 64) * nkt);
 }
 
 hipError_t launch_prefill_bf16(const LaunchArgs& a) {
@@ -1083,7 +1087,10 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
         const int Bm = a.msb != 0 ? a.B : 1;
         if (t) t->begin(kPrefillMaskTiles, a.stream);
         const dim3 mgrid((unsigned)((long)Bm * nqt * nkt));
-        if (p.bm == 128)
+        if (p.bm == 64)
+            hipLaunchKernelGGL(prefill_mask_tiles_kernel<64>, mgrid, dim3(64), 0, a.stream,
+                               a.mask, a.msb, a.msi, a.Sq, a.Skv, nqt, nkt, a.causal, tmap);
+        else if (p.bm == 128)
             hipLaunchKernelGGL(prefill_mask_tiles_kernel<128>, mgrid, dim3(128), 0, a.stream,
                                a.mask, a.msb, a.msi, a.Sq, a.Skv, nqt, nkt, a.causal, tmap);
         else
@@ -1114,7 +1121,9 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
               : go(prefill_bf16_kernel<D, DV, false, false, BM>);
     };
     auto pick = [&](auto dk, auto dvk) {
-        if (p.bm == 128)
+        if (p.bm == 64)
+            pick_bm(dk, dvk, std::integral_constant<int, 64>{});
+        else if (p.bm == 128)
             pick_bm(dk, dvk, std::integral_constant<int, 128>{});
         else
             pick_bm(dk, dvk, std::integral_constant<int, kBM>{});
