@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 6
+#define ATTN_ABI_VERSION 7
 
 typedef enum {
     ATTN_OK = 0,
@@ -309,6 +309,19 @@ int attn_abi_version(void);
  */
 int attn_last_hip_error(void);
 const char* attn_last_hip_error_name(void);
+
+/*
+ * attn_prefill_plan -- how a bf16 prefill of these sizes is launched, for
+ * tests and tuning: *key_splits key-range splits per query tile (1 = none),
+ * *rows_per_block query rows per block (256, or 128 / 64 on small grids) and
+ * *key_groups wave sets per block that split its keys (1 or 2).  masked: an
+ * allowed-mask is given; general: a bias, or a scale that is not positive.
+ * Output pointers may be NULL.  Returns ATTN_E_SHAPE for invalid sizes and
+ * ATTN_E_UNSUPPORTED when the sizes do not take the prefill kernel (Sq == 1,
+ * d or d_v outside {64, 128}).  Makes no HIP call.
+ */
+int attn_prefill_plan(int B, int H, int H_kv, int Sq, int Skv, int d, int d_v, int masked,
+                      int general, int* key_splits, int* rows_per_block, int* key_groups);
 
 /*
  * attn_release -- frees the library-owned workspace of every device.  The

@@ -13,6 +13,15 @@ BF16_TOL = 2e-2   # max-abs error, bf16 inputs with fp32 accumulation
 F32_TOL = 1e-5    # max-abs error, fp32 inputs
 
 
+def key_groups(B, H, Sq, Skv, d, dv=None, dtype="bf16", masked=False, general=False):
+    """Wave sets that split each prefill block's keys (1 or 2; 1 for every
+    other kernel).  Two calls give the same bits only when they agree on it:
+    two key groups sum each row's keys in another order."""
+    if dtype != "bf16" or Sq == 1:
+        return 1
+    return attn.prefill_plan(B, H, Sq, Skv, d, dv, masked=masked, general=general)[2]
+
+
 def gpu_run(q, k, v, scale, causal, kv_lens=None, device="cuda", **kw):
     """Upload numpy inputs (float32, or uint16 bf16 bits), run attn.fwd,
     return (out as float64 numpy, out tensor)."""

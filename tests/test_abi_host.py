@@ -42,6 +42,28 @@ def test_abi_version_and_status_strings():
     assert attn.status_string(99) == "unknown status"
 
 
+def test_prefill_plan():
+    """Launch plans of the measured workloads (no GPU call)."""
+    assert attn.prefill_plan(1, 32, 4096, 4096, 128) == (1, 256, 1)   # prefill4096
+    assert attn.prefill_plan(8, 32, 2048, 2048, 128) == (1, 256, 1)   # padded2048
+    assert attn.prefill_plan(4, 12, 512, 512, 64) == (1, 128, 2)      # mha768
+    assert attn.prefill_plan(4, 12, 512, 512, 64, masked=True) == (1, 128, 1)
+    assert attn.prefill_plan(4, 12, 512, 512, 64, general=True) == (1, 128, 1)
+    assert attn.prefill_plan(1, 32, 1024, 1024, 128) == (1, 128, 1)   # would spill at 128 rows
+    assert attn.prefill_plan(1, 32, 512, 512, 128) == (1, 64, 2)
+    assert attn.prefill_plan(1, 32, 256, 256, 128) == (1, 64, 1)      # 4 key tiles: one group
+    assert attn.prefill_plan(1, 32, 512, 4096, 128) == (4, 256, 1)    # chunk: key-range splits
+    with pytest.raises(attn.AttnError) as e:
+        attn.prefill_plan(1, 32, 1, 4096, 128)                          # decode
+    assert e.value.status == attn.E_UNSUPPORTED
+    with pytest.raises(attn.AttnError) as e:
+        attn.prefill_plan(1, 32, 64, 64, 96)
+    assert e.value.status == attn.E_UNSUPPORTED
+    with pytest.raises(attn.AttnError) as e:
+        attn.prefill_plan(1, 32, 65, 64, 128)                           # Sq > Skv
+    assert e.value.status == attn.E_SHAPE
+
+
 def test_no_hip_error_recorded_before_a_launch_failure():
     assert attn.last_hip_error() == (0, "hipSuccess")
 

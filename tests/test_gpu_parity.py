@@ -110,8 +110,8 @@ def test_block_height_does_not_change_rows(mask_kind, B):
     batch item makes 64 or 68 blocks of 256 rows (run as 64- and 128-row
     blocks), two make 128 or 136 (run as 128- and 256-row blocks).  Both
     match the oracle, and the first 16 heads of the larger problem are
-    bit-identical to the smaller one: a row's result does not depend on the
-    block height."""
+    bit-identical to the smaller one when both split their blocks' keys the
+    same way: a row's result does not depend on the block height."""
     import torch
     S, d, lens = 1000, 128, [1000, 777][:B]
     prob = W.random_problem(91, B, 17, S, S, d, "bf16", lens)
@@ -129,7 +129,40 @@ def test_block_height_does_not_change_rows(mask_kind, B):
         ref = oracle.attention(q, k, v, prob["scale"], 1, lens, mask=mask)
         assert_matches(got, ref, BF16_TOL, lens, S, f"H{H} mask {mask_kind}")
         runs[H] = out
-    assert torch.equal(runs[17][:, :16], runs[16]), "block height changed the rows"
+    plans = {H: attn.prefill_plan(B, H, S, S, d, masked=mask is not None) for H in (16, 17)}
+    _say("plans (splits, rows per block, key groups):", plans)
+    assert plans[16][1] < plans[17][1], plans  # the two runs straddle a block-height switch
+    if plans[16][2] == plans[17][2]:
+        assert torch.equal(runs[17][:, :16], runs[16]), "block height changed the rows"
+
+
+# Small unmasked grids whose blocks split their keys between two wave sets
+KEY_GROUP_CASES = [
+    # seed, B, H, Sq, Skv, d, dv, causal, kv_lens
+    (51, 1, 4, 1000, 1000, 64, 64, 1, None),
+    (52, 1, 4, 777, 777, 128, 128, 1, [700]),
+    (53, 2, 2, 513, 513, 64, 128, 0, [513, 200]),
+    (54, 1, 2, 300, 1100, 128, 64, 1, None),     # fewer queries than keys
+    (55, 1, 1, 576, 576, 64, 64, 1, None),       # an odd number of key tiles
+    (56, 1, 1, 2, 600, 64, 64, 1, None),         # two queries, ten key tiles
+    (57, 3, 2, 640, 640, 128, 128, 1, [640, 0, 65]),
+    (58, 4, 12, 512, 512, 64, 64, 1, None),      # the mha768 shape
+]
+
+
+@pytest.mark.parametrize("case", KEY_GROUP_CASES, ids=lambda c: f"s{c[0]}")
+def test_key_group_prefill(case):
+    """The plan splits these blocks' keys between two wave sets (tiles of each
+    parity, two online softmaxes merged at the end); every element matches the
+    oracle and padded rows are zero."""
+    seed, B, H, Sq, Skv, d, dv, causal, lens = case
+    plan = attn.prefill_plan(B, H, Sq, Skv, d, dv)
+    _say("key-group case", case, "plan", plan)
+    assert plan[0] == 1 and plan[2] == 2, plan
+    prob = W.random_problem(seed, B, H, Sq, Skv, d, "bf16", lens, dv=dv)
+    got, _ = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], causal, lens)
+    ref = oracle.attention(prob["q"], prob["k"], prob["v"], prob["scale"], causal, lens)
+    assert_matches(got, ref, BF16_TOL, lens, Skv, f"key groups {case}")
 
 
 # ---------------------------------------------------------- bf16 decode path

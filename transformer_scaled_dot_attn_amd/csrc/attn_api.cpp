@@ -449,6 +449,18 @@ int attn_abi_version(void) { return ATTN_ABI_VERSION; }
 
 int attn_last_hip_error(void) { return static_cast<int>(g_last_hip); }
 
+int attn_prefill_plan(int B, int H, int H_kv, int Sq, int Skv, int d, int d_v, int masked,
+                      int general, int* key_splits, int* rows_per_block, int* key_groups) {
+    const int st = check_shape(B, H, H_kv, Sq, Skv, d, d_v);
+    if (st != ATTN_OK) return st;
+    if (choose_path(Sq, d, ATTN_BF16, d_v) != kPathPrefill) return ATTN_E_UNSUPPORTED;
+    const PrefillPlan p = prefill_plan(B, H, Sq, Skv, d, d_v, masked != 0, general != 0);
+    if (key_splits) *key_splits = p.nsplit;
+    if (rows_per_block) *rows_per_block = p.bm;
+    if (key_groups) *key_groups = p.kg;
+    return ATTN_OK;
+}
+
 const char* attn_last_hip_error_name(void) { return hipGetErrorName(g_last_hip); }
 
 void attn_release(void) {

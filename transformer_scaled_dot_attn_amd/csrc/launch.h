@@ -48,8 +48,11 @@ size_t decode_mask_workspace_bytes(int B, int H, int Hkv, int Skv, int d, int dv
 struct PrefillPlan {
     int nsplit;  // key-range splits per query tile (1: none)
     int bm;      // query rows per block: 256, or 128 / 64 on small unsplit grids
+    int kg;      // key groups per block: 2 splits each block's keys between two wave sets
 };
-PrefillPlan prefill_plan(int B, int H, int Sq, int Skv);
+// masked: an allowed-mask is given; general: a bias, or a scale that is not positive
+PrefillPlan prefill_plan(int B, int H, int Sq, int Skv, int d = 128, int dv = 128,
+                         bool masked = false, bool general = false);
 size_t prefill_workspace_bytes(int B, int H, int Sq, int Skv, int dv);  // dv: partial width
 // extra bytes a masked prefill needs for its key-tile marks (after the above)
 size_t prefill_mask_workspace_bytes(int B, int Sq, int Skv);

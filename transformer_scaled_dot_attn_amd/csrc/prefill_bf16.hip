@@ -151,8 +151,8 @@ __device__ __attribute__((aligned(16))) uint16_t g_zero_bias[8];
 
 // BM: query rows per block (256, or 128 or 64 on grids that leave CUs
 // idle); a wave owns 32 of them.
-template <int D, int DV, bool MASK, bool GEN, int BM>
-__global__ __launch_bounds__(2 * BM, 1) void prefill_bf16_kernel(
+template <int D, int DV, bool MASK, bool GEN, int BM, int KG>
+__global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
     const int32_t* __restrict__ kv_lens, int BH, int H, int Hkv, int Sq, int Skv, float scale_log2,
@@ -161,7 +161,9 @@ __global__ __launch_bounds__(2 * BM, 1) void prefill_bf16_kernel(
     const uint8_t* __restrict__ tmap, int nkt, const uint16_t* __restrict__ bias, long long bsb,
     long long bsh, long long bsi, float scale) {
     constexpr int kBMb = BM;            // query rows of this block
-    constexpr int kThreads = 2 * BM;    // 64 lanes x BM / 32 waves
+    constexpr int kRowWaves = BM / 32;  // waves per key group, 32 rows each
+    constexpr int kThreads = 64 * kRowWaves * KG;
+    static_assert(KG == 1 || (KG == 2 && !MASK && !GEN), "key groups: unmasked plain logits");
     using S = Shape<D, kThreads>;    // the key side: Q K^T over D features
     using SV = Shape<DV, kThreads>;  // the value side: V rows and outputs of DV features
     __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][S::kTileK];
@@ -171,10 +173,14 @@ __global__ __launch_bounds__(2 * BM, 1) void prefill_bf16_kernel(
     __shared__ int lds_tn;                            // their number
     __shared__ int lds_tcut;                          // some listed tile is cut by the mask
     __shared__ u32x4 lds_b[GEN ? 4 * kThreads : 1];   // parked bias, 64 bytes per lane
+    // key group 1's (acc, m, l) per lane for the merge (KG = 2)
+    __shared__ float lds_x[KG == 2 ? kRowWaves * (SV::kDBlocks * 16 + 2) * 64 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int rg = wave % kRowWaves;  // row group: rows 32 rg .. 32 rg + 31 of the block
+    const int kg = wave / kRowWaves;  // key group (KG = 2: tiles of parity kg)
     const int half = lane >> 5;
 
     const int bid = blockIdx.x;
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(2 * BM, 1) void prefill_bf16_kernel(
     const int per_split = (ntiles_q + nsplit - 1) / nsplit;
     const int t0 = min(ntiles_q, split * per_split);
     const int t1 = min(ntiles_q, t0 + per_split);
-    const int qw = q0 + wave * 32;
+    const int qw = q0 + rg * 32;
     const bool wave_live = qw < n && qw + 32 > 0;
     const int p_lo = off + qw;
     const int p_hi = off + min(qw + 32, n) - 1;
@@ -435,34 +441,38 @@ __global__ __launch_bounds__(2 * BM, 1) void prefill_bf16_kernel(
     const char* khead = reinterpret_cast<const char*>(k + (size_t)bk * Skv * D);
     const char* vhead = reinterpret_cast<const char*>(v + (size_t)bk * Skv * DV);
     u32x4 kreg[S::kPerThread], vreg[SV::kPerThread];
-    auto fetch_k = [&](int tile) {
+    auto fetch_k_to = [&](int tile, u32x4 (&dst)[S::kPerThread]) {
         const int kbase = tile * kBN;
 #pragma unroll
         for (int i = 0; i < S::kPerThread; ++i) {
             const int row = min(kbase + st_row + i * S::kRowsPerPass, L - 1);
-            kreg[i] = ldg16(khead + ((uint32_t)row * (2u * D) + (uint32_t)st_col * 2u));
+            dst[i] = ldg16(khead + ((uint32_t)row * (2u * D) + (uint32_t)st_col * 2u));
         }
     };
-    auto fetch_v = [&](int tile) {
+    auto fetch_v_to = [&](int tile, u32x4 (&dst)[SV::kPerThread]) {
         const int kbase = tile * kBN;
 #pragma unroll
         for (int i = 0; i < SV::kPerThread; ++i) {
             const int row = min(kbase + st_row_v + i * SV::kRowsPerPass, L - 1);
-            vreg[i] = ldg16(vhead + ((uint32_t)row * (2u * DV) + (uint32_t)st_col_v * 2u));
+            dst[i] = ldg16(vhead + ((uint32_t)row * (2u * DV) + (uint32_t)st_col_v * 2u));
         }
     };
-    auto stash_k = [&](int tile) {
+    auto stash_k_from = [&](int tile, const u32x4 (&src)[S::kPerThread]) {
         uint16_t* dk = lds_k[tile & 1] + st_row * S::kStrideK + st_col;
 #pragma unroll
         for (int i = 0; i < S::kPerThread; ++i)
-            *reinterpret_cast<u32x4*>(dk + i * S::kRowsPerPass * S::kStrideK) = kreg[i];
+            *reinterpret_cast<u32x4*>(dk + i * S::kRowsPerPass * S::kStrideK) = src[i];
     };
-    auto stash_v = [&](int tile) {
+    auto stash_v_from = [&](int tile, const u32x4 (&src)[SV::kPerThread]) {
         uint16_t* dv = lds_v[tile & 1] + st_row_v * SV::kStrideV + st_col_v;
 #pragma unroll
         for (int i = 0; i < SV::kPerThread; ++i)
-            *reinterpret_cast<u32x4*>(dv + i * SV::kRowsPerPass * SV::kStrideV) = vreg[i];
+            *reinterpret_cast<u32x4*>(dv + i * SV::kRowsPerPass * SV::kStrideV) = src[i];
     };
+    auto fetch_k = [&](int tile) { fetch_k_to(tile, kreg); };
+    auto fetch_v = [&](int tile) { fetch_v_to(tile, vreg); };
+    auto stash_k = [&](int tile) { stash_k_from(tile, kreg); };
+    auto stash_v = [&](int tile) { stash_v_from(tile, vreg); };
 
     // Per-lane LDS read bases (element offsets within a slot).
     //  K operand of S^T: row 32*kb + lane%32, features 16*ks + 8*(lane/32).
@@ -798,6 +808,68 @@ __global__ __launch_bounds__(2 * BM, 1) void prefill_bf16_kernel(
             if (t + 1 < tb) step(t + 1, s1, s0);
         }
     };
+    // The key-group walk (KG = 2, unmasked small grids): waves rg and
+    // rg + BM/32 own the same 32 rows, and key group kg computes the tiles
+    // ta + kg, ta + kg + 2, ... of them, each with its own online softmax,
+    // merged at the end.  The staging moves tiles in pairs (ta + 2s,
+    // ta + 2s + 1) into the two LDS slots, so group kg always reads slot kg
+    // (ta is 0: these grids are unsplit).  Step s: group kg scores its next
+    // tile u + 2 (K of pair s + 1) under the weights of its tile
+    // u = ta + 2s + kg and mixes u (V of pair s); after a barrier the block
+    // stores K of pair s + 2 and V of pair s + 1, then a second barrier.  Both
+    // groups run the same ceil((tb - ta) / 2) steps.
+    u32x4 kp0[S::kPerThread], kp1[S::kPerThread], vp0[SV::kPerThread], vp1[SV::kPerThread];
+    auto step_kg = [&](int st, f32x16 (&sc)[2], f32x16 (&sn)[2], int ta) __attribute__((always_inline)) {
+        const int u = ta + 2 * st + kg;
+        const bool pipe = u + 2 < t1w;  // this wave scores its next tile
+        fetch_k_to(ta + 2 * st + 4, kp0);
+        fetch_k_to(ta + 2 * st + 5, kp1);
+        fetch_v_to(ta + 2 * st + 2, vp0);
+        fetch_v_to(ta + 2 * st + 3, vp1);
+        if (pipe) {
+            score(u + 2, sn, &sc);
+            mask(std::false_type{}, u + 2, sn);
+            const float mx = mix(u, &sn, &sc);
+            reference(mx);
+        } else if (u < t1w) {
+            weigh(sc);
+            mix(u, nullptr, nullptr);
+        }
+        __syncthreads();  // K of pair s + 1 and V of pair s are read
+        stash_k_from(ta + 2 * st + 4, kp0);
+        stash_k_from(ta + 2 * st + 5, kp1);
+        stash_v_from(ta + 2 * st + 2, vp0);
+        stash_v_from(ta + 2 * st + 3, vp1);
+        __syncthreads();
+    };
+    auto walk_kg = [&](int ta, int tb) __attribute__((always_inline)) {
+        const int u0 = ta + kg;
+        fetch_k_to(ta, kp0);
+        fetch_k_to(ta + 1, kp1);
+        fetch_v_to(ta, vp0);
+        fetch_v_to(ta + 1, vp1);
+        stash_k_from(ta, kp0);
+        stash_k_from(ta + 1, kp1);
+        fetch_k_to(ta + 2, kp0);
+        fetch_k_to(ta + 3, kp1);
+        __syncthreads();
+        if (u0 < t1w) {
+            score(u0, s0, nullptr);
+            mask(std::false_type{}, u0, s0);
+            reference(scan(s0));
+        }
+        __syncthreads();  // K of pair 0 is read by every wave before pair 1 replaces it
+        stash_k_from(ta + 2, kp0);
+        stash_k_from(ta + 3, kp1);
+        stash_v_from(ta, vp0);
+        stash_v_from(ta + 1, vp1);
+        __syncthreads();
+        const int nsteps = (tb - ta + 1) >> 1;
+        for (int st = 0; st < nsteps; st += 2) {
+            step_kg(st, s0, s1, ta);
+            if (st + 1 < nsteps) step_kg(st + 1, s1, s0, ta);
+        }
+    };
     // The masked walk over list positions pp0 <= t < pp1, with the same
     // prologue; the tile scored first is the first one the wave computes.
     auto walk_m = [&]() __attribute__((always_inline)) {
@@ -836,11 +908,34 @@ __global__ __launch_bounds__(2 * BM, 1) void prefill_bf16_kernel(
         } else {
             walk_m();
         }
+    } else if constexpr (KG == 2) {
+        walk_kg(t0, t1);
+        // merge the two key groups' softmax states of each row, in group 0
+        constexpr int kO = SV::kDBlocks * 16;
+        float* xs = lds_x + (size_t)rg * (kO + 2) * 64;
+        if (kg == 1) {
+#pragma unroll
+            for (int i = 0; i < kO; ++i) xs[i * 64 + lane] = oacc[i >> 4][i & 15];
+            xs[kO * 64 + lane] = m_run;
+            xs[(kO + 1) * 64 + lane] = l_run;
+        }
+        __syncthreads();
+        if (kg == 0) {
+            const float m1 = xs[kO * 64 + lane], l1 = xs[(kO + 1) * 64 + lane];
+            const float mn = fmaxf(m_run, m1);
+            const float a0 = m_run == -INFINITY ? 0.0f : fast_exp2((m_run - mn) * scale_log2);
+            const float a1 = m1 == -INFINITY ? 0.0f : fast_exp2((m1 - mn) * scale_log2);
+#pragma unroll
+            for (int i = 0; i < kO; ++i)
+                oacc[i >> 4][i & 15] = a0 * oacc[i >> 4][i & 15] + a1 * xs[i * 64 + lane];
+            l_run = a0 * l_run + a1 * l1;
+            m_run = mn;
+        }
     } else {
         walk(t0, t1);
     }
 
-    if (nsplit > 1) {
+    if (KG == 1 && nsplit > 1) {  // (key groups run unsplit grids only)
         // ---- split epilogue: this split's (m, l, acc) of every live row, the
         // reference in exp2 units (-inf with l = 0 when the split saw none of
         // the row's keys); the combine kernel merges the splits.
@@ -867,7 +962,7 @@ __global__ __launch_bounds__(2 * BM, 1) void prefill_bf16_kernel(
 
     // ---- epilogue: out = acc / l; with a mask this tile's rows past n_b are
     // zero too (without one the pad rows were zeroed above)
-    if (MASK ? qi < Sq : q_live) {
+    if ((MASK ? qi < Sq : q_live) && kg == 0) {
         const float l_tot = halves_sum(l_run);
         const float inv = (q_live && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
         uint16_t* orow = obase + (size_t)qi * DV;
@@ -1011,7 +1106,7 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(
 
 }  // namespace
 
-PrefillPlan prefill_plan(int B, int H, int Sq, int Skv) {
+PrefillPlan prefill_plan(int B, int H, int Sq, int Skv, int d, int dv, bool masked, bool general) {
     // Each query tile is one block.  When that leaves CUs idle (short query
     // chunks against a long cache), the key range of every query tile is
     // split over about one block per CU in all, each split at least 16 key
@@ -1034,7 +1129,17 @@ PrefillPlan prefill_plan(int B, int H, int Sq, int Skv) {
     long nsplit = 256 / blocks;
     nsplit = std::max(1L, std::min({nsplit, tiles / 16, (long)kMaxSplit}));
     const int bm = nsplit > 1 ? kBM : 4 * blocks <= 256 ? 64 : blocks <= 128 ? 128 : kBM;
-    return PrefillPlan{(int)nsplit, bm};
+    // Small unmasked grids with plain logits and at least 8 key tiles split
+    // each block's keys between two wave sets (the kernel's key-group walk),
+    // halving the longest walk: B=4, H=12, S=512, d=64 15.6 -> 13.7 us;
+    // B=1, H=8, S=1024, d=64 22.0 -> 17.0 us; B=1, H=32, S=512, d=128
+    // 19.0 -> 17.6 us.  Shorter walks lose (S = 128, 256: +10 %, +1.5 %), and
+    // 128-row blocks at d = d_v = 128 would spill registers.
+    const int kg = bm < kBM && !masked && !general && tiles >= 8 &&
+                           !(d == 128 && dv == 128 && bm == 128)
+                       ? 2
+                       : 1;
+    return PrefillPlan{(int)nsplit, bm, kg};
 }
 
 size_t prefill_workspace_bytes(int B, int H, int Sq, int Skv, int d) {
@@ -1054,7 +1159,8 @@ size_t prefill_mask_workspace_bytes(int B, int Sq, int Skv) {
 }
 
 hipError_t launch_prefill_bf16(const LaunchArgs& a) {
-    const PrefillPlan p = prefill_plan(a.B, a.H, a.Sq, a.Skv);
+    const PrefillPlan p = prefill_plan(a.B, a.H, a.Sq, a.Skv, a.d, a.dv, a.mask != nullptr,
+                                       a.bias != nullptr || !(a.scale > 0.0f));
     const int nqt = (a.Sq + p.bm - 1) / p.bm;
     const int BH = a.B * a.H;
     const dim3 grid((unsigned)((long)nqt * BH * p.nsplit));
@@ -1101,8 +1207,9 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
         if (e != hipSuccess) return e;
     }
     if (t) t->begin(kPrefillBf16, a.stream);
+    const int kg = p.kg;
     auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, dim3(2 * p.bm), 0, a.stream, q, k, v, o, a.kv_lens, BH, a.H,
+        hipLaunchKernelGGL(kern, grid, dim3(2 * p.bm * kg), 0, a.stream, q, k, v, o, a.kv_lens, BH, a.H,
                            a.Hkv, a.Sq, a.Skv, sl, a.causal, nqt, p.nsplit, ws_acc, ws_ml, a.mask,
                            a.msb, a.msh, a.msi, tmap, nkt, static_cast<const uint16_t*>(a.bias),
                            a.bsb, a.bsh, a.bsi, a.scale);
@@ -1114,11 +1221,15 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
         constexpr int D = decltype(dk)::value, DV = decltype(dvk)::value;
         constexpr int BM = decltype(bmk)::value;
         if (gen)
-            m ? go(prefill_bf16_kernel<D, DV, true, true, BM>)
-              : go(prefill_bf16_kernel<D, DV, false, true, BM>);
+            m ? go(prefill_bf16_kernel<D, DV, true, true, BM, 1>)
+              : go(prefill_bf16_kernel<D, DV, false, true, BM, 1>);
+        else if (m)
+            go(prefill_bf16_kernel<D, DV, true, false, BM, 1>);
+        else if constexpr (BM < kBM && !(D == 128 && DV == 128 && BM == 128))
+            kg == 2 ? go(prefill_bf16_kernel<D, DV, false, false, BM, 2>)
+                    : go(prefill_bf16_kernel<D, DV, false, false, BM, 1>);
         else
-            m ? go(prefill_bf16_kernel<D, DV, true, false, BM>)
-              : go(prefill_bf16_kernel<D, DV, false, false, BM>);
+            go(prefill_bf16_kernel<D, DV, false, false, BM, 1>);
     };
     auto pick = [&](auto dk, auto dvk) {
         if (p.bm == 64)
