@@ -49,7 +49,7 @@ def test_prefill_plan():
     assert attn.prefill_plan(4, 12, 512, 512, 64) == (1, 128, 2)      # mha768
     assert attn.prefill_plan(4, 12, 512, 512, 64, masked=True) == (1, 128, 1)
     assert attn.prefill_plan(4, 12, 512, 512, 64, general=True) == (1, 128, 1)
-    assert attn.prefill_plan(1, 32, 1024, 1024, 128) == (1, 128, 1)   # would spill at 128 rows
+    assert attn.prefill_plan(1, 32, 1024, 1024, 128) == (1, 128, 2)
     assert attn.prefill_plan(1, 32, 512, 512, 128) == (1, 64, 2)
     assert attn.prefill_plan(1, 32, 256, 256, 128) == (1, 64, 1)      # 4 key tiles: one group
     assert attn.prefill_plan(1, 32, 512, 4096, 128) == (4, 256, 1)    # chunk: key-range splits

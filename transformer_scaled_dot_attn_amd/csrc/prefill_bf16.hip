@@ -822,18 +822,27 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
     auto step_kg = [&](int st, f32x16 (&sc)[2], f32x16 (&sn)[2], int ta) __attribute__((always_inline)) {
         const int u = ta + 2 * st + kg;
         const bool pipe = u + 2 < t1w;  // this wave scores its next tile
-        fetch_k_to(ta + 2 * st + 4, kp0);
-        fetch_k_to(ta + 2 * st + 5, kp1);
-        fetch_v_to(ta + 2 * st + 2, vp0);
-        fetch_v_to(ta + 2 * st + 3, vp1);
+        // The next pairs' loads are issued after the scores, in each branch
+        // (their registers do not fit beside the score phase's at d = d_v =
+        // 128; placed once before the branch they spill).
         if (pipe) {
             score(u + 2, sn, &sc);
+            fetch_k_to(ta + 2 * st + 4, kp0);
+            fetch_k_to(ta + 2 * st + 5, kp1);
+            fetch_v_to(ta + 2 * st + 2, vp0);
+            fetch_v_to(ta + 2 * st + 3, vp1);
             mask(std::false_type{}, u + 2, sn);
             const float mx = mix(u, &sn, &sc);
             reference(mx);
-        } else if (u < t1w) {
-            weigh(sc);
-            mix(u, nullptr, nullptr);
+        } else {
+            fetch_k_to(ta + 2 * st + 4, kp0);
+            fetch_k_to(ta + 2 * st + 5, kp1);
+            fetch_v_to(ta + 2 * st + 2, vp0);
+            fetch_v_to(ta + 2 * st + 3, vp1);
+            if (u < t1w) {
+                weigh(sc);
+                mix(u, nullptr, nullptr);
+            }
         }
         __syncthreads();  // K of pair s + 1 and V of pair s are read
         stash_k_from(ta + 2 * st + 4, kp0);
@@ -1133,12 +1142,11 @@ PrefillPlan prefill_plan(int B, int H, int Sq, int Skv, int d, int dv, bool mask
     // each block's keys between two wave sets (the kernel's key-group walk),
     // halving the longest walk: B=4, H=12, S=512, d=64 15.6 -> 13.7 us;
     // B=1, H=8, S=1024, d=64 22.0 -> 17.0 us; B=1, H=32, S=512, d=128
-    // 19.0 -> 17.6 us.  Shorter walks lose (S = 128, 256: +10 %, +1.5 %), and
-    // 128-row blocks at d = d_v = 128 would spill registers.
-    const int kg = bm < kBM && !masked && !general && tiles >= 8 &&
-                           !(d == 128 && dv == 128 && bm == 128)
-                       ? 2
-                       : 1;
+    // 19.0 -> 17.6 us; B=1, H=32, S=1024, d=128 31.3 -> 27.6 us.  Shorter
+    // walks lose (S = 128, 256: +10 %, +1.5 %).
+    (void)d;
+    (void)dv;
+    const int kg = bm < kBM && !masked && !general && tiles >= 8 ? 2 : 1;
     return PrefillPlan{(int)nsplit, bm, kg};
 }
 
@@ -1225,7 +1233,7 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
               : go(prefill_bf16_kernel<D, DV, false, true, BM, 1>);
         else if (m)
             go(prefill_bf16_kernel<D, DV, true, false, BM, 1>);
-        else if constexpr (BM < kBM && !(D == 128 && DV == 128 && BM == 128))
+        else if constexpr (BM < kBM)
             kg == 2 ? go(prefill_bf16_kernel<D, DV, false, false, BM, 2>)
                     : go(prefill_bf16_kernel<D, DV, false, false, BM, 1>);
         else
