@@ -52,6 +52,9 @@ def test_prefill_plan():
     assert attn.prefill_plan(1, 32, 1024, 1024, 128) == (1, 128, 2)
     assert attn.prefill_plan(1, 32, 512, 512, 128) == (1, 64, 2)
     assert attn.prefill_plan(1, 32, 256, 256, 128) == (1, 64, 1)      # 4 key tiles: one group
+    assert attn.prefill_plan(1, 32, 2048, 2048, 128) == (1, 128, 2)   # 256 blocks of 256 rows
+    assert attn.prefill_plan(1, 32, 2048, 2048, 128, masked=True) == (1, 256, 1)
+    assert attn.prefill_plan(2, 32, 2048, 2048, 128) == (1, 256, 1)   # 512 blocks
     assert attn.prefill_plan(1, 32, 512, 4096, 128) == (4, 256, 1)    # chunk: key-range splits
     with pytest.raises(attn.AttnError) as e:
         attn.prefill_plan(1, 32, 1, 4096, 128)                          # decode

@@ -102,38 +102,48 @@ def test_bf16_prefill_shapes(case):
     check_problem(prob, causal, BF16_TOL, f"prefill {case}")
 
 
-@pytest.mark.parametrize("B", [1, 2])
+def _straddle(B, S, d, masked, rows):
+    """Smallest H for which H and H + 1 heads of this shape take blocks of
+    rows[0] and rows[1] query rows (unsplit)."""
+    for H in range(1, 200):
+        a = attn.prefill_plan(B, H, S, S, d, masked=masked)
+        c = attn.prefill_plan(B, H + 1, S, S, d, masked=masked)
+        if a[0] == c[0] == 1 and (a[1], c[1]) == rows:
+            return H
+    raise AssertionError(f"no head count switches {rows} at B={B} S={S}")
+
+
+@pytest.mark.parametrize("rows", [(64, 128), (128, 256)])
 @pytest.mark.parametrize("mask_kind", [None, "padding", "per_query"])
-def test_block_height_does_not_change_rows(mask_kind, B):
+def test_block_height_does_not_change_rows(mask_kind, rows):
     """Small unsplit grids run blocks of 64 or 128 query rows, larger ones
-    blocks of 256.  With 1000 rows (4 tiles of 256) and 16 or 17 heads, one
-    batch item makes 64 or 68 blocks of 256 rows (run as 64- and 128-row
-    blocks), two make 128 or 136 (run as 128- and 256-row blocks).  Both
-    match the oracle, and the first 16 heads of the larger problem are
+    blocks of 256.  For each switch, H heads of 1000 rows take the smaller
+    blocks and H + 1 heads the larger ones (H found from the launch plan).
+    Both match the oracle, and the first H heads of the larger problem are
     bit-identical to the smaller one when both split their blocks' keys the
     same way: a row's result does not depend on the block height."""
     import torch
-    S, d, lens = 1000, 128, [1000, 777][:B]
-    prob = W.random_problem(91, B, 17, S, S, d, "bf16", lens)
+    B, S, d = 2, 1000, 128
+    lens = [1000, 777]
+    H = _straddle(B, S, d, mask_kind is not None, rows)
+    prob = W.random_problem(91, B, H + 1, S, S, d, "bf16", lens)
     mask = None
     if mask_kind == "padding":
-        mask = W.key_padding_mask([0, 64][:B], lens, S)
+        mask = W.key_padding_mask([0, 64], lens, S)
     elif mask_kind == "per_query":
         mask = W.random_mask(92, (B, 1, S, S), 0.7)
     tm = None if mask is None else W.mask_to_torch(mask)
-    _say(f"block heights, B {B}, mask {mask_kind}")
+    plans = {h: attn.prefill_plan(B, h, S, S, d, masked=mask is not None) for h in (H, H + 1)}
+    _say(f"block heights {rows}, mask {mask_kind}, H {H}: plans", plans)
     runs = {}
-    for H in (16, 17):
-        q, k, v = (np.ascontiguousarray(prob[x][:, :H]) for x in ("q", "k", "v"))
+    for h in (H, H + 1):
+        q, k, v = (np.ascontiguousarray(prob[x][:, :h]) for x in ("q", "k", "v"))
         got, out = gpu_run(q, k, v, prob["scale"], 1, lens, mask=tm)
         ref = oracle.attention(q, k, v, prob["scale"], 1, lens, mask=mask)
-        assert_matches(got, ref, BF16_TOL, lens, S, f"H{H} mask {mask_kind}")
-        runs[H] = out
-    plans = {H: attn.prefill_plan(B, H, S, S, d, masked=mask is not None) for H in (16, 17)}
-    _say("plans (splits, rows per block, key groups):", plans)
-    assert plans[16][1] < plans[17][1], plans  # the two runs straddle a block-height switch
-    if plans[16][2] == plans[17][2]:
-        assert torch.equal(runs[17][:, :16], runs[16]), "block height changed the rows"
+        assert_matches(got, ref, BF16_TOL, lens, S, f"H{h} mask {mask_kind}")
+        runs[h] = out
+    if plans[H][2] == plans[H + 1][2]:
+        assert torch.equal(runs[H + 1][:, :H], runs[H]), "block height changed the rows"
 
 
 # Small unmasked grids whose blocks split their keys between two wave sets

@@ -1137,7 +1137,19 @@ PrefillPlan prefill_plan(int B, int H, int Sq, int Skv, int d, int dv, bool mask
     const long tiles = (Skv + kBN - 1) / kBN;
     long nsplit = 256 / blocks;
     nsplit = std::max(1L, std::min({nsplit, tiles / 16, (long)kMaxSplit}));
-    const int bm = nsplit > 1 ? kBM : 4 * blocks <= 256 ? 64 : blocks <= 128 ? 128 : kBM;
+    // Plain unmasked grids of up to 256 such blocks with at least 8 key
+    // tiles take 128-row blocks with key groups (below) too: B=1, H=32,
+    // S=2048 64.6 -> 57.4 us; B=1, H=16, S=4096 116.7 -> 92.6 us (two rounds
+    // of blocks, each block's walk halved).  Larger grids lose with them
+    // (prefill4096 145 -> 176 us: the pair steps cost more per tile).
+    const bool plain = !masked && !general;
+    int bm = kBM;
+    if (nsplit == 1) {
+        if (4 * blocks <= 256)
+            bm = 64;
+        else if (blocks <= 128 || (plain && blocks <= 256 && tiles >= 8))
+            bm = 128;
+    }
     // Small unmasked grids with plain logits and at least 8 key tiles split
     // each block's keys between two wave sets (the kernel's key-group walk),
     // halving the longest walk: B=4, H=12, S=512, d=64 15.6 -> 13.7 us;
@@ -1146,7 +1158,7 @@ PrefillPlan prefill_plan(int B, int H, int Sq, int Skv, int d, int dv, bool mask
     // walks lose (S = 128, 256: +10 %, +1.5 %).
     (void)d;
     (void)dv;
-    const int kg = bm < kBM && !masked && !general && tiles >= 8 ? 2 : 1;
+    const int kg = bm < kBM && plain && tiles >= 8 ? 2 : 1;
     return PrefillPlan{(int)nsplit, bm, kg};
 }
 
