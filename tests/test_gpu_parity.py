@@ -157,7 +157,27 @@ KEY_GROUP_CASES = [
     (56, 1, 1, 2, 600, 64, 64, 1, None),         # two queries, ten key tiles
     (57, 3, 2, 640, 640, 128, 128, 1, [640, 0, 65]),
     (58, 4, 12, 512, 512, 64, 64, 1, None),      # the mha768 shape
+    (59, 1, 24, 2048, 2048, 128, 128, 1, None),  # 128-row blocks, two rounds of them
 ]
+KEY_GROUP_KV_HEADS = {59: 6}  # grouped K/V heads for these seeds
+
+
+@pytest.mark.parametrize("seed,Hkv", [(52, 2), (58, 3)])
+def test_key_group_prefill_grouped_heads(seed, Hkv):
+    """Key groups with grouped K/V heads equal the same call on K/V expanded
+    to one head per query head, bit for bit (same plan, same bits read)."""
+    case = next(c for c in KEY_GROUP_CASES if c[0] == seed)
+    _, B, H, Sq, Skv, d, dv, causal, lens = case
+    assert attn.prefill_plan(B, H, Sq, Skv, d, dv, H_kv=Hkv)[2] == 2
+    prob = W.random_problem(seed, B, H, Sq, Skv, d, "bf16", lens, dv=dv, Hkv=Hkv)
+    got, _ = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], causal, lens)
+    g = H // Hkv
+    k = np.repeat(prob["k"], g, axis=1)
+    v = np.repeat(prob["v"], g, axis=1)
+    exp, _ = gpu_run(prob["q"], k, v, prob["scale"], causal, lens)
+    assert np.array_equal(got, exp)
+    ref = oracle.attention(prob["q"], prob["k"], prob["v"], prob["scale"], causal, lens)
+    assert_matches(got, ref, BF16_TOL, lens, Skv, f"grouped key groups s{seed}")
 
 
 @pytest.mark.parametrize("case", KEY_GROUP_CASES, ids=lambda c: f"s{c[0]}")
@@ -169,7 +189,8 @@ def test_key_group_prefill(case):
     plan = attn.prefill_plan(B, H, Sq, Skv, d, dv)
     _say("key-group case", case, "plan", plan)
     assert plan[0] == 1 and plan[2] == 2, plan
-    prob = W.random_problem(seed, B, H, Sq, Skv, d, "bf16", lens, dv=dv)
+    Hkv = KEY_GROUP_KV_HEADS.get(seed, H)
+    prob = W.random_problem(seed, B, H, Sq, Skv, d, "bf16", lens, dv=dv, Hkv=Hkv)
     got, _ = gpu_run(prob["q"], prob["k"], prob["v"], prob["scale"], causal, lens)
     ref = oracle.attention(prob["q"], prob["k"], prob["v"], prob["scale"], causal, lens)
     assert_matches(got, ref, BF16_TOL, lens, Skv, f"key groups {case}")
