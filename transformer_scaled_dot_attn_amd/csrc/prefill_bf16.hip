@@ -11,7 +11,10 @@
 // tiles of 64, staging K and V tiles in two-slot LDS rings.  Grids of at
 // most 128 such blocks run blocks of 4 wavefronts = 128 rows instead, and
 // grids of at most 64 blocks of 2 wavefronts = 64 rows, so more CUs share
-// the walk; a row's arithmetic is the same at every block height.
+// the walk; a row's arithmetic is the same at every block height.  On such
+// small grids (and on plain grids of up to 256 blocks, with 128-row blocks)
+// a block may also run two key groups: twice the waves, the second set
+// computing the odd key tiles of the same rows, merged at the end.
 //
 // Transposed products.  Each wave computes S^T = K Q^T (K from LDS as the A
 // operand, Q^T held in registers as the B operand).  In the accumulator of
