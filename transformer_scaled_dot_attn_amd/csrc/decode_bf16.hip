@@ -412,15 +412,43 @@ __global__ __launch_bounds__(256) void decode_mask_tiles_kernel(
         for (int i = tid; i < nc; i += 256) flag[i] = 0;
         __syncthreads();
         const int words = nc * 8;  // 4-key words of the chunk, per head
-        for (int idx = tid; idx < heads * words; idx += 256) {
-            const int hh = idx / words, w = idx - hh * words;
-            const int key = c0 * 32 + 4 * w;
-            if (key < L) {
-                const uint32_t wd = ldg_word(mrow + hh * msh + min(key, mlast));
-                uint32_t any = 0;
+        const int nwords = heads * words;
+        if (heads > 1) {
+            // several head rows: eight words per thread in flight before any
+            // is tested (one memory round trip per eight)
+            for (int i0 = tid; i0 < nwords; i0 += 8 * 256) {
+                uint32_t wd[8];
+                int wk[8];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) any |= (key + e < L) & byte_set(wd, e);
-                if (any) flag[w >> 3] = 1;
+                for (int u = 0; u < 8; ++u) {
+                    const int idx = i0 + u * 256;
+                    const int hh = idx / words, w = idx - hh * words;
+                    const int key = c0 * 32 + 4 * w;
+                    const bool ok = idx < nwords && key < L;
+                    wd[u] = ok ? ldg_word(mrow + hh * msh + min(key, mlast)) : 0u;
+                    wk[u] = ok ? w : -1;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    if (wk[u] < 0) continue;
+                    const int key = c0 * 32 + 4 * wk[u];
+                    uint32_t any = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) any |= (key + e < L) & byte_set(wd[u], e);
+                    if (any) flag[wk[u] >> 3] = 1;
+                }
+            }
+        } else {
+            for (int idx = tid; idx < nwords; idx += 256) {
+                const int w = idx;
+                const int key = c0 * 32 + 4 * w;
+                if (key < L) {
+                    const uint32_t wd = ldg_word(mrow + min(key, mlast));
+                    uint32_t any = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) any |= (key + e < L) & byte_set(wd, e);
+                    if (any) flag[w >> 3] = 1;
+                }
             }
         }
         __syncthreads();
