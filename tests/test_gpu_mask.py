@@ -136,6 +136,11 @@ STRUCTURED = [
     ("sliding window", 1, 4, 1200, 128, 1, None, lambda S: W.window_mask(S, 130)),
     ("window split", 1, 2, 4500, 128, 0, None, lambda S: W.window_mask(S, 70)),
     ("tile edges only", 1, 2, 602, 128, 0, None, _edge_mask),
+    # keys a multiple of 64 and 16-byte rows: the pre-pass reads 16 keys per load
+    ("documents, whole key tiles", 1, 4, 1024, 128, 1, None,
+     lambda S: W.document_mask([200, 577, 247])),
+    ("tile edges only, whole key tiles", 1, 2, 640, 128, 0, None, _edge_mask),
+    ("sliding window, whole key tiles", 1, 2, 1024, 64, 1, None, lambda S: W.window_mask(S, 100)),
 ]
 
 
@@ -178,6 +183,14 @@ WHOLE_TILES = [
      lambda B, Sq, Skv: W.key_padding_mask([320, 130], [Skv, Skv], Skv), False),
     ("per-item padding, ragged", 3, 2, 333, 1030, 64, 0, [1030, 1000, 700],
      lambda B, Sq, Skv: W.key_padding_mask([0, 64, 192], [1030, 1030, 641], Skv), False),
+    # whole key tiles and 16-byte rows (the pre-pass's 16-key loads)
+    ("one hidden byte per tile, whole key tiles", 1, 2, 512, 512, 64, 0, None,
+     lambda B, Sq, Skv: _hole_mask(Sq, Skv, [(0, 0), (255, 63), (256, 64), (511, 511), (300, 450)]),
+     False),
+    ("causal rule given with the rule, whole key tiles", 2, 2, 640, 640, 64, 1, [640, 401],
+     lambda B, Sq, Skv: np.tril(np.ones((Sq, Skv), dtype=bool))[None, None], True),
+    ("zeros only above the diagonal, whole key tiles", 1, 2, 300, 1024, 128, 1, None,
+     lambda B, Sq, Skv: _hole_mask(Sq, Skv, [(0, 725), (0, 1023), (255, 980)]), True),
     # one-row masks past 64 key tiles take the pre-pass instead of the blocks' own marks
     ("long all-true row", 1, 2, 256, 5000, 64, 1, None,
      lambda B, Sq, Skv: np.ones((1, 1, 1, Skv), dtype=bool), True),

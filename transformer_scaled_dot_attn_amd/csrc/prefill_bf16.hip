@@ -1005,7 +1005,10 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
 // instruction covers 4 whole 64-byte row segments.  Key tiles past the last
 // key a causal row of the tile can reach are marked 0 unread (the prefill
 // never visits them).
-template <int BM>  // query rows per query tile (the prefill's block)
+// VEC: whole 64-key tiles (Skv a multiple of 64) and 16-byte aligned rows;
+// then each lane reads 16 keys of a row with one load (4 lanes per row of
+// the tile, 16 rows per wave-wide load) instead of one 4-key word.
+template <int BM, bool VEC>  // BM: query rows per query tile (the prefill's block)
 __global__ __launch_bounds__(BM) void prefill_mask_tiles_kernel(
     const uint8_t* __restrict__ mask, long long msb, long long msi, int Sq, int Skv, int nqt,
     int nkt, int causal, uint8_t* __restrict__ tmap) {
@@ -1022,23 +1025,45 @@ __global__ __launch_bounds__(BM) void prefill_mask_tiles_kernel(
         }
     }
     const int lane = threadIdx.x & 63;
-    const int r0 = q0 + (int)(threadIdx.x >> 6) * 64 + (lane >> 4);
-    const int c = kt * kBN + 4 * (lane & 15);  // first key of this lane's word
-    const int col = min(c, mask_last_word(Skv));
-    const uint8_t* mtile = mask + bm * msb + col;
     uint32_t any = 0;   // OR of the counted bytes
     uint32_t hole = 0;  // nonzero if a counted byte is zero
+    if constexpr (VEC) {
+        const int r0 = q0 + (int)(threadIdx.x >> 6) * 64 + (lane >> 2);
+        const int c = kt * kBN + 16 * (lane & 3);  // first key of this lane's 16
+        const uint8_t* mtile = mask + bm * msb + c;
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-        const int row = r0 + 4 * it;
-        if (row < Sq) {
-            const uint32_t w = ldg_word(mtile + (long long)row * msi);
-            // bytes counted: keys c .. c + nb - 1 (none for a clamped word)
-            int nb = c == col ? Skv - c : 0;
-            if (causal) nb = min(nb, Skv - Sq + row - c + 1);
-            const uint32_t ign = nb >= 4 ? 0u : nb <= 0 ? ~0u : ~0u << (8 * nb);
-            any |= w & ~ign;
-            hole |= has_zero_byte(w | ign);
+        for (int it = 0; it < 4; ++it) {
+            const int row = r0 + 16 * it;
+            if (row < Sq) {
+                const u32x4 w4 = ldg16(mtile + (long long)row * msi);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    // keys c + 4 g .. + 3, all below Skv; the causal rule may cut them
+                    int nb = 4;
+                    if (causal) nb = min(nb, Skv - Sq + row - (c + 4 * g) + 1);
+                    const uint32_t ign = nb >= 4 ? 0u : nb <= 0 ? ~0u : ~0u << (8 * nb);
+                    any |= w4[g] & ~ign;
+                    hole |= has_zero_byte(w4[g] | ign);
+                }
+            }
+        }
+    } else {
+        const int r0 = q0 + (int)(threadIdx.x >> 6) * 64 + (lane >> 4);
+        const int c = kt * kBN + 4 * (lane & 15);  // first key of this lane's word
+        const int col = min(c, mask_last_word(Skv));
+        const uint8_t* mtile = mask + bm * msb + col;
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            const int row = r0 + 4 * it;
+            if (row < Sq) {
+                const uint32_t w = ldg_word(mtile + (long long)row * msi);
+                // bytes counted: keys c .. c + nb - 1 (none for a clamped word)
+                int nb = c == col ? Skv - c : 0;
+                if (causal) nb = min(nb, Skv - Sq + row - c + 1);
+                const uint32_t ign = nb >= 4 ? 0u : nb <= 0 ? ~0u : ~0u << (8 * nb);
+                any |= w & ~ign;
+                hole |= has_zero_byte(w | ign);
+            }
         }
     }
     const bool wa = __builtin_amdgcn_ballot_w64(any != 0) != 0;
@@ -1216,15 +1241,21 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
         const int Bm = a.msb != 0 ? a.B : 1;
         if (t) t->begin(kPrefillMaskTiles, a.stream);
         const dim3 mgrid((unsigned)((long)Bm * nqt * nkt));
+        const bool vec = a.Skv % kBN == 0 && (reinterpret_cast<uintptr_t>(a.mask) & 15u) == 0 &&
+                         (a.msb & 15) == 0 && (a.msi & 15) == 0;
+        auto marks = [&](auto kern, int threads) {
+            hipLaunchKernelGGL(kern, mgrid, dim3(threads), 0, a.stream, a.mask, a.msb, a.msi,
+                               a.Sq, a.Skv, nqt, nkt, a.causal, tmap);
+        };
         if (p.bm == 64)
-            hipLaunchKernelGGL(prefill_mask_tiles_kernel<64>, mgrid, dim3(64), 0, a.stream,
-                               a.mask, a.msb, a.msi, a.Sq, a.Skv, nqt, nkt, a.causal, tmap);
+            vec ? marks(prefill_mask_tiles_kernel<64, true>, 64)
+                : marks(prefill_mask_tiles_kernel<64, false>, 64);
         else if (p.bm == 128)
-            hipLaunchKernelGGL(prefill_mask_tiles_kernel<128>, mgrid, dim3(128), 0, a.stream,
-                               a.mask, a.msb, a.msi, a.Sq, a.Skv, nqt, nkt, a.causal, tmap);
+            vec ? marks(prefill_mask_tiles_kernel<128, true>, 128)
+                : marks(prefill_mask_tiles_kernel<128, false>, 128);
         else
-            hipLaunchKernelGGL(prefill_mask_tiles_kernel<kBM>, mgrid, dim3(kBM), 0, a.stream,
-                               a.mask, a.msb, a.msi, a.Sq, a.Skv, nqt, nkt, a.causal, tmap);
+            vec ? marks(prefill_mask_tiles_kernel<kBM, true>, kBM)
+                : marks(prefill_mask_tiles_kernel<kBM, false>, kBM);
         hipError_t e = hipGetLastError();
         if (t) t->end(kPrefillMaskTiles, a.stream);
         if (e != hipSuccess) return e;
