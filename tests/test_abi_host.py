@@ -7,6 +7,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 import transformer_scaled_dot_attn_amd as attn
@@ -65,6 +66,28 @@ def test_prefill_plan():
     with pytest.raises(attn.AttnError) as e:
         attn.prefill_plan(1, 32, 65, 64, 128)                           # Sq > Skv
     assert e.value.status == attn.E_SHAPE
+
+
+def test_prefill_plan_properties():
+    """Over random shapes: rows per block in {64, 128, 256}; key-range splits
+    only with 256-row blocks and one key group; two key groups only without a
+    mask or general logits, on blocks under 256 rows, with at least 8 key
+    tiles; a mask or general logits never change the splits."""
+    rng = np.random.default_rng(5)
+    for _ in range(3000):
+        B = int(rng.integers(1, 65))
+        H = int(rng.choice([1, 2, 4, 8, 12, 16, 32, 64]))
+        Skv = int(rng.integers(2, 70000))
+        Sq = int(rng.integers(2, min(Skv, 9000) + 1))
+        d, dv = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+        masked, general = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+        ns, bm, kg = attn.prefill_plan(B, H, Sq, Skv, d, dv, masked=masked, general=general)
+        assert bm in (64, 128, 256) and kg in (1, 2) and 1 <= ns <= 16, (ns, bm, kg)
+        if ns > 1:
+            assert bm == 256 and kg == 1
+        if kg == 2:
+            assert not masked and not general and bm < 256 and (Skv + 63) // 64 >= 8
+        assert attn.prefill_plan(B, H, Sq, Skv, d, dv)[0] == ns
 
 
 def test_no_hip_error_recorded_before_a_launch_failure():
