@@ -468,8 +468,8 @@ def sweep_slopes(rows):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build runs attention on a single MI355X "
-              "and has no multi-GPU path (pass --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU only: the attention kernels run on a single MI355X "
+              "and there is no multi-GPU path (pass --gpus 1).", file=sys.stderr)
         sys.exit(2)
     parts = [p.strip() for p in args.parts.split(",") if p.strip()]
 
