@@ -253,15 +253,62 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
     const bool q_live = qi >= 0 && qi < n;
 
     // Q^T fragments: B operand of S^T = K Q^T.  Lane l holds 8 consecutive
-    // features 16*ks + 8*(l/32) .. +7 of query (l%32).  Issued before the
-    // key-tile list is built, so their latency overlaps it.
+    // features 16*ks + 8*(l/32) .. +7 of query (l%32).
+    // Loaded directly, each of a lane's loads would touch 32 rows, 32 bytes
+    // each; so the block reads its Q rows coalesced instead (thread t: the
+    // 16-byte chunks t + kThreads i of the row-major tile, consecutive
+    // threads on consecutive bytes), together with the walk's first K/V
+    // tiles, and hands them to the fragments through per-wave LDS regions
+    // (stage_q) before those tiles are stored there.  Rows outside the
+    // sequence's queries read as zero.  Where the regions do not fit in the
+    // K/V slots (d = 128 with d_v = 64 at 256 rows), lanes load their
+    // fragments directly, before the key-tile list is built.
+    constexpr int kQRegion = 32 * S::kStrideK;                // one wave's Q rows
+    constexpr int kQRegK = 2 * S::kTileK / kQRegion;          // regions in lds_k
+    constexpr int kQRegV = 2 * SV::kTileV / kQRegion;         // regions in lds_v
+    constexpr bool kQStaged = kQRegK + kQRegV >= kRowWaves;
+    constexpr int kQChunks = kQStaged ? kBMb * S::kChunks / kThreads : 1;
+    static_assert(!kQStaged || kQChunks * kThreads == kBMb * S::kChunks, "Q tile must split evenly");
     u32x4 qf[S::kKSteps];
-    {
+    u32x4 qtmp[kQChunks];
+    if constexpr (!kQStaged) {
         const uint16_t* qrow = q + ((size_t)bh * Sq + (q_live ? qi : 0)) * D + half * 8;
 #pragma unroll
         for (int ks = 0; ks < S::kKSteps; ++ks)
             qf[ks] = q_live ? ldg16(qrow + ks * 16) : u32x4{0, 0, 0, 0};
     }
+    auto q_region = [&](int w) -> uint16_t* {
+        return w < kQRegK ? &lds_k[0][0] + w * kQRegion : &lds_v[0][0] + (w - kQRegK) * kQRegion;
+    };
+    // Issued with the first K/V loads of the walk (one memory round trip).
+    auto load_q = [&]() {
+        if constexpr (kQStaged) {
+#pragma unroll
+            for (int i = 0; i < kQChunks; ++i) {
+                const int c = tid + kThreads * i;
+                const int r = min(max(q0 + c / S::kChunks, 0), Sq - 1);
+                qtmp[i] = ldg16(q + ((size_t)bh * Sq + r) * D + (c % S::kChunks) * 8);
+            }
+        }
+    };
+    // Called once by every wave, while no K/V tile is in LDS yet.
+    auto stage_q = [&]() {
+        if constexpr (kQStaged) {
+#pragma unroll
+            for (int i = 0; i < kQChunks; ++i) {
+                const int c = tid + kThreads * i;
+                const int r = c / S::kChunks, qr = q0 + r;
+                const u32x4 z = {0, 0, 0, 0};
+                *reinterpret_cast<u32x4*>(q_region(r >> 5) + (r & 31) * S::kStrideK +
+                                          (c % S::kChunks) * 8) = qr >= 0 && qr < n ? qtmp[i] : z;
+            }
+            __syncthreads();
+            const uint16_t* src = q_region(rg) + (lane & 31) * S::kStrideK + half * 8;
+#pragma unroll
+            for (int ks = 0; ks < S::kKSteps; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(src + ks * 16);
+            __syncthreads();
+        }
+    };
 
 
     // Masked calls walk list positions pp0 <= pos < pp1 of the key tiles the
@@ -790,13 +837,16 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
     // The unmasked walk over key tiles ta <= t < tb.  Prologue: K(ta), V(ta),
     // K(ta+1) staged; S^T(ta) scored and its reference set.
     auto walk = [&](int ta, int tb) __attribute__((always_inline)) {
+        load_q();
         bload(ta);
         fetch_k(ta);
         fetch_v(ta);
+        u32x4 k1[S::kPerThread];
+        fetch_k_to(ta + 1, k1);
+        stage_q();
         stash_k(ta);
         stash_v(ta);
-        fetch_k(ta + 1);
-        stash_k(ta + 1);
+        stash_k_from(ta + 1, k1);
         __syncthreads();
         bpark();
         if (ta < t1w) {
@@ -856,10 +906,12 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
     };
     auto walk_kg = [&](int ta, int tb) __attribute__((always_inline)) {
         const int u0 = ta + kg;
+        load_q();
         fetch_k_to(ta, kp0);
         fetch_k_to(ta + 1, kp1);
         fetch_v_to(ta, vp0);
         fetch_v_to(ta + 1, vp1);
+        stage_q();
         stash_k_from(ta, kp0);
         stash_k_from(ta + 1, kp1);
         fetch_k_to(ta + 2, kp0);
@@ -885,10 +937,12 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
     // The masked walk over list positions pp0 <= t < pp1, with the same
     // prologue; the tile scored first is the first one the wave computes.
     auto walk_m = [&]() __attribute__((always_inline)) {
+        load_q();
         mload(tix(pp0));
         bload(tix(pp0));
         fetch_k(tix(pp0));
         fetch_v(tix(pp0));
+        stage_q();
         stash_k(pp0);
         stash_v(pp0);
         fetch_k(tix(pp0 + 1));
@@ -973,7 +1027,52 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
     }
 
     // ---- epilogue: out = acc / l; with a mask this tile's rows past n_b are
-    // zero too (without one the pad rows were zeroed above)
+    // zero too (without one the pad rows were zeroed above).
+    // A lane holds 4-feature pieces of one row, so storing them directly
+    // writes 8 bytes into each of 32 rows per instruction.  Instead each wave
+    // packs its 32 x DV outputs into its own LDS region (the K/V slots are
+    // free after the walk's last barrier) and stores whole rows from there:
+    // 16 bytes a lane, consecutive lanes on consecutive bytes.
+    constexpr int kOutStride = DV + 8;                          // row stride (elements)
+    constexpr int kOutRegion = 32 * kOutStride;                 // one wave's rows
+    constexpr int kRegionsK = 2 * S::kTileK / kOutRegion;       // regions in lds_k
+    constexpr int kRegionsV = 2 * SV::kTileV / kOutRegion;      // regions in lds_v
+    constexpr bool kStaged = kRegionsK + kRegionsV >= kRowWaves;
+    if constexpr (kStaged) {
+        uint16_t* region = rg < kRegionsK ? &lds_k[0][0] + rg * kOutRegion
+                                          : &lds_v[0][0] + (rg - kRegionsK) * kOutRegion;
+        if (kg == 0) {
+            const float l_tot = halves_sum(l_run);
+            const float inv = (q_live && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
+            uint16_t* lrow = region + (lane & 31) * kOutStride;
+#pragma unroll
+            for (int db = 0; db < SV::kDBlocks; ++db)
+#pragma unroll
+                for (int rg4 = 0; rg4 < 4; ++rg4) {
+                    const int d0 = db * 32 + 8 * rg4 + 4 * half;
+                    u32x2 w = {0, 0};
+                    if (q_live) {
+                        w[0] = pack_bf16(oacc[db][4 * rg4] * inv, oacc[db][4 * rg4 + 1] * inv);
+                        w[1] = pack_bf16(oacc[db][4 * rg4 + 2] * inv, oacc[db][4 * rg4 + 3] * inv);
+                    }
+                    *reinterpret_cast<u32x2*>(lrow + d0) = w;
+                }
+        }
+        __syncthreads();
+        if (kg == 0) {
+            constexpr int kRowChunks = DV / 8;  // 16-byte chunks per row
+#pragma unroll
+            for (int i = 0; i < 32 * kRowChunks / 64; ++i) {
+                const int c = i * 64 + lane;
+                const int r = c / kRowChunks, col = (c % kRowChunks) * 8;
+                const int qr = qw + r;
+                const u32x4 val = *reinterpret_cast<const u32x4*>(region + r * kOutStride + col);
+                if (MASK ? qr < Sq : (qr >= 0 && qr < n))
+                    *reinterpret_cast<u32x4*>(obase + (size_t)qr * DV + col) = val;
+            }
+        }
+        return;
+    }
     if ((MASK ? qi < Sq : q_live) && kg == 0) {
         const float l_tot = halves_sum(l_run);
         const float inv = (q_live && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
