@@ -1061,14 +1061,21 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
         __syncthreads();
         if (kg == 0) {
             constexpr int kRowChunks = DV / 8;  // 16-byte chunks per row
+            constexpr int kPer = 32 * kRowChunks / 64;
+            // every read first, then the stores (each behind its row's test)
+            u32x4 val[kPer];
 #pragma unroll
-            for (int i = 0; i < 32 * kRowChunks / 64; ++i) {
+            for (int i = 0; i < kPer; ++i) {
                 const int c = i * 64 + lane;
-                const int r = c / kRowChunks, col = (c % kRowChunks) * 8;
-                const int qr = qw + r;
-                const u32x4 val = *reinterpret_cast<const u32x4*>(region + r * kOutStride + col);
+                val[i] = *reinterpret_cast<const u32x4*>(region + (c / kRowChunks) * kOutStride +
+                                                         (c % kRowChunks) * 8);
+            }
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int c = i * 64 + lane;
+                const int qr = qw + c / kRowChunks;
                 if (MASK ? qr < Sq : (qr >= 0 && qr < n))
-                    *reinterpret_cast<u32x4*>(obase + (size_t)qr * DV + col) = val;
+                    *reinterpret_cast<u32x4*>(obase + (size_t)qr * DV + (c % kRowChunks) * 8) = val[i];
             }
         }
         return;
