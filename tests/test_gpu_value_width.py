@@ -75,6 +75,11 @@ BF16_CASES = [
     (128, 2, 4, 4, 1, 2000, 128, 64, 0, [2000, 500], "mask"),
     (129, 2, 4, 2, 200, 200, 128, 64, 1, [200, 60], "bias"),
     (130, 2, 8, 2, 1, 1500, 64, 128, 0, [1500, 70], "bias"),
+    # unsplit grids of 256-row blocks: with d = 64, d_v = 128 the outputs are
+    # stored without the LDS staging, with d = 128, d_v = 64 the Q fragments
+    # are loaded without it (the per-wave regions do not fit)
+    (131, 3, 44, 4, 512, 512, 64, 128, 1, [512, 300, 17], None),
+    (132, 3, 44, 4, 512, 512, 128, 64, 1, [512, 300, 17], None),
 ]
 
 
