@@ -171,7 +171,8 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
     using SV = Shape<DV, kThreads>;  // the value side: V rows and outputs of DV features
     __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][S::kTileK];
     __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][SV::kTileV];
-    __shared__ u32x4 lds_m[MASK ? 2 * kThreads : 1];  // parked mask words, 32 bytes per lane
+    // parked mask words, 32 bytes per lane, two buffers (list positions of each parity)
+    __shared__ u32x4 lds_m[MASK ? 4 * kThreads : 1];
     __shared__ int lds_tl[MASK ? kMaxListTiles : 1];  // this query tile's listed key tiles
     __shared__ int lds_tn;                            // their number
     __shared__ int lds_tcut;                          // some listed tile is cut by the mask
@@ -386,44 +387,101 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
 
     // ---- allowed-mask words of this lane's query row for one key tile:
     // word w holds keys 32 (w/4) + 8 (w%4) + 4 half .. +3, the keys of
-    // score elements 4 (w%4) .. +3 of block w/4.  Word offsets are clamped
-    // to the row's last readable word; keys past it are >= Skv >= L and
-    // hidden by the length rule anyway.
-    u32x4 mw[2];  // in flight: word w is mw[w / 4][w % 4]
+    // score elements 4 (w%4) .. +3 of block w/4.  A list position's words
+    // are loaded one step ahead (mload), stored into the LDS buffer of the
+    // position's parity before a barrier (mwrite) and read back by their
+    // lane after it (mread, which also sets mcut and mnone); mask() reads
+    // them from the same buffer.
+    // Two ways to load them, the same words either way:
+    //  - coalesced (mvec: keys in whole 64-key tiles, 16-byte aligned rows):
+    //    the block reads its rows' 64 bytes of the tile as 16-byte chunks,
+    //    consecutive threads on consecutive chunks, and mwrite scatters each
+    //    chunk's four words to the two lanes that own them;
+    //  - per lane: each lane reads its own 8 words, offsets clamped to the
+    //    row's last readable word (keys past it are >= Skv >= L and hidden
+    //    by the length rule anyway).
+    // Reading its own words, each load of a lane touches 32 rows; the
+    // coalesced loads were measured 15 % faster on a per-element mask.
+    u32x4 mw[2];  // in flight: word w is mw[w / 4][w % 4], or the two chunks (mvec)
     bool mcut = false;   // some lane of the wave hides a key of the parked tile
     bool mnone = false;  // no live lane of the wave sees a key of the parked tile
-    // addressed as a wave-uniform row base (row min(qw, Sq-1)) plus a 32-bit
+    int mbuf = 0;        // the LDS buffer of the parked tile
+    // per lane: a wave-uniform row base (row min(qw, Sq-1)) plus a 32-bit
     // lane offset (qi - that row) * msi, below 32 * msi <= 2^32; pad lanes
     // read the base row
+    // (coalesced: the block's first row as the base, 32-bit row offsets)
     const uint8_t* mbase = nullptr;
+    const uint8_t* mblk = nullptr;
     uint32_t mlane = 0;
+    bool mvec = false;
     if constexpr (MASK) {
         const int r0 = __builtin_amdgcn_readfirstlane(min(qw, Sq - 1));  // uniform: SGPR base
-        mbase = allowed + b * msb + (long long)(bh - b * H) * msh + (long long)r0 * msi;
+        const uint8_t* mhead = allowed + b * msb + (long long)(bh - b * H) * msh;
+        mbase = mhead + (long long)r0 * msi;
+        mblk = mhead + (long long)qz * msi;  // qz < Sq
         mlane = q_live ? (uint32_t)(qi - r0) * (uint32_t)msi : 0u;
+        mvec = Skv % kBN == 0 && (reinterpret_cast<uintptr_t>(mblk) & 15u) == 0 && (msi & 15) == 0 &&
+               (long long)kBMb * msi + Skv <= (long long)UINT32_MAX;
     }
     const int mlast = mask_last_word(Skv);
+    constexpr int kMChunks = kBMb * 4 / kThreads;  // 16-byte chunks per thread (coalesced)
+    static_assert(!MASK || kMChunks == 2, "two mask chunks per thread");
     auto mload = [&](int tile) {
         if constexpr (MASK) {
+            if (mvec) {
 #pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                const int j = tile * kBN + 32 * (w >> 2) + 8 * (w & 3) + 4 * half;
-                mw[w >> 2][w & 3] = ldg_word(mbase + (mlane + (uint32_t)min(j, mlast)));
+                for (int i = 0; i < kMChunks; ++i) {
+                    const int c = tid + kThreads * i;  // row c / 4, keys 16 (c % 4) ..
+                    const uint32_t rr = (uint32_t)min(c / 4, Sq - 1 - qz);
+                    mw[i] = ldg16(mblk + (rr * (uint32_t)msi + (uint32_t)(tile * kBN + (c % 4) * 16)));
+                }
+            } else {
+#pragma unroll
+                for (int w = 0; w < 8; ++w) {
+                    const int j = tile * kBN + 32 * (w >> 2) + 8 * (w & 3) + 4 * half;
+                    mw[w >> 2][w & 3] = ldg_word(mbase + (mlane + (uint32_t)min(j, mlast)));
+                }
             }
         }
     };
-    auto mpark = [&]() {
+    // Before a barrier; the buffer's last readers are behind the one before.
+    auto mwrite = [&](int pos) {
         if constexpr (MASK) {
+            u32x4* buf = lds_m + (pos & 1) * 2 * kThreads;
+            if (mvec) {
+#pragma unroll
+                for (int i = 0; i < kMChunks; ++i) {
+                    // chunk part p holds words w0, w0 + 1 (w0 = 4 (p/2) + 2 (p%2)) of
+                    // the row's two lanes: its words 0, 2 for half 0, 1, 3 for half 1
+                    const int c = tid + kThreads * i;
+                    const int r = c / 4, part = c % 4;
+                    const int w0 = 4 * (part >> 1) + 2 * (part & 1);
+                    const int lt = 64 * (r >> 5) + (r & 31);  // the row's half-0 lane
+                    uint32_t* b0 = reinterpret_cast<uint32_t*>(buf + 2 * lt) + w0;
+                    uint32_t* b1 = reinterpret_cast<uint32_t*>(buf + 2 * (lt + 32)) + w0;
+                    *reinterpret_cast<u32x2*>(b0) = u32x2{mw[i][0], mw[i][2]};
+                    *reinterpret_cast<u32x2*>(b1) = u32x2{mw[i][1], mw[i][3]};
+                }
+            } else {
+                buf[2 * tid] = mw[0];
+                buf[2 * tid + 1] = mw[1];
+            }
+        }
+    };
+    // After the barrier that follows mwrite(pos).
+    auto mread = [&](int pos) {
+        if constexpr (MASK) {
+            mbuf = pos & 1;
+            const u32x4* buf = lds_m + mbuf * 2 * kThreads;
+            const u32x4 m0 = buf[2 * tid], m1 = buf[2 * tid + 1];
             uint32_t z = 0, nz = 0;
 #pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                z |= has_zero_byte(mw[w >> 2][w & 3]);
-                nz |= mw[w >> 2][w & 3];
+            for (int w = 0; w < 4; ++w) {
+                z |= has_zero_byte(m0[w]) | has_zero_byte(m1[w]);
+                nz |= m0[w] | m1[w];
             }
             mcut = __builtin_amdgcn_ballot_w64(z != 0) != 0;
             mnone = __builtin_amdgcn_ballot_w64(q_live && nz != 0) == 0;
-            lds_m[2 * tid] = mw[0];
-            lds_m[2 * tid + 1] = mw[1];
         }
     };
 
@@ -659,8 +717,8 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
         if (kbase + kBN > kfull_w) {
             // the rules cut this tile (and the allowed-mask may)
             if constexpr (UM) {
-                mk[0] = lds_m[2 * tid];
-                mk[1] = lds_m[2 * tid + 1];
+                mk[0] = lds_m[mbuf * 2 * kThreads + 2 * tid];
+                mk[1] = lds_m[mbuf * 2 * kThreads + 2 * tid + 1];
             }
             const int rel = lim - kbase - 4 * half;  // element visible iff its offset <= rel
 #pragma unroll
@@ -674,8 +732,8 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
         } else if constexpr (UM) {
             if (mcut) {
                 // only the allowed-mask cuts it
-                mk[0] = lds_m[2 * tid];
-                mk[1] = lds_m[2 * tid + 1];
+                mk[0] = lds_m[mbuf * 2 * kThreads + 2 * tid];
+                mk[1] = lds_m[mbuf * 2 * kThreads + 2 * tid + 1];
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -807,7 +865,7 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
     // prologue, the pipelined step and the wave's last tile do.
     bool have = false;
     auto step_m = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {  // t: list position
-        mpark();  // mask words of position t+1
+        mread(t + 1);  // mask words of position t+1
         bpark();
         const bool next = t + 1 < pp1 && tix(t + 1) < tw && !mnone;  // this wave computes t+1
         fetch_k(tix(t + 2));
@@ -831,6 +889,7 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
         bload(tix(t + 2));
         stash_k(t + 2);
         stash_v(t + 1);
+        mwrite(t + 2);
         __syncthreads();
     };
 
@@ -947,9 +1006,10 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
         stash_v(pp0);
         fetch_k(tix(pp0 + 1));
         stash_k(pp0 + 1);
+        mwrite(pp0);
         __syncthreads();
         bpark();
-        mpark();
+        mread(pp0);
         have = pp0 < pp1 && tix(pp0) < tw && !mnone;
         if (have) {
             score(pp0, s0, nullptr);
@@ -958,6 +1018,7 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
         }
         mload(tix(pp0 + 1));
         bload(tix(pp0 + 1));
+        mwrite(pp0 + 1);
         __syncthreads();
         for (int t = pp0; t < pp1; t += 2) {
             step_m(t, s0, s1);
