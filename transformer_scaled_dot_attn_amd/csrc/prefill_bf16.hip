@@ -1198,20 +1198,23 @@ __global__ __launch_bounds__(BM) void prefill_mask_tiles_kernel(
         const int r0 = q0 + (int)(threadIdx.x >> 6) * 64 + (lane >> 2);
         const int c = kt * kBN + 16 * (lane & 3);  // first key of this lane's 16
         const uint8_t* mtile = mask + bm * msb + c;
+        // all loads first (rows past Sq read row Sq - 1 and count nothing),
+        // so they are in flight together
+        u32x4 w4[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+            w4[it] = ldg16(mtile + (long long)min(r0 + 16 * it, Sq - 1) * msi);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int row = r0 + 16 * it;
-            if (row < Sq) {
-                const u32x4 w4 = ldg16(mtile + (long long)row * msi);
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    // keys c + 4 g .. + 3, all below Skv; the causal rule may cut them
-                    int nb = 4;
-                    if (causal) nb = min(nb, Skv - Sq + row - (c + 4 * g) + 1);
-                    const uint32_t ign = nb >= 4 ? 0u : nb <= 0 ? ~0u : ~0u << (8 * nb);
-                    any |= w4[g] & ~ign;
-                    hole |= has_zero_byte(w4[g] | ign);
-                }
+            for (int g = 0; g < 4; ++g) {
+                // keys c + 4 g .. + 3, all below Skv; the causal rule may cut them
+                int nb = row < Sq ? 4 : 0;
+                if (causal) nb = min(nb, Skv - Sq + row - (c + 4 * g) + 1);
+                const uint32_t ign = nb >= 4 ? 0u : nb <= 0 ? ~0u : ~0u << (8 * nb);
+                any |= w4[it][g] & ~ign;
+                hole |= has_zero_byte(w4[it][g] | ign);
             }
         }
     } else {
@@ -1219,18 +1222,19 @@ __global__ __launch_bounds__(BM) void prefill_mask_tiles_kernel(
         const int c = kt * kBN + 4 * (lane & 15);  // first key of this lane's word
         const int col = min(c, mask_last_word(Skv));
         const uint8_t* mtile = mask + bm * msb + col;
+        uint32_t wd[16];
+#pragma unroll
+        for (int it = 0; it < 16; ++it)
+            wd[it] = ldg_word(mtile + (long long)min(r0 + 4 * it, Sq - 1) * msi);
 #pragma unroll
         for (int it = 0; it < 16; ++it) {
             const int row = r0 + 4 * it;
-            if (row < Sq) {
-                const uint32_t w = ldg_word(mtile + (long long)row * msi);
-                // bytes counted: keys c .. c + nb - 1 (none for a clamped word)
-                int nb = c == col ? Skv - c : 0;
-                if (causal) nb = min(nb, Skv - Sq + row - c + 1);
-                const uint32_t ign = nb >= 4 ? 0u : nb <= 0 ? ~0u : ~0u << (8 * nb);
-                any |= w & ~ign;
-                hole |= has_zero_byte(w | ign);
-            }
+            // bytes counted: keys c .. c + nb - 1 (none for a clamped word or row)
+            int nb = c == col && row < Sq ? Skv - c : 0;
+            if (causal) nb = min(nb, Skv - Sq + row - c + 1);
+            const uint32_t ign = nb >= 4 ? 0u : nb <= 0 ? ~0u : ~0u << (8 * nb);
+            any |= wd[it] & ~ign;
+            hole |= has_zero_byte(wd[it] | ign);
         }
     }
     const bool wa = __builtin_amdgcn_ballot_w64(any != 0) != 0;
