@@ -176,7 +176,8 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
     __shared__ int lds_tl[MASK ? kMaxListTiles : 1];  // this query tile's listed key tiles
     __shared__ int lds_tn;                            // their number
     __shared__ int lds_tcut;                          // some listed tile is cut by the mask
-    __shared__ u32x4 lds_b[GEN ? 4 * kThreads : 1];   // parked bias, 64 bytes per lane
+    // parked bias, 64 bytes per lane (two buffers without a mask: tiles of each parity)
+    __shared__ u32x4 lds_b[GEN ? (MASK ? 1 : 2) * 4 * kThreads : 1];
     // key group 1's (acc, m, l) per lane for the merge (KG = 2)
     __shared__ float lds_x[KG == 2 ? kRowWaves * (SV::kDBlocks * 16 + 2) * 64 : 1];
 
@@ -429,6 +430,9 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
     auto mload = [&](int tile) {
         if constexpr (MASK) {
             if (mvec) {
+                // run-ahead positions past the last key tile (unlisted masks)
+                // read the last tile; their words are never used
+                tile = min(tile, Skv / kBN - 1);
 #pragma unroll
                 for (int i = 0; i < kMChunks; ++i) {
                     const int c = tid + kThreads * i;  // row c / 4, keys 16 (c % 4) ..
@@ -491,25 +495,56 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
     // wave-uniform row base plus a 32-bit lane offset; group offsets are
     // clamped to the row's last readable group (keys past it are >= Skv >= L
     // and hidden).  Without a bias every group reads the zero array.
+    // Without a mask, where the keys come in whole 64-key tiles and the rows
+    // are 16-byte aligned (bvec), the block reads its rows' 128 bytes of the
+    // tile coalesced instead, as 16-byte chunks (four per thread, held in
+    // bw), and bwrite scatters each chunk's two groups to their lanes through
+    // the LDS buffer of the tile's parity (written before a barrier, read
+    // after it; the scheme of the mask words below).
     u32x2 bw[2][4];
     const uint8_t* bbase = nullptr;  // byte addresses: 32-bit lane offsets below 2^32
+    const uint8_t* bblk = nullptr;   // (bvec: the block's first row in the sequence)
     uint32_t blane = 0;
     int blast = 0;
+    int brb = 0;
+    bool bvec = false;
+    int bbuf = 0;  // the LDS buffer of the parked tile
     if constexpr (GEN) {
         // without a mask a tile's first waves may start at a negative row
         // (tiles end at the last valid row): the base row is clamped to 0
         const int r0 = __builtin_amdgcn_readfirstlane(min(max(qw, 0), Sq - 1));
         if (bias != nullptr) {
-            bbase = reinterpret_cast<const uint8_t*>(bias + b * bsb + (long long)(bh - b * H) * bsh +
-                                                     (long long)r0 * bsi);
+            const uint16_t* bhead = bias + b * bsb + (long long)(bh - b * H) * bsh;
+            bbase = reinterpret_cast<const uint8_t*>(bhead + (long long)r0 * bsi);
             blane = q_live ? 2u * (uint32_t)(qi - r0) * (uint32_t)bsi : 0u;
             blast = bias_last_group(Skv);
+            brb = min(max(q0, 0), Sq - 1);
+            bblk = reinterpret_cast<const uint8_t*>(bhead + (long long)brb * bsi);
+            bvec = !MASK && Skv % kBN == 0 && (reinterpret_cast<uintptr_t>(bblk) & 15u) == 0 &&
+                   (bsi & 7) == 0 && 2LL * kBMb * bsi + 2LL * Skv <= (long long)UINT32_MAX;
         } else {
             bbase = reinterpret_cast<const uint8_t*>(g_zero_bias);
         }
     }
+    constexpr int kBChunks = kBMb * 8 / kThreads;  // 16-byte chunks per thread (bvec)
+    static_assert(!GEN || kBChunks == 4, "four bias chunks per thread");
     auto bload = [&](int tile) {
         if constexpr (GEN) {
+            if (bvec) {
+                // the steps load two tiles ahead: past the last key tile they
+                // read the last one, never used
+                tile = min(tile, Skv / kBN - 1);
+#pragma unroll
+                for (int i = 0; i < kBChunks; ++i) {
+                    const int c = tid + kThreads * i;  // row c / 8, keys 8 (c % 8) ..
+                    const int rr = min(max(q0 + c / 8, 0), Sq - 1);
+                    const u32x4 ch = ldg16(bblk + (2u * (uint32_t)(rr - brb) * (uint32_t)bsi +
+                                                   (uint32_t)(2 * tile * kBN + 16 * (c % 8))));
+                    bw[i >> 1][2 * (i & 1)] = u32x2{ch[0], ch[1]};
+                    bw[i >> 1][2 * (i & 1) + 1] = u32x2{ch[2], ch[3]};
+                }
+                return;
+            }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -529,6 +564,40 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
                     lds_b[4 * tid + 2 * kb + h2] = u32x4{bw[kb][2 * h2][0], bw[kb][2 * h2][1],
                                                          bw[kb][2 * h2 + 1][0], bw[kb][2 * h2 + 1][1]};
         }
+    };
+    // Without a mask: before a barrier, into the buffer of the tile's parity,
+    // whose last readers are behind the barrier before.
+    auto bwrite = [&](int tile) {
+        if constexpr (GEN && !MASK) {
+            u32x4* buf = lds_b + (tile & 1) * 4 * kThreads;
+            if (bvec) {
+#pragma unroll
+                for (int i = 0; i < kBChunks; ++i) {
+                    // chunk part p: group (p / 4, p % 4) of the row's half-0 lane,
+                    // then the same group of its half-1 lane
+                    const int c = tid + kThreads * i;
+                    const int r = c / 8, part = c % 8, kb = part >> 2, g = part & 3;
+                    const int lt = 64 * (r >> 5) + (r & 31);
+                    *(reinterpret_cast<u32x2*>(buf + 4 * lt + 2 * kb + (g >> 1)) + (g & 1)) =
+                        bw[i >> 1][2 * (i & 1)];
+                    *(reinterpret_cast<u32x2*>(buf + 4 * (lt + 32) + 2 * kb + (g >> 1)) + (g & 1)) =
+                        bw[i >> 1][2 * (i & 1) + 1];
+                }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
+                        buf[4 * tid + 2 * kb + h2] = u32x4{bw[kb][2 * h2][0], bw[kb][2 * h2][1],
+                                                           bw[kb][2 * h2 + 1][0], bw[kb][2 * h2 + 1][1]};
+            }
+        }
+    };
+    // bias of a tile: parked at the step's start with a mask, else written
+    // before the last barrier (bwrite) and taken from the tile's buffer
+    auto bhere = [&](int tile) {
+        if constexpr (MASK) bpark();
+        else bbuf = tile & 1;
     };
 
     // ---- tile staging: thread t moves 16-byte chunks t + 512 i of the
@@ -702,7 +771,7 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
-                    const u32x4 w4 = lds_b[4 * tid + 2 * kb + h2];
+                    const u32x4 w4 = lds_b[bbuf * 4 * kThreads + 4 * tid + 2 * kb + h2];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int r = 8 * h2 + e;  // groups 2 h2, 2 h2 + 1: elements 8 h2 .. +7
@@ -838,7 +907,7 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
     // kernel's blocks whose listed tiles all open whole take this step.
     auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
         const bool pipe = t + 1 < t1w;  // this wave scores tile t+1
-        bpark();  // bias of tile t+1
+        bhere(t + 1);  // bias of tile t+1
         fetch_k(t + 2);
         // S^T(t+1) under which P(t) is formed
         if (pipe) score(t + 1, sn, &sc);
@@ -855,6 +924,7 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
         bload(t + 2);
         stash_k(t + 2);
         stash_v(t + 1);
+        bwrite(t + 2);
         __syncthreads();
     };
 
@@ -906,14 +976,16 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
         stash_k(ta);
         stash_v(ta);
         stash_k_from(ta + 1, k1);
+        bwrite(ta);
         __syncthreads();
-        bpark();
+        bhere(ta);
         if (ta < t1w) {
             score(ta, s0, nullptr);
             mask(std::false_type{}, ta, s0);
             reference(scan(s0));
         }
         bload(ta + 1);
+        bwrite(ta + 1);
         __syncthreads();  // K(ta) is read by every wave before K(ta+2) replaces it
         for (int t = ta; t < tb; t += 2) {
             step(t, s0, s1);
