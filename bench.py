@@ -234,7 +234,9 @@ def prefill_configs(attn, W, dev, steps, warmup,
 def mask_runs(attn, W, runs, steps, warmup):
     """The step's workloads again with explicit allowed-masks (True = may
     attend, ANDed with the causal and length rules; "Attention from Scratch",
-    KubeDojo module 1.4.3, Part 3), against the same call unmasked.  Prefill
+    KubeDojo module 1.4.3, Part 3), and the prefill with an additive bias of
+    finite values (the float mask of its Part 7; every pair stays visible),
+    against the same call unmasked.  Prefill
     counts 4*d flops per visible (query, key) pair -- allowed by the mask and
     by the causal rule -- the algorithmic work; decode counts the bytes of the
     K/V rows some query head of their group may see, plus q, out and the mask."""
@@ -252,6 +254,8 @@ def mask_runs(attn, W, runs, steps, warmup):
                      ("random [1,1,S,S], density 0.5", W.random_mask(5, (1, 1, w.Sq, S), 0.5)),
                      ("8 packed documents of 512 [1,1,S,S]", W.document_mask([S // 8] * 8)),
                      ("sliding window of 256 [1,1,S,S]", W.window_mask(S, 256))]
+            biases = [("bias [1,1,S,S], N(0, 4) values", W.random_bias(8, (1, 1, w.Sq, S), "bf16")),
+                      ("bias [1,H,1,S], N(0, 4) values", W.random_bias(9, (1, w.H, 1, S), "bf16"))]
             kernels = ("prefill_bf16_mfma", "prefill_mask_tiles")
         else:
             lens = x["kv_lens_host"]
@@ -261,14 +265,21 @@ def mask_runs(attn, W, runs, steps, warmup):
                       W.key_padding_mask(starts, np.full(w.B, w.Skv), w.Skv)),
                      ("random [B,H,1,Skv], density 0.5",
                       W.random_mask(6, (w.B, w.H, 1, w.Skv), 0.5))]
+            biases = []
             kernels = ("decode_bf16_partial", "decode_bf16_combine", "decode_mask_tiles")
         base = None
         tms = [None if m is None else W.mask_to_torch(m) for _, m in masks]
+        tbs = [W.bias_to_torch(bb) for _, bb in biases]
         fns = [(lambda tm=tm: attn.fwd(x["q"], x["k"], x["v"], out, causal=w.causal,
                                        kv_lens=x["kv_lens"], scale=x["scale"], mask=tm))
                for tm in tms]
-        stats = timed_rounds(attn, fns, steps, warmup, kernels)  # the masks interleaved
-        for (label, m), t in zip(masks, stats):
+        fns += [(lambda tb=tb: attn.fwd(x["q"], x["k"], x["v"], out, causal=w.causal,
+                                        kv_lens=x["kv_lens"], scale=x["scale"], bias=tb))
+                for tb in tbs]
+        # the masks and biases interleaved
+        stats = timed_rounds(attn, fns, steps, warmup, kernels)
+        # a bias hides no pair: its rows count as unmasked ones
+        for (label, m), t in zip(masks + [(lb, None) for lb, _ in biases], stats):
             ms, med, mn = op_stats(t, kernels)  # kernels a call did not launch are left out
             base = ms if base is None else base
             row = {"workload": w.name, "mask": label, "ms_per_call": ms, "median_us": med,
@@ -297,7 +308,7 @@ def mask_runs(attn, W, runs, steps, warmup):
                         w.kv_heads * lens.clip(0, w.Skv).sum())
                 row["GB/s"] = nbytes / (ms * 1e-3) / 1e9
             rows.append(row)
-        del tms, fns
+        del tms, tbs, fns
         torch.cuda.empty_cache()
     return rows
 

@@ -42,9 +42,10 @@ def _stub_timing(monkeypatch):
 
 
 def _host_workloads():
-    # mask_to_torch would upload; the bookkeeping only needs the array
+    # mask_to_torch and bias_to_torch would upload; the bookkeeping only needs the array
     names = {k: getattr(W, k) for k in dir(W) if not k.startswith("__")}
     names["mask_to_torch"] = lambda m, device="cuda": m
+    names["bias_to_torch"] = lambda b, device="cuda": b
     return types.SimpleNamespace(**names)
 
 
@@ -63,14 +64,18 @@ def test_mask_rows(monkeypatch):
         w = W.WORKLOADS[name]
         runs.append((kind, w, _inputs(w), None))
     rows = bench.mask_runs(_Attn(), _host_workloads(), runs, steps=1, warmup=0)
-    assert len(rows) == 7 + 3 + 3 and len(calls) == len(rows)
+    assert len(rows) == 9 + 3 + 3 and len(calls) == len(rows)
     for r in rows:
         assert r["ms_per_call"] > 0 and math.isfinite(r["time_vs_unmasked"])
     pre = [r for r in rows if r["workload"] == "prefill4096_bf16"]
     assert pre[0]["mask"] == "none" and pre[0]["visible_pairs_share"] == 1.0
     assert pre[1]["visible_pairs_share"] == 1.0 and pre[2]["visible_pairs_share"] == 1.0
-    for r in pre[3:]:
+    for r in pre[3:7]:
         assert 0.0 < r["visible_pairs_share"] < 1.0 and r["TFLOP/s"] > 0
+    # the two additive biases (finite values) hide no pair
+    assert [r["mask"].split()[0] for r in pre[7:]] == ["bias", "bias"]
+    for r in pre[7:]:
+        assert r["visible_pairs_share"] == 1.0
     # documents of 512 and a window of 256 open about an eighth of the causal pairs
     assert 0.10 < pre[5]["visible_pairs_share"] < 0.15
     assert 0.10 < pre[6]["visible_pairs_share"] < 0.15
