@@ -55,12 +55,14 @@
 // Explicit allowed-mask (the MASK instantiation).  A byte per (query row,
 // key), nonzero = visible, ANDed with the rules above (the boolean allowed-
 // mask of "Attention from Scratch", KubeDojo module 1.4.3, Part 3).  Each
-// lane reads the 32 bytes of its query row that its score registers hold,
-// as eight 4-byte words issued one iteration ahead (under the P V MFMAs);
-// at the start of the next iteration the wave parks them in a per-lane LDS
-// slot, so they hold no registers across the score MFMAs, and decides once
-// whether any of its lanes hides a key of the tile.  Only then are they read
-// back for the per-element pass.  A tile that the mask hides entirely from
+// lane needs the 32 bytes of its query row that its score registers hold.
+// They are loaded one iteration ahead (under the P V MFMAs) -- by the block
+// as coalesced 16-byte chunks of its rows where the rows allow it, else by
+// each lane as eight 4-byte words -- and stored into per-lane LDS slots of
+// the buffer of the tile's parity before the iteration's barrier, so they
+// hold no registers across the score MFMAs.  After the barrier each lane
+// reads its words back, the wave decides once whether any of its lanes
+// hides a key of the tile, and the per-element pass reads them again.  A tile that the mask hides entirely from
 // every live row of a wave is skipped by that wave (its weights would all be
 // exactly zero and its maximum -inf).  For a mask shared by all heads, a
 // small kernel first reads it once (prefill_mask_tiles_kernel) and marks,
@@ -84,8 +86,10 @@
 // that is not positive: each score is rewritten as scale * s + bias before
 // the online softmax, which then tracks the maximum of those logits.  The
 // lane's 32 bias values of a tile (8-byte groups of 4 keys) are loaded two
-// tiles ahead, under the P V MFMAs, and parked in a per-lane LDS slot like
-// the mask words.  Without a bias the kernel reads a zero array instead.
+// tiles ahead, under the P V MFMAs, and parked in per-lane LDS slots like
+// the mask words (coalesced, through two buffers, when there is no mask;
+// with a mask, by each lane into one buffer at the next step's start).
+// Without a bias the kernel reads a zero array instead.
 //
 // Order.  Block ids are mapped heaviest query tile first; within a query
 // tile rank the (b, h) pairs are laid out so that each XCD (ids are dealt
