@@ -54,6 +54,11 @@ CASES = [
     (7, 2, 4, 4, 1, 3000, 128, 0, [3000, 1000], "heads", 0.3),   # decode
     (8, 3, 8, 2, 1, 900, 64, 0, [900, 31, 0], "batch", 0.0),    # decode, GQA
     (9, 1, 32, 1, 1, 4100, 128, 0, [4100], "heads", 0.1),     # decode, MQA
+    # whole 64-key tiles: bias rows read by the block as 16-byte chunks, with
+    # ragged lengths (dead rows in a sequence's first query tile), at block
+    # heights 64 and 256
+    (10, 2, 4, 2, 640, 640, 128, 1, [640, 333], "heads", 0.1),
+    (11, 3, 48, 8, 512, 512, 128, 1, [512, 300, 17], "heads", 0.1),
 ]
 
 
