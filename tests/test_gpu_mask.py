@@ -39,6 +39,9 @@ CASES = [
     (79, "bf16", 1, 32, 1, 1, 2049, 128, 0, None, "b11k", 0.02),
     (80, "f32", 2, 3, 3, 70, 90, 40, 1, [90, 50], "bhqk", 0.6),
     (81, "f32", 1, 4, 2, 1, 150, 128, 0, None, "1h1k", 0.5),
+    # per-head planes (no key-tile lists) on whole 64-key tiles, 256-row
+    # blocks: the mask words read by the block as 16-byte chunks
+    (82, "bf16", 3, 48, 8, 512, 512, 128, 1, [512, 300, 17], "bhqk", 0.6),
 ]
 
 _SHAPES = {"bhqk": "BHQK", "b1qk": "B1QK", "1hqk": "1HQK", "bh1k": "BH1K", "11qk": "11QK",
