@@ -1255,53 +1255,68 @@ template <int BM, bool VEC>  // BM: query rows per query tile (the prefill's blo
 __global__ __launch_bounds__(BM) void prefill_mask_tiles_kernel(
     const uint8_t* __restrict__ mask, long long msb, long long msi, int Sq, int Skv, int nqt,
     int nkt, int causal, uint8_t* __restrict__ tmap) {
-    const int kt = blockIdx.x % nkt;
-    const int qt = (blockIdx.x / nkt) % nqt;
-    const int bm = blockIdx.x / (nkt * nqt);
+    // VEC: a workgroup marks kKT consecutive key tiles, its loads of all of
+    // them in flight together
+    constexpr int kKT = VEC ? 4 : 1;
+    const int nkg = (nkt + kKT - 1) / kKT;
+    const int kt0 = (blockIdx.x % nkg) * kKT;
+    const int qt = (blockIdx.x / nkg) % nqt;
+    const int bm = blockIdx.x / (nkg * nqt);
     const int q0 = qt * BM;
-    __shared__ int flags[2 * (BM / 64)];
-    if (causal) {
-        const int hi = Skv - Sq + min(q0 + BM, Sq);
-        if (kt * kBN >= hi) {
-            if (threadIdx.x == 0) tmap[blockIdx.x] = 0;
-            return;
-        }
+    uint8_t* marks = tmap + ((size_t)bm * nqt + qt) * nkt;
+    __shared__ int flags[kKT][2 * (BM / 64)];
+    // keys any row of the query tile may reach: tiles from hi on are marked 0
+    // unread (the prefill never visits them)
+    const int hi = causal ? Skv - Sq + min(q0 + BM, Sq) : Skv;
+    if (kt0 * kBN >= hi) {  // every tile of the workgroup: nothing to read
+        if ((int)threadIdx.x < kKT && kt0 + (int)threadIdx.x < nkt) marks[kt0 + threadIdx.x] = 0;
+        return;
     }
     const int lane = threadIdx.x & 63;
-    uint32_t any = 0;   // OR of the counted bytes
-    uint32_t hole = 0;  // nonzero if a counted byte is zero
+    uint32_t any[kKT], hole[kKT];  // OR of the counted bytes; nonzero if one is zero
     if constexpr (VEC) {
         const int r0 = q0 + (int)(threadIdx.x >> 6) * 64 + (lane >> 2);
-        const int c = kt * kBN + 16 * (lane & 3);  // first key of this lane's 16
-        const uint8_t* mtile = mask + bm * msb + c;
+        // a tile that is not marked from its bytes reads the last one that is
+        // (or tile 0), which is in bounds
+        const int kmax = max(0, min(nkt - 1, (hi - 1) / kBN));
         // all loads first (rows past Sq read row Sq - 1 and count nothing),
         // so they are in flight together
-        u32x4 w4[4];
+        u32x4 w4[kKT][4];
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
-            w4[it] = ldg16(mtile + (long long)min(r0 + 16 * it, Sq - 1) * msi);
+        for (int j = 0; j < kKT; ++j) {
+            const int c = min(kt0 + j, kmax) * kBN + 16 * (lane & 3);
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int row = r0 + 16 * it;
+            for (int it = 0; it < 4; ++it)
+                w4[j][it] = ldg16(mask + bm * msb + c + (long long)min(r0 + 16 * it, Sq - 1) * msi);
+        }
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                // keys c + 4 g .. + 3, all below Skv; the causal rule may cut them
-                int nb = row < Sq ? 4 : 0;
-                if (causal) nb = min(nb, Skv - Sq + row - (c + 4 * g) + 1);
-                const uint32_t ign = nb >= 4 ? 0u : nb <= 0 ? ~0u : ~0u << (8 * nb);
-                any |= w4[it][g] & ~ign;
-                hole |= has_zero_byte(w4[it][g] | ign);
+        for (int j = 0; j < kKT; ++j) {
+            const int c = (kt0 + j) * kBN + 16 * (lane & 3);  // first key of this lane's 16
+            any[j] = hole[j] = 0;
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int row = r0 + 16 * it;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    // keys c + 4 g .. + 3, below Skv; the causal rule may cut them
+                    int nb = row < Sq ? 4 : 0;
+                    if (causal) nb = min(nb, Skv - Sq + row - (c + 4 * g) + 1);
+                    const uint32_t ign = nb >= 4 ? 0u : nb <= 0 ? ~0u : ~0u << (8 * nb);
+                    any[j] |= w4[j][it][g] & ~ign;
+                    hole[j] |= has_zero_byte(w4[j][it][g] | ign);
+                }
             }
         }
     } else {
         const int r0 = q0 + (int)(threadIdx.x >> 6) * 64 + (lane >> 4);
-        const int c = kt * kBN + 4 * (lane & 15);  // first key of this lane's word
+        const int c = kt0 * kBN + 4 * (lane & 15);  // first key of this lane's word
         const int col = min(c, mask_last_word(Skv));
         const uint8_t* mtile = mask + bm * msb + col;
         uint32_t wd[16];
 #pragma unroll
         for (int it = 0; it < 16; ++it)
             wd[it] = ldg_word(mtile + (long long)min(r0 + 4 * it, Sq - 1) * msi);
+        any[0] = hole[0] = 0;
 #pragma unroll
         for (int it = 0; it < 16; ++it) {
             const int row = r0 + 4 * it;
@@ -1309,24 +1324,28 @@ __global__ __launch_bounds__(BM) void prefill_mask_tiles_kernel(
             int nb = c == col && row < Sq ? Skv - c : 0;
             if (causal) nb = min(nb, Skv - Sq + row - c + 1);
             const uint32_t ign = nb >= 4 ? 0u : nb <= 0 ? ~0u : ~0u << (8 * nb);
-            any |= wd[it] & ~ign;
-            hole |= has_zero_byte(wd[it] | ign);
+            any[0] |= wd[it] & ~ign;
+            hole[0] |= has_zero_byte(wd[it] | ign);
         }
     }
-    const bool wa = __builtin_amdgcn_ballot_w64(any != 0) != 0;
-    const bool wh = __builtin_amdgcn_ballot_w64(hole != 0) != 0;
-    if ((threadIdx.x & 63) == 0) {
-        flags[threadIdx.x >> 6] = wa;
-        flags[BM / 64 + (threadIdx.x >> 6)] = wh;
+#pragma unroll
+    for (int j = 0; j < kKT; ++j) {
+        const bool wa = __builtin_amdgcn_ballot_w64(any[j] != 0) != 0;
+        const bool wh = __builtin_amdgcn_ballot_w64(hole[j] != 0) != 0;
+        if ((threadIdx.x & 63) == 0) {
+            flags[j][threadIdx.x >> 6] = wa;
+            flags[j][BM / 64 + (threadIdx.x >> 6)] = wh;
+        }
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if ((int)threadIdx.x < kKT && kt0 + (int)threadIdx.x < nkt) {
+        const int j = threadIdx.x, kt = kt0 + j;
         int fa = 0, fh = 0;
         for (int w = 0; w < BM / 64; ++w) {
-            fa |= flags[w];
-            fh |= flags[BM / 64 + w];
+            fa |= flags[j][w];
+            fh |= flags[j][BM / 64 + w];
         }
-        tmap[blockIdx.x] = fa ? (fh ? 1 : 2) : 0;
+        marks[kt] = kt * kBN >= hi ? 0 : fa ? (fh ? 1 : 2) : 0;
     }
 }
 
@@ -1487,9 +1506,10 @@ hipError_t launch_prefill_bf16(const LaunchArgs& a) {
     if (tmap && !(a.msi == 0 && nkt <= 64)) {  // short one-row masks are marked in the prefill
         const int Bm = a.msb != 0 ? a.B : 1;
         if (t) t->begin(kPrefillMaskTiles, a.stream);
-        const dim3 mgrid((unsigned)((long)Bm * nqt * nkt));
         const bool vec = a.Skv % kBN == 0 && (reinterpret_cast<uintptr_t>(a.mask) & 15u) == 0 &&
                          (a.msb & 15) == 0 && (a.msi & 15) == 0;
+        // VEC: four key tiles per workgroup
+        const dim3 mgrid((unsigned)((long)Bm * nqt * (vec ? (nkt + 3) / 4 : nkt)));
         auto marks = [&](auto kern, int threads) {
             hipLaunchKernelGGL(kern, mgrid, dim3(threads), 0, a.stream, a.mask, a.msb, a.msi,
                                a.Sq, a.Skv, nqt, nkt, a.causal, tmap);
