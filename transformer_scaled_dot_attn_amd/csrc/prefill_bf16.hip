@@ -62,9 +62,9 @@
 // the buffer of the tile's parity before the iteration's barrier, so they
 // hold no registers across the score MFMAs.  After the barrier each lane
 // reads its words back, the wave decides once whether any of its lanes
-// hides a key of the tile, and the per-element pass reads them again.  A tile that the mask hides entirely from
-// every live row of a wave is skipped by that wave (its weights would all be
-// exactly zero and its maximum -inf).  For a mask shared by all heads, a
+// hides a key of the tile, and the per-element pass reads them again.  A
+// tile that the mask hides entirely from every live row of a wave is skipped
+// by that wave (its weights would all be exactly zero and its maximum -inf).  For a mask shared by all heads, a
 // small kernel first reads it once (prefill_mask_tiles_kernel) and marks,
 // per query tile and key tile, whether any row of the query tile may see a
 // key of the key tile (a mask with one row for all queries and at most 64
@@ -1250,7 +1250,9 @@ __global__ __launch_bounds__(2 * BM * KG, 1) void prefill_bf16_kernel(
 // never visits them).
 // VEC: whole 64-key tiles (Skv a multiple of 64) and 16-byte aligned rows;
 // then each lane reads 16 keys of a row with one load (4 lanes per row of
-// the tile, 16 rows per wave-wide load) instead of one 4-key word.
+// the tile, 16 rows per wave-wide load) instead of one 4-key word, and a
+// workgroup marks four consecutive key tiles, its loads of all four issued
+// before any is tested.
 template <int BM, bool VEC>  // BM: query rows per query tile (the prefill's block)
 __global__ __launch_bounds__(BM) void prefill_mask_tiles_kernel(
     const uint8_t* __restrict__ mask, long long msb, long long msi, int Sq, int Skv, int nqt,
